@@ -1,0 +1,218 @@
+/*
+ * libmoeffn — activation-sparse MoE expert FFN for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every buffer argument is a plain device pointer (memory from
+ * hipMalloc or a PyTorch CUDA/HIP tensor) unless a comment says "host".
+ * Descriptor structs (moe_expert_view, moe_layer, moe_layer_trace) are host
+ * structs whose pointer fields are device pointers.
+ *
+ * What is computed (sources are reviews of the papers, cited by page title and
+ * section):
+ *   FloE review, "MoE 专家前向计算": a SwiGLU expert computes
+ *       a_E(x) = (SiLU(x W^gate) (.) x W^up) W^down.
+ *   FloE review, "混合压缩策略": gate and down are activation-sparsified, up
+ *       is stored in INT2.
+ *   FloE review, "高效稀疏 GEMV 内核" (Algorithm 1 and the optimisations after
+ *       it): v = x W^up, mask = |v| > t, x' = SiLU(x W^gate[mask]) (.) v[mask],
+ *       output = x' W^down_T with W^down transposed so that only the selected
+ *       rows are read, SiLU fused with the product.
+ *   MoE-Infinity review, "A3 背景" and MoE-Lightning review, "MoE 模型架构":
+ *       a router sends each token to its top-k experts.
+ *   MoE-Infinity review, "4.3": per layer, the number of tokens routed to each
+ *       expert (one row of the expert activation matrix).
+ *
+ * Data layout (all row-major, one expert):
+ *   up_q   [f][d/4]   uint8: INT2 codes of W^up, row j = output channel j.
+ *                     A row is d/16 little-endian 32-bit words; word i holds
+ *                     inputs 16i..16i+15, the code of input 16i + 2m + h
+ *                     (m = 0..7, h = 0/1) in bits 16h + 2m (even inputs in the
+ *                     low half-word, odd inputs in the high half-word).
+ *   up_sz  [f][d/64][2] fp16 bits {s, z}: for group g = k/64 of channel j the
+ *                     up weight is w = s * (q - z).
+ *   gate_t [f][d]     row j = column j of W^gate (fp16 or bf16).
+ *   down   [f][d]     row j = row j of W^down, i.e. W^down transposed and stored
+ *                     column-major, so an active channel's row is contiguous.
+ * A layer stores its E routed experts then its S shared experts back to back at
+ * a fixed per-expert stride in each of these four arrays.
+ *
+ * Constraints checked on the host before anything is enqueued:
+ *   d % 512 == 0 or d in {64,128,256};  f % 64 == 0;  T >= 1;
+ *   activations and gate/down weights have the same 16-bit type (fp16 or bf16);
+ *   16-byte aligned up_q/gate_t/down/x and 4-byte aligned up_sz.
+ *
+ * Workspace: every forward call takes a device workspace of at least
+ * moe_workspace_size(...) bytes.  It must be zero-filled before its first use
+ * (moe_workspace_init, or a zero-initialised tensor); each call returns it to
+ * all-zero before its kernels finish.  Calls that share a workspace must be
+ * ordered (same stream); overlapping calls need distinct workspaces.
+ *
+ * Execution: calls are asynchronous on `stream` (a hipStream_t passed as void*,
+ * NULL = the null stream).  Forward calls do no host synchronisation and no
+ * device-to-host copy.  The library allocates nothing and keeps no pointer
+ * after a call returns.
+ *
+ * Errors: invalid arguments return a negative moe_status and enqueue nothing;
+ * a failed kernel launch returns MOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *
+ * Determinism: routing, grouping, masks and v are bit-reproducible.  y is
+ * accumulated across workgroups with fp32 atomics, so its last bits may vary
+ * from run to run.
+ */
+#ifndef MOEFFN_H
+#define MOEFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, k outside [1, E], ... */
+    MOE_ERR_UNSUPPORTED = -2,   /* shape or dtype combination not implemented    */
+    MOE_ERR_ALIGNMENT = -3,     /* a pointer is not aligned as required          */
+    MOE_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required    */
+    MOE_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed    */
+} moe_status;
+
+typedef enum { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
+
+typedef enum {
+    MOE_PATH_SPARSE = 0,        /* Algorithm 1: INT2 up, threshold mask, row gathers */
+    MOE_PATH_DENSE = 1          /* bf16 MFMA grouped GEMM, threshold off            */
+} moe_path;
+
+typedef enum {
+    MOE_OP_EXPERT = 0,          /* moe_expert_forward_sparse */
+    MOE_OP_ROUTE = 1,           /* moe_route_topk           */
+    MOE_OP_LAYER = 2            /* moe_layer_forward        */
+} moe_op;
+
+/* One compressed expert (FloE review, "混合压缩策略": {W^S(gate), W^S(down),
+ * W^Q(up)}; Algorithm 1 inputs E_ij and t_ij). */
+typedef struct {
+    const uint8_t *up_q;        /* [f][d/4]        */
+    const uint16_t *up_sz;      /* [f][d/64][2]    */
+    const void *gate_t;         /* [f][d] wdt      */
+    const void *down;           /* [f][d] wdt      */
+    float threshold;            /* channel j is active iff |v_j| > threshold (fp32);
+                                   t < 0 keeps all channels, +inf keeps none */
+} moe_expert_view;
+
+/* One MoE layer: E routed experts (top-k) followed by S shared experts (always
+ * applied with weight 1), all in the compressed format at a fixed stride. */
+typedef struct {
+    int d, f;                   /* hidden size, intermediate size          */
+    int n_routed, n_shared;     /* E, S                                     */
+    int top_k;                  /* k, 1 <= k <= E                           */
+    int renormalize;            /* 1: softmax over the k chosen logits;
+                                   0: full softmax taken at the chosen ones */
+    moe_dtype wdt;              /* gate/down (and activation) type          */
+    const void *router_w;       /* [E][d] in rdt                            */
+    moe_dtype rdt;
+    const float *router_bias;   /* [E] or NULL                              */
+    const uint8_t *up_q;        /* [E+S][f][d/4]                            */
+    const uint16_t *up_sz;      /* [E+S][f][d/64][2]                        */
+    const void *gate_t;         /* [E+S][f][d]                              */
+    const void *down;           /* [E+S][f][d]                              */
+    const float *thresholds;    /* [E+S] fp32, device                       */
+    const uint16_t *up_dense;   /* [E+S][f][d] bf16 up weights for MOE_PATH_DENSE
+                                   (moe_materialize_up_bf16), else NULL     */
+} moe_layer;
+
+/* Optional device outputs of moe_layer_forward (any field may be NULL). */
+typedef struct {
+    int32_t *topk_idx;          /* [T][k]                                   */
+    float *topk_w;              /* [T][k]                                   */
+    float *logits;              /* [T][E]                                   */
+    int32_t *expert_count;      /* [E] tokens per routed expert             */
+    uint8_t *masks;             /* [T][k+S][f] 0/1, sparse path only: slot s<k is
+                                   the token's s-th routed expert, slot k+i its
+                                   i-th shared expert                        */
+} moe_layer_trace;
+
+/*
+ * Router: logits = x R^T (+ bias), top-k experts per token with ties going to
+ * the lower expert index, weights = softmax over the k chosen logits
+ * (renormalize=1) or the full softmax at the chosen experts (renormalize=0);
+ * then the T*k (token, slot) pairs grouped by expert
+ * (MoE-Infinity review, "A3 背景" and "4.3"; MoE-Lightning review, "MoE 模型架构").
+ *   x [T][d] in xdt (f16/bf16/f32), router_w [E][d] in rdt, router_bias [E] or NULL.
+ * Outputs:
+ *   topk_idx [T][k] int32, topk_w [T][k] fp32,
+ *   expert_count [E] int32, expert_offset [E+1] int32 (exclusive prefix),
+ *   pair_by_expert [T*k] int32: pairs p = t*k + s of expert e, ascending, at
+ *   expert_offset[e] ..; logits_out [T][E] fp32 or NULL.
+ * Limits: 1 <= k <= E <= 1024, T*k <= 65536.
+ */
+moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d,
+                          const void *router_w, moe_dtype rdt, const float *router_bias,
+                          int E, int k, int renormalize,
+                          int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_count, int32_t *expert_offset,
+                          int32_t *pair_by_expert, float *logits_out,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One compressed expert on T tokens (FloE review, Algorithm 1):
+ *   v = x W^up (INT2, fp32 accumulation), mask = |v| > threshold,
+ *   h = SiLU(x gate_t[mask]^T) * v[mask], y_t = token_scale_t * h W^down[mask].
+ *   x [T][d] in xdt (must equal wdt), y [T][d] in ydt (f16/bf16/f32);
+ *   token_scale [T] fp32 or NULL (= 1); accumulate != 0 adds into y.
+ * Optional exports: mask_out [T][f] uint8 0/1, v_out [T][f] fp32.
+ */
+moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe_dtype wdt,
+                                     const void *x, moe_dtype xdt, int T,
+                                     const float *token_scale, int accumulate,
+                                     void *y, moe_dtype ydt,
+                                     uint8_t *mask_out, float *v_out,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One MoE layer: route (as moe_route_topk) and combine
+ *   y_t = sum_s w_{t,s} a_{e(t,s)}(x_t) + sum_i a_{E+i}(x_t)
+ * where a_e is Algorithm 1 (MOE_PATH_SPARSE) or the dense SwiGLU with the bf16
+ * up weights in L->up_dense (MOE_PATH_DENSE, which needs wdt == MOE_BF16).
+ *   x [T][d] in xdt (== L->wdt), y [T][d] in ydt (overwritten).
+ * trace (host struct, NULL allowed) receives the optional exports.
+ */
+moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, int T,
+                             void *y, moe_dtype ydt, moe_path path,
+                             const moe_layer_trace *trace,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by `op` at these sizes (0 when the sizes are invalid). */
+size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S);
+
+/* Zero-fill a workspace with a kernel (safe inside stream capture). */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Quantise up weights to the INT2 format above (FloE review, "混合压缩策略").
+ *   w_up_t [f][d] in dt (f32/f16/bf16), row j = column j of W^up.
+ *   Per channel j and group of 64 inputs, in fp32: mn, mx = min, max;
+ *   s = fp16_rne((mx - mn) / 3) (1 if that is 0); z = fp16_rne(-mn / s);
+ *   q = clamp(round_half_even(w / s + z), 0, 3).
+ * Outputs up_q [f][d/4], up_sz [f][d/64][2].  d % 64 == 0, f >= 1.
+ * Inputs are expected finite with |w| small enough that (mx - mn) / 3 fits fp16.
+ */
+moe_status moe_pack_up_int2(const void *w_up_t, moe_dtype dt, int d, int f,
+                            uint8_t *up_q, uint16_t *up_sz, void *stream);
+
+/*
+ * Dense-path up weights: out[j][k] = bf16_rne(s * (q - z)) evaluated exactly,
+ * from the INT2 format (one-off preparation for MOE_PATH_DENSE).
+ */
+moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
+                                   uint16_t *out, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEFFN_H */

@@ -39,8 +39,10 @@
  *   R4  One scalar threshold per (layer, expert); strict comparison |v| > t.
  *       t < 0 keeps every channel (dense expert), t = +inf keeps none.
  *   R5  INT2 up: groups of 64 consecutive inputs k per output channel j,
- *       asymmetric, w = s * (q - z) with fp16 s and fp16 (fractional) z.  Code
- *       of input k of channel j sits in bits 2*(k%4) of byte k/4 of row j.
+ *       asymmetric, w = s * (q - z) with fp16 s and fp16 (fractional) z.  Row j
+ *       is d/16 little-endian 32-bit words; word i holds the 16 codes of inputs
+ *       16i..16i+15, the code of input 16i + 2m + h (m in 0..7, h in {0,1}) in
+ *       bits 16h + 2m: even inputs in the low half-word, odd ones in the high.
  *   R6  The dequantised INT2 up weights feed both the mask and the product.
  *   R7  Router: logits = x R^T (+ bias); top-k by (-logit, index) so ties go to
  *       the lowest index; weights are the softmax over the k chosen logits when
@@ -155,6 +157,20 @@ uint16_t oracle_double_to_bf16_rne(double v)
 
 /* ------------------------------------------------------ C0: INT2 up format */
 
+/* Bit position of input k's code inside row j (reading R5): word k/16,
+ * half-word k%2, pair slot (k%16)/2.  Words are little-endian. */
+static size_t code_bit(size_t k)
+{
+    return 32 * (k / 16) + 16 * (k % 2) + 2 * ((k % 16) / 2);
+}
+
+static void put_code(uint8_t *up_q, int d, int j, size_t k, int q)
+{
+    size_t b = code_bit(k);
+    uint8_t *byte = up_q + (size_t)j * (d / 4) + b / 8;
+    *byte = (uint8_t)((*byte & ~(3u << (b % 8))) | ((unsigned)q << (b % 8)));
+}
+
 /*
  * Quantiser for the INT2 up projection ([FloE-comp], reading R5).  Input is
  * the fp32 up weights stored channel-major, w_t[j][k] = W^up[k][j], f x d.
@@ -163,7 +179,7 @@ uint16_t oracle_double_to_bf16_rne(double v)
  *   s = fp16((mx - mn) / 3), replaced by 1 when it rounds to 0
  *   z = fp16(-mn / s)
  *   q = clamp(round_half_even(w / s + z), 0, 3)
- * Outputs: up_q [f][d/4] (4 codes per byte, code of k in bits 2*(k%4)),
+ * Outputs: up_q [f][d/4] bytes holding the codes in the word order of R5,
  *          up_sz [f][d/64][2] fp16 bits {s, z}.
  * The float32 steps are written out one operation at a time; the compiler is
  * told not to contract or reassociate (built with -ffp-contract=off).
@@ -198,9 +214,7 @@ void oracle_pack_up_int2(const float *w_t, int d, int f, uint8_t *up_q, uint16_t
                 if (r < 0.0f) q = 0;
                 if (r > 3.0f) q = 3;
                 size_t k = (size_t)g * 64 + i;
-                uint8_t *byte = up_q + (size_t)j * (d / 4) + k / 4;
-                if (k % 4 == 0) *byte = 0;
-                *byte |= (uint8_t)(q << (2 * (k % 4)));
+                put_code(up_q, d, j, k, q);
             }
         }
     }
@@ -209,7 +223,8 @@ void oracle_pack_up_int2(const float *w_t, int d, int f, uint8_t *up_q, uint16_t
 /* The INT2 code of input k of channel j. */
 static int code_at(const uint8_t *up_q, int d, int j, int k)
 {
-    return (up_q[(size_t)j * (d / 4) + k / 4] >> (2 * (k % 4))) & 3;
+    size_t b = code_bit((size_t)k);
+    return (up_q[(size_t)j * (d / 4) + b / 8] >> (b % 8)) & 3;
 }
 
 /* Dequantised up weight w'_{k,j} = s_{g,j} * (q_{k,j} - z_{g,j}) (exact in double). */

@@ -25,6 +25,15 @@ def bits16(a_f16):
     return np.ascontiguousarray(a_f16).view(np.uint16)
 
 
+def unpack_codes(up_q, d):
+    """Codes [f][d] from the INT2 rows: little-endian 32-bit words of 16 codes,
+    input 16i + 2m + h in bits 16h + 2m of word i."""
+    w = np.ascontiguousarray(up_q).view("<u4").astype(np.int64)     # [f][d/16]
+    k = np.arange(d)
+    shift = 16 * (k % 2) + 2 * ((k % 16) // 2)
+    return (w[:, k // 16] >> shift) & 3
+
+
 def exact_int2_expert(rng, d, f, s_pow=-7):
     """Up weights that INT2 represents exactly: per (channel, group) pick
     codes with 0 and 3 both present, s = 2^s_pow, z in {0.5,1,1.5,2}, and
@@ -109,9 +118,7 @@ def test_pack_exact_weights_round_trip():
     # scales and zeros are exactly the ones used to build the weights
     assert np.all(up_sz[..., 0] == bits16(f16(np.full((f, d // 64), s))))
     assert np.all(up_sz[..., 1] == bits16(f16(z)))
-    # codes are stored 4 per byte, code of input k in bits 2*(k%4)
-    unpacked = np.stack([(up_q >> (2 * i)) & 3 for i in range(4)], axis=-1).reshape(f, d)
-    assert np.array_equal(unpacked, q)
+    assert np.array_equal(unpack_codes(up_q, d), q)
     # dequantisation gives the original weights back exactly
     assert np.array_equal(oracle.dequant_up(up_q, up_sz, d), w.astype(np.float64))
 
@@ -122,9 +129,12 @@ def test_pack_code_layout_single_code():
         w = np.zeros((1, d), dtype=np.float32)
         w[0, k] = 3.0          # group min 0, max 3 -> s = 1, z = 0
         up_q, up_sz = oracle.pack_up_int2(w)
+        # input 16i + 2m + h -> bits 16h + 2m of little-endian word i
+        i, m, h = k // 16, (k % 16) // 2, k % 2
+        bit = 32 * i + 16 * h + 2 * m
         expect = np.zeros(d // 4, dtype=np.uint8)
-        expect[k // 4] = 3 << (2 * (k % 4))
-        assert np.array_equal(up_q[0], expect)
+        expect[bit // 8] = 3 << (bit % 8)
+        assert np.array_equal(up_q[0], expect), k
         # -mn = -0.0 for a group whose minimum is +0, so z is the fp16 -0
         assert up_sz[0, 0, 0] == 0x3C00 and up_sz[0, 0, 1] in (0, 0x8000)
 
@@ -137,7 +147,7 @@ def test_pack_error_bound_and_extremes():
     err = np.abs(deq - w.astype(np.float64))
     # half a step plus the fp16 rounding of s and z (each < 2^-11 relative)
     assert np.all(err <= 0.5 * s + 4 * s * 2.0 ** -11 + 1e-12)
-    codes = np.stack([(up_q >> (2 * i)) & 3 for i in range(4)], axis=-1).reshape(64, 512)
+    codes = unpack_codes(up_q, 512)
     g = w.reshape(64, 8, 64)
     cg = codes.reshape(64, 8, 64)
     amin = g.argmin(-1)
