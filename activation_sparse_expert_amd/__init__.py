@@ -1,0 +1,267 @@
+"""Python binding of libmoeffn (activation-sparse MoE expert FFN, MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmoeffn.so``.  PyTorch provides device memory and the current
+stream.  If the shared library has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoeffn.so")
+
+MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
+PATH_SPARSE, PATH_DENSE = 0, 1
+OP_EXPERT, OP_ROUTE, OP_LAYER = 0, 1, 2
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
+
+EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
+            "moe_workspace_size", "moe_workspace_init", "moe_pack_up_int2",
+            "moe_materialize_up_bf16", "moe_status_string"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class ExpertView(C.Structure):
+    _fields_ = [("up_q", C.c_void_p), ("up_sz", C.c_void_p), ("gate_t", C.c_void_p),
+                ("down", C.c_void_p), ("threshold", C.c_float)]
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("d", C.c_int), ("f", C.c_int), ("n_routed", C.c_int), ("n_shared", C.c_int),
+                ("top_k", C.c_int), ("renormalize", C.c_int), ("wdt", C.c_int),
+                ("router_w", C.c_void_p), ("rdt", C.c_int), ("router_bias", C.c_void_p),
+                ("up_q", C.c_void_p), ("up_sz", C.c_void_p), ("gate_t", C.c_void_p),
+                ("down", C.c_void_p), ("thresholds", C.c_void_p), ("up_dense", C.c_void_p)]
+
+
+class LayerTrace(C.Structure):
+    _fields_ = [("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("logits", C.c_void_p),
+                ("expert_count", C.c_void_p), ("masks", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoeffn (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmoeffn.so not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        P, I, Z = C.c_void_p, C.c_int, C.c_size_t
+        L.moe_route_topk.restype = I
+        L.moe_route_topk.argtypes = [P, I, I, I, P, I, P, I, I, I, P, P, P, P, P, P, P, Z, P]
+        L.moe_expert_forward_sparse.restype = I
+        L.moe_expert_forward_sparse.argtypes = [C.POINTER(ExpertView), I, I, I, P, I, I, P, I,
+                                                P, I, P, P, P, Z, P]
+        L.moe_layer_forward.restype = I
+        L.moe_layer_forward.argtypes = [C.POINTER(LayerDesc), P, I, I, P, I, I,
+                                        C.POINTER(LayerTrace), P, Z, P]
+        L.moe_workspace_size.restype = Z
+        L.moe_workspace_size.argtypes = [I, I, I, I, I, I, I]
+        L.moe_workspace_init.restype = I
+        L.moe_workspace_init.argtypes = [P, Z, P]
+        L.moe_pack_up_int2.restype = I
+        L.moe_pack_up_int2.argtypes = [P, I, I, I, P, P, P]
+        L.moe_materialize_up_bf16.restype = I
+        L.moe_materialize_up_bf16.argtypes = [P, P, I, I, P, P]
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_status_string.argtypes = [I]
+        _lib = L
+    return _lib
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise MoeError(st, what)
+
+
+def _dt(t) -> int:
+    import torch
+    m = {torch.float16: MOE_F16, torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoeffn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def workspace_size(op: int, T: int, d: int, f: int = 0, E: int = 1, k: int = 1, S: int = 0) -> int:
+    return int(lib().moe_workspace_size(op, T, d, f, E, k, S))
+
+
+def new_workspace(nbytes: int, device="cuda"):
+    """A zero-filled workspace tensor (uint8) of at least ``nbytes``."""
+    import torch
+    return torch.zeros(max(256, (nbytes + 255) // 256 * 256), dtype=torch.uint8, device=device)
+
+
+def workspace_init(ws) -> None:
+    _check(lib().moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "moe_workspace_init")
+
+
+@dataclass
+class Expert:
+    """One compressed expert on the device (layouts as in include/moeffn.h)."""
+    up_q: "torch.Tensor"        # [f][d/4] uint8
+    up_sz: "torch.Tensor"       # [f][d/64][2] int16/uint16 (fp16 bits)
+    gate_t: "torch.Tensor"      # [f][d] fp16/bf16
+    down: "torch.Tensor"        # [f][d] fp16/bf16
+    threshold: float
+
+    @property
+    def d(self):
+        return self.gate_t.shape[1]
+
+    @property
+    def f(self):
+        return self.gate_t.shape[0]
+
+    def view(self) -> ExpertView:
+        return ExpertView(_ptr(self.up_q), _ptr(self.up_sz), _ptr(self.gate_t), _ptr(self.down),
+                          float(self.threshold))
+
+
+def expert_forward_sparse(expert: Expert, x, *, y=None, out_dtype=None, token_scale=None,
+                          accumulate: bool = False, mask_out=None, v_out=None, ws=None):
+    """Algorithm 1 of the FloE review on x [T][d]; returns y [T][d]."""
+    import torch
+    T, d = x.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=out_dtype or torch.float32, device=x.device)
+    if ws is None:
+        ws = new_workspace(workspace_size(OP_EXPERT, T, d, expert.f), x.device)
+    v = expert.view()
+    st = lib().moe_expert_forward_sparse(
+        C.byref(v), d, expert.f, _dt(expert.gate_t), _ptr(x), _dt(x), T, _ptr(token_scale),
+        int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_out), _ptr(v_out), _ptr(ws),
+        ws.numel(), _stream())
+    _check(st, "moe_expert_forward_sparse")
+    return y
+
+
+def route_topk(x, router_w, k: int, *, renormalize: bool = True, bias=None, logits=False, ws=None):
+    """Top-k routing and grouping; returns a dict of device tensors."""
+    import torch
+    T, d = x.shape
+    E = router_w.shape[0]
+    dev = x.device
+    out = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               expert_count=torch.empty(E, dtype=torch.int32, device=dev),
+               expert_offset=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               pair_by_expert=torch.empty(T * k, dtype=torch.int32, device=dev))
+    if logits:
+        out["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = new_workspace(workspace_size(OP_ROUTE, T, d, 0, E, k), dev)
+    st = lib().moe_route_topk(_ptr(x), _dt(x), T, d, _ptr(router_w), _dt(router_w), _ptr(bias), E,
+                              k, int(bool(renormalize)), _ptr(out["topk_idx"]), _ptr(out["topk_w"]),
+                              _ptr(out["expert_count"]), _ptr(out["expert_offset"]),
+                              _ptr(out["pair_by_expert"]), _ptr(out.get("logits")), _ptr(ws),
+                              ws.numel(), _stream())
+    _check(st, "moe_route_topk")
+    return out
+
+
+@dataclass
+class Layer:
+    """One MoE layer: E routed + S shared experts at a fixed stride."""
+    d: int
+    f: int
+    E: int
+    S: int
+    k: int
+    renormalize: bool
+    router_w: "torch.Tensor"      # [E][d]
+    up_q: "torch.Tensor"          # [E+S][f][d/4]
+    up_sz: "torch.Tensor"         # [E+S][f][d/64][2]
+    gate_t: "torch.Tensor"        # [E+S][f][d]
+    down: "torch.Tensor"          # [E+S][f][d]
+    thresholds: "torch.Tensor"    # [E+S] fp32
+    router_bias: Optional["torch.Tensor"] = None
+    up_dense: Optional["torch.Tensor"] = None   # [E+S][f][d] bf16
+
+    def desc(self) -> LayerDesc:
+        return LayerDesc(self.d, self.f, self.E, self.S, self.k, int(bool(self.renormalize)),
+                         _dt(self.gate_t), _ptr(self.router_w), _dt(self.router_w),
+                         _ptr(self.router_bias), _ptr(self.up_q), _ptr(self.up_sz),
+                         _ptr(self.gate_t), _ptr(self.down), _ptr(self.thresholds),
+                         _ptr(self.up_dense))
+
+    def workspace_bytes(self, T: int) -> int:
+        return workspace_size(OP_LAYER, T, self.d, self.f, self.E, self.k, self.S)
+
+
+def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype=None,
+                  trace: Optional[dict] = None, ws=None):
+    """Route and combine one layer on x [T][d]; returns y [T][d].
+
+    ``trace`` may map any of topk_idx, topk_w, logits, expert_count, masks to
+    preallocated device tensors that receive those exports."""
+    import torch
+    T, d = x.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=out_dtype or torch.float32, device=x.device)
+    if ws is None:
+        ws = new_workspace(layer.workspace_bytes(T), x.device)
+    tr = None
+    if trace:
+        tr = LayerTrace(_ptr(trace.get("topk_idx")), _ptr(trace.get("topk_w")),
+                        _ptr(trace.get("logits")), _ptr(trace.get("expert_count")),
+                        _ptr(trace.get("masks")))
+    desc = layer.desc()
+    st = lib().moe_layer_forward(C.byref(desc), _ptr(x), _dt(x), T, _ptr(y), _dt(y), path,
+                                 C.byref(tr) if tr is not None else None, _ptr(ws), ws.numel(),
+                                 _stream())
+    _check(st, "moe_layer_forward")
+    return y
+
+
+def pack_up_int2(w_up_t, *, up_q=None, up_sz=None):
+    """INT2 group-64 quantisation of up weights [f][d] on the device."""
+    import torch
+    f, d = w_up_t.shape
+    if up_q is None:
+        up_q = torch.empty((f, d // 4), dtype=torch.uint8, device=w_up_t.device)
+    if up_sz is None:
+        up_sz = torch.empty((f, d // 64, 2), dtype=torch.int16, device=w_up_t.device)
+    st = lib().moe_pack_up_int2(_ptr(w_up_t), _dt(w_up_t), d, f, _ptr(up_q), _ptr(up_sz),
+                                _stream())
+    _check(st, "moe_pack_up_int2")
+    return up_q, up_sz
+
+
+def materialize_up_bf16(up_q, up_sz, d: int, *, out=None):
+    """bf16 up weights [f][d] = bf16_rne(s (q - z)) for the dense path."""
+    import torch
+    f = up_q.shape[0]
+    if out is None:
+        out = torch.empty((f, d), dtype=torch.bfloat16, device=up_q.device)
+    st = lib().moe_materialize_up_bf16(_ptr(up_q), _ptr(up_sz), d, f, _ptr(out), _stream())
+    _check(st, "moe_materialize_up_bf16")
+    return out

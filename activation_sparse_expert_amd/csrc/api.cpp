@@ -1,0 +1,389 @@
+// C ABI of libmoeffn: argument validation, workspace layout and dispatch.
+// Every check runs on the host before anything is enqueued; no HIP call is made
+// for an invalid request, so the error paths can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/moeffn.h"
+#include "internal.hpp"
+
+using namespace moeffn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool is16(moe_dtype t) { return t == MOE_F16 || t == MOE_BF16; }
+
+bool valid_out(moe_dtype t) { return t == MOE_F16 || t == MOE_BF16 || t == MOE_F32; }
+
+// Hidden sizes the kernels are built for: powers of two up to 2048, or
+// multiples of 512 from 4096 to 16384.
+bool supported_d(int d)
+{
+    if (d == 64 || d == 128 || d == 256 || d == 512 || d == 1024 || d == 2048) return true;
+    return d >= 4096 && d <= 16384 && d % 512 == 0;
+}
+
+int pow2ceil(int v)
+{
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// Work split of the sparse kernel: about 256 workgroups over all expert slots
+// (one per compute unit), channels per tile a multiple of 8 and at most 1024,
+// and the fp32 partial rows (rows x tiles x d) kept under 256 MiB.
+struct TilePlan {
+    int cpw, tiles;
+};
+
+TilePlan plan_tiles(int f, int slots, long long rows, int d)
+{
+    const int fr = (f + 7) / 8 * 8;
+    int tiles = (256 + slots - 1) / slots;
+    int cpw = (f + tiles - 1) / tiles;
+    cpw = (cpw + 7) / 8 * 8;
+    if (cpw < 8) cpw = 8;
+    if (cpw > 1024) cpw = 1024;
+    const long long cap = 256ll << 20;
+    for (;;) {
+        tiles = (f + cpw - 1) / cpw;
+        if (rows * tiles * d * 4 <= cap || cpw >= fr || cpw >= 1024) break;
+        cpw = cpw * 2 > 1024 ? 1024 : cpw * 2;
+    }
+    if (cpw > fr) cpw = fr;
+    tiles = (f + cpw - 1) / cpw;
+    return {cpw, tiles};
+}
+
+// LDS bytes of the sparse kernel (mirrors its layout, rounded up).
+size_t sparse_lds(int d, int cpw, int tb)
+{
+    const int G = d / 64;
+    auto a16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
+    return a16((size_t)tb * G * 72 * 2) + a16((size_t)tb * G * 4) + a16((size_t)tb * cpw * 4) +
+           a16((size_t)tb * cpw) + a16((size_t)cpw * 2) + a16((size_t)8 * 8 * tb * 4) +
+           4 * a16((size_t)tb * 4) + 16;
+}
+
+int choose_tb(int T, int d, int cpw)
+{
+    int tb = pow2ceil(T);
+    const int tbmax = d <= 4096 ? 8 : 4;
+    if (tb > tbmax) tb = tbmax;
+    while (tb > 1 && sparse_lds(d, cpw, tb) > 150 * 1024) tb /= 2;
+    return tb;
+}
+
+int layer_slots(int T, int E, int k, int S)
+{
+    const long long tk = (long long)T * k;
+    return S + (int)(E < tk ? E : tk);
+}
+
+size_t expert_ws_bytes(int T, int d, int f)
+{
+    const TilePlan tp = plan_tiles(f, 1, T, d);
+    return up((size_t)T * tp.tiles * d * 4);
+}
+
+struct LayerWs {
+    uint32_t *route_done;
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *count, *offset, *pairs, *pair_pos, *active, *n_active;
+    float *part;
+    float *h;
+};
+
+size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, void *base)
+{
+    const long long rows = (long long)T * (k + S);
+    const TilePlan tp = plan_tiles(f, layer_slots(T, E, k, S), rows, d);
+    const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
+    size_t o = 0;
+    size_t off[11];
+    off[0] = o; o += up(4);
+    off[1] = o; o += up((size_t)T * k * 4);
+    off[2] = o; o += up((size_t)T * k * 4);
+    off[3] = o; o += up((size_t)E * 4);
+    off[4] = o; o += up((size_t)(E + 1) * 4);
+    off[5] = o; o += up((size_t)T * k * 4);
+    off[6] = o; o += up((size_t)T * k * 4);
+    off[7] = o; o += up((size_t)E * 4);
+    off[8] = o; o += up(4);
+    off[9] = o; o += up((size_t)rows * part_tiles * d * 4);
+    off[10] = o; o += up(dense_h_bytes(T, f, k, S));
+    if (out) {
+        char *p = (char *)base;
+        out->route_done = (uint32_t *)(p + off[0]);
+        out->topk_idx = (int32_t *)(p + off[1]);
+        out->topk_w = (float *)(p + off[2]);
+        out->count = (int32_t *)(p + off[3]);
+        out->offset = (int32_t *)(p + off[4]);
+        out->pairs = (int32_t *)(p + off[5]);
+        out->pair_pos = (int32_t *)(p + off[6]);
+        out->active = (int32_t *)(p + off[7]);
+        out->n_active = (int32_t *)(p + off[8]);
+        out->part = (float *)(p + off[9]);
+        out->h = (float *)(p + off[10]);
+    }
+    return o;
+}
+
+hipError_t launch_sparse(const SparseArgs &a, bool bf16, int tb, hipStream_t s)
+{
+    return bf16 ? launch_sparse_expert_bf16(a, tb, s) : launch_sparse_expert_f16(a, tb, s);
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_route_args(const void *x, moe_dtype xdt, int T, int d, const void *rw,
+                            moe_dtype rdt, int E, int k)
+{
+    if (!x || !rw) return MOE_ERR_INVALID_ARG;
+    if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if ((long long)T * k > 65536) return MOE_ERR_UNSUPPORTED;
+    if (!valid_out(xdt) || !valid_out(rdt)) return MOE_ERR_UNSUPPORTED;
+    if ((size_t)d * 4 + (size_t)E * 4 + (size_t)k * 4 + 16 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(x, xdt == MOE_F32 ? 4 : 2) || !aligned(rw, rdt == MOE_F32 ? 4 : 2))
+        return MOE_ERR_ALIGNMENT;
+    return MOE_OK;
+}
+
+moe_status check_expert_shape(int d, int f, moe_dtype wdt, moe_dtype xdt, int T, moe_dtype ydt)
+{
+    if (T < 1 || T > 65536 || d < 1 || f < 1) return MOE_ERR_INVALID_ARG;
+    if (f % 64 != 0) return MOE_ERR_INVALID_ARG;
+    if (!supported_d(d)) return MOE_ERR_UNSUPPORTED;
+    if (!is16(wdt) || xdt != wdt || !valid_out(ydt)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_weight_ptrs(const uint8_t *q, const uint16_t *sz, const void *g, const void *dn)
+{
+    if (!q || !sz || !g || !dn) return MOE_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(g, 16) || !aligned(dn, 16) || !aligned(sz, 4))
+        return MOE_ERR_ALIGNMENT;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S)
+{
+    if (T < 1 || d < 1) return 0;
+    switch (op) {
+    case MOE_OP_EXPERT: return f < 1 ? 0 : expert_ws_bytes(T, d, f);
+    case MOE_OP_ROUTE: return up(4);
+    case MOE_OP_LAYER:
+        if (E < 1 || k < 1 || k > E || S < 0 || f < 1) return 0;
+        return layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr);
+    }
+    return 0;
+}
+
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ws || ws_bytes == 0) return MOE_ERR_INVALID_ARG;
+    if (!aligned(ws, 4) || ws_bytes % 4 != 0) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void *router_w,
+                          moe_dtype rdt, const float *router_bias, int E, int k, int renormalize,
+                          int32_t *topk_idx, float *topk_w, int32_t *expert_count,
+                          int32_t *expert_offset, int32_t *pair_by_expert, float *logits_out,
+                          void *ws, size_t ws_bytes, void *stream)
+{
+    moe_status st = check_route_args(x, xdt, T, d, router_w, rdt, E, k);
+    if (st != MOE_OK) return st;
+    if (!topk_idx || !topk_w || !expert_count || !expert_offset || !pair_by_expert)
+        return MOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < moe_workspace_size(MOE_OP_ROUTE, T, d, 0, E, k, 0))
+        return MOE_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
+    RouteArgs a{};
+    a.x = x; a.xdt = xdt; a.T = T; a.d = d;
+    a.rw = router_w; a.rdt = rdt; a.bias = router_bias;
+    a.E = E; a.k = k; a.renorm = renormalize ? 1 : 0;
+    a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits = logits_out;
+    a.count = expert_count; a.offset = expert_offset; a.pairs = pair_by_expert;
+    a.pair_pos = nullptr; a.active = nullptr; a.n_active = nullptr;
+    a.done = (uint32_t *)ws;
+    return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe_dtype wdt,
+                                     const void *x, moe_dtype xdt, int T,
+                                     const float *token_scale, int accumulate, void *y,
+                                     moe_dtype ydt, uint8_t *mask_out, float *v_out, void *ws,
+                                     size_t ws_bytes, void *stream)
+{
+    if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
+    if (st != MOE_OK) return st;
+    st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
+    if (st != MOE_OK) return st;
+    if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||
+        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)))
+        return MOE_ERR_ALIGNMENT;
+    if (!ws || ws_bytes < expert_ws_bytes(T, d, f)) return MOE_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
+
+    hipStream_t s = (hipStream_t)stream;
+    const TilePlan tp = plan_tiles(f, 1, T, d);
+    SparseArgs a{};
+    a.d = d; a.f = f;
+    a.slots = 1;
+    a.cpw = tp.cpw;
+    a.tiles = tp.tiles;
+    a.up_q = e->up_q; a.up_sz = e->up_sz;
+    a.gate = (const uint16_t *)e->gate_t; a.down = (const uint16_t *)e->down;
+    a.q_stride = 0; a.sz_stride = 0; a.w_stride = 0;
+    a.thr_dev = nullptr; a.thr = e->threshold;
+    a.x = (const uint16_t *)x; a.T = T;
+    a.token_scale = token_scale;
+    a.layer = 0;
+    a.part = (float *)ws;
+    a.mask_out = mask_out; a.v_out = v_out;
+    hipError_t he = launch_sparse(a, wdt == MOE_BF16, choose_tb(T, d, tp.cpw), s);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+    ReduceArgs r{};
+    r.part = (const float *)ws; r.tiles = tp.tiles; r.d = d; r.T = T;
+    r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0; r.pair_pos = nullptr;
+    r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
+    return hip_status(launch_reduce(r, s));
+}
+
+moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, int T, void *y,
+                             moe_dtype ydt, moe_path path, const moe_layer_trace *trace, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    if (!L || !x || !y) return MOE_ERR_INVALID_ARG;
+    const int d = L->d, f = L->f, E = L->n_routed, S = L->n_shared, k = L->top_k;
+    if (S < 0) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_route_args(x, xdt, T, d, L->router_w, L->rdt, E, k);
+    if (st != MOE_OK) return st;
+    st = check_expert_shape(d, f, L->wdt, xdt, T, ydt);
+    if (st != MOE_OK) return st;
+    st = check_weight_ptrs(L->up_q, L->up_sz, L->gate_t, L->down);
+    if (st != MOE_OK) return st;
+    if (!L->thresholds) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) || !aligned(L->thresholds, 4))
+        return MOE_ERR_ALIGNMENT;
+    if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE) return MOE_ERR_INVALID_ARG;
+    if (path == MOE_PATH_DENSE) {
+        if (L->wdt != MOE_BF16 || !L->up_dense) return MOE_ERR_UNSUPPORTED;
+        if (!aligned(L->up_dense, 16)) return MOE_ERR_ALIGNMENT;
+        if (trace && trace->masks) return MOE_ERR_UNSUPPORTED;
+        if (f % 256 != 0 || d % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    }
+    if (!ws || ws_bytes < layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr))
+        return MOE_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
+
+    hipStream_t s = (hipStream_t)stream;
+    LayerWs w;
+    layer_ws_bytes(T, d, f, E, k, S, &w, ws);
+
+    RouteArgs r{};
+    r.x = x; r.xdt = xdt; r.T = T; r.d = d;
+    r.rw = L->router_w; r.rdt = L->rdt; r.bias = L->router_bias;
+    r.E = E; r.k = k; r.renorm = L->renormalize ? 1 : 0;
+    r.topk_idx = (trace && trace->topk_idx) ? trace->topk_idx : w.topk_idx;
+    r.topk_w = (trace && trace->topk_w) ? trace->topk_w : w.topk_w;
+    r.logits = trace ? trace->logits : nullptr;
+    r.count = (trace && trace->expert_count) ? trace->expert_count : w.count;
+    r.offset = w.offset; r.pairs = w.pairs; r.pair_pos = w.pair_pos;
+    r.active = w.active; r.n_active = w.n_active;
+    r.done = w.route_done;
+    hipError_t he = launch_route(r, s);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+
+    const size_t qs = (size_t)f * (d / 4), szs = (size_t)f * (d / 64) * 2, wst = (size_t)f * d;
+    const int slots = layer_slots(T, E, k, S);
+    ReduceArgs red{};
+    red.d = d; red.T = T; red.layer = 1; red.rows_per_tok = k + S; red.k = k; red.S = S;
+    red.pair_pos = w.pair_pos; red.part = w.part;
+    red.y = y; red.ydt = (int)ydt; red.accumulate = 0;
+    if (path == MOE_PATH_DENSE) {
+        DenseArgs a{};
+        a.d = d; a.f = f; a.E = E; a.k = k; a.S = S; a.T = T;
+        a.x = (const uint16_t *)x;
+        a.gate = (const uint16_t *)L->gate_t; a.up = L->up_dense; a.down = (const uint16_t *)L->down;
+        a.active = w.active; a.n_active = w.n_active; a.offset = w.offset; a.pairs = w.pairs;
+        a.topk_w = r.topk_w;
+        a.h = w.h; a.part = w.part;
+        he = launch_dense_layer(a, s);
+        if (he != hipSuccess) return MOE_ERR_HIP;
+        red.tiles = kDenseKSplit;
+        return hip_status(launch_reduce(red, s));
+    }
+
+    const TilePlan tp = plan_tiles(f, slots, (long long)T * (k + S), d);
+    SparseArgs a{};
+    a.d = d; a.f = f;
+    a.slots = slots;
+    a.cpw = tp.cpw;
+    a.tiles = tp.tiles;
+    a.up_q = L->up_q; a.up_sz = L->up_sz;
+    a.gate = (const uint16_t *)L->gate_t; a.down = (const uint16_t *)L->down;
+    a.q_stride = qs; a.sz_stride = szs; a.w_stride = wst;
+    a.thr_dev = L->thresholds; a.thr = 0.f;
+    a.x = (const uint16_t *)x; a.T = T;
+    a.token_scale = nullptr;
+    a.layer = 1; a.E = E; a.k = k; a.S = S;
+    a.active = w.active; a.n_active = w.n_active; a.offset = w.offset; a.pairs = w.pairs;
+    a.topk_w = r.topk_w;
+    a.part = w.part;
+    a.mask_out = trace ? trace->masks : nullptr; a.v_out = nullptr;
+    he = launch_sparse(a, L->wdt == MOE_BF16, choose_tb(T, d, tp.cpw), s);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+    red.tiles = tp.tiles;
+    return hip_status(launch_reduce(red, s));
+}
+
+moe_status moe_pack_up_int2(const void *w_up_t, moe_dtype dt, int d, int f, uint8_t *up_q,
+                            uint16_t *up_sz, void *stream)
+{
+    if (!w_up_t || !up_q || !up_sz) return MOE_ERR_INVALID_ARG;
+    if (d < 64 || d % 64 != 0 || f < 1) return MOE_ERR_INVALID_ARG;
+    if (!valid_out(dt)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(up_q, 16) || !aligned(up_sz, 4) || !aligned(w_up_t, dt == MOE_F32 ? 4 : 2))
+        return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_pack_int2(w_up_t, (int)dt, d, f, up_q, up_sz, (hipStream_t)stream));
+}
+
+moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
+                                   uint16_t *out, void *stream)
+{
+    if (!up_q || !up_sz || !out) return MOE_ERR_INVALID_ARG;
+    if (d < 64 || d % 64 != 0 || f < 1) return MOE_ERR_INVALID_ARG;
+    if (!aligned(up_sz, 4) || !aligned(out, 2)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_materialize_bf16(up_q, up_sz, d, f, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,576 @@
+// Fused activation-sparse SwiGLU expert for gfx950 (FloE review, "高效稀疏 GEMV 内核",
+// Algorithm 1 and the optimisations listed after it), templated on the geometry
+// of the hidden size.  Included by the per-dtype instantiation files.
+//
+// One workgroup owns a tile of `cpw` intermediate channels of one expert and a
+// chunk of up to TB tokens, and runs the whole algorithm for them:
+//   A  v = x W^up over its channels.  A lane takes 16 bytes of codes (one
+//      group of 64 inputs of one channel), turns every pair of codes into a
+//      packed 16-bit pair (1 + q/4) with one mask-and-or and accumulates
+//      x . (1 + q/4) with packed dot products in fp32.  Per group,
+//      sum x q = 4 (S' - X_g), so the group's share of v is
+//      s (4 S' - (4 + z) X_g) with X_g the group sum of x.  SEG lanes share one
+//      channel; the per-channel sums of up to 8 passes are reduced together by
+//      a transposed butterfly (each step halves the values a lane carries).
+//   B  mask = |v| > t (fp32), union over the chunk's tokens, compacted into an
+//      ascending list of active channels with a wave ballot.
+//   C  for each active channel j: every thread reads its 16-byte chunk(s) of
+//      gate row j and down row j (the only gate/down bytes touched), the gate
+//      dot product is reduced across the workgroup, h = SiLU(g) v (fused), and
+//      the thread accumulates h * down into its fp32 slice of y.
+//   D  the workgroup's fp32 slice of y (scaled by the token's router weight) is
+//      stored as one partial row; a second kernel sums the partials of each
+//      token in a fixed order and writes the output.  No atomics, no fences:
+//      the result is bit-reproducible.
+// All loads are unconditional (indices clamped to valid rows, contributions of
+// padding zeroed), so every load of a phase is in flight at once.
+#pragma once
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moeffn {
+namespace sparse {
+
+constexpr int kXPad = 72;               // halves per 64-element group slot in LDS (16 B pad)
+constexpr int kPB = 8;                  // channel passes loaded and reduced together
+
+template <int N>
+struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
+template <>
+struct Log2<1> { static constexpr int v = 0; };
+
+// Compile-time shift that moves code slot m (bits 2m of each half-word) to the
+// two mantissa bits that make (1 + q/4): bits 8-9 (fp16) or 5-6 (bf16).
+template <bool BF16, int M>
+__device__ __forceinline__ uint32_t pair_word(uint32_t w)
+{
+    constexpr int target = BF16 ? 5 : 8;
+    constexpr int sh = target - 2 * M;
+    constexpr uint32_t mask = BF16 ? 0x00600060u : 0x03000300u;
+    constexpr uint32_t one = BF16 ? 0x3F803F80u : 0x3C003C00u;
+    uint32_t t;
+    if constexpr (sh > 0) t = w << sh;
+    else if constexpr (sh < 0) t = w >> (-sh);
+    else t = w;
+    return (t & mask) | one;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void decode_unit(const uint4 &c, uint32_t (&p)[32])
+{
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[8 * i + 0] = pair_word<BF16, 0>(w[i]);
+        p[8 * i + 1] = pair_word<BF16, 1>(w[i]);
+        p[8 * i + 2] = pair_word<BF16, 2>(w[i]);
+        p[8 * i + 3] = pair_word<BF16, 3>(w[i]);
+        p[8 * i + 4] = pair_word<BF16, 4>(w[i]);
+        p[8 * i + 5] = pair_word<BF16, 5>(w[i]);
+        p[8 * i + 6] = pair_word<BF16, 6>(w[i]);
+        p[8 * i + 7] = pair_word<BF16, 7>(w[i]);
+    }
+}
+
+// sum_k x_k (1 + q_k/4) over one 64-input group: 32 packed dot products
+template <bool BF16>
+__device__ __forceinline__ float group_dot(const uint32_t (&pw)[32], const uint32_t (&xp)[32])
+{
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int m = 0; m < 32; m += 2) {
+        a0 = dot2<BF16>(pw[m], xp[m], a0);
+        a1 = dot2<BF16>(pw[m + 1], xp[m + 1], a1);
+    }
+    return a0 + a1;
+}
+
+// Transposed butterfly over the SEG lanes of a segment: on entry every lane
+// holds P partial values (P a power of two <= SEG); on exit value 0 of a lane is
+// the segment total of value index (go >> (log2 SEG - log2 P)), go being the
+// lane's position in the segment.  Each step at stride S halves the values a
+// lane carries (it keeps one half and receives its partner's copy of that
+// half); once one value is left the remaining strides are plain butterflies.
+// Fixed order: bit-reproducible.
+template <int P, int S, int N>
+__device__ __forceinline__ float treduce_step(float (&v)[P], int lane)
+{
+    if constexpr (S == 0) {
+        return v[0];
+    } else {
+        const bool hi = (lane & S) != 0;
+        if constexpr (N > 1) {
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                const float send = hi ? v[i] : v[i + N / 2];
+                const float keep = hi ? v[i + N / 2] : v[i];
+                v[i] = keep + __shfl_xor(send, S, 64);
+            }
+            return treduce_step<P, S / 2, N / 2>(v, lane);
+        } else {
+            v[0] += __shfl_xor(v[0], S, 64);
+            return treduce_step<P, S / 2, 1>(v, lane);
+        }
+    }
+}
+
+template <int P, int SEG>
+__device__ __forceinline__ float transposed_reduce(float (&v)[P], int lane)
+{
+    static_assert(P <= SEG || SEG == 1, "values per lane exceed the segment");
+    return treduce_step<P, SEG / 2, P>(v, lane);
+}
+
+struct Lds {
+    uint16_t *xs;       // [TB][G][kXPad] activations (16-bit), group-padded
+    float *xg;          // [TB][G] group sums of x
+    float *vs;          // [TB][cpw]
+    uint8_t *mk;        // [TB][cpw]
+    uint16_t *list;     // [cpw] active channels (union over the chunk's tokens)
+    float *gp;          // [W][RB][TB] partial gate dots
+    int32_t *tok_t;     // [TB] token index
+    int32_t *tok_slot;  // [TB] mask slot (layer mode)
+    int32_t *tok_row;   // [TB] partial row
+    float *tok_sc;      // [TB] scale
+    int32_t *misc;      // [0] n_act
+};
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+__host__ __device__ inline size_t lds_layout(int d, int cpw, int tb, int waves, int rb, size_t *off)
+{
+    const int G = d / 64;
+    size_t o = 0;
+    off[0] = o; o = align16(o + (size_t)tb * G * kXPad * 2);
+    off[1] = o; o = align16(o + (size_t)tb * G * 4);
+    off[2] = o; o = align16(o + (size_t)tb * cpw * 4);
+    off[3] = o; o = align16(o + (size_t)tb * cpw);
+    off[4] = o; o = align16(o + (size_t)cpw * 2);
+    off[5] = o; o = align16(o + (size_t)waves * rb * tb * 4);
+    off[6] = o; o = align16(o + (size_t)tb * 4);
+    off[7] = o; o = align16(o + (size_t)tb * 4);
+    off[8] = o; o = align16(o + (size_t)tb * 4);
+    off[9] = o; o = align16(o + (size_t)tb * 4);
+    off[10] = o; o = align16(o + 16);
+    return o;
+}
+
+// Compile-time geometry for a hidden size class.
+//   SEG     lanes sharing one channel in phase A (= d/64 when d <= 4096)
+//   NG      64-input groups per lane in phase A
+//   NCH     16-byte column chunks per thread in phase C
+//   THREADS workgroup size
+template <int SEG_, int NG_, int NCH_, int THREADS_>
+struct Geo {
+    static constexpr int SEG = SEG_, NG = NG_, NCH = NCH_, THREADS = THREADS_;
+    static constexpr int W = THREADS / 64;
+};
+
+template <int TB, int NCH>
+__host__ __device__ constexpr int rows_per_batch()
+{
+    return (8 / (NCH * (TB >= 8 ? 2 : 1))) < 1 ? 1 : (8 / (NCH * (TB >= 8 ? 2 : 1)));
+}
+
+template <bool BF16, int TB, class GEO>
+__global__ void __launch_bounds__(GEO::THREADS)
+expert_kernel(SparseArgs a)
+{
+    constexpr int SEG = GEO::SEG, NG = GEO::NG, NCH = GEO::NCH, THREADS = GEO::THREADS;
+    constexpr int W = GEO::W;
+    constexpr int RPW = 64 / SEG;                   // channels per wave pass
+    constexpr int ROWS_PASS = W * RPW;              // channels per workgroup pass
+    constexpr int RB = rows_per_batch<TB, NCH>();
+    constexpr int LOGSEG = Log2<SEG>::v;
+    // channel passes loaded and reduced together (<= SEG; fewer when a lane
+    // carries several tokens or groups, to bound registers)
+    constexpr int PB = (kPB / (TB * NG)) < 1 ? 1 : (kPB / (TB * NG));
+    constexpr int PR = PB < SEG ? PB : SEG;
+    constexpr bool XREG = (TB * NG) <= 2;           // x pairs of the lane's groups kept in registers
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int d = a.d, f = a.f, G = d / 64;
+    const int cpw = a.cpw;
+
+    size_t off[11];
+    lds_layout(d, cpw, TB, W, RB, off);
+    Lds L;
+    L.xs = (uint16_t *)(smem + off[0]);
+    L.xg = (float *)(smem + off[1]);
+    L.vs = (float *)(smem + off[2]);
+    L.mk = (uint8_t *)(smem + off[3]);
+    L.list = (uint16_t *)(smem + off[4]);
+    L.gp = (float *)(smem + off[5]);
+    L.tok_t = (int32_t *)(smem + off[6]);
+    L.tok_slot = (int32_t *)(smem + off[7]);
+    L.tok_row = (int32_t *)(smem + off[8]);
+    L.tok_sc = (float *)(smem + off[9]);
+    L.misc = (int32_t *)(smem + off[10]);
+
+    // ---- which expert and which tokens ------------------------------------
+    const int slot = blockIdx.x / a.tiles;
+    const int tile = blockIdx.x - slot * a.tiles;
+    int e = 0, ntok = a.T, pair0 = 0;
+    bool shared_slot = false;
+    if (a.layer) {
+        if (slot < a.S) {
+            e = a.E + slot;
+            shared_slot = true;
+        } else {
+            const int ai = slot - a.S;
+            if (ai >= *a.n_active) return;          // no tokens for this slot
+            e = a.active[ai];
+            pair0 = a.offset[e];
+            ntok = a.offset[e + 1] - pair0;
+        }
+    }
+    const float thr = a.thr_dev ? a.thr_dev[e] : a.thr;
+    const int j0 = tile * cpw;
+    const int nrows = min(cpw, f - j0);
+    if (nrows <= 0) return;
+
+    const uint8_t *upq = a.up_q + (size_t)e * a.q_stride + (size_t)j0 * (d / 4);
+    const uint16_t *upsz = a.up_sz + (size_t)e * a.sz_stride + (size_t)j0 * G * 2;
+    const uint16_t *gate = a.gate + (size_t)e * a.w_stride + (size_t)j0 * d;
+    const uint16_t *down = a.down + (size_t)e * a.w_stride + (size_t)j0 * d;
+
+    const int go = lane & (SEG - 1);                // position in the channel's segment
+    const int rs = lane / SEG;                      // segment (channel slot) in the wave
+    const int passes = (nrows + ROWS_PASS - 1) / ROWS_PASS;
+    const int CPR = d / 8;                          // 16-byte chunks per d-row
+
+    for (int t0 = 0; t0 < ntok; t0 += TB) {
+        const int nt = min(TB, ntok - t0);
+
+        // ---- token bookkeeping and x staging ------------------------------
+        if (tid < TB) {
+            int t = 0, sl = 0, row = 0;
+            float sc = 0.f;
+            if (tid < nt) {
+                if (!a.layer) {
+                    t = t0 + tid;
+                    row = t;
+                    sc = a.token_scale ? a.token_scale[t] : 1.0f;
+                } else if (shared_slot) {
+                    t = t0 + tid;
+                    sl = a.k + slot;
+                    row = a.T * a.k + slot * a.T + t;
+                    sc = 1.0f;
+                } else {
+                    const int pos = pair0 + t0 + tid;
+                    const int p = a.pairs[pos];
+                    t = p / a.k;
+                    sl = p - t * a.k;
+                    row = pos;
+                    sc = a.topk_w[p];
+                }
+            }
+            L.tok_t[tid] = t;
+            L.tok_slot[tid] = sl;
+            L.tok_row[tid] = row;
+            L.tok_sc[tid] = sc;
+        }
+        __syncthreads();
+        for (int i = tid; i < TB * CPR; i += THREADS) {
+            const int tb = i / CPR, c = i - tb * CPR;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (tb < nt) v = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
+            *(uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8) = v;
+        }
+        __syncthreads();
+        for (int i = tid; i < TB * G; i += THREADS) {
+            const uint32_t *xp = (const uint32_t *)(L.xs + (size_t)i * kXPad);
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+            for (int m = 0; m < 32; ++m) {
+                s0 += lo16_to_float<BF16>(xp[m]);
+                s1 += hi16_to_float<BF16>(xp[m]);
+            }
+            L.xg[i] = s0 + s1;
+        }
+        __syncthreads();
+
+        // ---- A: v = x W^up for this tile ------------------------------------
+        uint32_t xr_a[XREG ? TB * NG : 1][32];
+        float xg_a[TB][NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int g = min(go + SEG * gi, G - 1);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                xg_a[tb][gi] = L.xg[tb * G + g];
+                if constexpr (XREG) {
+                    const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const uint4 xx = xv[q];
+                        xr_a[tb * NG + gi][4 * q + 0] = xx.x;
+                        xr_a[tb * NG + gi][4 * q + 1] = xx.y;
+                        xr_a[tb * NG + gi][4 * q + 2] = xx.z;
+                        xr_a[tb * NG + gi][4 * q + 3] = xx.w;
+                    }
+                }
+            }
+        }
+        for (int p0 = 0; p0 < passes; p0 += PR) {
+            uint4 cq[PR][NG];
+            uint32_t csz[PR][NG];
+#pragma unroll
+            for (int p = 0; p < PR; ++p) {
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    const int r = (p0 + p) * ROWS_PASS + wave * RPW + rs;
+                    const int g = go + SEG * gi;
+                    const bool ok = r < nrows && g < G;
+                    const int rr = ok ? r : 0, gg = ok ? g : 0;
+                    cq[p][gi] = *(const uint4 *)(upq + (size_t)rr * (d / 4) + (size_t)gg * 16);
+                    const uint32_t w = *(const uint32_t *)(upsz + ((size_t)rr * G + gg) * 2);
+                    csz[p][gi] = ok ? w : 0u;           // s = 0: the unit contributes nothing
+                }
+            }
+            float part[TB][PR];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int p = 0; p < PR; ++p) part[tb][p] = 0.f;
+#pragma unroll
+            for (int p = 0; p < PR; ++p) {
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    uint32_t pw[32];
+                    decode_unit<BF16>(cq[p][gi], pw);
+                    const float s = half_bits_to_float(csz[p][gi] & 0xFFFFu);
+                    const float z = half_bits_to_float(csz[p][gi] >> 16);
+                    const int g = min(go + SEG * gi, G - 1);
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        float sp;
+                        if constexpr (XREG) {
+                            sp = group_dot<BF16>(pw, xr_a[tb * NG + gi]);
+                        } else {
+                            uint32_t xp[32];
+                            const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) {
+                                const uint4 xx = xv[q];
+                                xp[4 * q + 0] = xx.x;
+                                xp[4 * q + 1] = xx.y;
+                                xp[4 * q + 2] = xx.z;
+                                xp[4 * q + 3] = xx.w;
+                            }
+                            sp = group_dot<BF16>(pw, xp);
+                        }
+                        part[tb][p] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
+                    }
+                }
+            }
+            // reduce the PR passes of each token over the segment's lanes
+            constexpr int LOGPR = Log2<PR>::v;
+            const int psel = go >> (LOGSEG - LOGPR);              // pass this lane ends up with
+            const bool writer = (go & ((SEG / PR) - 1)) == 0;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const float v = transposed_reduce<PR, SEG>(part[tb], lane);
+                const int r = (p0 + psel) * ROWS_PASS + wave * RPW + rs;
+                if (writer && r < nrows && tb < nt && p0 + psel < passes) {
+                    L.vs[tb * cpw + r] = v;
+                    L.mk[tb * cpw + r] = fabsf(v) > thr ? 1 : 0;
+                }
+            }
+        }
+        __syncthreads();
+
+        // exports
+        if (a.v_out || a.mask_out) {
+            for (int i = tid; i < nt * nrows; i += THREADS) {
+                const int tb = i / nrows, r = i - tb * nrows;
+                const int t = L.tok_t[tb];
+                if (a.layer) {
+                    if (a.mask_out)
+                        a.mask_out[((size_t)t * (a.k + a.S) + L.tok_slot[tb]) * f + j0 + r] =
+                            L.mk[tb * cpw + r];
+                } else {
+                    if (a.mask_out) a.mask_out[(size_t)t * f + j0 + r] = L.mk[tb * cpw + r];
+                    if (a.v_out) a.v_out[(size_t)t * f + j0 + r] = L.vs[tb * cpw + r];
+                }
+            }
+        }
+
+        // ---- B: compaction of the union mask -------------------------------
+        if (wave == 0) {
+            int n = 0;
+            for (int r0 = 0; r0 < nrows; r0 += 64) {
+                const int r = r0 + lane;
+                int on = 0;
+                if (r < nrows)
+                    for (int tb = 0; tb < nt; ++tb) on |= L.mk[tb * cpw + r];
+                const uint64_t bal = __ballot(on);
+                const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+                if (on) L.list[n + pre] = (uint16_t)r;
+                n += __popcll(bal);
+            }
+            if (lane == 0) L.misc[0] = n;
+        }
+        __syncthreads();
+        const int n_act = L.misc[0];
+
+        // ---- C: gate / down gathers over the active channels -----------------
+        float yacc[TB][NCH][8];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) yacc[tb][i][q] = 0.f;
+
+        if (n_act > 0) {
+            uint4 xr[TB][NCH];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    const int c = min(tid + THREADS * i, CPR - 1);
+                    xr[tb][i] = *(const uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8);
+                    if (tid + THREADS * i >= CPR) xr[tb][i] = make_uint4(0, 0, 0, 0);
+                }
+            for (int b0 = 0; b0 < n_act; b0 += RB) {
+                uint4 gw[RB][NCH], dw[RB][NCH];
+                int rows[RB];
+#pragma unroll
+                for (int q = 0; q < RB; ++q) {
+                    const int ent = min(b0 + q, n_act - 1);
+                    rows[q] = (int)L.list[ent];
+#pragma unroll
+                    for (int i = 0; i < NCH; ++i) {
+                        const int c = min(tid + THREADS * i, CPR - 1);
+                        gw[q][i] = *(const uint4 *)(gate + (size_t)rows[q] * d + (size_t)c * 8);
+                        dw[q][i] = *(const uint4 *)(down + (size_t)rows[q] * d + (size_t)c * 8);
+                    }
+                }
+                // partial gate dots, reduced over the wave, then over waves in LDS
+                float p[TB * RB];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int q = 0; q < RB; ++q) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int i = 0; i < NCH; ++i) {
+                            acc = dot2<BF16>(gw[q][i].x, xr[tb][i].x, acc);
+                            acc = dot2<BF16>(gw[q][i].y, xr[tb][i].y, acc);
+                            acc = dot2<BF16>(gw[q][i].z, xr[tb][i].z, acc);
+                            acc = dot2<BF16>(gw[q][i].w, xr[tb][i].w, acc);
+                        }
+                        p[tb * RB + q] = acc;
+                    }
+                {
+                    constexpr int NP = TB * RB;
+                    constexpr int NPR = NP < 64 ? NP : 64;
+                    static_assert(NP <= 64, "too many gate partials per batch");
+                    const float v = transposed_reduce<NPR, 64>(p, lane);
+                    constexpr int LOGNP = Log2<NPR>::v;
+                    const int idx = lane >> (6 - LOGNP);
+                    if ((lane & ((64 / NPR) - 1)) == 0) L.gp[wave * NP + idx] = v;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < RB; ++q) {
+                    const bool valid = b0 + q < n_act;
+                    const int r = rows[q];
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        float g = 0.f;
+#pragma unroll
+                        for (int w = 0; w < W; ++w) g += L.gp[w * TB * RB + tb * RB + q];
+                        const float h = (valid && tb < nt && L.mk[tb * cpw + r])
+                                            ? silu(g) * L.vs[tb * cpw + r] : 0.f;
+#pragma unroll
+                        for (int i = 0; i < NCH; ++i) {
+                            const uint32_t dv[4] = {dw[q][i].x, dw[q][i].y, dw[q][i].z, dw[q][i].w};
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) {
+                                yacc[tb][i][2 * m] += h * lo16_to_float<BF16>(dv[m]);
+                                yacc[tb][i][2 * m + 1] += h * hi16_to_float<BF16>(dv[m]);
+                            }
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // ---- D: this workgroup's scaled partial rows -------------------------
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            if (tb >= nt) continue;
+            const float sc = L.tok_sc[tb];
+            float *dst = a.part + ((size_t)L.tok_row[tb] * a.tiles + tile) * d;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = tid + THREADS * i;
+                if (c >= CPR) continue;
+                float4 lo = make_float4(sc * yacc[tb][i][0], sc * yacc[tb][i][1],
+                                        sc * yacc[tb][i][2], sc * yacc[tb][i][3]);
+                float4 hi = make_float4(sc * yacc[tb][i][4], sc * yacc[tb][i][5],
+                                        sc * yacc[tb][i][6], sc * yacc[tb][i][7]);
+                *(float4 *)(dst + (size_t)c * 8) = lo;
+                *(float4 *)(dst + (size_t)c * 8 + 4) = hi;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <bool BF16, int TB, class GEO>
+hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
+{
+    size_t off[11];
+    const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off);
+    auto kern = expert_kernel<BF16, TB, GEO>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.slots * a.tiles), dim3(GEO::THREADS), lds, s, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, class GEO>
+hipError_t launch_geo(const SparseArgs &a, int tb, hipStream_t s)
+{
+    switch (tb) {
+    case 1: return launch_tb<BF16, 1, GEO>(a, s);
+    case 2: return launch_tb<BF16, 2, GEO>(a, s);
+    case 4: return launch_tb<BF16, 4, GEO>(a, s);
+    case 8:
+        if constexpr (GEO::NCH == 1) return launch_tb<BF16, 8, GEO>(a, s);
+        break;
+    default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+// Geometry by hidden size: see Geo.
+template <bool BF16>
+hipError_t launch_dtype(const SparseArgs &a, int tb, hipStream_t s)
+{
+    switch (a.d) {
+    case 64: return launch_geo<BF16, Geo<1, 1, 1, 64>>(a, tb, s);
+    case 128: return launch_geo<BF16, Geo<2, 1, 1, 64>>(a, tb, s);
+    case 256: return launch_geo<BF16, Geo<4, 1, 1, 64>>(a, tb, s);
+    case 512: return launch_geo<BF16, Geo<8, 1, 1, 64>>(a, tb, s);
+    case 1024: return launch_geo<BF16, Geo<16, 1, 1, 128>>(a, tb, s);
+    case 2048: return launch_geo<BF16, Geo<32, 1, 1, 256>>(a, tb, s);
+    case 4096: return launch_geo<BF16, Geo<64, 1, 1, 512>>(a, tb, s);
+    default: break;
+    }
+    if (a.d > 4096 && a.d <= 8192) return launch_geo<BF16, Geo<64, 2, 2, 512>>(a, tb, s);
+    if (a.d > 8192 && a.d <= 16384) return launch_geo<BF16, Geo<64, 4, 4, 512>>(a, tb, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sparse
+}  // namespace moeffn

@@ -1,0 +1,9 @@
+// fp16 instantiations of the sparse expert kernel.
+#include "expert_sparse.hpp"
+
+namespace moeffn {
+hipError_t launch_sparse_expert_f16(const SparseArgs &a, int tb, hipStream_t s)
+{
+    return sparse::launch_dtype<false>(a, tb, s);
+}
+}  // namespace moeffn

@@ -1,0 +1,94 @@
+// Host-side declarations shared by the C ABI (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeffn {
+
+// Everything the sparse expert kernel needs, passed by value.
+struct SparseArgs {
+    int d, f;
+    int cpw;                            // channels per workgroup tile
+    int tiles;                          // workgroups per expert
+    int slots;                          // expert slots in the grid
+    const uint8_t *up_q;                // expert 0 of a fixed-stride pool
+    const uint16_t *up_sz;
+    const uint16_t *gate;
+    const uint16_t *down;
+    size_t q_stride, sz_stride, w_stride;   // per-expert strides (elements)
+    const float *thr_dev;               // [E+S] or nullptr
+    float thr;                          // single-expert threshold
+    const uint16_t *x;                  // [T][d]
+    int T;
+    // single-expert mode
+    const float *token_scale;           // [T] or nullptr
+    // layer mode (layer != 0)
+    int layer, E, k, S;
+    const int32_t *active;              // [E] ascending ids of experts with tokens
+    const int32_t *n_active;            // [1]
+    const int32_t *offset;              // [E+1]
+    const int32_t *pairs;               // [T*k]
+    const float *topk_w;                // [T*k]
+    // outputs
+    float *part;                        // partial rows [rows][tiles][d] (workspace)
+    uint8_t *mask_out;                  // single: [T][f]; layer: [T][k+S][f]
+    float *v_out;                       // single only: [T][f]
+};
+
+// Launch the fused Algorithm-1 kernel; tb = tokens per chunk (1, 2, 4, 8).
+hipError_t launch_sparse_expert_f16(const SparseArgs &a, int tb, hipStream_t s);
+hipError_t launch_sparse_expert_bf16(const SparseArgs &a, int tb, hipStream_t s);
+
+// Second kernel: output rows from the partial rows.
+struct ReduceArgs {
+    const float *part;                  // [rows][tiles][d]
+    int tiles, d, T;
+    int layer;                          // 0: row of token t is t; 1: routed + shared rows
+    int rows_per_tok;                   // 1 or k + S
+    int k, S;
+    const int32_t *pair_pos;            // [T*k] grouped position of pair t*k + s
+    void *y;
+    int ydt;
+    int accumulate;
+};
+hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
+
+struct RouteArgs {
+    const void *x;
+    int xdt;
+    int T, d;
+    const void *rw;
+    int rdt;
+    const float *bias;
+    int E, k, renorm;
+    int32_t *topk_idx;
+    float *topk_w;
+    float *logits;                      // nullable
+    int32_t *count, *offset, *pairs;    // nullable as a group (grouping skipped)
+    int32_t *pair_pos;                  // nullable: grouped position of each pair
+    int32_t *active, *n_active;         // nullable
+    uint32_t *done;                     // completion counter (workspace)
+};
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+
+struct DenseArgs {
+    int d, f, E, k, S, T;
+    const uint16_t *x;                  // [T][d] bf16
+    const uint16_t *gate, *up, *down;   // [E+S][f][d] bf16
+    const int32_t *active, *n_active, *offset, *pairs;
+    const float *topk_w;
+    float *h;                           // [T*(k+S)][f] fp32 intermediate (workspace)
+    float *part;                        // [T*(k+S)][kDenseKSplit][d] partial rows (workspace)
+};
+constexpr int kDenseKSplit = 4;         // split of the intermediate dimension in the down GEMM
+hipError_t launch_dense_layer(const DenseArgs &a, hipStream_t s);
+size_t dense_h_bytes(int T, int f, int k, int S);
+
+hipError_t launch_pack_int2(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz,
+                            hipStream_t s);
+hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, int f,
+                                   uint16_t *out, hipStream_t s);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+
+}  // namespace moeffn

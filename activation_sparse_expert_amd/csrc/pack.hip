@@ -1,0 +1,145 @@
+// INT2 group-64 packing of the up projection (FloE review, "混合压缩策略": up is
+// the projection least sensitive to very low bit widths and is stored in INT2),
+// the bf16 materialisation of those weights for the dense path, and a
+// workspace fill kernel.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moeffn {
+
+namespace {
+
+__device__ __forceinline__ float load_w(const void *p, int dt, size_t i)
+{
+    if (dt == 2) return ((const float *)p)[i];
+    const uint16_t b = ((const uint16_t *)p)[i];
+    return dt == 1 ? bf16_bits_to_float(b) : half_bits_to_float(b);
+}
+
+// One thread per (channel, group of 64 inputs).  All steps are single fp32
+// operations with round-to-nearest-even, in this order:
+//   mn, mx;  s = fp16((mx - mn) / 3) (1 if 0);  z = fp16(-mn / s);
+//   q = clamp(rint(w / s + z), 0, 3)
+// Output word i of the row holds inputs 16i..16i+15: input 16i + 2m + h at
+// bits 16h + 2m.
+__global__ void __launch_bounds__(256)
+pack_int2_kernel(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz)
+{
+    const int G = d / 64;
+    const size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= (size_t)f * G) return;
+    const size_t j = u / G, g = u - j * G;
+    const size_t base = j * d + g * 64;
+    float mn = load_w(w, dt, base), mx = mn;
+    for (int i = 1; i < 64; ++i) {
+        const float v = load_w(w, dt, base + i);
+        if (v < mn) mn = v;             // plain comparisons: a signed zero never replaces
+        if (v > mx) mx = v;             // an equal earlier value
+    }
+    const float third = __fdiv_rn(mx - mn, 3.0f);
+    uint16_t sb = float_to_half_bits(third);
+    float s = half_bits_to_float(sb);
+    if (s == 0.0f) { sb = 0x3C00; s = 1.0f; }
+    const uint16_t zb = float_to_half_bits(__fdiv_rn(-mn, s));
+    const float z = half_bits_to_float(zb);
+    sz[u * 2 + 0] = sb;
+    sz[u * 2 + 1] = zb;
+    uint32_t words[4] = {0, 0, 0, 0};
+    for (int i = 0; i < 64; ++i) {
+        const float a = __fdiv_rn(load_w(w, dt, base + i), s);
+        const float r = rintf(__fadd_rn(a, z));
+        int c = (int)r;
+        if (r < 0.0f) c = 0;
+        if (r > 3.0f) c = 3;
+        const int wi = i / 16, h = i & 1, m = (i & 15) >> 1;
+        words[wi] |= (uint32_t)c << (16 * h + 2 * m);
+    }
+    *(uint4 *)(q + j * (d / 4) + g * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+}
+
+// Round a double to bfloat16, nearest-even, from its bits (finite inputs).
+__device__ __forceinline__ uint16_t double_to_bf16_bits(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t sign = u >> 63;
+    uint64_t mag = u & 0x7FFFFFFFFFFFFFFFull;
+    if (mag == 0) return (uint16_t)(sign << 15);
+    // rebias exponent from double (1023) to float (127) and keep 7 mantissa bits
+    int e = (int)(mag >> 52) - 1023 + 127;
+    uint64_t m = (mag & 0xFFFFFFFFFFFFFull) | (1ull << 52);   // 53-bit significand
+    int drop;                                                   // bits to drop to keep 8
+    if (e >= 1) {
+        drop = 52 - 7;
+    } else {                                                   // subnormal bf16
+        drop = 52 - 7 + (1 - e);
+        e = 0;
+        if (drop > 60) return (uint16_t)(sign << 15);
+    }
+    uint64_t keep = m >> drop;
+    const uint64_t rem = m & ((1ull << drop) - 1);
+    const uint64_t half = 1ull << (drop - 1);
+    if (rem > half || (rem == half && (keep & 1))) keep++;
+    uint32_t bits;
+    if (e == 0) {
+        bits = (uint32_t)keep;                                  // may carry into exponent 1
+    } else {
+        if (keep >> 8) { keep >>= 1; e++; }                     // carry out of the significand
+        if (e >= 255) return (uint16_t)((sign << 15) | 0x7F80);
+        bits = ((uint32_t)e << 7) | (uint32_t)(keep & 0x7F);
+    }
+    return (uint16_t)((sign << 15) | bits);
+}
+
+__global__ void __launch_bounds__(256)
+materialize_bf16_kernel(const uint8_t *q, const uint16_t *sz, int d, int f, uint16_t *out)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)f * d) return;
+    const size_t j = i / d, k = i - j * d;
+    const int G = d / 64;
+    const size_t bit = 32 * (k / 16) + 16 * (k & 1) + 2 * ((k & 15) >> 1);
+    const int c = (q[j * (d / 4) + bit / 8] >> (bit % 8)) & 3;
+    const double s = (double)half_bits_to_float(sz[(j * G + k / 64) * 2 + 0]);
+    const double z = (double)half_bits_to_float(sz[(j * G + k / 64) * 2 + 1]);
+    out[i] = double_to_bf16_bits(s * ((double)c - z));         // exact product in double
+}
+
+__global__ void __launch_bounds__(256)
+fill_zero_kernel(uint32_t *p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_pack_int2(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz,
+                            hipStream_t s)
+{
+    const size_t n = (size_t)f * (d / 64);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(pack_int2_kernel, dim3(blocks), dim3(256), 0, s, w, dt, d, f, q, sz);
+    return hipGetLastError();
+}
+
+hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, int f,
+                                   uint16_t *out, hipStream_t s)
+{
+    const size_t n = (size_t)f * d;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(materialize_bf16_kernel, dim3(blocks), dim3(256), 0, s, q, sz, d, f, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
+{
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, n);
+    return hipGetLastError();
+}
+
+}  // namespace moeffn

@@ -1,0 +1,164 @@
+// Top-k router and token -> expert grouping (MoE-Infinity review, "A3 背景" and
+// "4.3"; MoE-Lightning review, "MoE 模型架构").
+//
+// One workgroup per token computes the E logits (every expert with the same
+// code path and reduction order, so identical router rows tie exactly), picks
+// the top-k with ties going to the lower index, and writes the softmax
+// weights.  The last workgroup to finish (completion counter, which it resets)
+// groups the T*k (token, slot) pairs by expert: counts, exclusive offsets, the
+// pairs of each expert in ascending order, and the list of experts that
+// received tokens.  No host synchronisation is involved.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moeffn {
+
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+__device__ __forceinline__ float load_any(const void *p, int dt, size_t i)
+{
+    if (dt == 2) return ((const float *)p)[i];
+    const uint16_t b = ((const uint16_t *)p)[i];
+    return dt == 1 ? bf16_bits_to_float(b) : half_bits_to_float(b);
+}
+
+// argmax over (value, index) with the lower index winning ties
+__device__ __forceinline__ void argmax_pair(float &v, int &i, float ov, int oi)
+{
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_kernel(RouteArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *xs = (float *)smem;                        // [d]
+    float *lg = xs + a.d;                             // [E]
+    int *sel = (int *)(lg + a.E);                     // [k]
+    int *flag = sel + a.k;                            // [1]
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int d = a.d, E = a.E, k = a.k;
+
+    for (int i = tid; i < d; i += kRouteThreads) xs[i] = load_any(a.x, a.xdt, (size_t)t * d + i);
+    __syncthreads();
+
+    // logits: one wave per expert, lanes stride over d, fixed butterfly
+    for (int e = wave; e < E; e += kRouteWaves) {
+        float p = 0.f;
+        for (int i = lane; i < d; i += 64) p += xs[i] * load_any(a.rw, a.rdt, (size_t)e * d + i);
+        p = seg_sum<64>(p);
+        if (lane == 0) lg[e] = p + (a.bias ? a.bias[e] : 0.f);
+    }
+    __syncthreads();
+
+    if (wave == 0) {
+        // top-k by repeated wave argmax; chosen experts are knocked out
+        float m_sel = -INFINITY;
+        for (int s = 0; s < k; ++s) {
+            float bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+            for (int e = lane; e < E; e += 64) {
+                bool taken = false;
+                for (int q = 0; q < s; ++q) taken |= (sel[q] == e);
+                if (!taken) argmax_pair(bv, bi, lg[e], e);
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off, 64);
+                const int oi = __shfl_xor(bi, off, 64);
+                argmax_pair(bv, bi, ov, oi);
+            }
+            sel[s] = bi;              // every lane stores the same value and reads its own
+            if (s == 0) m_sel = bv;
+        }
+        // weights
+        float m = m_sel, den = 0.f;
+        if (a.renorm) {
+            for (int s = lane; s < k; s += 64) den += __expf(lg[sel[s]] - m);
+        } else {
+            for (int e = lane; e < E; e += 64) den += __expf(lg[e] - m);
+        }
+        den = seg_sum<64>(den);
+        for (int s = lane; s < k; s += 64) {
+            const int e = sel[s];
+            a.topk_idx[(size_t)t * k + s] = e;
+            a.topk_w[(size_t)t * k + s] = __expf(lg[e] - m) / den;
+        }
+        if (a.logits)
+            for (int e = lane; e < E; e += 64) a.logits[(size_t)t * E + e] = lg[e];
+    }
+
+    if (!a.count) return;
+
+    // ---- grouping by the last workgroup -------------------------------------
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) flag[0] = (atomicInc(a.done, (uint32_t)a.T - 1) == (uint32_t)a.T - 1);
+    __syncthreads();
+    if (!flag[0]) return;
+    __threadfence();
+
+    int *cnt = (int *)smem;                          // reuse: [E] counts
+    int *run = cnt + E;                              // [E] running placement base
+    int *ce = run + E;                               // [kRouteThreads] chunk experts
+    const int P = a.T * k;
+    for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kRouteThreads)
+        atomicAdd(&cnt[load_coherent_i32(a.topk_idx + p)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int o = 0, na = 0;
+        for (int e = 0; e < E; ++e) {
+            a.offset[e] = o;
+            run[e] = o;
+            a.count[e] = cnt[e];
+            if (a.active && cnt[e] > 0) a.active[na++] = e;
+            o += cnt[e];
+        }
+        a.offset[E] = o;
+        if (a.n_active) *a.n_active = na;
+    }
+    __syncthreads();
+    // stable placement, one chunk of pairs at a time
+    for (int b = 0; b < P; b += kRouteThreads) {
+        const int p = b + tid;
+        const int e = p < P ? load_coherent_i32(a.topk_idx + p) : -1;
+        ce[tid] = e;
+        __syncthreads();
+        if (e >= 0) {
+            int rank = 0;
+            for (int q = 0; q < tid; ++q) rank += (ce[q] == e);
+            a.pairs[run[e] + rank] = p;
+            if (a.pair_pos) a.pair_pos[p] = run[e] + rank;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const int n = min(kRouteThreads, P - b);
+            for (int q = 0; q < n; ++q) run[ce[q]]++;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s)
+{
+    size_t lds = (size_t)a.d * 4 + (size_t)a.E * 4 + (size_t)a.k * 4 + 16;
+    const size_t lds_group = (size_t)a.E * 8 + kRouteThreads * 4 + 16;
+    if (lds_group > lds) lds = lds_group;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)route_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(kRouteThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moeffn

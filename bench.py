@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of the activation-sparse expert FFN on one MI355X.
+
+Workload: one Mixtral-8x7B-shaped SwiGLU expert (d=4096, f=14336), fp16 gate /
+down rows, INT2 group-64 up weights, thresholds calibrated to 90% activation
+sparsity, one token per call (decode).  A step is one call of
+moe_expert_forward_sparse on one token: the fused kernel (INT2 up GEMV, mask,
+compaction, gate/down row gathers, fused SiLU, partial rows) and the small
+kernel that sums the partial rows into y.  Steps rotate over R distinct expert
+instances (R * 253 MB far exceeds the 256 MB Infinity Cache) and 16 tokens, so
+the weights come from HBM, as they would when 32 layers x 8 experts are
+resident.  Inputs are resident in HBM before the timed region starts; the K
+launches are captured once in a HIP graph and replayed, so the host's launch
+overhead is not what is measured.
+
+Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "expert-FFN tokens/s + achieved HBM GB/s (d=4096,f=14336, 90% sparse, batch 1)"
+HBM_PEAK_GBS = 8000.0
+D, F = 4096, 14336
+NTOK = 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_instances(R, sparsity, dev):
+    import torch
+    import activation_sparse_expert_amd as moe
+    import synth
+    cfg = synth.CFG_MIXTRAL
+    xs = synth.CONFIGS[cfg]["x_scale"]
+    experts = []
+    for i in range(R):
+        g = synth.device_normal(synth.seed_of(cfg, 0, i, synth.T_GATE), (F, D), 0.02, dev, torch.float16)
+        dn = synth.device_normal(synth.seed_of(cfg, 0, i, synth.T_DOWN), (F, D), 0.02, dev, torch.float16)
+        u = synth.device_normal(synth.seed_of(cfg, 0, i, synth.T_UP), (F, D), 0.02, dev)
+        q, sz = moe.pack_up_int2(u)
+        del u
+        ex = moe.Expert(q, sz, g, dn, float("inf"))
+        # calibration: |v| of the 64 seeded calibration vectors, from the library
+        xc = torch.from_numpy(synth.calibration_f32(cfg, D, xs, 0, i)).half().to(dev)
+        v = torch.empty((64, F), dtype=torch.float32, device=dev)
+        moe.expert_forward_sparse(ex, xc, v_out=v)
+        torch.cuda.synchronize()
+        ex.threshold = float(np.float32(np.quantile(np.abs(v.cpu().numpy()).ravel(), sparsity)))
+        experts.append(ex)
+    return experts
+
+
+def cpu_baseline(sparsity, budget_s):
+    """The fp64 oracle, as it stands, on instance 0 and the same tokens."""
+    import oracle
+    import synth
+    cfg = synth.CFG_MIXTRAL
+    xs = synth.CONFIGS[cfg]["x_scale"]
+    g, u, dn = synth.expert_weights_f32(cfg, 0, 0, D, F)
+    q, sz = oracle.pack_up_int2(u)
+    gb, db = synth.to_f16_bits(g), synth.to_f16_bits(dn)
+    W = oracle.dequant_up(q, sz, D)
+    xc = synth.to_f16_bits(synth.calibration_f32(cfg, D, xs, 0, 0))
+    vcal = xc.view(np.float16).astype(np.float64) @ W.T
+    del W
+    thr = oracle.calibrate_threshold(np.abs(vcal), sparsity)
+    toks = synth.to_f16_bits(synth.tokens_f32(cfg, NTOK, D, xs))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.expert_forward(toks[n % NTOK:n % NTOK + 1], "f16", q, sz, gb, db, "f16", thr)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= NTOK:
+            break
+    return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n} single-token calls of the fp64 oracle on expert instance 0 "
+                       f"(d={D}, f={F}, {int(sparsity * 100)}% threshold), {el:.1f} s, one thread")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--sparsity", type=float, default=0.9)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the expert path here runs on a single MI355X "
+              "and has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import activation_sparse_expert_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"building {args.instances} expert instances d={D} f={F}")
+    experts = build_instances(args.instances, args.sparsity, dev)
+    cfg = synth.CFG_MIXTRAL
+    x_all = torch.from_numpy(synth.tokens_f32(cfg, NTOK, D, synth.CONFIGS[cfg]["x_scale"])).half().to(dev)
+    xs = [x_all[i:i + 1] for i in range(NTOK)]
+    y = torch.empty((1, D), dtype=torch.float32, device=dev)
+    ws = moe.new_workspace(moe.workspace_size(moe.OP_EXPERT, 1, D, F), dev)
+
+    # untimed pass: realised active rows per (instance, token) -> algorithmic bytes
+    R = len(experts)
+    nnz = np.zeros((R, NTOK))
+    m = torch.empty((1, F), dtype=torch.uint8, device=dev)
+    for r in range(R):
+        for t in range(NTOK):
+            moe.expert_forward_sparse(experts[r], xs[t], y=y, ws=ws, mask_out=m)
+            nnz[r, t] = float(m.sum().item())
+    fixed = D * F // 4 + F * (D // 64) * 4 + D * 2 + D * 4     # INT2 up + scales + x + y
+    per_call = fixed + 2 * nnz * D * 2                            # + gate and down rows
+    sched = [(i % R, (i // R) % NTOK) for i in range(args.steps)]
+    bytes_timed = float(sum(per_call[r, t] for r, t in sched))
+
+    stream = torch.cuda.Stream()
+    # warmup (eager), then capture the K steps in one graph
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            r, t = i % R, (i // R) % NTOK
+            moe.expert_forward_sparse(experts[r], xs[t], y=y, ws=ws)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for r, t in sched:
+            moe.expert_forward_sparse(experts[r], xs[t], y=y, ws=ws)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):     # replay runs on the current stream
+        graph.replay()                  # one untimed replay
+        stream.synchronize()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    sec = ms / 1e3
+    K = args.steps
+    avg_launch_s = sec / K
+    achieved = bytes_timed / K / avg_launch_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": K * 1 / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "one Mixtral-8x7B-shaped SwiGLU expert, INT2 up + fp16 gate/down, "
+                        "90% activation sparsity, batch 1 (decode)",
+            "d": D, "f": F, "tokens_per_step": 1, "sparsity_target": args.sparsity,
+            "sparsity_realised": float(1 - nnz.mean() / F), "instances": R,
+            "bytes_per_step_mean": bytes_timed / K,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(args.sparsity, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

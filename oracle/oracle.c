@@ -279,32 +279,43 @@ void oracle_expert_forward(const void *x, int xdt, int T, int d, int f,
                            float thr, const double *scale, const uint8_t *mask_in,
                            double *v_out, uint8_t *mask_out, double *y_out, int accumulate)
 {
-    double *xr = (double *)malloc(sizeof(double) * (size_t)d);
-    double *yr = (double *)malloc(sizeof(double) * (size_t)d);
-    for (int t = 0; t < T; ++t) {
-        for (int k = 0; k < d; ++k) xr[k] = load_typed(x, xdt, (size_t)t * d + k);
-        for (int c = 0; c < d; ++c) yr[c] = 0.0;
-        for (int j = 0; j < f; ++j) {
+    double *xr = (double *)malloc(sizeof(double) * (size_t)T * d);
+    double *yr = (double *)calloc((size_t)T * d, sizeof(double));
+    double *wu = (double *)malloc(sizeof(double) * (size_t)d);
+    double *wg = (double *)malloc(sizeof(double) * (size_t)d);
+    double *wd = (double *)malloc(sizeof(double) * (size_t)d);
+    for (size_t i = 0; i < (size_t)T * d; ++i) xr[i] = load_typed(x, xdt, i);
+    /* channel by channel; each token's arithmetic is independent of the others */
+    for (int j = 0; j < f; ++j) {
+        for (int k = 0; k < d; ++k) {
+            wu[k] = up_weight(up_q, up_sz, d, j, k);
+            wg[k] = load_typed(gate_t, wdt, (size_t)j * d + k);
+            wd[k] = load_typed(down, wdt, (size_t)j * d + k);
+        }
+        for (int t = 0; t < T; ++t) {
+            const double *xt = xr + (size_t)t * d;
             double v = 0.0;
-            for (int k = 0; k < d; ++k) v += xr[k] * up_weight(up_q, up_sz, d, j, k);
-            int m = mask_in ? (mask_in[(size_t)t * f + j] != 0) : (fabs(v) > (double)thr);
+            for (int k = 0; k < d; ++k) v += xt[k] * wu[k];                     /* step 1 */
+            int m = mask_in ? (mask_in[(size_t)t * f + j] != 0) : (fabs(v) > (double)thr); /* 2 */
             if (v_out) v_out[(size_t)t * f + j] = v;
             if (mask_out) mask_out[(size_t)t * f + j] = (uint8_t)m;
             if (!m) continue;
             double g = 0.0;
-            for (int k = 0; k < d; ++k) g += xr[k] * load_typed(gate_t, wdt, (size_t)j * d + k);
-            double h = silu(g) * v;
-            for (int c = 0; c < d; ++c) yr[c] += h * load_typed(down, wdt, (size_t)j * d + c);
+            for (int k = 0; k < d; ++k) g += xt[k] * wg[k];
+            double h = silu(g) * v;                                             /* step 3 */
+            double *yt = yr + (size_t)t * d;
+            for (int c = 0; c < d; ++c) yt[c] += h * wd[c];                     /* step 4 */
         }
+    }
+    for (int t = 0; t < T; ++t) {
         double sc = scale ? scale[t] : 1.0;
         if (y_out)
             for (int c = 0; c < d; ++c) {
-                double o = sc * yr[c];
+                double o = sc * yr[(size_t)t * d + c];
                 y_out[(size_t)t * d + c] = accumulate ? y_out[(size_t)t * d + c] + o : o;
             }
     }
-    free(xr);
-    free(yr);
+    free(xr); free(yr); free(wu); free(wg); free(wd);
 }
 
 /* ------------------------------------------------------ C2: router */

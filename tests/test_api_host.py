@@ -1,0 +1,187 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+sizes workspaces, and rejects invalid requests on the host before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import activation_sparse_expert_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeffn.h")
+
+
+def _lib_or_skip():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("libmoeffn.so not built")
+    return moe.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward"):
+        assert n in names
+    assert sorted(moe.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib_or_skip()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    # and nothing from the oracle leaks into it
+    assert not hasattr(C.CDLL(moe.LIB_PATH), "oracle_expert_forward")
+
+
+def test_status_strings():
+    L = _lib_or_skip()
+    for code in (0, -1, -2, -3, -4, -5):
+        s = L.moe_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert L.moe_status_string(7).decode() == "unknown status"
+
+
+def test_workspace_sizes():
+    _lib_or_skip()
+    # one fp32 partial row per (token, channel tile): about 256 tiles at f=14336
+    e = moe.workspace_size(moe.OP_EXPERT, 4, 4096, 14336)
+    assert e >= 4 * 4096 * 4 * 200 and e % 256 == 0
+    assert moe.workspace_size(moe.OP_EXPERT, 0, 4096, 14336) == 0
+    assert moe.workspace_size(moe.OP_EXPERT, 4, 4096, 0) == 0
+    # partial rows stay bounded for many tokens
+    assert moe.workspace_size(moe.OP_EXPERT, 256, 4096, 14336) <= (256 << 20) + 256
+    assert moe.workspace_size(moe.OP_ROUTE, 16, 4096, 0, 8, 2) >= 4
+    l1 = moe.workspace_size(moe.OP_LAYER, 16, 4096, 14336, 8, 2, 0)
+    l2 = moe.workspace_size(moe.OP_LAYER, 32, 4096, 14336, 8, 2, 0)
+    assert 0 < l1 < l2
+    assert moe.workspace_size(moe.OP_LAYER, 16, 4096, 14336, 8, 9, 0) == 0   # k > E
+
+
+FAKE = 0x10000          # 64 KiB-aligned fake device address; never dereferenced
+
+
+def _view(**kw):
+    v = dict(up_q=FAKE, up_sz=FAKE, gate_t=FAKE, down=FAKE, threshold=0.1)
+    v.update(kw)
+    return moe.ExpertView(v["up_q"], v["up_sz"], v["gate_t"], v["down"], v["threshold"])
+
+
+def _expert(view=None, d=4096, f=14336, wdt=0, x=FAKE, xdt=0, T=1, y=FAKE, ydt=2, ws=FAKE,
+            ws_bytes=1 << 26, scale=None, v_out=None):
+    L = _lib_or_skip()
+    v = view if view is not None else _view()
+    return L.moe_expert_forward_sparse(C.byref(v), d, f, wdt, x, xdt, T, scale, 0, y, ydt, None,
+                                       v_out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1),
+    (dict(y=None), -1),
+    (dict(T=0), -1),
+    (dict(f=100), -1),                  # f % 64 != 0
+    (dict(d=4160), -2),                 # d unsupported
+    (dict(d=1536), -2),
+    (dict(wdt=2), -2),                  # weights must be 16-bit
+    (dict(xdt=1), -2),                  # x type differs from weight type
+    (dict(ydt=7), -2),
+    (dict(x=FAKE + 8), -3),             # x not 16-byte aligned
+    (dict(y=FAKE + 2, ydt=2), -3),      # fp32 output not 4-byte aligned
+    (dict(ws=None), -4),
+    (dict(ws_bytes=1024), -4),
+    (dict(ws=FAKE + 4), -3),
+])
+def test_expert_rejects(kw, code):
+    assert _expert(**kw) == code
+
+
+@pytest.mark.parametrize("field,val,code", [
+    ("up_q", None, -1), ("gate_t", None, -1), ("down", None, -1), ("up_sz", None, -1),
+    ("up_q", FAKE + 4, -3), ("gate_t", FAKE + 2, -3), ("down", FAKE + 8, -3), ("up_sz", FAKE + 2, -3),
+])
+def test_expert_rejects_weight_pointers(field, val, code):
+    assert _expert(view=_view(**{field: val})) == code
+
+
+def test_expert_null_view():
+    L = _lib_or_skip()
+    assert L.moe_expert_forward_sparse(None, 4096, 14336, 0, FAKE, 0, 1, None, 0, FAKE, 2, None,
+                                       None, FAKE, 1 << 20, None) == -1
+
+
+def _route(x=FAKE, xdt=0, T=4, d=4096, rw=FAKE, rdt=0, E=8, k=2, outs=True, ws=FAKE, ws_bytes=256):
+    L = _lib_or_skip()
+    o = FAKE if outs else None
+    return L.moe_route_topk(x, xdt, T, d, rw, rdt, None, E, k, 1, o, o, o, o, o, None, ws, ws_bytes,
+                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(rw=None), -1), (dict(T=0), -1), (dict(k=0), -1), (dict(k=9), -1),
+    (dict(E=0), -1), (dict(E=2000, k=2), -1), (dict(outs=False), -1), (dict(ws=None), -4),
+    (dict(ws_bytes=0), -4), (dict(xdt=5), -2), (dict(x=FAKE + 1), -3), (dict(T=40000, k=2), -2),
+    (dict(d=60000), -2),
+])
+def test_route_rejects(kw, code):
+    assert _route(**kw) == code
+
+
+def _layer_desc(**kw):
+    base = dict(d=4096, f=14336, n_routed=8, n_shared=0, top_k=2, renormalize=1, wdt=0,
+                router_w=FAKE, rdt=0, router_bias=None, up_q=FAKE, up_sz=FAKE, gate_t=FAKE,
+                down=FAKE, thresholds=FAKE, up_dense=None)
+    base.update(kw)
+    return moe.LayerDesc(*[base[n] for n, _ in moe.LayerDesc._fields_])
+
+
+def _layer(desc=None, x=FAKE, xdt=0, T=4, y=FAKE, ydt=2, path=0, ws=FAKE, ws_bytes=1 << 30):
+    L = _lib_or_skip()
+    dsc = desc if desc is not None else _layer_desc()
+    return L.moe_layer_forward(C.byref(dsc), x, xdt, T, y, ydt, path, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), -1), (dict(T=0), -1), (dict(path=3), -1), (dict(ws=None), -4),
+    (dict(ws_bytes=4096), -4), (dict(xdt=1), -2), (dict(path=1), -2),   # dense needs bf16 + up_dense
+])
+def test_layer_rejects(kw, code):
+    assert _layer(**kw) == code
+
+
+@pytest.mark.parametrize("dkw,code", [
+    (dict(top_k=0), -1), (dict(top_k=9), -1), (dict(n_shared=-1), -1), (dict(thresholds=None), -1),
+    (dict(up_q=None), -1), (dict(router_w=None), -1), (dict(f=1000), -1), (dict(d=3000), -2),
+    (dict(thresholds=FAKE + 2), -3), (dict(gate_t=FAKE + 4), -3),
+])
+def test_layer_rejects_desc(dkw, code):
+    assert _layer(desc=_layer_desc(**dkw)) == code
+
+
+def test_layer_dense_shape_limits():
+    d = _layer_desc(wdt=1, up_dense=FAKE, f=14336 + 64)   # f % 256 != 0 for the dense path
+    assert _layer(desc=d, xdt=1, path=1) == -2
+
+
+def test_pack_and_materialize_reject():
+    L = _lib_or_skip()
+    assert L.moe_pack_up_int2(None, 2, 4096, 8, FAKE, FAKE, None) == -1
+    assert L.moe_pack_up_int2(FAKE, 2, 100, 8, FAKE, FAKE, None) == -1
+    assert L.moe_pack_up_int2(FAKE, 2, 4096, 0, FAKE, FAKE, None) == -1
+    assert L.moe_pack_up_int2(FAKE, 9, 4096, 8, FAKE, FAKE, None) == -2
+    assert L.moe_pack_up_int2(FAKE, 2, 4096, 8, FAKE + 4, FAKE, None) == -3
+    assert L.moe_materialize_up_bf16(None, FAKE, 4096, 8, FAKE, None) == -1
+    assert L.moe_materialize_up_bf16(FAKE, FAKE, 4095, 8, FAKE, None) == -1
+    assert L.moe_workspace_init(None, 256, None) == -1
+    assert L.moe_workspace_init(FAKE + 2, 256, None) == -3
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoeffn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.lib()

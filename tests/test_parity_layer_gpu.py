@@ -1,0 +1,213 @@
+"""GPU parity of routing, grouping and whole MoE layers (sparse and dense paths)
+against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_expert_amd as moe
+import oracle
+import synth
+from gpu_helpers import (DEV, HostExpert, bits_to_f64, check_mask, check_y, dev_bits, say,
+                         to_dev_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+# ------------------------------------------------------------------ router
+
+def check_route(x_bits, xdt, R_bits, rdt, E, k, renorm, bias, out, what):
+    """Top-k bit-exact against the oracle except at fp32-vs-fp64 near-ties,
+    where it must equal the stable top-k of the GPU's own fp32 logits."""
+    ref = oracle.route_topk(x_bits, xdt, R_bits, rdt, E, k, renormalize=renorm, bias=bias)
+    idx = out["topk_idx"].cpu().numpy()
+    lg = out["logits"].cpu().numpy().astype(np.float64)
+    X = bits_to_f64(x_bits, xdt) if xdt != "f32" else np.asarray(x_bits, np.float64)
+    Rm = bits_to_f64(R_bits, rdt) if rdt != "f32" else np.asarray(R_bits, np.float64)
+    mag = np.abs(X) @ np.abs(Rm).T                     # sum_k |x_k R_ek|
+    L = ref["logits"]
+    srt = np.sort(L, axis=1)[:, ::-1]
+    gap = srt[:, k - 1] - (srt[:, k] if k < E else -np.inf)
+    near = gap <= 2.0 ** -16 * mag.max(axis=1)
+    own = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    for t in range(idx.shape[0]):
+        if near[t]:
+            assert np.array_equal(idx[t], own[t]), f"{what}: token {t} near-tie"
+        else:
+            assert np.array_equal(idx[t], ref["topk_idx"][t]), f"{what}: token {t}"
+    np.testing.assert_allclose(lg, L, rtol=1e-4, atol=1e-5 * mag.max())
+    w = out["topk_w"].cpu().numpy()
+    ok = ~near
+    np.testing.assert_allclose(w[ok], ref["topk_w"][ok], rtol=2e-5, atol=1e-6)
+    # grouping is fixed exactly by the GPU's own top-k
+    flat = idx.ravel()
+    cnt = np.bincount(flat, minlength=E)
+    assert np.array_equal(out["expert_count"].cpu().numpy(), cnt)
+    assert np.array_equal(out["expert_offset"].cpu().numpy(), np.concatenate([[0], np.cumsum(cnt)]))
+    assert np.array_equal(out["pair_by_expert"].cpu().numpy(), np.argsort(flat, kind="stable"))
+    say(f"{what}: near-ties {int(near.sum())}/{len(near)}")
+
+
+@pytest.mark.parametrize("T,d,E,k,renorm,xdt,zipf,xscale", [
+    (1, 4096, 8, 2, True, "f16", False, 1 / 64),
+    (16, 4096, 8, 2, True, "f16", False, 1 / 64),
+    (64, 2048, 64, 6, True, "f16", True, 1.0),
+    (256, 6144, 8, 2, True, "bf16", False, 1 / 64),
+    (33, 512, 16, 4, False, "f32", False, 1.0),
+    (5, 256, 7, 7, True, "f16", False, 1.0),
+    (300, 1024, 128, 8, True, "f16", True, 1.0),
+])
+def test_router(T, d, E, k, renorm, xdt, zipf, xscale):
+    xf = synth.tokens_f32(50, T, d, xscale, layer=E)
+    Rf = synth.router_f32(50, E, E, d)
+    x_bits = xf if xdt == "f32" else synth.to_bits(xf, xdt)
+    rdt = "bf16" if xdt == "bf16" else "f16"
+    R_bits = synth.to_bits(Rf, rdt)
+    bias = synth.zipf_bias(5, E, E, 1.1) if zipf else None
+    x = torch.from_numpy(xf).to(DEV) if xdt == "f32" else to_dev_bits(x_bits, xdt)
+    R = to_dev_bits(R_bits, rdt)
+    b = None if bias is None else torch.from_numpy(bias).to(DEV)
+    out = moe.route_topk(x, R, k, renormalize=renorm, bias=b, logits=True)
+    torch.cuda.synchronize()
+    check_route(x_bits, xdt, R_bits, rdt, E, k, renorm, bias, out, f"router T={T} E={E} k={k}")
+
+
+def test_router_exact_ties_lowest_index():
+    T, d, E, k = 9, 512, 8, 3
+    Rf = synth.router_f32(51, 0, E, d)
+    Rf[5] = Rf[2]
+    Rf[7] = Rf[0]
+    Rf[6] = Rf[2]
+    x_bits = synth.to_f16_bits(synth.tokens_f32(52, T, d, 1.0))
+    R_bits = synth.to_f16_bits(Rf)
+    out = moe.route_topk(to_dev_bits(x_bits, "f16"), to_dev_bits(R_bits, "f16"), k, logits=True)
+    torch.cuda.synchronize()
+    lg = out["logits"].cpu().numpy()
+    assert np.array_equal(lg[:, 5], lg[:, 2]) and np.array_equal(lg[:, 6], lg[:, 2])
+    check_route(x_bits, "f16", R_bits, "f16", E, k, True, None, out, "router ties")
+    idx = out["topk_idx"].cpu().numpy()
+    for t in range(T):
+        row = list(idx[t])
+        for a, b in ((2, 5), (2, 6), (5, 6), (0, 7)):
+            if a in row and b in row:
+                assert row.index(a) < row.index(b)
+
+
+# ------------------------------------------------------------------ small layers
+
+def build_host_layer(cfg, E, S, d, f, wdt, sparsity, xscale, layer=0):
+    experts = [HostExpert(cfg, layer, e, d, f, wdt=wdt) for e in range(E + S)]
+    thr = np.array([hx.calibrate(cfg, xscale, sparsity, layer, e) for e, hx in enumerate(experts)],
+                   dtype=np.float32)
+    return experts, thr
+
+
+def device_layer(experts, thr, R_bits, rdt, E, S, k, renorm=True, bias=None, dense=False):
+    wdt = experts[0].wdt
+    d, f = experts[0].d, experts[0].f
+    up_q = torch.from_numpy(np.stack([h.up_q for h in experts])).to(DEV)
+    up_sz = torch.from_numpy(np.stack([h.up_sz for h in experts]).view(np.int16)).to(DEV)
+    gate = to_dev_bits(np.stack([h.gate for h in experts]), wdt)
+    down = to_dev_bits(np.stack([h.down for h in experts]), wdt)
+    L = moe.Layer(d=d, f=f, E=E, S=S, k=k, renormalize=renorm, router_w=to_dev_bits(R_bits, rdt),
+                  up_q=up_q, up_sz=up_sz, gate_t=gate, down=down,
+                  thresholds=torch.from_numpy(thr).to(DEV),
+                  router_bias=None if bias is None else torch.from_numpy(bias).to(DEV))
+    if dense:
+        L.up_dense = torch.empty((E + S, f, d), dtype=torch.bfloat16, device=DEV)
+        for e in range(E + S):
+            moe.materialize_up_bf16(up_q[e], up_sz[e], d, out=L.up_dense[e])
+    return L
+
+
+def run_layer(L, x, path, want_masks=True):
+    T = x.shape[0]
+    tr = dict(topk_idx=torch.empty((T, L.k), dtype=torch.int32, device=DEV),
+              topk_w=torch.empty((T, L.k), dtype=torch.float32, device=DEV),
+              logits=torch.empty((T, L.E), dtype=torch.float32, device=DEV),
+              expert_count=torch.empty(L.E, dtype=torch.int32, device=DEV))
+    if want_masks and path == moe.PATH_SPARSE:
+        tr["masks"] = torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=DEV)
+    y = moe.layer_forward(L, x, path=path, trace=tr)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in tr.items()}
+
+
+def oracle_layer_check(experts, thr, R_bits, rdt, bias, E, S, k, x_bits, y, tr, tokens, dense,
+                       what, renorm=True):
+    wdt = experts[0].wdt
+    sub = x_bits[tokens]
+    uq = np.stack([h.up_q for h in experts])
+    us = np.stack([h.up_sz for h in experts])
+    g = np.stack([h.gate for h in experts])
+    dn = np.stack([h.down for h in experts])
+    masks_in = None if dense else tr["masks"][tokens]
+    y_ref, idx_ref, w_ref, m_ref = oracle.layer_forward(
+        sub, wdt, R_bits, rdt, bias, E, k, S, renorm, uq, us, g, dn, wdt, thr, dense=dense,
+        topk_in=tr["topk_idx"][tokens], masks_in=masks_in)
+    np.testing.assert_allclose(tr["topk_w"][tokens], w_ref, rtol=2e-5, atol=1e-6)
+    if not dense:
+        # masks against the oracle's own v: recompute per (token, slot)
+        for i, t in enumerate(tokens):
+            for s in range(k + S):
+                e = tr["topk_idx"][t, s] if s < k else E + (s - k)
+                v_ref, _, _ = experts[e].oracle_forward(x_bits[t:t + 1], thr[e])
+                check_mask(tr["masks"][t, s][None], v_ref, thr[e], f"{what} t={t} slot={s}")
+    err = check_y(y[tokens], y_ref, 2e-3, what)
+    say(f"{what}: tokens {list(tokens)} max relL2={err:.2e}")
+
+
+@pytest.mark.parametrize("T,E,S,k,d,f", [(5, 6, 2, 2, 512, 256), (1, 8, 0, 2, 1024, 512),
+                                         (12, 4, 1, 4, 2048, 320)])
+def test_small_layer_sparse(T, E, S, k, d, f):
+    experts, thr = build_host_layer(60, E, S, d, f, "f16", 0.7, 1.0, layer=d)
+    R_bits = synth.to_f16_bits(synth.router_f32(60, d, E, d))
+    x_bits = synth.to_f16_bits(synth.tokens_f32(61, T, d, 1.0, layer=d))
+    L = device_layer(experts, thr, R_bits, "f16", E, S, k)
+    y, tr = run_layer(L, to_dev_bits(x_bits, "f16"), moe.PATH_SPARSE)
+    check_route(x_bits, "f16", R_bits, "f16", E, k, True, None,
+                {"topk_idx": torch.from_numpy(tr["topk_idx"]), "topk_w": torch.from_numpy(tr["topk_w"]),
+                 "logits": torch.from_numpy(tr["logits"]),
+                 "expert_count": torch.from_numpy(tr["expert_count"]),
+                 "expert_offset": torch.from_numpy(np.concatenate([[0], np.cumsum(tr["expert_count"])])),
+                 "pair_by_expert": torch.from_numpy(np.argsort(tr["topk_idx"].ravel(), kind="stable"))},
+                f"layer router T={T}")
+    oracle_layer_check(experts, thr, R_bits, "f16", None, E, S, k, x_bits, y, tr, np.arange(T),
+                       False, f"sparse layer T={T} E={E}+{S} k={k} d={d} f={f}")
+
+
+@pytest.mark.parametrize("T,E,S,k,d,f", [(150, 4, 0, 2, 512, 512), (9, 6, 1, 2, 1024, 256)])
+def test_small_layer_dense(T, E, S, k, d, f):
+    experts, thr = build_host_layer(62, E, S, d, f, "bf16", 0.7, 1 / 16, layer=d)
+    R_bits = synth.to_bf16_bits(synth.router_f32(62, d, E, d))
+    x_bits = synth.to_bf16_bits(synth.tokens_f32(63, T, d, 1 / 16, layer=d))
+    L = device_layer(experts, thr, R_bits, "bf16", E, S, k, dense=True)
+    y, tr = run_layer(L, to_dev_bits(x_bits, "bf16"), moe.PATH_DENSE)
+    tokens = np.arange(T) if T <= 16 else np.array([0, 1, 63, 64, 100, T - 1])
+    oracle_layer_check(experts, thr, R_bits, "bf16", None, E, S, k, x_bits, y, tr, tokens, True,
+                       f"dense layer T={T} E={E}+{S} k={k} d={d} f={f}")
+
+
+def test_layer_repeatable_and_workspace_clean():
+    T, E, S, k, d, f = 7, 8, 1, 2, 512, 128
+    experts, thr = build_host_layer(64, E, S, d, f, "f16", 0.6, 1.0)
+    R_bits = synth.to_f16_bits(synth.router_f32(64, 0, E, d))
+    x = to_dev_bits(synth.to_f16_bits(synth.tokens_f32(65, T, d, 1.0)), "f16")
+    L = device_layer(experts, thr, R_bits, "f16", E, S, k)
+    ws = moe.new_workspace(L.workspace_bytes(T))
+    masks = []
+    for _ in range(3):
+        tr = dict(masks=torch.empty((T, k + S, f), dtype=torch.uint8, device=DEV))
+        y = moe.layer_forward(L, x, trace=tr, ws=ws)
+        torch.cuda.synchronize()
+        masks.append(tr["masks"].cpu().numpy())
+    assert all(np.array_equal(masks[0], m) for m in masks[1:])
+    # the accumulator and counters are zero again after every call
+    lw = moe.workspace_size(moe.OP_LAYER, T, d, f, E, k, S)
+    assert ws.numel() >= lw
