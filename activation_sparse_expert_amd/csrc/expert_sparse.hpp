@@ -39,50 +39,76 @@ struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
 template <>
 struct Log2<1> { static constexpr int v = 0; };
 
+// Decode constants: `mask` keeps the two mantissa bits that make (1 + q/4) in
+// each 16-bit half (bits 8-9 for fp16, 5-6 for bf16), `one` is the packed 1.0.
+// They reach the kernel as arguments so that they sit in scalar registers: the
+// compiler can then use one v_and_or_b32 per pair (gfx9 VOP3 encodings take no
+// literal operands).
+struct DecodeConst {
+    uint32_t mask, one;
+};
+
+template <bool BF16>
+__host__ __device__ constexpr DecodeConst decode_const()
+{
+    return BF16 ? DecodeConst{0x00600060u, 0x3F803F80u} : DecodeConst{0x03000300u, 0x3C003C00u};
+}
+
+// (a & mask) | one in one VALU instruction; mask and one are wave-uniform.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t one)
+{
+    uint32_t r;
+    // one scalar operand at most (constant bus): `one` is kept in a vector register
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(one));
+    return r;
+}
+
 // Compile-time shift that moves code slot m (bits 2m of each half-word) to the
-// two mantissa bits that make (1 + q/4): bits 8-9 (fp16) or 5-6 (bf16).
+// two mantissa bits that make (1 + q/4).
 template <bool BF16, int M>
-__device__ __forceinline__ uint32_t pair_word(uint32_t w)
+__device__ __forceinline__ uint32_t pair_word(uint32_t w, uint32_t mask, uint32_t one)
 {
     constexpr int target = BF16 ? 5 : 8;
     constexpr int sh = target - 2 * M;
-    constexpr uint32_t mask = BF16 ? 0x00600060u : 0x03000300u;
-    constexpr uint32_t one = BF16 ? 0x3F803F80u : 0x3C003C00u;
     uint32_t t;
     if constexpr (sh > 0) t = w << sh;
     else if constexpr (sh < 0) t = w >> (-sh);
     else t = w;
-    return (t & mask) | one;
+    return and_or(t, mask, one);
 }
 
 template <bool BF16>
-__device__ __forceinline__ void decode_unit(const uint4 &c, uint32_t (&p)[32])
+__device__ __forceinline__ void decode_unit(const uint4 &c, uint32_t (&p)[32], uint32_t mask,
+                                            uint32_t one)
 {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        p[8 * i + 0] = pair_word<BF16, 0>(w[i]);
-        p[8 * i + 1] = pair_word<BF16, 1>(w[i]);
-        p[8 * i + 2] = pair_word<BF16, 2>(w[i]);
-        p[8 * i + 3] = pair_word<BF16, 3>(w[i]);
-        p[8 * i + 4] = pair_word<BF16, 4>(w[i]);
-        p[8 * i + 5] = pair_word<BF16, 5>(w[i]);
-        p[8 * i + 6] = pair_word<BF16, 6>(w[i]);
-        p[8 * i + 7] = pair_word<BF16, 7>(w[i]);
+        p[8 * i + 0] = pair_word<BF16, 0>(w[i], mask, one);
+        p[8 * i + 1] = pair_word<BF16, 1>(w[i], mask, one);
+        p[8 * i + 2] = pair_word<BF16, 2>(w[i], mask, one);
+        p[8 * i + 3] = pair_word<BF16, 3>(w[i], mask, one);
+        p[8 * i + 4] = pair_word<BF16, 4>(w[i], mask, one);
+        p[8 * i + 5] = pair_word<BF16, 5>(w[i], mask, one);
+        p[8 * i + 6] = pair_word<BF16, 6>(w[i], mask, one);
+        p[8 * i + 7] = pair_word<BF16, 7>(w[i], mask, one);
     }
 }
 
-// sum_k x_k (1 + q_k/4) over one 64-input group: 32 packed dot products
+// sum_k x_k (1 + q_k/4) over one 64-input group: 32 packed dot products in four
+// independent chains
 template <bool BF16>
 __device__ __forceinline__ float group_dot(const uint32_t (&pw)[32], const uint32_t (&xp)[32])
 {
-    float a0 = 0.f, a1 = 0.f;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-    for (int m = 0; m < 32; m += 2) {
+    for (int m = 0; m < 32; m += 4) {
         a0 = dot2<BF16>(pw[m], xp[m], a0);
         a1 = dot2<BF16>(pw[m + 1], xp[m + 1], a1);
+        a2 = dot2<BF16>(pw[m + 2], xp[m + 2], a2);
+        a3 = dot2<BF16>(pw[m + 3], xp[m + 3], a3);
     }
-    return a0 + a1;
+    return (a0 + a1) + (a2 + a3);
 }
 
 // Transposed butterfly over the SEG lanes of a segment: on entry every lane
@@ -242,43 +268,74 @@ expert_kernel(SparseArgs a)
     const int passes = (nrows + ROWS_PASS - 1) / ROWS_PASS;
     const int CPR = d / 8;                          // 16-byte chunks per d-row
 
+    // phase-A code units of one block of PR passes: loads only, no use
+    uint4 cq[PR][NG];
+    uint32_t csz[PR][NG];
+    uint32_t okm = 0;
+    auto load_block = [&](int p0) {
+        okm = 0;
+#pragma unroll
+        for (int p = 0; p < PR; ++p) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int r = (p0 + p) * ROWS_PASS + wave * RPW + rs;
+                const int g = go + SEG * gi;
+                const bool ok = r < nrows && g < G;
+                const int rr = ok ? r : 0, gg = ok ? g : 0;
+                cq[p][gi] = *(const uint4 *)(upq + (size_t)rr * (d / 4) + (size_t)gg * 16);
+                csz[p][gi] = *(const uint32_t *)(upsz + ((size_t)rr * G + gg) * 2);
+                okm |= (ok ? 1u : 0u) << (p * NG + gi);
+            }
+        }
+    };
+
+    // 16-byte x chunks each thread stages per token chunk
+    constexpr int XL = (TB * 8 * SEG * NG + THREADS - 1) / THREADS;
+
     for (int t0 = 0; t0 < ntok; t0 += TB) {
         const int nt = min(TB, ntok - t0);
 
-        // ---- token bookkeeping and x staging ------------------------------
+        // ---- token bookkeeping (small loads, before the streams start) --------
         if (tid < TB) {
             int t = 0, sl = 0, row = 0;
-            float sc = 0.f;
             if (tid < nt) {
                 if (!a.layer) {
                     t = t0 + tid;
                     row = t;
-                    sc = a.token_scale ? a.token_scale[t] : 1.0f;
                 } else if (shared_slot) {
                     t = t0 + tid;
                     sl = a.k + slot;
                     row = a.T * a.k + slot * a.T + t;
-                    sc = 1.0f;
                 } else {
                     const int pos = pair0 + t0 + tid;
                     const int p = a.pairs[pos];
                     t = p / a.k;
                     sl = p - t * a.k;
                     row = pos;
-                    sc = a.topk_w[p];
                 }
             }
             L.tok_t[tid] = t;
             L.tok_slot[tid] = sl;
             L.tok_row[tid] = row;
-            L.tok_sc[tid] = sc;
         }
         __syncthreads();
-        for (int i = tid; i < TB * CPR; i += THREADS) {
+
+        // ---- x loads, then the up-code loads; only x is waited for here -------
+        uint4 xl[XL];
+#pragma unroll
+        for (int u = 0; u < XL; ++u) {
+            const int i = tid + u * THREADS;
             const int tb = i / CPR, c = i - tb * CPR;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (tb < nt) v = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
-            *(uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8) = v;
+            xl[u] = make_uint4(0, 0, 0, 0);
+            if (i < TB * CPR && tb < nt) xl[u] = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
+        }
+        load_block(0);          // up codes do not depend on x: in flight while x is staged
+#pragma unroll
+        for (int u = 0; u < XL; ++u) {
+            const int i = tid + u * THREADS;
+            const int tb = i / CPR, c = i - tb * CPR;
+            if (i < TB * CPR)
+                *(uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8) = xl[u];
         }
         __syncthreads();
         for (int i = tid; i < TB * G; i += THREADS) {
@@ -316,21 +373,9 @@ expert_kernel(SparseArgs a)
             }
         }
         for (int p0 = 0; p0 < passes; p0 += PR) {
-            uint4 cq[PR][NG];
-            uint32_t csz[PR][NG];
-#pragma unroll
-            for (int p = 0; p < PR; ++p) {
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    const int r = (p0 + p) * ROWS_PASS + wave * RPW + rs;
-                    const int g = go + SEG * gi;
-                    const bool ok = r < nrows && g < G;
-                    const int rr = ok ? r : 0, gg = ok ? g : 0;
-                    cq[p][gi] = *(const uint4 *)(upq + (size_t)rr * (d / 4) + (size_t)gg * 16);
-                    const uint32_t w = *(const uint32_t *)(upsz + ((size_t)rr * G + gg) * 2);
-                    csz[p][gi] = ok ? w : 0u;           // s = 0: the unit contributes nothing
-                }
-            }
+            if (p0 > 0) load_block(p0);
+            // units outside the tile (ok bit clear) get s = 0 when used: the select
+            // is kept away from the loads so that they all issue back to back
             float part[TB][PR];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
@@ -338,11 +383,13 @@ expert_kernel(SparseArgs a)
                 for (int p = 0; p < PR; ++p) part[tb][p] = 0.f;
 #pragma unroll
             for (int p = 0; p < PR; ++p) {
+                if (p0 + p >= passes) continue;         // uniform: padding passes of the block
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     uint32_t pw[32];
-                    decode_unit<BF16>(cq[p][gi], pw);
-                    const float s = half_bits_to_float(csz[p][gi] & 0xFFFFu);
+                    decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
+                    const bool ok = (okm >> (p * NG + gi)) & 1u;
+                    const float s = ok ? half_bits_to_float(csz[p][gi] & 0xFFFFu) : 0.f;
                     const float z = half_bits_to_float(csz[p][gi] >> 16);
                     const int g = min(go + SEG * gi, G - 1);
 #pragma unroll
@@ -505,7 +552,12 @@ expert_kernel(SparseArgs a)
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             if (tb >= nt) continue;
-            const float sc = L.tok_sc[tb];
+            float sc = 1.0f;                            // router weight / caller's scale
+            if (!a.layer) {
+                if (a.token_scale) sc = a.token_scale[t0 + tb];
+            } else if (!shared_slot) {
+                sc = a.topk_w[a.pairs[pair0 + t0 + tb]];
+            }
             float *dst = a.part + ((size_t)L.tok_row[tb] * a.tiles + tile) * d;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
@@ -529,12 +581,15 @@ hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
     size_t off[11];
     const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off);
     auto kern = expert_kernel<BF16, TB, GEO>;
+    SparseArgs args = a;
+    args.dec_mask = decode_const<BF16>().mask;
+    args.dec_one = decode_const<BF16>().one;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.slots * a.tiles), dim3(GEO::THREADS), lds, s, a);
+    hipLaunchKernelGGL(kern, dim3(a.slots * a.tiles), dim3(GEO::THREADS), lds, s, args);
     return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@ namespace moeffn {
 
 // Everything the sparse expert kernel needs, passed by value.
 struct SparseArgs {
+    uint32_t dec_mask, dec_one;         // INT2 decode constants (set by the launcher)
     int d, f;
     int cpw;                            // channels per workgroup tile
     int tiles;                          // workgroups per expert

@@ -13,18 +13,21 @@ namespace moeffn {
 namespace {
 
 constexpr int kRedThreads = 256;
-constexpr int kGroups = 16;             // contribution groups per 64 columns
-constexpr int kBatch = 16;              // loads in flight per thread
+constexpr int kCols = 16;               // output columns per workgroup (4 threads x float4)
+constexpr int kGroups = kRedThreads / 4;  // contribution groups per workgroup
+constexpr int kBatch = 8;               // loads in flight per thread
 
+// One workgroup per (token, 16 columns): about d/16 * T workgroups, so the
+// partial rows are read by many compute units at once.
 __global__ void __launch_bounds__(kRedThreads)
 reduce_kernel(ReduceArgs a)
 {
-    __shared__ float4 sm[kGroups][16];
-    const int cblocks = a.d / 64;
+    __shared__ float4 sm[kGroups][4];
+    const int cblocks = a.d / kCols;
     const int t = blockIdx.x / cblocks;
     const int cb = blockIdx.x - t * cblocks;
-    const int cq = threadIdx.x & 15, tg = threadIdx.x >> 4;
-    const int col = cb * 64 + cq * 4;
+    const int cq = threadIdx.x & 3, tg = threadIdx.x >> 2;
+    const int col = cb * kCols + cq * 4;
     const int n = a.rows_per_tok * a.tiles;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     // kBatch loads in flight per thread, then added in order
@@ -68,8 +71,8 @@ reduce_kernel(ReduceArgs a)
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
-    if (a.d % 64 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(reduce_kernel, dim3(a.T * (a.d / 64)), dim3(kRedThreads), 0, s, a);
+    if (a.d % kCols != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(reduce_kernel, dim3(a.T * (a.d / kCols)), dim3(kRedThreads), 0, s, a);
     return hipGetLastError();
 }
 
