@@ -13,13 +13,25 @@ resident.  Inputs are resident in HBM before the timed region starts; the K
 launches are captured once in a HIP graph and replayed, so the host's launch
 overhead is not what is measured.
 
-Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the path runs on one GPU.
+
+``roofline.achieved`` is the algorithmic bytes of a call (INT2 up codes, fp16
+scales and zeros, x, y, and the gate and down rows of the channels the mask
+selects, counted from an identical untimed pass) divided by the event-timed
+duration of the whole call, i.e. of both of its kernels.  ``roofline.traffic``
+is the HBM traffic per call that rocprofv3 counted (FETCH_SIZE + WRITE_SIZE of
+both kernels, each scaled by what the same counter reads for an elementwise
+kernel of known size, ``--copy-probe``); it is read from the committed
+counter summary and reported only while the kernel sources it was taken on
+are unchanged (their SHA-256 is recorded there), else null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +44,9 @@ METRIC = "expert-FFN tokens/s + achieved HBM GB/s (d=4096,f=14336, 90% sparse, b
 HBM_PEAK_GBS = 8000.0
 D, F = 4096, 14336
 NTOK = 16
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_expert_sparse_mixtral_b1_s90.md")
+KERNEL_SOURCES = ["expert_sparse.hpp", "expert_sparse_f16.hip", "reduce.hip", "internal.hpp",
+                  "device.hpp", "api.cpp"]
 
 
 def log(*a):
@@ -60,6 +75,41 @@ def build_instances(R, sparsity, dev):
         ex.threshold = float(np.float32(np.quantile(np.abs(v.cpu().numpy()).ravel(), sparsity)))
         experts.append(ex)
     return experts
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "activation_sparse_expert_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic():
+    """HBM bytes per call from the committed counter summary, or None when
+    there is none or the kernels changed since it was taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_call:\s*([0-9]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sources_sha():
+        return None
+    return int(val.group(1))
+
+
+def copy_probe(mib):
+    """Elementwise kernel of known size for scaling FETCH_SIZE / WRITE_SIZE:
+    out = -src over `mib` MiB of fp32 (reads and writes exactly that much)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "kernel": "neg (elementwise)", "launches": 10}), flush=True)
 
 
 def cpu_baseline(sparsity, budget_s):
@@ -98,11 +148,17 @@ def main():
     ap.add_argument("--sparsity", type=float, default=0.9)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run the known-size elementwise kernel (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the expert path here runs on a single MI355X "
               "and has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     import activation_sparse_expert_amd as moe
@@ -184,7 +240,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": counted_traffic(),
         },
     }
     if not args.no_cpu:

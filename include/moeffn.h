@@ -36,15 +36,19 @@
  * a fixed per-expert stride in each of these four arrays.
  *
  * Constraints checked on the host before anything is enqueued:
- *   d % 512 == 0 or d in {64,128,256};  f % 64 == 0;  T >= 1;
+ *   d a power of two from 64 to 2048, or a multiple of 512 from 4096 to 16384;
+ *   f % 64 == 0;  T >= 1;
  *   activations and gate/down weights have the same 16-bit type (fp16 or bf16);
  *   16-byte aligned up_q/gate_t/down/x and 4-byte aligned up_sz.
  *
  * Workspace: every forward call takes a device workspace of at least
- * moe_workspace_size(...) bytes.  It must be zero-filled before its first use
- * (moe_workspace_init, or a zero-initialised tensor); each call returns it to
- * all-zero before its kernels finish.  Calls that share a workspace must be
- * ordered (same stream); overlapping calls need distinct workspaces.
+ * moe_workspace_size(...) bytes (fp32 partial rows, routing tables and a
+ * completion counter).  Its first 256 bytes must be zero before its first use
+ * by moe_route_topk or moe_layer_forward (moe_workspace_init, or a
+ * zero-initialised tensor); those calls leave the counter at zero again when
+ * their kernels finish.  moe_expert_forward_sparse needs no initialisation.
+ * Calls that share a workspace must be ordered (same stream); overlapping calls
+ * need distinct workspaces.
  *
  * Execution: calls are asynchronous on `stream` (a hipStream_t passed as void*,
  * NULL = the null stream).  Forward calls do no host synchronisation and no
@@ -54,9 +58,10 @@
  * Errors: invalid arguments return a negative moe_status and enqueue nothing;
  * a failed kernel launch returns MOE_ERR_HIP.  No C++ exception crosses the ABI.
  *
- * Determinism: routing, grouping, masks and v are bit-reproducible.  y is
- * accumulated across workgroups with fp32 atomics, so its last bits may vary
- * from run to run.
+ * Determinism: routing, grouping, masks, v and y are bit-reproducible for the
+ * same inputs and shapes.  Each workgroup writes its share of y as an fp32
+ * partial row and a second kernel sums the partial rows in a fixed order; no
+ * floating-point atomics are used.
  */
 #ifndef MOEFFN_H
 #define MOEFFN_H

@@ -103,3 +103,179 @@ def check_y(y_gpu, y_ref, tol=REL_L2, what=""):
     e = rel_l2_rows(y_gpu, y_ref)
     assert e.max() <= tol, f"{what}: max relative L2 {e.max():.3e} > {tol}"
     return float(e.max())
+
+
+def check_route(x_bits, xdt, R_bits, rdt, E, k, renorm, bias, out, what):
+    """Top-k bit-exact against the oracle except at fp32-vs-fp64 near-ties,
+    where it must equal the stable top-k of the GPU's own fp32 logits."""
+    ref = oracle.route_topk(x_bits, xdt, R_bits, rdt, E, k, renormalize=renorm, bias=bias)
+    idx = out["topk_idx"].cpu().numpy()
+    lg = out["logits"].cpu().numpy().astype(np.float64)
+    X = bits_to_f64(x_bits, xdt) if xdt != "f32" else np.asarray(x_bits, np.float64)
+    Rm = bits_to_f64(R_bits, rdt) if rdt != "f32" else np.asarray(R_bits, np.float64)
+    mag = np.abs(X) @ np.abs(Rm).T                     # sum_k |x_k R_ek|
+    L = ref["logits"]
+    srt = np.sort(L, axis=1)[:, ::-1]
+    gap = srt[:, k - 1] - (srt[:, k] if k < E else -np.inf)
+    near = gap <= 2.0 ** -16 * mag.max(axis=1)
+    own = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+    for t in range(idx.shape[0]):
+        if near[t]:
+            assert np.array_equal(idx[t], own[t]), f"{what}: token {t} near-tie"
+        else:
+            assert np.array_equal(idx[t], ref["topk_idx"][t]), f"{what}: token {t}"
+    np.testing.assert_allclose(lg, L, rtol=1e-4, atol=1e-5 * mag.max())
+    w = out["topk_w"].cpu().numpy()
+    ok = ~near
+    np.testing.assert_allclose(w[ok], ref["topk_w"][ok], rtol=2e-5, atol=1e-6)
+    # grouping is fixed exactly by the GPU's own top-k
+    flat = idx.ravel()
+    cnt = np.bincount(flat, minlength=E)
+    assert np.array_equal(out["expert_count"].cpu().numpy(), cnt)
+    assert np.array_equal(out["expert_offset"].cpu().numpy(), np.concatenate([[0], np.cumsum(cnt)]))
+    assert np.array_equal(out["pair_by_expert"].cpu().numpy(), np.argsort(flat, kind="stable"))
+    say(f"{what}: near-ties {int(near.sum())}/{len(near)}")
+
+
+def run_layer(L, x, path, want_masks=True):
+    T = x.shape[0]
+    tr = dict(topk_idx=torch.empty((T, L.k), dtype=torch.int32, device=DEV),
+              topk_w=torch.empty((T, L.k), dtype=torch.float32, device=DEV),
+              logits=torch.empty((T, L.E), dtype=torch.float32, device=DEV),
+              expert_count=torch.empty(L.E, dtype=torch.int32, device=DEV))
+    if want_masks and path == moe.PATH_SPARSE:
+        tr["masks"] = torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=DEV)
+    y = moe.layer_forward(L, x, path=path, trace=tr)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in tr.items()}
+
+
+# ---------------------------------------------------------------------------
+# Full-size layers generated on the device.  torch draws the weights; the INT2
+# bytes come from the library's packer, which the tests hold bit-exact against
+# the oracle's packer on every expert the oracle later reads, so the oracle is
+# always fed its own packing of the same fp32 draws.
+# ---------------------------------------------------------------------------
+
+def device_draws(cfg, layer, e, d, f, wdt, std=0.02):
+    """(gate_t, up_t fp32, down) drawn on the device for one expert."""
+    g = synth.device_normal(synth.seed_of(cfg, layer, e, synth.T_GATE), (f, d), std, DEV,
+                            TORCH_DT[wdt])
+    u = synth.device_normal(synth.seed_of(cfg, layer, e, synth.T_UP), (f, d), std, DEV)
+    dn = synth.device_normal(synth.seed_of(cfg, layer, e, synth.T_DOWN), (f, d), std, DEV,
+                             TORCH_DT[wdt])
+    return g, u, dn
+
+
+def torch_dequant(up_q, up_sz, d):
+    """fp32 [f][d] = s (q - z) from the INT2 bytes, in torch on the device
+    (calibration only).  Word i of a row holds input 16i+2m+h at bits 16h+2m."""
+    f = up_q.shape[0]
+    w = up_q.view(torch.int32).reshape(f, d // 16, 1)
+    j = torch.arange(16, device=up_q.device, dtype=torch.int32)
+    shift = 16 * (j % 2) + 2 * (j // 2)
+    q = ((w >> shift) & 3).reshape(f, d).float()
+    sz = up_sz.view(torch.float16).float()
+    s = sz[..., 0].repeat_interleave(64, dim=1)
+    z = sz[..., 1].repeat_interleave(64, dim=1)
+    return s * (q - z)
+
+
+def torch_threshold(up_q, up_sz, cfg, layer, e, d, wdt, xscale, sparsity):
+    """Threshold at the `sparsity` quantile of |x_c . w'| over the 64 seeded
+    calibration vectors, w' the dequantised INT2 up weights (torch fp32).  It
+    only places the realised sparsity; parity never depends on it."""
+    xc = torch.from_numpy(synth.calibration_f32(cfg, d, xscale, layer, e)).to(TORCH_DT[wdt])
+    v = xc.to(DEV).float() @ torch_dequant(up_q, up_sz, d).T
+    return oracle.calibrate_threshold(v.abs().cpu().numpy(), sparsity)
+
+
+class DeviceLayer:
+    """E routed + S shared experts of one layer, stacked on the device."""
+
+    def __init__(self, cfg, layer, E, S, k, d, f, wdt, xscale, sparsity, router_std=0.02,
+                 bias=None, dense=False):
+        self.cfg, self.layer, self.E, self.S, self.k = cfg, layer, E, S, k
+        self.d, self.f, self.wdt = d, f, wdt
+        n = E + S
+        up_q = torch.empty((n, f, d // 4), dtype=torch.uint8, device=DEV)
+        up_sz = torch.empty((n, f, d // 64, 2), dtype=torch.int16, device=DEV)
+        gate = torch.empty((n, f, d), dtype=TORCH_DT[wdt], device=DEV)
+        down = torch.empty((n, f, d), dtype=TORCH_DT[wdt], device=DEV)
+        thr = np.zeros(n, dtype=np.float32)
+        for e in range(n):
+            g, u, dn = device_draws(cfg, layer, e, d, f, wdt)
+            gate[e].copy_(g)
+            down[e].copy_(dn)
+            del g, dn
+            moe.pack_up_int2(u, up_q=up_q[e], up_sz=up_sz[e])
+            del u
+            thr[e] = torch_threshold(up_q[e], up_sz[e], cfg, layer, e, d, wdt, xscale,
+                                     sparsity)
+        self.thr = thr
+        self.R_bits = synth.to_bits(synth.router_f32(cfg, layer, E, d, router_std), wdt)
+        self.bias = bias
+        self.L = moe.Layer(d=d, f=f, E=E, S=S, k=k, renormalize=True,
+                           router_w=to_dev_bits(self.R_bits, wdt), up_q=up_q, up_sz=up_sz,
+                           gate_t=gate, down=down, thresholds=torch.from_numpy(thr).to(DEV),
+                           router_bias=None if bias is None else torch.from_numpy(bias).to(DEV))
+        if dense:
+            self.L.up_dense = torch.empty((n, f, d), dtype=torch.bfloat16, device=DEV)
+            for e in range(n):
+                moe.materialize_up_bf16(up_q[e], up_sz[e], d, out=self.L.up_dense[e])
+        torch.cuda.synchronize()
+
+    def host_weights(self, experts):
+        """Host copies for the oracle: the oracle's own INT2 packing of the
+        regenerated fp32 up draws (asserted bit-exact against the device
+        packing) and the gate/down bit patterns.  Experts not listed are left
+        zero; the oracle reads only the experts it is fed."""
+        n = self.E + self.S
+        d, f = self.d, self.f
+        uq = np.zeros((n, f, d // 4), np.uint8)
+        us = np.zeros((n, f, d // 64, 2), np.uint16)
+        g = np.zeros((n, f, d), np.uint16)
+        dn = np.zeros((n, f, d), np.uint16)
+        for e in sorted(set(int(x) for x in experts)):
+            _, u, _ = device_draws(self.cfg, self.layer, e, d, f, self.wdt)
+            q_ref, sz_ref = oracle.pack_up_int2(u.cpu().numpy())
+            del u
+            assert np.array_equal(self.L.up_q[e].cpu().numpy(), q_ref), f"pack codes e={e}"
+            assert np.array_equal(self.L.up_sz[e].cpu().numpy().view(np.uint16), sz_ref), \
+                f"pack scales e={e}"
+            uq[e], us[e] = q_ref, sz_ref
+            g[e] = dev_bits(self.L.gate_t[e])
+            dn[e] = dev_bits(self.L.down[e])
+        return uq, us, g, dn
+
+    def free(self):
+        self.L = None
+        torch.cuda.empty_cache()
+
+
+def check_layer_tokens(lay: DeviceLayer, x_bits, y, tr, tokens, dense, what):
+    """Oracle check of a layer's output on the listed tokens, fed the GPU's
+    top-k (and masks on the sparse path); each mask against the oracle's v."""
+    k, S, E = lay.k, lay.S, lay.E
+    used = set(range(E, E + S))
+    for t in tokens:
+        used.update(int(e) for e in tr["topk_idx"][t])
+    uq, us, g, dn = lay.host_weights(used)
+    sub = x_bits[tokens]
+    masks_in = None if dense else tr["masks"][tokens]
+    y_ref, _, w_ref, _ = oracle.layer_forward(
+        sub, lay.wdt, lay.R_bits, lay.wdt, lay.bias, E, k, S, True, uq, us, g, dn, lay.wdt,
+        lay.thr, dense=dense, topk_in=tr["topk_idx"][tokens], masks_in=masks_in)
+    np.testing.assert_allclose(tr["topk_w"][tokens], w_ref, rtol=2e-5, atol=1e-6)
+    ndiff = 0
+    if not dense:
+        for i, t in enumerate(tokens):
+            for s in range(k + S):
+                e = int(tr["topk_idx"][t, s]) if s < k else E + (s - k)
+                v_ref, _, _ = oracle.expert_forward(x_bits[t:t + 1], lay.wdt, uq[e], us[e], g[e],
+                                                    dn[e], lay.wdt, np.inf)
+                ndiff += check_mask(tr["masks"][t, s][None], v_ref, lay.thr[e],
+                                    f"{what} t={t} slot={s}")
+    err = check_y(y[tokens], y_ref, REL_L2, what)
+    say(f"{what}: tokens {list(tokens)} band-diffs={ndiff} max relL2={err:.2e}")
+    return err

@@ -192,3 +192,45 @@ def test_workspace_init_and_reuse():
         torch.cuda.synchronize()
         for yy in ys:                   # the workspace stays usable call after call
             torch.testing.assert_close(yy, y_ref, rtol=1e-5, atol=1e-7)
+
+
+def test_mixtral_graph_replay_launch_config(mixtral):
+    """The benchmark's launch configuration: batch-1 calls at 90% sparsity
+    sharing one workspace, captured in a HIP graph and replayed.  Every replay
+    must reproduce the eager outputs bit for bit (the partial-row reduction
+    has a fixed order), and the eager outputs match the oracle."""
+    hx, thr, c = mixtral
+    ex = hx.to_device(thr[0.9])
+    x_bits = synth.to_f16_bits(synth.tokens_f32(synth.CFG_MIXTRAL, 6, c["d"], c["x_scale"],
+                                                tensor_id=synth.T_NOISE))
+    x = to_dev_bits(x_bits, "f16")
+    n = 12
+    ws = moe.new_workspace(moe.workspace_size(moe.OP_EXPERT, 1, hx.d, hx.f))
+    ys = torch.zeros((n, 1, hx.d), dtype=torch.float32, device=DEV)
+    masks = torch.zeros((n, 1, hx.f), dtype=torch.uint8, device=DEV)
+    for i in range(n):
+        moe.expert_forward_sparse(ex, x[i % 6:i % 6 + 1], y=ys[i], ws=ws, mask_out=masks[i])
+    torch.cuda.synchronize()
+    y_eager, m_eager = ys.cpu().numpy().copy(), masks.cpu().numpy().copy()
+    for i in (0, 5):
+        v_ref, _, _ = hx.oracle_forward(x_bits[i:i + 1], thr[0.9])
+        check_mask(m_eager[i], v_ref, thr[0.9], f"graph config token {i}")
+        _, _, y_ref = hx.oracle_forward(x_bits[i:i + 1], thr[0.9], mask_in=m_eager[i])
+        check_y(y_eager[i], y_ref, 2e-3, f"graph config token {i}")
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(n):
+            moe.expert_forward_sparse(ex, x[i % 6:i % 6 + 1], y=ys[i], ws=ws, mask_out=masks[i])
+    for rep in range(3):
+        ys.fill_(7.0)
+        masks.fill_(9)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        stream.synchronize()
+        assert np.array_equal(ys.cpu().numpy(), y_eager), f"replay {rep}"
+        assert np.array_equal(masks.cpu().numpy(), m_eager), f"replay {rep}"
+        # eager work on the same workspace between replays
+        moe.expert_forward_sparse(ex, x[3:4], y=ys[0], ws=ws)
+    say("graph replays reproduce the eager outputs bit for bit")

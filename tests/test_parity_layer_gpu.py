@@ -7,7 +7,7 @@ import torch
 import activation_sparse_expert_amd as moe
 import oracle
 import synth
-from gpu_helpers import (DEV, HostExpert, bits_to_f64, check_mask, check_y, dev_bits, say,
+from gpu_helpers import (DEV, HostExpert, check_mask, check_route, check_y, run_layer, say,
                          to_dev_bits)
 
 pytestmark = pytest.mark.gpu
@@ -22,36 +22,6 @@ def _gpu():
 
 # ------------------------------------------------------------------ router
 
-def check_route(x_bits, xdt, R_bits, rdt, E, k, renorm, bias, out, what):
-    """Top-k bit-exact against the oracle except at fp32-vs-fp64 near-ties,
-    where it must equal the stable top-k of the GPU's own fp32 logits."""
-    ref = oracle.route_topk(x_bits, xdt, R_bits, rdt, E, k, renormalize=renorm, bias=bias)
-    idx = out["topk_idx"].cpu().numpy()
-    lg = out["logits"].cpu().numpy().astype(np.float64)
-    X = bits_to_f64(x_bits, xdt) if xdt != "f32" else np.asarray(x_bits, np.float64)
-    Rm = bits_to_f64(R_bits, rdt) if rdt != "f32" else np.asarray(R_bits, np.float64)
-    mag = np.abs(X) @ np.abs(Rm).T                     # sum_k |x_k R_ek|
-    L = ref["logits"]
-    srt = np.sort(L, axis=1)[:, ::-1]
-    gap = srt[:, k - 1] - (srt[:, k] if k < E else -np.inf)
-    near = gap <= 2.0 ** -16 * mag.max(axis=1)
-    own = np.argsort(-lg, axis=1, kind="stable")[:, :k]
-    for t in range(idx.shape[0]):
-        if near[t]:
-            assert np.array_equal(idx[t], own[t]), f"{what}: token {t} near-tie"
-        else:
-            assert np.array_equal(idx[t], ref["topk_idx"][t]), f"{what}: token {t}"
-    np.testing.assert_allclose(lg, L, rtol=1e-4, atol=1e-5 * mag.max())
-    w = out["topk_w"].cpu().numpy()
-    ok = ~near
-    np.testing.assert_allclose(w[ok], ref["topk_w"][ok], rtol=2e-5, atol=1e-6)
-    # grouping is fixed exactly by the GPU's own top-k
-    flat = idx.ravel()
-    cnt = np.bincount(flat, minlength=E)
-    assert np.array_equal(out["expert_count"].cpu().numpy(), cnt)
-    assert np.array_equal(out["expert_offset"].cpu().numpy(), np.concatenate([[0], np.cumsum(cnt)]))
-    assert np.array_equal(out["pair_by_expert"].cpu().numpy(), np.argsort(flat, kind="stable"))
-    say(f"{what}: near-ties {int(near.sum())}/{len(near)}")
 
 
 @pytest.mark.parametrize("T,d,E,k,renorm,xdt,zipf,xscale", [
@@ -126,17 +96,6 @@ def device_layer(experts, thr, R_bits, rdt, E, S, k, renorm=True, bias=None, den
     return L
 
 
-def run_layer(L, x, path, want_masks=True):
-    T = x.shape[0]
-    tr = dict(topk_idx=torch.empty((T, L.k), dtype=torch.int32, device=DEV),
-              topk_w=torch.empty((T, L.k), dtype=torch.float32, device=DEV),
-              logits=torch.empty((T, L.E), dtype=torch.float32, device=DEV),
-              expert_count=torch.empty(L.E, dtype=torch.int32, device=DEV))
-    if want_masks and path == moe.PATH_SPARSE:
-        tr["masks"] = torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=DEV)
-    y = moe.layer_forward(L, x, path=path, trace=tr)
-    torch.cuda.synchronize()
-    return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in tr.items()}
 
 
 def oracle_layer_check(experts, thr, R_bits, rdt, bias, E, S, k, x_bits, y, tr, tokens, dense,
