@@ -192,9 +192,14 @@ struct Geo {
     static constexpr int W = THREADS / 64;
 };
 
+// Gate/down rows gathered per batch in phase C.  Each batch costs at least one
+// memory round trip and the workgroup with the most active rows sets the
+// kernel's duration, so a single token takes 16 rows at once (about three
+// standard deviations above the mean at 90% sparsity and 56 channels).
 template <int TB, int NCH>
 __host__ __device__ constexpr int rows_per_batch()
 {
+    if (TB == 1 && NCH == 1) return 16;
     return (8 / (NCH * (TB >= 8 ? 2 : 1))) < 1 ? 1 : (8 / (NCH * (TB >= 8 ? 2 : 1)));
 }
 
@@ -492,9 +497,13 @@ expert_kernel(SparseArgs a)
                     rows[q] = (int)L.list[ent];
 #pragma unroll
                     for (int i = 0; i < NCH; ++i) {
-                        const int c = min(tid + THREADS * i, CPR - 1);
-                        gw[q][i] = *(const uint4 *)(gate + (size_t)rows[q] * d + (size_t)c * 8);
-                        dw[q][i] = *(const uint4 *)(down + (size_t)rows[q] * d + (size_t)c * 8);
+                        gw[q][i] = make_uint4(0, 0, 0, 0);
+                        dw[q][i] = make_uint4(0, 0, 0, 0);
+                        if (b0 + q < n_act) {                   // uniform: no loads past the list
+                            const int c = min(tid + THREADS * i, CPR - 1);
+                            gw[q][i] = *(const uint4 *)(gate + (size_t)rows[q] * d + (size_t)c * 8);
+                            dw[q][i] = *(const uint4 *)(down + (size_t)rows[q] * d + (size_t)c * 8);
+                        }
                     }
                 }
                 // partial gate dots, reduced over the wave, then over waves in LDS
