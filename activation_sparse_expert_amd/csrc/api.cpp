@@ -95,7 +95,6 @@ size_t expert_ws_bytes(int T, int d, int f)
 }
 
 struct LayerWs {
-    uint32_t *route_done;
     int32_t *topk_idx;
     float *topk_w;
     int32_t *count, *offset, *pairs, *pair_pos, *active, *n_active;
@@ -123,7 +122,6 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     off[10] = o; o += up(dense_h_bytes(T, f, k, S));
     if (out) {
         char *p = (char *)base;
-        out->route_done = (uint32_t *)(p + off[0]);
         out->topk_idx = (int32_t *)(p + off[1]);
         out->topk_w = (float *)(p + off[2]);
         out->count = (int32_t *)(p + off[3]);
@@ -232,7 +230,6 @@ moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void
     a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits = logits_out;
     a.count = expert_count; a.offset = expert_offset; a.pairs = pair_by_expert;
     a.pair_pos = nullptr; a.active = nullptr; a.n_active = nullptr;
-    a.done = (uint32_t *)ws;
     return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -319,7 +316,6 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.count = (trace && trace->expert_count) ? trace->expert_count : w.count;
     r.offset = w.offset; r.pairs = w.pairs; r.pair_pos = w.pair_pos;
     r.active = w.active; r.n_active = w.n_active;
-    r.done = w.route_done;
     hipError_t he = launch_route(r, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
 

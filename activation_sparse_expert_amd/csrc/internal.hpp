@@ -69,7 +69,6 @@ struct RouteArgs {
     int32_t *count, *offset, *pairs;    // nullable as a group (grouping skipped)
     int32_t *pair_pos;                  // nullable: grouped position of each pair
     int32_t *active, *n_active;         // nullable
-    uint32_t *done;                     // completion counter (workspace)
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 

@@ -4,10 +4,11 @@
 // One workgroup per token computes the E logits (every expert with the same
 // code path and reduction order, so identical router rows tie exactly), picks
 // the top-k with ties going to the lower index, and writes the softmax
-// weights.  The last workgroup to finish (completion counter, which it resets)
-// groups the T*k (token, slot) pairs by expert: counts, exclusive offsets, the
-// pairs of each expert in ascending order, and the list of experts that
-// received tokens.  No host synchronisation is involved.
+// weights.  A second kernel of one workgroup then groups the T*k (token, slot)
+// pairs by expert: counts, exclusive offsets, the pairs of each expert in
+// ascending order, their grouped positions, and the list of experts that
+// received tokens.  A single token is grouped by its own workgroup.  No
+// host synchronisation, atomics across workgroups or fences are involved.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -31,6 +32,56 @@ __device__ __forceinline__ void argmax_pair(float &v, int &i, float ov, int oi)
     if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
 }
 
+// Counting sort of the T*k pairs by expert, stable in pair order.  Reads the
+// top-k indices through coherent loads (they were written by this or an
+// earlier kernel).
+__device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
+{
+    const int tid = threadIdx.x;
+    const int E = a.E;
+    int *cnt = (int *)smem;                          // [E] counts
+    int *run = cnt + E;                              // [E] running placement base
+    int *ce = run + E;                               // [kRouteThreads] chunk experts
+    const int P = a.T * a.k;
+    for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += kRouteThreads)
+        atomicAdd(&cnt[load_coherent_i32(a.topk_idx + p)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int o = 0, na = 0;
+        for (int e = 0; e < E; ++e) {
+            a.offset[e] = o;
+            run[e] = o;
+            a.count[e] = cnt[e];
+            if (a.active && cnt[e] > 0) a.active[na++] = e;
+            o += cnt[e];
+        }
+        a.offset[E] = o;
+        if (a.n_active) *a.n_active = na;
+    }
+    __syncthreads();
+    // stable placement, one chunk of pairs at a time
+    for (int b = 0; b < P; b += kRouteThreads) {
+        const int p = b + tid;
+        const int e = p < P ? load_coherent_i32(a.topk_idx + p) : -1;
+        ce[tid] = e;
+        __syncthreads();
+        if (e >= 0) {
+            int rank = 0;
+            for (int q = 0; q < tid; ++q) rank += (ce[q] == e);
+            a.pairs[run[e] + rank] = p;
+            if (a.pair_pos) a.pair_pos[p] = run[e] + rank;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            const int n = min(kRouteThreads, P - b);
+            for (int q = 0; q < n; ++q) run[ce[q]]++;
+        }
+        __syncthreads();
+    }
+}
+
 __global__ void __launch_bounds__(kRouteThreads)
 route_kernel(RouteArgs a)
 {
@@ -38,7 +89,6 @@ route_kernel(RouteArgs a)
     float *xs = (float *)smem;                        // [d]
     float *lg = xs + a.d;                             // [E]
     int *sel = (int *)(lg + a.E);                     // [k]
-    int *flag = sel + a.k;                            // [1]
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, E = a.E, k = a.k;
@@ -92,57 +142,17 @@ route_kernel(RouteArgs a)
             for (int e = lane; e < E; e += 64) a.logits[(size_t)t * E + e] = lg[e];
     }
 
-    if (!a.count) return;
+    if (!a.count || gridDim.x != 1) return;
+    __syncthreads();            // one token: its own workgroup groups it
+    group_pairs(a, smem);
+}
 
-    // ---- grouping by the last workgroup -------------------------------------
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) flag[0] = (atomicInc(a.done, (uint32_t)a.T - 1) == (uint32_t)a.T - 1);
-    __syncthreads();
-    if (!flag[0]) return;
-    __threadfence();
-
-    int *cnt = (int *)smem;                          // reuse: [E] counts
-    int *run = cnt + E;                              // [E] running placement base
-    int *ce = run + E;                               // [kRouteThreads] chunk experts
-    const int P = a.T * k;
-    for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
-    __syncthreads();
-    for (int p = tid; p < P; p += kRouteThreads)
-        atomicAdd(&cnt[load_coherent_i32(a.topk_idx + p)], 1);
-    __syncthreads();
-    if (tid == 0) {
-        int o = 0, na = 0;
-        for (int e = 0; e < E; ++e) {
-            a.offset[e] = o;
-            run[e] = o;
-            a.count[e] = cnt[e];
-            if (a.active && cnt[e] > 0) a.active[na++] = e;
-            o += cnt[e];
-        }
-        a.offset[E] = o;
-        if (a.n_active) *a.n_active = na;
-    }
-    __syncthreads();
-    // stable placement, one chunk of pairs at a time
-    for (int b = 0; b < P; b += kRouteThreads) {
-        const int p = b + tid;
-        const int e = p < P ? load_coherent_i32(a.topk_idx + p) : -1;
-        ce[tid] = e;
-        __syncthreads();
-        if (e >= 0) {
-            int rank = 0;
-            for (int q = 0; q < tid; ++q) rank += (ce[q] == e);
-            a.pairs[run[e] + rank] = p;
-            if (a.pair_pos) a.pair_pos[p] = run[e] + rank;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            const int n = min(kRouteThreads, P - b);
-            for (int q = 0; q < n; ++q) run[ce[q]]++;
-        }
-        __syncthreads();
-    }
+// Grouping of all T*k pairs by one workgroup (after the per-token kernel).
+__global__ void __launch_bounds__(kRouteThreads)
+group_kernel(RouteArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    group_pairs(a, smem);
 }
 
 }  // namespace
@@ -158,6 +168,9 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(kRouteThreads), lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.count || a.T == 1) return e;
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kRouteThreads), lds_group, s, a);
     return hipGetLastError();
 }
 

@@ -112,6 +112,79 @@ def copy_probe(mib):
                       "kernel": "neg (elementwise)", "launches": 10}), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def batched_measure(reps=10, T=256):
+    """The batched layer: 8 experts (d=6144, f=16384, bf16), top-2, T tokens.
+    Times moe_layer_forward on the dense bf16 MFMA path and on the 70%-sparse
+    path (HIP events around `reps` calls each, after warm-up)."""
+    import torch
+    import activation_sparse_expert_amd as moe
+    import synth
+    cfg = synth.CFG_WIDE
+    c = synth.CONFIGS[cfg]
+    d, f, E, k = c["d"], c["f"], c["E"], c["k"]
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    gate = torch.empty((E, f, d), dtype=bf, device=dev)
+    down = torch.empty((E, f, d), dtype=bf, device=dev)
+    up_q = torch.empty((E, f, d // 4), dtype=torch.uint8, device=dev)
+    up_sz = torch.empty((E, f, d // 64, 2), dtype=torch.int16, device=dev)
+    up_dense = torch.empty((E, f, d), dtype=bf, device=dev)
+    thr = torch.empty(E, dtype=torch.float32, device=dev)
+    for e in range(E):
+        gate[e].copy_(synth.device_normal(synth.seed_of(cfg, 0, e, synth.T_GATE), (f, d), 0.02, dev, bf))
+        down[e].copy_(synth.device_normal(synth.seed_of(cfg, 0, e, synth.T_DOWN), (f, d), 0.02, dev, bf))
+        u = synth.device_normal(synth.seed_of(cfg, 0, e, synth.T_UP), (f, d), 0.02, dev)
+        moe.pack_up_int2(u, up_q=up_q[e], up_sz=up_sz[e])
+        del u
+        moe.materialize_up_bf16(up_q[e], up_sz[e], d, out=up_dense[e])
+        ex = moe.Expert(up_q[e], up_sz[e], gate[e], down[e], float("inf"))
+        xc = torch.from_numpy(synth.calibration_f32(cfg, d, c["x_scale"], 0, e)).to(bf).to(dev)
+        v = torch.empty((64, f), dtype=torch.float32, device=dev)
+        moe.expert_forward_sparse(ex, xc, v_out=v)
+        torch.cuda.synchronize()
+        thr[e] = float(np.quantile(np.abs(v.cpu().numpy()).ravel(), c["sparsity"]))
+    R = torch.from_numpy(synth.router_f32(cfg, 0, E, d)).to(bf).to(dev)
+    L = moe.Layer(d=d, f=f, E=E, S=0, k=k, renormalize=True, router_w=R, up_q=up_q, up_sz=up_sz,
+                  gate_t=gate, down=down, thresholds=thr, up_dense=up_dense)
+    x = torch.from_numpy(synth.tokens_f32(cfg, T, d, c["x_scale"])).to(bf).to(dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    ws = moe.new_workspace(L.workspace_bytes(T), dev)
+    cnt = torch.empty(E, dtype=torch.int32, device=dev)
+    out = {}
+    for name, path in (("dense_mfma", moe.PATH_DENSE), ("sparse", moe.PATH_SPARSE)):
+        for _ in range(3):
+            moe.layer_forward(L, x, path=path, y=y, ws=ws, trace={"expert_count": cnt})
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            moe.layer_forward(L, x, path=path, y=y, ws=ws)
+        e1.record()
+        e1.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        used = int((cnt.cpu().numpy() > 0).sum())
+        flops = 2.0 * 3 * T * k * d * f                      # three products per (token, slot)
+        wbytes = used * 3 * d * f * 2                         # bf16 weights of the experts used
+        out[name] = {"ms_per_layer": sec * 1e3, "tokens_per_s": T / sec,
+                     "tflops": flops / sec / 1e12}
+        if path == moe.PATH_DENSE:
+            out[name]["mfma_util"] = flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
+            out[name]["weight_gbs"] = wbytes / sec / 1e9
+            out[name]["hbm_frac"] = wbytes / sec / 1e9 / HBM_PEAK_GBS
+            # roofline-attainable MFMA share at this intensity (flop per weight byte)
+            out[name]["mfma_attainable"] = min(1.0, flops / wbytes * HBM_PEAK_GBS / 1e3
+                                               / MFMA_BF16_PEAK_TFLOPS)
+    out["workload"] = (f"Mixtral-8x22B-shaped layer, 8 experts d={d} f={f} bf16, top-2, "
+                       f"{T} tokens; dense = threshold off on bf16 MFMA, sparse = 70% thresholds")
+    del L, gate, down, up_q, up_sz, up_dense
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(sparsity, budget_s):
     """The fp64 oracle, as it stands, on instance 0 and the same tokens."""
     import oracle
@@ -148,6 +221,10 @@ def main():
     ap.add_argument("--sparsity", type=float, default=0.9)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="only the batched-layer measurement (for profiling)")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batched-layer (dense MFMA vs sparse) measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run the known-size elementwise kernel (counter scaling)")
     args = ap.parse_args()
@@ -158,6 +235,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.batched_only:
+        print(json.dumps({"batched": batched_measure()}), flush=True)
         return
 
     import torch
@@ -243,6 +323,11 @@ def main():
             "traffic": counted_traffic(),
         },
     }
+    if not args.no_batched:
+        del experts
+        torch.cuda.empty_cache()
+        log("measuring the batched layer (dense MFMA and sparse paths)")
+        out["batched"] = batched_measure()
     if not args.no_cpu:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args.sparsity, args.cpu_budget)

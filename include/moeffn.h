@@ -42,13 +42,10 @@
  *   16-byte aligned up_q/gate_t/down/x and 4-byte aligned up_sz.
  *
  * Workspace: every forward call takes a device workspace of at least
- * moe_workspace_size(...) bytes (fp32 partial rows, routing tables and a
- * completion counter).  Its first 256 bytes must be zero before its first use
- * by moe_route_topk or moe_layer_forward (moe_workspace_init, or a
- * zero-initialised tensor); those calls leave the counter at zero again when
- * their kernels finish.  moe_expert_forward_sparse needs no initialisation.
- * Calls that share a workspace must be ordered (same stream); overlapping calls
- * need distinct workspaces.
+ * moe_workspace_size(...) bytes (fp32 partial rows and routing tables).  It
+ * needs no initialisation and holds nothing from one call to the next.  Calls
+ * that share a workspace must be ordered (same stream); overlapping calls need
+ * distinct workspaces.
  *
  * Execution: calls are asynchronous on `stream` (a hipStream_t passed as void*,
  * NULL = the null stream).  Forward calls do no host synchronisation and no
