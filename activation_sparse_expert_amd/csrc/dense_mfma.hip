@@ -10,14 +10,21 @@
 // one expert (32 per wave) and loops over the expert's tokens in 64-row
 // chunks.  v_mfma_f32_32x32x16_bf16 runs with the tokens as rows (A) and the
 // weight rows as columns (B); weights are read once, straight from HBM into
-// registers with 16-byte loads.  The reduction index k is permuted inside
+// registers with 16-byte loads, one 64-wide k block ahead of the one being
+// multiplied.  The x tile of a k block is loaded once per workgroup into a
+// double-buffered LDS tile that the four waves share.  The reduction index k is permuted inside
 // every 64-wide block (lane half h takes k = 32h + 8s + 0..7 at step s); A and
 // B use the same permutation, which leaves the sum unchanged.  Epilogue:
 // h = SiLU(g) * u in fp32 to the workspace.
 // Kernel 2 (down): a workgroup owns 128 output columns and one quarter of the
 // intermediate channels (split-K); A = H split into bf16 hi + lo parts (so H
-// keeps ~16 significant bits), B = W^down.  Results are scaled by the router
-// weight and stored as partial rows; the shared reduction kernel sums them.
+// keeps ~16 significant bits), B = W^down.  W^down is stored channel-major
+// ([f][d], the layout the sparse path gathers rows from), so a 64 x 128 tile
+// is loaded with coalesced row reads into LDS and each lane collects its 8
+// consecutive k values of one column from there; H is staged in LDS as bf16
+// hi and lo tiles once per workgroup.  Both are double-buffered, one k block
+// ahead.  Results are scaled by the router weight and stored as partial rows;
+// the shared reduction kernel sums them.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -27,6 +34,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));    // register-friendly 16-byte value
 
 constexpr int kDenseThreads = 256;
 constexpr int kNB = 128;        // columns per workgroup (4 waves x 32)
@@ -73,54 +81,100 @@ __device__ __forceinline__ int token_of(const DenseArgs &a, const SlotInfo &s, i
     return s.shared ? m : a.pairs[s.pair0 + m] / a.k;
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi)
+{
+    return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+constexpr int kXP = 72;         // halves per LDS row of a 64-wide k block (16-byte pad)
+
 __global__ void __launch_bounds__(kDenseThreads)
 gateup_kernel(DenseArgs a)
 {
+    // x tile of the current and the next k block, shared by the four waves
+    __shared__ __align__(16) uint16_t xs[2][64 * kXP];
     const int nblk = a.f / kNB;
     const int slot = blockIdx.x / nblk;
     const int nb = blockIdx.x - slot * nblk;
     const SlotInfo si = slot_info(a, slot);
     if (!si.valid) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, li = lane & 31;
     const int d = a.d;
     const int j = nb * kNB + wave * 32 + li;                       // this lane's B column
     const uint16_t *grow = a.gate + (size_t)si.e * a.f * d + (size_t)j * d + 32 * h;
     const uint16_t *urow = a.up + (size_t)si.e * a.f * d + (size_t)j * d + 32 * h;
+    // x tile loader: 64 rows x 8 chunks of 16 bytes, two chunks per thread
+    const int lr0 = tid >> 3, lc = tid & 7;                        // rows lr0 and lr0 + 32
 
     for (int m0 = 0; m0 < si.ntok; m0 += 64) {
-        const uint16_t *xrow[2];
-        bool xv[2];
-        for (int mt = 0; mt < 2; ++mt) {
-            const int m = m0 + 32 * mt + li;
-            xv[mt] = m < si.ntok;
-            xrow[mt] = a.x + (size_t)(xv[mt] ? token_of(a, si, m) : 0) * d + 32 * h;
+        const uint16_t *xsrc[2];
+        bool xok[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int m = m0 + lr0 + 32 * q;
+            xok[q] = m < si.ntok;
+            xsrc[q] = a.x + (size_t)(xok[q] ? token_of(a, si, m) : 0) * d + lc * 8;
         }
         floatx16 ag[2], au[2];
         for (int mt = 0; mt < 2; ++mt)
             for (int r = 0; r < 16; ++r) { ag[mt][r] = 0.f; au[mt][r] = 0.f; }
         const bool two = (m0 + 32) < si.ntok;
+
+        // prologue: x tile and weights of k block 0
+        uint4 xn[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) xn[q] = xok[q] ? *(const uint4 *)xsrc[q] : make_uint4(0, 0, 0, 0);
+        uint4 bg[4], bu[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bg[s] = *(const uint4 *)(grow + 8 * s);
+            bu[s] = *(const uint4 *)(urow + 8 * s);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) *(uint4 *)&xs[0][(lr0 + 32 * q) * kXP + lc * 8] = xn[q];
+        __syncthreads();
+
+        int cur = 0;
         for (int kb = 0; kb < d; kb += 64) {
-            uint4 bg[4], bu[4], ax[2][4];
+            const bool more = kb + 64 < d;
+            // prefetch block kb + 64 while block kb is multiplied
+            uint4 gn[4], un[4];
+            if (more) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bg[s] = *(const uint4 *)(grow + kb + 8 * s);
-                bu[s] = *(const uint4 *)(urow + kb + 8 * s);
-            }
+                for (int q = 0; q < 2; ++q)
+                    xn[q] = xok[q] ? *(const uint4 *)(xsrc[q] + kb + 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    ax[mt][s] = xv[mt] ? *(const uint4 *)(xrow[mt] + kb + 8 * s) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                ag[0] = mfma(ax[0][s], bg[s], ag[0]);
-                au[0] = mfma(ax[0][s], bu[s], au[0]);
-                if (two) {
-                    ag[1] = mfma(ax[1][s], bg[s], ag[1]);
-                    au[1] = mfma(ax[1][s], bu[s], au[1]);
+                for (int s = 0; s < 4; ++s) {
+                    gn[s] = *(const uint4 *)(grow + kb + 64 + 8 * s);
+                    un[s] = *(const uint4 *)(urow + kb + 64 + 8 * s);
                 }
             }
+            const uint16_t *xt = xs[cur];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 a0 = *(const uint4 *)&xt[li * kXP + 32 * h + 8 * s];
+                ag[0] = mfma(a0, bg[s], ag[0]);
+                au[0] = mfma(a0, bu[s], au[0]);
+                if (two) {
+                    const uint4 a1 = *(const uint4 *)&xt[(32 + li) * kXP + 32 * h + 8 * s];
+                    ag[1] = mfma(a1, bg[s], ag[1]);
+                    au[1] = mfma(a1, bu[s], au[1]);
+                }
+            }
+            if (more) {
+                // the other buffer was last read before the previous barrier
+#pragma unroll
+                for (int q = 0; q < 2; ++q) *(uint4 *)&xs[cur ^ 1][(lr0 + 32 * q) * kXP + lc * 8] = xn[q];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bg[s] = gn[s];
+                    bu[s] = un[s];
+                }
+            }
+            __syncthreads();
+            cur ^= 1;
         }
         // D layout: value r of lane l is row 8(r/4) + 4h + r%4, column l%32
         for (int mt = 0; mt < 2; ++mt) {
@@ -135,14 +189,20 @@ gateup_kernel(DenseArgs a)
     }
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi)
-{
-    return (uint32_t)lo | ((uint32_t)hi << 16);
-}
+
+constexpr int kBP = 136;        // halves per LDS row of a down-weight tile (128 columns + pad)
+constexpr size_t kDownHs = (size_t)2 * 64 * kXP;                  // hi + lo H tiles (halves)
+constexpr size_t kDownBs = (size_t)64 * kBP;                      // one weight tile (halves)
+constexpr size_t kDownLds = (2 * kDownHs + 2 * kDownBs) * 2 + 64 * 8;
 
 __global__ void __launch_bounds__(kDenseThreads)
 down_kernel(DenseArgs a)
 {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t *hs = (uint16_t *)smem;                                // [2 buf][hi, lo][64][kXP]
+    uint16_t *bs = hs + 2 * kDownHs;                                // [2 buf][64 k][kBP]
+    int *row_s = (int *)(bs + 2 * kDownBs);                         // [64]
+    float *sc_s = (float *)(row_s + 64);                            // [64]
     const int nblk = a.d / kNB;
     const int per_slot = nblk * kKSplit;
     const int slot = blockIdx.x / per_slot;
@@ -150,81 +210,110 @@ down_kernel(DenseArgs a)
     const int nb = rem / kKSplit, ks = rem - nb * kKSplit;
     const SlotInfo si = slot_info(a, slot);
     if (!si.valid) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, li = lane & 31;
     const int d = a.d, f = a.f;
     const int c = nb * kNB + wave * 32 + li;                        // this lane's output column
     const int kspan = f / kKSplit;
     const int k_beg = ks * kspan, k_end = k_beg + kspan;
-    const uint16_t *dcol = a.down + (size_t)si.e * f * d + c;
-
-    __shared__ int row_s[64];
-    __shared__ float sc_s[64];
+    const uint16_t *dtile = a.down + (size_t)si.e * f * d + nb * kNB;
+    // loaders: H tile 64 x 64 fp32 (4 float4 per thread), weight tile 64 x 128
+    // bf16 (4 uint4 per thread)
+    const int hm = tid >> 4, hc = tid & 15;                         // H rows hm + 16q, k 4hc..
+    const int bk = tid >> 4, bc = tid & 15;                         // W rows bk + 16q, cols 8bc..
 
     for (int m0 = 0; m0 < si.ntok; m0 += 64) {
         const int nm = min(64, si.ntok - m0);
-        if (threadIdx.x < 64) {
-            const int m = m0 + threadIdx.x;
+        if (tid < 64) {
             int row = 0;
             float sc = 0.f;
-            if (threadIdx.x < nm) {
-                row = si.hrow0 + m;
-                sc = si.shared ? 1.f : a.topk_w[a.pairs[si.pair0 + m]];
+            if (tid < nm) {
+                row = si.hrow0 + m0 + tid;
+                sc = si.shared ? 1.f : a.topk_w[a.pairs[si.pair0 + m0 + tid]];
             }
-            row_s[threadIdx.x] = row;
-            sc_s[threadIdx.x] = sc;
+            row_s[tid] = row;
+            sc_s[tid] = sc;
         }
-        __syncthreads();
+        // rows past the chunk read row 0 and are zeroed when stored
+        const float *hbase = a.h + (size_t)(si.hrow0 + m0) * f + 4 * hc;
+        int hoff[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hoff[q] = (hm + 16 * q < nm ? hm + 16 * q : 0) * f;
+
         floatx16 acc[2];
         for (int mt = 0; mt < 2; ++mt)
             for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
         const bool two = 32 < nm;
-        const float *hrow[2];
-        bool hv[2];
-        for (int mt = 0; mt < 2; ++mt) {
-            const int m = 32 * mt + li;
-            hv[mt] = m < nm;
-            hrow[mt] = a.h + (size_t)(si.hrow0 + m0 + (hv[mt] ? m : 0)) * f + 32 * h;
-        }
+
+#define DOWN_LOAD(KB)                                                                          \
+    for (int q = 0; q < 4; ++q) {                                                              \
+        hv[q] = *(const float4 *)(hbase + hoff[q] + (KB));                                     \
+        wv[q] = *(const u32x4 *)(dtile + (size_t)((KB) + bk + 16 * q) * d + 8 * bc);           \
+    }
+#define DOWN_STORE(BUF)                                                                        \
+    for (int q = 0; q < 4; ++q) {                                                              \
+        const bool ok = hm + 16 * q < nm;                                                      \
+        const float v[4] = {ok ? hv[q].x : 0.f, ok ? hv[q].y : 0.f, ok ? hv[q].z : 0.f,        \
+                            ok ? hv[q].w : 0.f};                                               \
+        uint16_t hi[4], lo[4];                                                                 \
+        for (int e = 0; e < 4; ++e) {                                                          \
+            hi[e] = float_to_bf16_bits(v[e]);                                                  \
+            lo[e] = float_to_bf16_bits(v[e] - bf16_bits_to_float(hi[e]));                      \
+        }                                                                                      \
+        uint16_t *hhi = hs + (size_t)(BUF) * kDownHs;                                          \
+        const int o = (hm + 16 * q) * kXP + 4 * hc;                                            \
+        *(uint2 *)&hhi[o] = make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));  \
+        *(uint2 *)&hhi[64 * kXP + o] = make_uint2(pack_bf16x2(lo[0], lo[1]),                   \
+                                                  pack_bf16x2(lo[2], lo[3]));                  \
+        *(u32x4 *)&bs[(size_t)(BUF) * kDownBs + (bk + 16 * q) * kBP + 8 * bc] = wv[q];         \
+    }
+        float4 hv[4];
+        u32x4 wv[4];
+#pragma unroll
+        DOWN_LOAD(k_beg)
+#pragma unroll
+        DOWN_STORE(0)
+        __syncthreads();
+        int cur = 0;
         for (int kb = k_beg; kb < k_end; kb += 64) {
-            uint4 b[4];
+            const bool more = kb + 64 < k_end;
+            if (more) {                                             // in flight during the products
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint16_t v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = dcol[(size_t)(kb + 32 * h + 8 * s + e) * d];
-                b[s] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+                DOWN_LOAD(kb + 64)
             }
+            const uint16_t *hhi = hs + (size_t)cur * kDownHs;
+            const uint16_t *hlo = hhi + 64 * kXP;
+            const uint16_t *bt = bs + (size_t)cur * kDownBs;
+#pragma unroll 2
+            for (int s4 = 0; s4 < 4; ++s4) {
+                // B fragment: k = 32h + 8 s4 + 0..7 of this lane's column, read across rows
+                const int kr = 32 * h + 8 * s4;
+                uint16_t bv[8];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                if (mt == 1 && !two) break;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    float hv8[8];
-                    if (hv[mt]) {
-                        const float4 p0 = *(const float4 *)(hrow[mt] + kb + 8 * s);
-                        const float4 p1 = *(const float4 *)(hrow[mt] + kb + 8 * s + 4);
-                        hv8[0] = p0.x; hv8[1] = p0.y; hv8[2] = p0.z; hv8[3] = p0.w;
-                        hv8[4] = p1.x; hv8[5] = p1.y; hv8[6] = p1.z; hv8[7] = p1.w;
-                    } else {
-                        for (int e = 0; e < 8; ++e) hv8[e] = 0.f;
-                    }
-                    uint16_t hi[8], lo[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        hi[e] = float_to_bf16_bits(hv8[e]);
-                        lo[e] = float_to_bf16_bits(hv8[e] - bf16_bits_to_float(hi[e]));
-                    }
-                    const uint4 ahi = make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
-                                                 pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7]));
-                    const uint4 alo = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                                                 pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7]));
-                    acc[mt] = mfma(ahi, b[s], acc[mt]);
-                    acc[mt] = mfma(alo, b[s], acc[mt]);
+                for (int e = 0; e < 8; ++e) bv[e] = bt[(kr + e) * kBP + wave * 32 + li];
+                const uint4 b = make_uint4(pack_bf16x2(bv[0], bv[1]), pack_bf16x2(bv[2], bv[3]),
+                                           pack_bf16x2(bv[4], bv[5]), pack_bf16x2(bv[6], bv[7]));
+                const uint4 ahi0 = *(const uint4 *)&hhi[li * kXP + kr];
+                const uint4 alo0 = *(const uint4 *)&hlo[li * kXP + kr];
+                acc[0] = mfma(ahi0, b, acc[0]);
+                acc[0] = mfma(alo0, b, acc[0]);
+                if (two) {
+                    const uint4 ahi1 = *(const uint4 *)&hhi[(32 + li) * kXP + kr];
+                    const uint4 alo1 = *(const uint4 *)&hlo[(32 + li) * kXP + kr];
+                    acc[1] = mfma(ahi1, b, acc[1]);
+                    acc[1] = mfma(alo1, b, acc[1]);
                 }
             }
+            if (more) {         // the other buffers were last read before the previous barrier
+#pragma unroll
+                DOWN_STORE(cur ^ 1)
+            }
+            __syncthreads();
+            cur ^= 1;
         }
+#undef DOWN_LOAD
+#undef DOWN_STORE
         // scaled partial rows: [row][ks][d]
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -252,7 +341,10 @@ hipError_t launch_dense_layer(const DenseArgs &a, hipStream_t s)
     hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kNB)), dim3(kDenseThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(down_kernel, dim3(slots * (a.d / kNB) * kKSplit), dim3(kDenseThreads), 0, s, a);
+    e = hipFuncSetAttribute((const void *)down_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kDownLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(down_kernel, dim3(slots * (a.d / kNB) * kKSplit), dim3(kDenseThreads), kDownLds, s, a);
     return hipGetLastError();
 }
 
