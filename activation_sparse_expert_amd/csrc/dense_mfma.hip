@@ -9,10 +9,10 @@
 // Kernel 1 (gate/up): a workgroup of 4 waves owns 128 intermediate channels of
 // one expert (32 per wave) and loops over the expert's tokens in 64-row
 // chunks.  v_mfma_f32_32x32x16_bf16 runs with the tokens as rows (A) and the
-// weight rows as columns (B); weights are read once, straight from HBM into
-// registers with 16-byte loads, one 64-wide k block ahead of the one being
-// multiplied.  The x tile of a k block is loaded once per workgroup into a
-// double-buffered LDS tile that the four waves share.  The reduction index k is permuted inside
+// weight rows as columns (B).  Each 64-wide k block of the gate, up and x
+// tiles is copied straight from global memory into LDS (full 128-byte rows per
+// instruction), two blocks ahead of the one being multiplied, in a three-stage
+// ring; weights are read from HBM once.  The reduction index k is permuted inside
 // every 64-wide block (lane half h takes k = 32h + 8s + 0..7 at step s); A and
 // B use the same permutation, which leaves the sum unchanged.  Epilogue:
 // h = SiLU(g) * u in fp32 to the workspace.
@@ -88,11 +88,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi)
 
 constexpr int kXP = 72;         // halves per LDS row of a 64-wide k block (16-byte pad)
 
+// gate/up tiles per 64-wide k block, copied global -> LDS: 128 gate rows, 128
+// up rows and 64 x rows of 128 bytes.  A row's eight 16-byte chunks are stored
+// XOR-swizzled by (row & 7), so a fragment read (32 rows, one chunk each) hits
+// every bank group once.
+constexpr int kGuStages = 3;
+constexpr int kGuRows = 128 + 128 + 64;
+constexpr size_t kGuStage = (size_t)kGuRows * 128;                  // bytes
+constexpr size_t kGuLds = kGuStages * kGuStage;
+constexpr int kGuCopies = kGuRows * 8 / 64 / 4;                    // 16-byte copies per lane per stage (10)
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 16 * (chunk ^ (row & 7)); }
+
 __global__ void __launch_bounds__(kDenseThreads)
 gateup_kernel(DenseArgs a)
 {
-    // x tile of the current and the next k block, shared by the four waves
-    __shared__ __align__(16) uint16_t xs[2][64 * kXP];
+    extern __shared__ __align__(16) unsigned char smem[];
     const int nblk = a.f / kNB;
     const int slot = blockIdx.x / nblk;
     const int nb = blockIdx.x - slot * nblk;
@@ -103,79 +114,67 @@ gateup_kernel(DenseArgs a)
     const int h = lane >> 5, li = lane & 31;
     const int d = a.d;
     const int j = nb * kNB + wave * 32 + li;                       // this lane's B column
-    const uint16_t *grow = a.gate + (size_t)si.e * a.f * d + (size_t)j * d + 32 * h;
-    const uint16_t *urow = a.up + (size_t)si.e * a.f * d + (size_t)j * d + 32 * h;
-    // x tile loader: 64 rows x 8 chunks of 16 bytes, two chunks per thread
-    const int lr0 = tid >> 3, lc = tid & 7;                        // rows lr0 and lr0 + 32
+    const size_t wbase = (size_t)si.e * a.f * d + (size_t)nb * kNB * d;
+    const int nkb = d / 64;
 
     for (int m0 = 0; m0 < si.ntok; m0 += 64) {
-        const uint16_t *xsrc[2];
-        bool xok[2];
+        // copy sources of this lane for each of its kGuCopies copies (k block 0):
+        // copy q of wave w covers tile rows 8 (w kGuCopies + q) .. + 7
+        const uint16_t *src[kGuCopies];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int m = m0 + lr0 + 32 * q;
-            xok[q] = m < si.ntok;
-            xsrc[q] = a.x + (size_t)(xok[q] ? token_of(a, si, m) : 0) * d + lc * 8;
+        for (int q = 0; q < kGuCopies; ++q) {
+            const int p = (wave * kGuCopies + q) * 64 + lane;           // position in the stage
+            const int row = p >> 3, c = (p & 7) ^ (row & 7);            // tile row, source chunk
+            const uint16_t *rp;
+            if (row < 128) {
+                rp = a.gate + wbase + (size_t)row * d;
+            } else if (row < 256) {
+                rp = a.up + wbase + (size_t)(row - 128) * d;
+            } else {
+                const int m = m0 + row - 256;                           // rows past the chunk read
+                rp = a.x + (size_t)(m < si.ntok ? token_of(a, si, m) : 0) * d;   // a valid token
+            }
+            src[q] = rp + 8 * c;
         }
+        auto issue = [&](int kb, int stage) {
+            unsigned char *base = smem + (size_t)stage * kGuStage;
+#pragma unroll
+            for (int q = 0; q < kGuCopies; ++q)
+                copy16_to_lds(src[q] + (size_t)kb * 64, base + (size_t)(wave * kGuCopies + q) * 1024);
+        };
+
         floatx16 ag[2], au[2];
         for (int mt = 0; mt < 2; ++mt)
             for (int r = 0; r < 16; ++r) { ag[mt][r] = 0.f; au[mt][r] = 0.f; }
         const bool two = (m0 + 32) < si.ntok;
 
-        // prologue: x tile and weights of k block 0
-        uint4 xn[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) xn[q] = xok[q] ? *(const uint4 *)xsrc[q] : make_uint4(0, 0, 0, 0);
-        uint4 bg[4], bu[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bg[s] = *(const uint4 *)(grow + 8 * s);
-            bu[s] = *(const uint4 *)(urow + 8 * s);
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) *(uint4 *)&xs[0][(lr0 + 32 * q) * kXP + lc * 8] = xn[q];
-        __syncthreads();
-
-        int cur = 0;
-        for (int kb = 0; kb < d; kb += 64) {
-            const bool more = kb + 64 < d;
-            // prefetch block kb + 64 while block kb is multiplied
-            uint4 gn[4], un[4];
-            if (more) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    xn[q] = xok[q] ? *(const uint4 *)(xsrc[q] + kb + 64) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    gn[s] = *(const uint4 *)(grow + kb + 64 + 8 * s);
-                    un[s] = *(const uint4 *)(urow + kb + 64 + 8 * s);
-                }
-            }
-            const uint16_t *xt = xs[cur];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 a0 = *(const uint4 *)&xt[li * kXP + 32 * h + 8 * s];
-                ag[0] = mfma(a0, bg[s], ag[0]);
-                au[0] = mfma(a0, bu[s], au[0]);
-                if (two) {
-                    const uint4 a1 = *(const uint4 *)&xt[(32 + li) * kXP + 32 * h + 8 * s];
-                    ag[1] = mfma(a1, bg[s], ag[1]);
-                    au[1] = mfma(a1, bu[s], au[1]);
-                }
-            }
-            if (more) {
-                // the other buffer was last read before the previous barrier
-#pragma unroll
-                for (int q = 0; q < 2; ++q) *(uint4 *)&xs[cur ^ 1][(lr0 + 32 * q) * kXP + lc * 8] = xn[q];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    bg[s] = gn[s];
-                    bu[s] = un[s];
-                }
-            }
+        issue(0, 0);
+        if (nkb > 1) issue(1, 1);
+        for (int kb = 0; kb < nkb; ++kb) {
+            // block kb has landed once at most one stage of copies is younger
+            if (kb + 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGuCopies) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            cur ^= 1;
+            // the stage written next held block kb - 1, which every wave has finished
+            if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % kGuStages);
+            const unsigned char *st = smem + (size_t)(kb % kGuStages) * kGuStage;
+            const int gr = wave * 32 + li, ur = 128 + wave * 32 + li;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int c = 4 * h + s4;
+                const uint4 bg = *(const uint4 *)(st + swz(gr, c));
+                const uint4 bu = *(const uint4 *)(st + swz(ur, c));
+                const uint4 a0 = *(const uint4 *)(st + swz(256 + li, c));
+                ag[0] = mfma(a0, bg, ag[0]);
+                au[0] = mfma(a0, bu, au[0]);
+                if (two) {
+                    const uint4 a1 = *(const uint4 *)(st + swz(288 + li, c));
+                    ag[1] = mfma(a1, bg, ag[1]);
+                    au[1] = mfma(a1, bu, au[1]);
+                }
+            }
         }
+        __syncthreads();        // the stages are reused by the next token chunk
         // D layout: value r of lane l is row 8(r/4) + 4h + r%4, column l%32
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -188,7 +187,6 @@ gateup_kernel(DenseArgs a)
         }
     }
 }
-
 
 constexpr int kBP = 136;        // halves per LDS row of a down-weight tile (128 columns + pad)
 constexpr size_t kDownHs = (size_t)2 * 64 * kXP;                  // hi + lo H tiles (halves)
@@ -338,8 +336,11 @@ hipError_t launch_dense_layer(const DenseArgs &a, hipStream_t s)
 {
     if (a.f % kNB != 0 || a.d % kNB != 0 || (a.f / kKSplit) % 64 != 0) return hipErrorInvalidValue;
     const int slots = a.S + (a.E < a.T * a.k ? a.E : a.T * a.k);
-    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kNB)), dim3(kDenseThreads), 0, s, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e = hipFuncSetAttribute((const void *)gateup_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGuLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kNB)), dim3(kDenseThreads), kGuLds, s, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void *)down_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)kDownLds);

@@ -90,6 +90,25 @@ __device__ __forceinline__ int load_coherent_i32(const int32_t *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Asynchronous 16-byte copy global -> LDS (gfx950 global_load_lds_dwordx4):
+// lane l of the wave writes its 16 bytes to lds_base + 16 l; lds_base must be
+// the same for every lane.  Issued from inline assembly so that the compiler's
+// wait-count pass does not treat the copy as a possible alias of every later
+// LDS access (it would drain vmcnt before each): the issuing wave waits for its
+// copies itself (vmcnt) before a barrier that publishes them.  m0 is saved and
+// restored.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
+{
+    typedef __attribute__((address_space(3))) void lvoid;
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lvoid *)lds_base);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(m)
+                 : "memory");
+}
+
 // Store one fp32 result into an output of type dt (0 f16, 1 bf16, 2 f32),
 // optionally adding to what is there.
 __device__ __forceinline__ void store_out(void *y, int dt, size_t i, float v, int accumulate)
