@@ -6,13 +6,14 @@
 // and the layer adds each token's rows with its router weight (shared experts
 // with weight 1).
 //
-// Kernel 1 (gate/up): a workgroup of 4 waves owns 128 intermediate channels of
-// one expert (32 per wave) and loops over the expert's tokens in 64-row
-// chunks.  v_mfma_f32_32x32x16_bf16 runs with the tokens as rows (A) and the
-// weight rows as columns (B).  Each 64-wide k block of the gate, up and x
-// tiles is copied straight from global memory into LDS (full 128-byte rows per
-// instruction), two blocks ahead of the one being multiplied, in a three-stage
-// ring; weights are read from HBM once.  The reduction index k is permuted inside
+// Kernel 1 (gate/up): a workgroup of 4 waves owns 64 intermediate channels of
+// one expert and loops over the expert's tokens in 64-row chunks; wave w takes
+// token half w & 1 and channel half w >> 1.  v_mfma_f32_32x32x16_bf16 runs
+// with the tokens as rows (A) and the weight rows as columns (B).  Each
+// 128-wide k block of the gate, up and x tiles is copied straight from global
+// memory into LDS (whole 256-byte row pieces, four rows per instruction), two
+// blocks ahead of the one being multiplied, in a three-stage ring; weights are
+// read from HBM once.  The reduction index k is permuted inside
 // every 64-wide block (lane half h takes k = 32h + 8s + 0..7 at step s); A and
 // B use the same permutation, which leaves the sum unchanged.  Epilogue:
 // h = SiLU(g) * u in fp32 to the workspace.
@@ -88,23 +89,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi)
 
 constexpr int kXP = 72;         // halves per LDS row of a 64-wide k block (16-byte pad)
 
-// gate/up tiles per 64-wide k block, copied global -> LDS: 128 gate rows, 128
-// up rows and 64 x rows of 128 bytes.  A row's eight 16-byte chunks are stored
-// XOR-swizzled by (row & 7), so a fragment read (32 rows, one chunk each) hits
-// every bank group once.
+// gate/up tiles per 128-wide k block, copied global -> LDS: 64 gate rows, 64
+// up rows and 64 x rows of 256 bytes (a long run per weight row, which HBM
+// serves far better than 128-byte pieces).  A row's sixteen 16-byte chunks are
+// stored with the low three bits of the chunk index XOR-swizzled by (row & 7),
+// so a fragment read (32 rows, one chunk each) is free of bank conflicts.
+constexpr int kGuBN = 64;                                           // channels per workgroup
 constexpr int kGuStages = 3;
-constexpr int kGuRows = 128 + 128 + 64;
-constexpr size_t kGuStage = (size_t)kGuRows * 128;                  // bytes
+constexpr int kGuRows = 3 * 64;
+constexpr size_t kGuStage = (size_t)kGuRows * 256;                  // bytes
 constexpr size_t kGuLds = kGuStages * kGuStage;
-constexpr int kGuCopies = kGuRows * 8 / 64 / 4;                    // 16-byte copies per lane per stage (10)
+constexpr int kGuCopies = kGuRows * 16 / 64 / 4;                   // 16-byte copies per lane per stage (12)
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 16 * (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + 16 * (chunk ^ (row & 7)); }
 
 __global__ void __launch_bounds__(kDenseThreads)
 gateup_kernel(DenseArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int nblk = a.f / kNB;
+    const int nblk = a.f / kGuBN;
     const int slot = blockIdx.x / nblk;
     const int nb = blockIdx.x - slot * nblk;
     const SlotInfo si = slot_info(a, slot);
@@ -112,26 +115,26 @@ gateup_kernel(DenseArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, li = lane & 31;
+    const int mt = wave & 1, nt = wave >> 1;                        // token half, channel half
     const int d = a.d;
-    const int j = nb * kNB + wave * 32 + li;                       // this lane's B column
-    const size_t wbase = (size_t)si.e * a.f * d + (size_t)nb * kNB * d;
-    const int nkb = d / 64;
+    const int j = nb * kGuBN + nt * 32 + li;                        // this lane's B column
+    const size_t wbase = (size_t)si.e * a.f * d + (size_t)nb * kGuBN * d;
+    const int nkb = d / 128;
 
     for (int m0 = 0; m0 < si.ntok; m0 += 64) {
-        // copy sources of this lane for each of its kGuCopies copies (k block 0):
-        // copy q of wave w covers tile rows 8 (w kGuCopies + q) .. + 7
+        // copy q of wave w covers tile rows 4 (w kGuCopies + q) .. + 3
         const uint16_t *src[kGuCopies];
 #pragma unroll
         for (int q = 0; q < kGuCopies; ++q) {
-            const int p = (wave * kGuCopies + q) * 64 + lane;           // position in the stage
-            const int row = p >> 3, c = (p & 7) ^ (row & 7);            // tile row, source chunk
+            const int p = (wave * kGuCopies + q) * 64 + lane;           // 16-byte position in the stage
+            const int row = p >> 4, c = (p & 15) ^ (row & 7);           // tile row, source chunk
             const uint16_t *rp;
-            if (row < 128) {
+            if (row < 64) {
                 rp = a.gate + wbase + (size_t)row * d;
-            } else if (row < 256) {
-                rp = a.up + wbase + (size_t)(row - 128) * d;
+            } else if (row < 128) {
+                rp = a.up + wbase + (size_t)(row - 64) * d;
             } else {
-                const int m = m0 + row - 256;                           // rows past the chunk read
+                const int m = m0 + row - 128;                           // rows past the chunk read
                 rp = a.x + (size_t)(m < si.ntok ? token_of(a, si, m) : 0) * d;   // a valid token
             }
             src[q] = rp + 8 * c;
@@ -140,13 +143,12 @@ gateup_kernel(DenseArgs a)
             unsigned char *base = smem + (size_t)stage * kGuStage;
 #pragma unroll
             for (int q = 0; q < kGuCopies; ++q)
-                copy16_to_lds(src[q] + (size_t)kb * 64, base + (size_t)(wave * kGuCopies + q) * 1024);
+                copy16_to_lds(src[q] + (size_t)kb * 128, base + (size_t)(wave * kGuCopies + q) * 1024);
         };
 
-        floatx16 ag[2], au[2];
-        for (int mt = 0; mt < 2; ++mt)
-            for (int r = 0; r < 16; ++r) { ag[mt][r] = 0.f; au[mt][r] = 0.f; }
-        const bool two = (m0 + 32) < si.ntok;
+        floatx16 ag, au;
+        for (int r = 0; r < 16; ++r) { ag[r] = 0.f; au[r] = 0.f; }
+        const bool mine = m0 + 32 * mt < si.ntok;                   // this wave's token half has tokens
 
         issue(0, 0);
         if (nkb > 1) issue(1, 1);
@@ -157,32 +159,29 @@ gateup_kernel(DenseArgs a)
             __syncthreads();
             // the stage written next held block kb - 1, which every wave has finished
             if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % kGuStages);
-            const unsigned char *st = smem + (size_t)(kb % kGuStages) * kGuStage;
-            const int gr = wave * 32 + li, ur = 128 + wave * 32 + li;
+            if (mine) {
+                const unsigned char *st = smem + (size_t)(kb % kGuStages) * kGuStage;
+                const int gr = nt * 32 + li, ur = 64 + nt * 32 + li, xr = 128 + mt * 32 + li;
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const int c = 4 * h + s4;
-                const uint4 bg = *(const uint4 *)(st + swz(gr, c));
-                const uint4 bu = *(const uint4 *)(st + swz(ur, c));
-                const uint4 a0 = *(const uint4 *)(st + swz(256 + li, c));
-                ag[0] = mfma(a0, bg, ag[0]);
-                au[0] = mfma(a0, bu, au[0]);
-                if (two) {
-                    const uint4 a1 = *(const uint4 *)(st + swz(288 + li, c));
-                    ag[1] = mfma(a1, bg, ag[1]);
-                    au[1] = mfma(a1, bu, au[1]);
+                for (int s8 = 0; s8 < 8; ++s8) {
+                    const int c = 8 * h + s8;                       // k = 64h + 8 s8 + 0..7
+                    const uint4 bg = *(const uint4 *)(st + swz(gr, c));
+                    const uint4 bu = *(const uint4 *)(st + swz(ur, c));
+                    const uint4 ax = *(const uint4 *)(st + swz(xr, c));
+                    ag = mfma(ax, bg, ag);
+                    au = mfma(ax, bu, au);
                 }
             }
         }
         __syncthreads();        // the stages are reused by the next token chunk
         // D layout: value r of lane l is row 8(r/4) + 4h + r%4, column l%32
-        for (int mt = 0; mt < 2; ++mt) {
+        if (mine) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = 8 * (r >> 2) + 4 * h + (r & 3);
                 const int m = m0 + 32 * mt + i;
                 if (m < si.ntok)
-                    a.h[(size_t)(si.hrow0 + m) * a.f + j] = silu(ag[mt][r]) * au[mt][r];
+                    a.h[(size_t)(si.hrow0 + m) * a.f + j] = silu(ag[r]) * au[r];
             }
         }
     }
@@ -334,12 +333,13 @@ size_t dense_h_bytes(int T, int f, int k, int S)
 
 hipError_t launch_dense_layer(const DenseArgs &a, hipStream_t s)
 {
-    if (a.f % kNB != 0 || a.d % kNB != 0 || (a.f / kKSplit) % 64 != 0) return hipErrorInvalidValue;
+    if (a.f % kNB != 0 || a.d % kNB != 0 || (a.f / kKSplit) % 64 != 0 || a.f % kGuBN != 0)
+        return hipErrorInvalidValue;
     const int slots = a.S + (a.E < a.T * a.k ? a.E : a.T * a.k);
     hipError_t e = hipFuncSetAttribute((const void *)gateup_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGuLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kNB)), dim3(kDenseThreads), kGuLds, s, a);
+    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kGuBN)), dim3(kDenseThreads), kGuLds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void *)down_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
