@@ -282,6 +282,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     if (!L || !x || !y) return MOE_ERR_INVALID_ARG;
     const int d = L->d, f = L->f, E = L->n_routed, S = L->n_shared, k = L->top_k;
     if (S < 0) return MOE_ERR_INVALID_ARG;
+    if (k + S > kMaxExpertsPerToken) return MOE_ERR_UNSUPPORTED;
     moe_status st = check_route_args(x, xdt, T, d, L->router_w, L->rdt, E, k);
     if (st != MOE_OK) return st;
     st = check_expert_shape(d, f, L->wdt, xdt, T, ydt);

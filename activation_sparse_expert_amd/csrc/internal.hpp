@@ -42,6 +42,8 @@ hipError_t launch_sparse_expert_f16(const SparseArgs &a, int tb, hipStream_t s);
 hipError_t launch_sparse_expert_bf16(const SparseArgs &a, int tb, hipStream_t s);
 
 // Second kernel: output rows from the partial rows.
+constexpr int kMaxExpertsPerToken = 1024;   // k + S of a layer (routed + shared rows per token)
+
 struct ReduceArgs {
     const float *part;                  // [rows][tiles][d]
     int tiles, d, T;

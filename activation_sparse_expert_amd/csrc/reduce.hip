@@ -16,6 +16,7 @@ constexpr int kRedThreads = 256;
 constexpr int kCols = 16;               // output columns per workgroup (4 threads x float4)
 constexpr int kGroups = kRedThreads / 4;  // contribution groups per workgroup
 constexpr int kBatch = 8;               // loads in flight per thread
+constexpr int kMaxRowsPerTok = kMaxExpertsPerToken;
 
 __device__ __forceinline__ int part_row(const ReduceArgs &a, int t, int ri)
 {
@@ -30,9 +31,12 @@ __global__ void __launch_bounds__(kRedThreads)
 reduce_kernel(ReduceArgs a)
 {
     __shared__ float4 sm[kGroups][4];
+    __shared__ int rows_s[kMaxRowsPerTok];
     const int cblocks = a.d / kCols;
     const int t = blockIdx.x / cblocks;
     const int cb = blockIdx.x - t * cblocks;
+    for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRedThreads) rows_s[ri] = part_row(a, t, ri);
+    __syncthreads();
     const int cq = threadIdx.x & 3, tg = threadIdx.x >> 2;
     const int col = cb * kCols + cq * 4;
     const int n = a.rows_per_tok * a.tiles;
@@ -45,7 +49,7 @@ reduce_kernel(ReduceArgs a)
             const int ci = c0 + b * kGroups;
             const int cc = ci < n ? ci : tg;
             const int ri = cc / a.tiles, tile = cc - ri * a.tiles;
-            v[b] = *(const float4 *)(a.part + ((size_t)part_row(a, t, ri) * a.tiles + tile) * a.d + col);
+            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[ri] * a.tiles + tile) * a.d + col);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -81,9 +85,12 @@ constexpr int kRowBatch = 16;
 __global__ void __launch_bounds__(kRowThreads)
 reduce_rows_kernel(ReduceArgs a)
 {
+    __shared__ int rows_s[kMaxRowsPerTok];
     const int cblocks = (a.d + kRowCols - 1) / kRowCols;
     const int t = blockIdx.x / cblocks;
     const int col = (blockIdx.x - t * cblocks) * kRowCols + threadIdx.x * 4;
+    for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRowThreads) rows_s[ri] = part_row(a, t, ri);
+    __syncthreads();
     if (col >= a.d) return;
     const int n = a.rows_per_tok * a.tiles;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -93,7 +100,7 @@ reduce_rows_kernel(ReduceArgs a)
         for (int b = 0; b < kRowBatch; ++b) {
             const int ci = min(c0 + b, n - 1);
             const int ri = ci / a.tiles, tile = ci - ri * a.tiles;
-            v[b] = *(const float4 *)(a.part + ((size_t)part_row(a, t, ri) * a.tiles + tile) * a.d + col);
+            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[ri] * a.tiles + tile) * a.d + col);
         }
 #pragma unroll
         for (int b = 0; b < kRowBatch; ++b) {
@@ -113,7 +120,7 @@ reduce_rows_kernel(ReduceArgs a)
 
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
-    if (a.d % kCols != 0) return hipErrorInvalidValue;
+    if (a.d % kCols != 0 || a.rows_per_tok > kMaxRowsPerTok) return hipErrorInvalidValue;
     if (a.rows_per_tok * a.tiles <= kRowMax) {
         const int cblocks = (a.d + kRowCols - 1) / kRowCols;
         hipLaunchKernelGGL(reduce_rows_kernel, dim3(a.T * cblocks), dim3(kRowThreads), 0, s, a);

@@ -26,6 +26,30 @@ __device__ __forceinline__ float load_any(const void *p, int dt, size_t i)
     return dt == 1 ? bf16_bits_to_float(b) : half_bits_to_float(b);
 }
 
+// Eight consecutive elements starting at element i (i % 8 == 0) as floats.
+__device__ __forceinline__ void load8(const void *p, int dt, size_t i, float (&v)[8])
+{
+    if (dt == 2) {
+        const float4 a = *(const float4 *)((const float *)p + i);
+        const float4 b = *(const float4 *)((const float *)p + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        return;
+    }
+    const uint4 r = *(const uint4 *)((const uint16_t *)p + i);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (dt == 1) {
+            v[2 * q] = bf16_bits_to_float((uint16_t)(w[q] & 0xFFFFu));
+            v[2 * q + 1] = bf16_bits_to_float((uint16_t)(w[q] >> 16));
+        } else {
+            v[2 * q] = half_bits_to_float((uint16_t)(w[q] & 0xFFFFu));
+            v[2 * q + 1] = half_bits_to_float((uint16_t)(w[q] >> 16));
+        }
+    }
+}
+
 // argmax over (value, index) with the lower index winning ties
 __device__ __forceinline__ void argmax_pair(float &v, int &i, float ov, int oi)
 {
@@ -93,13 +117,46 @@ route_kernel(RouteArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, E = a.E, k = a.k;
 
-    for (int i = tid; i < d; i += kRouteThreads) xs[i] = load_any(a.x, a.xdt, (size_t)t * d + i);
+    // x in 8-element chunks (16 or 32 bytes per load), all of a thread's loads in flight
+    const int nch = d / 8;
+    for (int c0 = tid; c0 < nch; c0 += 4 * kRouteThreads) {
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(c0 + u * kRouteThreads, nch - 1);
+            load8(a.x, a.xdt, (size_t)t * d + (size_t)c * 8, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * kRouteThreads;
+            if (c < nch) {
+                *(float4 *)&xs[c * 8] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+                *(float4 *)&xs[c * 8 + 4] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+            }
+        }
+    }
     __syncthreads();
 
-    // logits: one wave per expert, lanes stride over d, fixed butterfly
+    // logits: one wave per expert; a lane takes chunks lane, lane + 64, ... of the
+    // router row in a fixed order (4 loads in flight), then a fixed butterfly
     for (int e = wave; e < E; e += kRouteWaves) {
         float p = 0.f;
-        for (int i = lane; i < d; i += 64) p += xs[i] * load_any(a.rw, a.rdt, (size_t)e * d + i);
+        for (int c0 = lane; c0 < nch; c0 += 4 * 64) {
+            float w[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = min(c0 + u * 64, nch - 1);
+                load8(a.rw, a.rdt, (size_t)e * d + (size_t)c * 8, w[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * 64;
+                if (c < nch) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) p += xs[c * 8 + q] * w[u][q];
+                }
+            }
+        }
         p = seg_sum<64>(p);
         if (lane == 0) lg[e] = p + (a.bias ? a.bias[e] : 0.f);
     }

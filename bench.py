@@ -14,6 +14,12 @@ launches are captured once in a HIP graph and replayed, so the host's launch
 overhead is not what is measured.
 
 Prints one JSON line.  --gpus above 1 is refused: the path runs on one GPU.
+Besides the headline, the line carries "more" (the same expert at batch 4;
+decode steps through the 32-layer Mixtral-shaped stack at 1 and 16 tokens and
+through the fine-grained 64+2 layer at 1 and 64 tokens, router included) and
+"batched" (the Mixtral-8x22B-shaped layer at 256 tokens on the dense MFMA path,
+with MFMA utilisation, and on the sparse path); --no-layers / --no-batched skip
+them.
 
 ``roofline.achieved`` is the algorithmic bytes of a call (INT2 up codes, fp16
 scales and zeros, x, y, and the gate and down rows of the channels the mask
@@ -185,6 +191,144 @@ def batched_measure(reps=10, T=256):
     return out
 
 
+def device_layer(cfg, layer, E, S, k, d, f, wdt, xscale, sparsity, bias=None, router_std=0.02):
+    """A layer drawn on the device: E routed + S shared experts, INT2 up packed
+    by the library, thresholds at the `sparsity` quantile of |v| over the 64
+    seeded calibration vectors (v from the library)."""
+    import torch
+    import activation_sparse_expert_amd as moe
+    import synth
+    dev = torch.device("cuda:0")
+    dt = torch.float16 if wdt == "f16" else torch.bfloat16
+    n = E + S
+    gate = torch.empty((n, f, d), dtype=dt, device=dev)
+    down = torch.empty((n, f, d), dtype=dt, device=dev)
+    up_q = torch.empty((n, f, d // 4), dtype=torch.uint8, device=dev)
+    up_sz = torch.empty((n, f, d // 64, 2), dtype=torch.int16, device=dev)
+    thr = torch.empty(n, dtype=torch.float32, device=dev)
+    v = torch.empty((64, f), dtype=torch.float32, device=dev)
+    for e in range(n):
+        gate[e].copy_(synth.device_normal(synth.seed_of(cfg, layer, e, synth.T_GATE), (f, d), 0.02, dev, dt))
+        down[e].copy_(synth.device_normal(synth.seed_of(cfg, layer, e, synth.T_DOWN), (f, d), 0.02, dev, dt))
+        u = synth.device_normal(synth.seed_of(cfg, layer, e, synth.T_UP), (f, d), 0.02, dev)
+        moe.pack_up_int2(u, up_q=up_q[e], up_sz=up_sz[e])
+        del u
+        xc = torch.from_numpy(synth.calibration_f32(cfg, d, xscale, layer, e)).to(dt).to(dev)
+        moe.expert_forward_sparse(moe.Expert(up_q[e], up_sz[e], gate[e], down[e], float("inf")), xc,
+                                  v_out=v)
+        thr[e] = torch.quantile(v.abs().flatten()[: 1 << 24].double(), sparsity).float()
+    R = torch.from_numpy(synth.router_f32(cfg, layer, E, d, router_std)).to(dt).to(dev)
+    return moe.Layer(d=d, f=f, E=E, S=S, k=k, renormalize=True, router_w=R, up_q=up_q, up_sz=up_sz,
+                     gate_t=gate, down=down, thresholds=thr,
+                     router_bias=None if bias is None else torch.from_numpy(bias).to(dev))
+
+
+def layer_bytes(L, masks, idx):
+    """Algorithmic bytes of one layer call: router rows, and for every expert
+    touched its INT2 codes, scales and the gate and down rows of the union of
+    its tokens' masks; x in and y out."""
+    T = masks.shape[0]
+    d, f, E, k = L.d, L.f, L.E, L.k
+    b = E * d * 2 + T * d * 2 + T * d * 4
+    for e in range(E + L.S):
+        if e < E:
+            sel = np.argwhere(idx == e)
+            if len(sel) == 0:
+                continue
+            union = np.zeros(f, dtype=bool)
+            for t, s_ in sel:
+                union |= masks[t, s_].astype(bool)
+        else:
+            union = masks[:, k + (e - E)].astype(bool).any(axis=0)
+        b += d * f // 4 + 4 * f * (d // 64) + 2 * int(union.sum()) * d * 2
+    return b
+
+
+def time_graph(fn, reps, inner):
+    """Capture `inner` calls of fn() in a HIP graph, replay `reps` times after
+    one untimed replay; returns seconds per call."""
+    import torch
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            fn()
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(inner):
+            fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (reps * inner)
+
+
+def layer_workload(layers, xs_by_layer, label):
+    """Decode step through `layers` (one moe_layer_forward each, captured in a
+    graph): tokens/s and algorithmic GB/s."""
+    import torch
+    import activation_sparse_expert_amd as moe
+    dev = torch.device("cuda:0")
+    T = xs_by_layer[0].shape[0]
+    ys = [torch.empty((T, L.d), dtype=torch.float32, device=dev) for L in layers]
+    wss = [moe.new_workspace(L.workspace_bytes(T), dev) for L in layers]
+    total_b = 0
+    for L, x, y, ws in zip(layers, xs_by_layer, ys, wss):
+        tr = dict(topk_idx=torch.empty((T, L.k), dtype=torch.int32, device=dev),
+                  masks=torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=dev))
+        moe.layer_forward(L, x, y=y, ws=ws, trace=tr)
+        torch.cuda.synchronize()
+        total_b += layer_bytes(L, tr["masks"].cpu().numpy(), tr["topk_idx"].cpu().numpy())
+
+    def step():
+        for L, x, y, ws in zip(layers, xs_by_layer, ys, wss):
+            moe.layer_forward(L, x, y=y, ws=ws)
+    sec = time_graph(step, reps=5, inner=4)
+    return {"workload": label, "tokens": T, "ms_per_step": sec * 1e3, "tokens_per_s": T / sec,
+            "bytes_per_step": total_b, "achieved_gbs": total_b / sec / 1e9,
+            "hbm_frac": total_b / sec / 1e9 / HBM_PEAK_GBS}
+
+
+def layers_measure():
+    """The 32-layer Mixtral stack (T = 1, 16) and the fine-grained 64+2 layer
+    (T = 1, 64), each as tokens/s of a decode step, router included."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    out = {}
+    c = synth.CONFIGS[synth.CFG_FINE]
+    bias = synth.zipf_bias(synth.CFG_FINE, 0, c["E"], c["zipf_s"])
+    fine = device_layer(synth.CFG_FINE, 0, c["E"], c["S"], c["k"], c["d"], c["f"], c["wdt"],
+                        c["x_scale"], c["sparsity"], bias=bias)
+    for T in (1, 64):
+        x = torch.from_numpy(synth.tokens_f32(synth.CFG_FINE, T, c["d"], c["x_scale"])).half().to(dev)
+        out[f"fine_T{T}"] = layer_workload(
+            [fine], [x], f"DeepSeek-V2-Lite-shaped layer, 64 routed (top-6) + 2 shared experts, "
+                         f"d=2048 f=1408, Zipf router bias, 70% sparsity, {T} tokens")
+    del fine
+    torch.cuda.empty_cache()
+    c = synth.CONFIGS[synth.CFG_STACK]
+    log("drawing the 32-layer stack (64.9 GB)")
+    stack = [device_layer(synth.CFG_STACK, l, c["E"], 0, c["k"], c["d"], c["f"], c["wdt"], c["x_scale"],
+                          c["sparsity"]) for l in range(c["L"])]
+    for T in (1, 16):
+        xs = synth.hidden_stream_f32(synth.CFG_STACK, c["L"], T, c["d"], c["x_scale"])
+        xl = [torch.from_numpy(xs[l]).half().to(dev) for l in range(c["L"])]
+        out[f"stack_T{T}"] = layer_workload(
+            stack, xl, f"32 Mixtral-8x7B-shaped layers x 8 experts (d=4096 f=14336), top-2, "
+                       f"80% sparsity, {T} tokens per decode step through all layers")
+    del stack
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(sparsity, budget_s):
     """The fp64 oracle, as it stands, on instance 0 and the same tokens."""
     import oracle
@@ -223,6 +367,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--batched-only", action="store_true",
                     help="only the batched-layer measurement (for profiling)")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the layer workloads (32-layer stack, fine-grained layer)")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched-layer (dense MFMA vs sparse) measurement")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -323,9 +469,36 @@ def main():
             "traffic": counted_traffic(),
         },
     }
+    # the same expert call at batch 4 (Mixtral shape, 90% sparsity)
+    x4 = [x_all[i:i + 4] for i in range(0, NTOK, 4)]
+    y4 = torch.empty((4, D), dtype=torch.float32, device=dev)
+    ws4 = moe.new_workspace(moe.workspace_size(moe.OP_EXPERT, 4, D, F), dev)
+    m4 = torch.empty((4, F), dtype=torch.uint8, device=dev)
+    b4 = 0.0
+    for r in range(R):
+        for t in range(len(x4)):
+            moe.expert_forward_sparse(experts[r], x4[t], y=y4, ws=ws4, mask_out=m4)
+            u = int(m4.any(dim=0).sum().item())
+            b4 += D * F // 4 + F * (D // 64) * 4 + 4 * D * (2 + 4) + 2 * u * D * 2
+    b4 /= R * len(x4)
+    calls = [(experts[i % R], x4[(i // R) % len(x4)]) for i in range(R * len(x4))]
+    ci = [0]
+
+    def call4():
+        e_, x_ = calls[ci[0] % len(calls)]
+        ci[0] += 1
+        moe.expert_forward_sparse(e_, x_, y=y4, ws=ws4)
+    sec4 = time_graph(call4, reps=5, inner=len(calls) * 8)
+    out["more"] = {"expert_b4": {
+        "workload": "one Mixtral-8x7B-shaped expert, 90% sparsity, batch 4 (union of the 4 masks read once)",
+        "ms_per_call": sec4 * 1e3, "tokens_per_s": 4 / sec4, "bytes_per_call": b4,
+        "achieved_gbs": b4 / sec4 / 1e9, "hbm_frac": b4 / sec4 / 1e9 / HBM_PEAK_GBS}}
+    del experts, calls
+    torch.cuda.empty_cache()
+    if not args.no_layers:
+        log("measuring the layer workloads")
+        out["more"].update(layers_measure())
     if not args.no_batched:
-        del experts
-        torch.cuda.empty_cache()
         log("measuring the batched layer (dense MFMA and sparse paths)")
         out["batched"] = batched_measure()
     if not args.no_cpu:

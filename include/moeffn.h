@@ -107,7 +107,7 @@ typedef struct {
  * applied with weight 1), all in the compressed format at a fixed stride. */
 typedef struct {
     int d, f;                   /* hidden size, intermediate size          */
-    int n_routed, n_shared;     /* E, S                                     */
+    int n_routed, n_shared;     /* E, S (k + S <= 1024)                     */
     int top_k;                  /* k, 1 <= k <= E                           */
     int renormalize;            /* 1: softmax over the k chosen logits;
                                    0: full softmax taken at the chosen ones */

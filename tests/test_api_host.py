@@ -157,6 +157,7 @@ def test_layer_rejects(kw, code):
     (dict(top_k=0), -1), (dict(top_k=9), -1), (dict(n_shared=-1), -1), (dict(thresholds=None), -1),
     (dict(up_q=None), -1), (dict(router_w=None), -1), (dict(f=1000), -1), (dict(d=3000), -2),
     (dict(thresholds=FAKE + 2), -3), (dict(gate_t=FAKE + 4), -3),
+    (dict(n_shared=1100), -2),          # more than 1024 routed + shared rows per token
 ])
 def test_layer_rejects_desc(dkw, code):
     assert _layer(desc=_layer_desc(**dkw)) == code
