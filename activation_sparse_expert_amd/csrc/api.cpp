@@ -73,10 +73,13 @@ size_t sparse_lds(int d, int cpw, int tb)
            4 * a16((size_t)tb * 4) + 16;
 }
 
-int choose_tb(int T, int d, int cpw)
+// Tokens per chunk of the sparse kernel for about `n` tokens per expert: at
+// most 4 up to d = 4096, 2 up to 8192 and 1 beyond (larger chunks need more
+// registers than the kernel has).
+int choose_tb(int n, int d, int cpw)
 {
-    int tb = pow2ceil(T);
-    const int tbmax = d <= 4096 ? 8 : 4;
+    int tb = pow2ceil(n);
+    const int tbmax = d <= 4096 ? 4 : (d <= 8192 ? 2 : 1);
     if (tb > tbmax) tb = tbmax;
     while (tb > 1 && sparse_lds(d, cpw, tb) > 150 * 1024) tb /= 2;
     return tb;
@@ -357,7 +360,8 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     a.topk_w = r.topk_w;
     a.part = w.part;
     a.mask_out = trace ? trace->masks : nullptr; a.v_out = nullptr;
-    he = launch_sparse(a, L->wdt == MOE_BF16, choose_tb(T, d, tp.cpw), s);
+    // chunks sized for the average number of tokens a routed expert receives
+    he = launch_sparse(a, L->wdt == MOE_BF16, choose_tb((T * k + E - 1) / E, d, tp.cpw), s);
     if (he != hipSuccess) return MOE_ERR_HIP;
     red.tiles = tp.tiles;
     return hip_status(launch_reduce(red, s));

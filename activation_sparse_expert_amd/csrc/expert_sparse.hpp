@@ -200,7 +200,7 @@ template <int TB, int NCH>
 __host__ __device__ constexpr int rows_per_batch()
 {
     if (TB == 1 && NCH == 1) return 16;
-    return (8 / (NCH * (TB >= 8 ? 2 : 1))) < 1 ? 1 : (8 / (NCH * (TB >= 8 ? 2 : 1)));
+    return (8 / NCH) < 1 ? 1 : 8 / NCH;
 }
 
 template <bool BF16, int TB, class GEO>
@@ -273,26 +273,28 @@ expert_kernel(SparseArgs a)
     const int passes = (nrows + ROWS_PASS - 1) / ROWS_PASS;
     const int CPR = d / 8;                          // 16-byte chunks per d-row
 
-    // phase-A code units of one block of PR passes: loads only, no use
-    uint4 cq[PR][NG];
-    uint32_t csz[PR][NG];
-    uint32_t okm = 0;
-    auto load_block = [&](int p0) {
-        okm = 0;
-#pragma unroll
-        for (int p = 0; p < PR; ++p) {
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const int r = (p0 + p) * ROWS_PASS + wave * RPW + rs;
-                const int g = go + SEG * gi;
-                const bool ok = r < nrows && g < G;
-                const int rr = ok ? r : 0, gg = ok ? g : 0;
-                cq[p][gi] = *(const uint4 *)(upq + (size_t)rr * (d / 4) + (size_t)gg * 16);
-                csz[p][gi] = *(const uint32_t *)(upsz + ((size_t)rr * G + gg) * 2);
-                okm |= (ok ? 1u : 0u) << (p * NG + gi);
-            }
-        }
-    };
+    // phase-A code units of one block of PR passes: loads only, no use.  With
+    // several tokens per chunk a tile has many blocks, and the next block's
+    // units are loaded (into cqn) while the current one is multiplied.
+    uint4 cq[PR][NG], cqn[PR][NG];
+    uint32_t csz[PR][NG], cszn[PR][NG];
+    uint32_t okm = 0, okmn = 0;
+#define LOAD_BLOCK(P0, CQ, CSZ, OKM)                                                        \
+    {                                                                                       \
+        OKM = 0;                                                                            \
+        _Pragma("unroll") for (int p = 0; p < PR; ++p) {                                    \
+            _Pragma("unroll") for (int gi = 0; gi < NG; ++gi) {                             \
+                const int r = ((P0) + p) * ROWS_PASS + wave * RPW + rs;                     \
+                const int g = go + SEG * gi;                                                \
+                const bool ok = r < nrows && g < G;                                         \
+                const int rr = ok ? r : 0, gg = ok ? g : 0;                                 \
+                CQ[p][gi] = *(const uint4 *)(upq + (size_t)rr * (d / 4) + (size_t)gg * 16); \
+                CSZ[p][gi] = *(const uint32_t *)(upsz + ((size_t)rr * G + gg) * 2);         \
+                OKM |= (ok ? 1u : 0u) << (p * NG + gi);                                     \
+            }                                                                               \
+        }                                                                                   \
+    }
+    auto load_block = [&](int p0) { LOAD_BLOCK(p0, cq, csz, okm) };
 
     // 16-byte x chunks each thread stages per token chunk
     constexpr int XL = (TB * 8 * SEG * NG + THREADS - 1) / THREADS;
@@ -378,7 +380,11 @@ expert_kernel(SparseArgs a)
             }
         }
         for (int p0 = 0; p0 < passes; p0 += PR) {
-            if (p0 > 0) load_block(p0);
+            if constexpr (TB > 1) {
+                if (p0 + PR < passes) LOAD_BLOCK(p0 + PR, cqn, cszn, okmn)
+            } else {
+                if (p0 > 0) load_block(p0);
+            }
             // units outside the tile (ok bit clear) get s = 0 when used: the select
             // is kept away from the loads so that they all issue back to back
             float part[TB][PR];
@@ -432,7 +438,18 @@ expert_kernel(SparseArgs a)
                     L.mk[tb * cpw + r] = fabsf(v) > thr ? 1 : 0;
                 }
             }
+            if constexpr (TB > 1) {
+#pragma unroll
+                for (int p = 0; p < PR; ++p)
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi) {
+                        cq[p][gi] = cqn[p][gi];
+                        csz[p][gi] = cszn[p][gi];
+                    }
+                okm = okmn;
+            }
         }
+#undef LOAD_BLOCK
         __syncthreads();
 
         // exports
@@ -607,10 +624,11 @@ hipError_t launch_geo(const SparseArgs &a, int tb, hipStream_t s)
 {
     switch (tb) {
     case 1: return launch_tb<BF16, 1, GEO>(a, s);
-    case 2: return launch_tb<BF16, 2, GEO>(a, s);
-    case 4: return launch_tb<BF16, 4, GEO>(a, s);
-    case 8:
-        if constexpr (GEO::NCH == 1) return launch_tb<BF16, 8, GEO>(a, s);
+    case 2:
+        if constexpr (GEO::NG <= 2) return launch_tb<BF16, 2, GEO>(a, s);
+        break;
+    case 4:
+        if constexpr (GEO::NG == 1) return launch_tb<BF16, 4, GEO>(a, s);
         break;
     default: break;
     }
