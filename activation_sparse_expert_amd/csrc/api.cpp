@@ -63,37 +63,52 @@ TilePlan plan_tiles(int f, int slots, long long rows, int d)
     return {cpw, tiles};
 }
 
-// LDS bytes of the sparse kernel (mirrors its layout, rounded up).
-size_t sparse_lds(int d, int cpw, int tb)
-{
-    const int G = d / 64;
-    auto a16 = [](size_t x) { return (x + 15) & ~(size_t)15; };
-    return a16((size_t)tb * G * 72 * 2) + a16((size_t)tb * G * 4) + a16((size_t)tb * cpw * 4) +
-           a16((size_t)tb * cpw) + a16((size_t)cpw * 2) + a16((size_t)8 * 8 * tb * 4) +
-           4 * a16((size_t)tb * 4) + 16;
-}
-
 // Tokens per chunk of the sparse kernel for about `n` tokens per expert: at
 // most 4 up to d = 4096, 2 up to 8192 and 1 beyond (larger chunks need more
 // registers than the kernel has).
-int choose_tb(int n, int d, int cpw)
+int choose_tb(long long n, int d)
 {
-    int tb = pow2ceil(n);
+    int tb = 1;
+    while (tb < n && tb < 4) tb <<= 1;
     const int tbmax = d <= 4096 ? 4 : (d <= 8192 ? 2 : 1);
-    if (tb > tbmax) tb = tbmax;
-    while (tb > 1 && sparse_lds(d, cpw, tb) > 150 * 1024) tb /= 2;
-    return tb;
+    return tb > tbmax ? tbmax : tb;
 }
 
-int layer_slots(int T, int E, int k, int S)
+// Grid of the sparse kernel: token chunks x tiles of channels.
+struct SparsePlan {
+    int tb;         // tokens per chunk
+    int slots;      // chunk slots (an upper bound in a layer: routed chunks are data-dependent)
+    TilePlan tp;
+};
+
+// (At most about 60 KB of LDS for every supported d, tb and cpw <= 1024.)
+SparsePlan expert_plan(int T, int d, int f)
+{
+    const int tb = choose_tb(T, d);
+    const int slots = (T + tb - 1) / tb;
+    return SparsePlan{tb, slots, plan_tiles(f, slots, T, d)};
+}
+
+// Layer: chunks sized for the average number of tokens a routed expert
+// receives.  The A experts that receive n_e tokens (sum n_e = T k) hold
+// sum ceil(n_e / tb) <= (T k + A (tb - 1)) / tb chunks, A <= min(E, T k); the
+// S shared experts hold ceil(T / tb) chunks each.  The grid covers that bound;
+// the tiles per chunk are sized for the expected count (half a chunk of
+// padding per expert), so that the chunks that do exist fill the chip.
+SparsePlan layer_plan(int T, int d, int f, int E, int k, int S)
 {
     const long long tk = (long long)T * k;
-    return S + (int)(E < tk ? E : tk);
+    const int tb = choose_tb((tk + E - 1) / E, d);
+    const long long act = E < tk ? E : tk;
+    const long long shared = (long long)S * ((T + tb - 1) / tb);
+    const long long bound = shared + (tk + act * (tb - 1)) / tb;
+    const long long expect = shared + (2 * tk + act * (tb - 1) + 2 * tb - 1) / (2 * tb);
+    return SparsePlan{tb, (int)bound, plan_tiles(f, (int)expect, (long long)T * (k + S), d)};
 }
 
 size_t expert_ws_bytes(int T, int d, int f)
 {
-    const TilePlan tp = plan_tiles(f, 1, T, d);
+    const TilePlan tp = expert_plan(T, d, f).tp;
     return up((size_t)T * tp.tiles * d * 4);
 }
 
@@ -101,6 +116,7 @@ struct LayerWs {
     int32_t *topk_idx;
     float *topk_w;
     int32_t *count, *offset, *pairs, *pair_pos, *active, *n_active;
+    int32_t *chunk_tab, *n_chunks;
     float *part;
     float *h;
 };
@@ -108,10 +124,10 @@ struct LayerWs {
 size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, void *base)
 {
     const long long rows = (long long)T * (k + S);
-    const TilePlan tp = plan_tiles(f, layer_slots(T, E, k, S), rows, d);
+    const TilePlan tp = layer_plan(T, d, f, E, k, S).tp;
     const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
     size_t o = 0;
-    size_t off[11];
+    size_t off[13];
     off[0] = o; o += up(4);
     off[1] = o; o += up((size_t)T * k * 4);
     off[2] = o; o += up((size_t)T * k * 4);
@@ -123,6 +139,8 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     off[8] = o; o += up(4);
     off[9] = o; o += up((size_t)rows * part_tiles * d * 4);
     off[10] = o; o += up(dense_h_bytes(T, f, k, S));
+    off[11] = o; o += up((size_t)T * k * 4);           // every chunk holds at least one pair
+    off[12] = o; o += up(4);
     if (out) {
         char *p = (char *)base;
         out->topk_idx = (int32_t *)(p + off[1]);
@@ -135,6 +153,8 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->n_active = (int32_t *)(p + off[8]);
         out->part = (float *)(p + off[9]);
         out->h = (float *)(p + off[10]);
+        out->chunk_tab = (int32_t *)(p + off[11]);
+        out->n_chunks = (int32_t *)(p + off[12]);
     }
     return o;
 }
@@ -254,10 +274,11 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
 
     hipStream_t s = (hipStream_t)stream;
-    const TilePlan tp = plan_tiles(f, 1, T, d);
+    const SparsePlan sp = expert_plan(T, d, f);
+    const TilePlan tp = sp.tp;
     SparseArgs a{};
     a.d = d; a.f = f;
-    a.slots = 1;
+    a.slots = sp.slots;
     a.cpw = tp.cpw;
     a.tiles = tp.tiles;
     a.up_q = e->up_q; a.up_sz = e->up_sz;
@@ -269,7 +290,7 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     a.layer = 0;
     a.part = (float *)ws;
     a.mask_out = mask_out; a.v_out = v_out;
-    hipError_t he = launch_sparse(a, wdt == MOE_BF16, choose_tb(T, d, tp.cpw), s);
+    hipError_t he = launch_sparse(a, wdt == MOE_BF16, sp.tb, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
     ReduceArgs r{};
     r.part = (const float *)ws; r.tiles = tp.tiles; r.d = d; r.T = T;
@@ -320,11 +341,14 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.count = (trace && trace->expert_count) ? trace->expert_count : w.count;
     r.offset = w.offset; r.pairs = w.pairs; r.pair_pos = w.pair_pos;
     r.active = w.active; r.n_active = w.n_active;
+    const SparsePlan sp = layer_plan(T, d, f, E, k, S);
+    if (path == MOE_PATH_SPARSE) {
+        r.chunk = sp.tb; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;
+    }
     hipError_t he = launch_route(r, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
 
     const size_t qs = (size_t)f * (d / 4), szs = (size_t)f * (d / 64) * 2, wst = (size_t)f * d;
-    const int slots = layer_slots(T, E, k, S);
     ReduceArgs red{};
     red.d = d; red.T = T; red.layer = 1; red.rows_per_tok = k + S; red.k = k; red.S = S;
     red.pair_pos = w.pair_pos; red.part = w.part;
@@ -343,10 +367,10 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         return hip_status(launch_reduce(red, s));
     }
 
-    const TilePlan tp = plan_tiles(f, slots, (long long)T * (k + S), d);
+    const TilePlan tp = sp.tp;
     SparseArgs a{};
     a.d = d; a.f = f;
-    a.slots = slots;
+    a.slots = sp.slots;
     a.cpw = tp.cpw;
     a.tiles = tp.tiles;
     a.up_q = L->up_q; a.up_sz = L->up_sz;
@@ -356,12 +380,12 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     a.x = (const uint16_t *)x; a.T = T;
     a.token_scale = nullptr;
     a.layer = 1; a.E = E; a.k = k; a.S = S;
-    a.active = w.active; a.n_active = w.n_active; a.offset = w.offset; a.pairs = w.pairs;
+    a.chunk_tab = w.chunk_tab; a.n_chunks = w.n_chunks;
+    a.offset = w.offset; a.pairs = w.pairs;
     a.topk_w = r.topk_w;
     a.part = w.part;
     a.mask_out = trace ? trace->masks : nullptr; a.v_out = nullptr;
-    // chunks sized for the average number of tokens a routed expert receives
-    he = launch_sparse(a, L->wdt == MOE_BF16, choose_tb((T * k + E - 1) / E, d, tp.cpw), s);
+    he = launch_sparse(a, L->wdt == MOE_BF16, sp.tb, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
     red.tiles = tp.tiles;
     return hip_status(launch_reduce(red, s));

@@ -242,22 +242,34 @@ expert_kernel(SparseArgs a)
     L.misc = (int32_t *)(smem + off[10]);
 
     // ---- which expert and which tokens ------------------------------------
-    const int slot = blockIdx.x / a.tiles;
-    const int tile = blockIdx.x - slot * a.tiles;
-    int e = 0, ntok = a.T, pair0 = 0;
+    // The grid is (token chunk) x (tile).  Single expert: chunk c holds tokens
+    // c TB ..; layer: the S shared experts' chunks of every token come first,
+    // then the routed chunks listed by the grouping kernel.
+    const int chunk = blockIdx.x / a.tiles;
+    const int tile = blockIdx.x - chunk * a.tiles;
+    int e = 0, nt = 0, pos0 = 0, tbase = 0, sh = 0;
     bool shared_slot = false;
-    if (a.layer) {
-        if (slot < a.S) {
-            e = a.E + slot;
+    if (!a.layer) {
+        tbase = chunk * TB;
+        nt = min(TB, a.T - tbase);
+    } else {
+        const int nsc = (a.T + TB - 1) / TB;        // chunks per shared expert
+        if (chunk < a.S * nsc) {
+            sh = chunk / nsc;
+            tbase = (chunk - sh * nsc) * TB;
+            nt = min(TB, a.T - tbase);
+            e = a.E + sh;
             shared_slot = true;
         } else {
-            const int ai = slot - a.S;
-            if (ai >= *a.n_active) return;          // no tokens for this slot
-            e = a.active[ai];
-            pair0 = a.offset[e];
-            ntok = a.offset[e + 1] - pair0;
+            const int ci = chunk - a.S * nsc;
+            if (ci >= *a.n_chunks) return;          // beyond this call's chunks
+            const int ent = a.chunk_tab[ci];
+            e = ent >> 16;
+            pos0 = ent & 0xFFFF;
+            nt = min(TB, a.offset[e + 1] - pos0);
         }
     }
+    if (nt <= 0) return;
     const float thr = a.thr_dev ? a.thr_dev[e] : a.thr;
     const int j0 = tile * cpw;
     const int nrows = min(cpw, f - j0);
@@ -299,305 +311,299 @@ expert_kernel(SparseArgs a)
     // 16-byte x chunks each thread stages per token chunk
     constexpr int XL = (TB * 8 * SEG * NG + THREADS - 1) / THREADS;
 
-    for (int t0 = 0; t0 < ntok; t0 += TB) {
-        const int nt = min(TB, ntok - t0);
-
-        // ---- token bookkeeping (small loads, before the streams start) --------
-        if (tid < TB) {
-            int t = 0, sl = 0, row = 0;
-            if (tid < nt) {
-                if (!a.layer) {
-                    t = t0 + tid;
-                    row = t;
-                } else if (shared_slot) {
-                    t = t0 + tid;
-                    sl = a.k + slot;
-                    row = a.T * a.k + slot * a.T + t;
-                } else {
-                    const int pos = pair0 + t0 + tid;
-                    const int p = a.pairs[pos];
-                    t = p / a.k;
-                    sl = p - t * a.k;
-                    row = pos;
-                }
-            }
-            L.tok_t[tid] = t;
-            L.tok_slot[tid] = sl;
-            L.tok_row[tid] = row;
-        }
-        __syncthreads();
-
-        // ---- x loads, then the up-code loads; only x is waited for here -------
-        uint4 xl[XL];
-#pragma unroll
-        for (int u = 0; u < XL; ++u) {
-            const int i = tid + u * THREADS;
-            const int tb = i / CPR, c = i - tb * CPR;
-            xl[u] = make_uint4(0, 0, 0, 0);
-            if (i < TB * CPR && tb < nt) xl[u] = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
-        }
-        load_block(0);          // up codes do not depend on x: in flight while x is staged
-#pragma unroll
-        for (int u = 0; u < XL; ++u) {
-            const int i = tid + u * THREADS;
-            const int tb = i / CPR, c = i - tb * CPR;
-            if (i < TB * CPR)
-                *(uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8) = xl[u];
-        }
-        __syncthreads();
-        for (int i = tid; i < TB * G; i += THREADS) {
-            const uint32_t *xp = (const uint32_t *)(L.xs + (size_t)i * kXPad);
-            float s0 = 0.f, s1 = 0.f;
-#pragma unroll 8
-            for (int m = 0; m < 32; ++m) {
-                s0 += lo16_to_float<BF16>(xp[m]);
-                s1 += hi16_to_float<BF16>(xp[m]);
-            }
-            L.xg[i] = s0 + s1;
-        }
-        __syncthreads();
-
-        // ---- A: v = x W^up for this tile ------------------------------------
-        uint32_t xr_a[XREG ? TB * NG : 1][32];
-        float xg_a[TB][NG];
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int g = min(go + SEG * gi, G - 1);
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                xg_a[tb][gi] = L.xg[tb * G + g];
-                if constexpr (XREG) {
-                    const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const uint4 xx = xv[q];
-                        xr_a[tb * NG + gi][4 * q + 0] = xx.x;
-                        xr_a[tb * NG + gi][4 * q + 1] = xx.y;
-                        xr_a[tb * NG + gi][4 * q + 2] = xx.z;
-                        xr_a[tb * NG + gi][4 * q + 3] = xx.w;
-                    }
-                }
-            }
-        }
-        for (int p0 = 0; p0 < passes; p0 += PR) {
-            if constexpr (TB > 1) {
-                if (p0 + PR < passes) LOAD_BLOCK(p0 + PR, cqn, cszn, okmn)
+    // ---- token bookkeeping (small loads, before the streams start) --------
+    if (tid < TB) {
+        int t = 0, sl = 0, row = 0;
+        float sc = 1.0f;                            // router weight / caller's scale
+        if (tid < nt) {
+            if (!a.layer) {
+                t = tbase + tid;
+                row = t;
+                if (a.token_scale) sc = a.token_scale[t];
+            } else if (shared_slot) {
+                t = tbase + tid;
+                sl = a.k + sh;
+                row = a.T * a.k + sh * a.T + t;
             } else {
-                if (p0 > 0) load_block(p0);
-            }
-            // units outside the tile (ok bit clear) get s = 0 when used: the select
-            // is kept away from the loads so that they all issue back to back
-            float part[TB][PR];
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                for (int p = 0; p < PR; ++p) part[tb][p] = 0.f;
-#pragma unroll
-            for (int p = 0; p < PR; ++p) {
-                if (p0 + p >= passes) continue;         // uniform: padding passes of the block
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    uint32_t pw[32];
-                    decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
-                    const bool ok = (okm >> (p * NG + gi)) & 1u;
-                    const float s = ok ? half_bits_to_float(csz[p][gi] & 0xFFFFu) : 0.f;
-                    const float z = half_bits_to_float(csz[p][gi] >> 16);
-                    const int g = min(go + SEG * gi, G - 1);
-#pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) {
-                        float sp;
-                        if constexpr (XREG) {
-                            sp = group_dot<BF16>(pw, xr_a[tb * NG + gi]);
-                        } else {
-                            uint32_t xp[32];
-                            const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
-#pragma unroll
-                            for (int q = 0; q < 8; ++q) {
-                                const uint4 xx = xv[q];
-                                xp[4 * q + 0] = xx.x;
-                                xp[4 * q + 1] = xx.y;
-                                xp[4 * q + 2] = xx.z;
-                                xp[4 * q + 3] = xx.w;
-                            }
-                            sp = group_dot<BF16>(pw, xp);
-                        }
-                        part[tb][p] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
-                    }
-                }
-            }
-            // reduce the PR passes of each token over the segment's lanes
-            constexpr int LOGPR = Log2<PR>::v;
-            const int psel = go >> (LOGSEG - LOGPR);              // pass this lane ends up with
-            const bool writer = (go & ((SEG / PR) - 1)) == 0;
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const float v = transposed_reduce<PR, SEG>(part[tb], lane);
-                const int r = (p0 + psel) * ROWS_PASS + wave * RPW + rs;
-                if (writer && r < nrows && tb < nt && p0 + psel < passes) {
-                    L.vs[tb * cpw + r] = v;
-                    L.mk[tb * cpw + r] = fabsf(v) > thr ? 1 : 0;
-                }
-            }
-            if constexpr (TB > 1) {
-#pragma unroll
-                for (int p = 0; p < PR; ++p)
-#pragma unroll
-                    for (int gi = 0; gi < NG; ++gi) {
-                        cq[p][gi] = cqn[p][gi];
-                        csz[p][gi] = cszn[p][gi];
-                    }
-                okm = okmn;
+                const int pos = pos0 + tid;
+                const int p = a.pairs[pos];
+                t = p / a.k;
+                sl = p - t * a.k;
+                row = pos;
+                sc = a.topk_w[p];
             }
         }
-#undef LOAD_BLOCK
-        __syncthreads();
+        L.tok_t[tid] = t;
+        L.tok_slot[tid] = sl;
+        L.tok_row[tid] = row;
+        L.tok_sc[tid] = sc;
+    }
+    __syncthreads();
 
-        // exports
-        if (a.v_out || a.mask_out) {
-            for (int i = tid; i < nt * nrows; i += THREADS) {
-                const int tb = i / nrows, r = i - tb * nrows;
-                const int t = L.tok_t[tb];
-                if (a.layer) {
-                    if (a.mask_out)
-                        a.mask_out[((size_t)t * (a.k + a.S) + L.tok_slot[tb]) * f + j0 + r] =
-                            L.mk[tb * cpw + r];
-                } else {
-                    if (a.mask_out) a.mask_out[(size_t)t * f + j0 + r] = L.mk[tb * cpw + r];
-                    if (a.v_out) a.v_out[(size_t)t * f + j0 + r] = L.vs[tb * cpw + r];
+    // ---- x loads, then the up-code loads; only x is waited for here -------
+    uint4 xl[XL];
+#pragma unroll
+    for (int u = 0; u < XL; ++u) {
+        const int i = tid + u * THREADS;
+        const int tb = i / CPR, c = i - tb * CPR;
+        xl[u] = make_uint4(0, 0, 0, 0);
+        if (i < TB * CPR && tb < nt) xl[u] = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
+    }
+    load_block(0);          // up codes do not depend on x: in flight while x is staged
+#pragma unroll
+    for (int u = 0; u < XL; ++u) {
+        const int i = tid + u * THREADS;
+        const int tb = i / CPR, c = i - tb * CPR;
+        if (i < TB * CPR)
+            *(uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8) = xl[u];
+    }
+    __syncthreads();
+    for (int i = tid; i < TB * G; i += THREADS) {
+        const uint32_t *xp = (const uint32_t *)(L.xs + (size_t)i * kXPad);
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+        for (int m = 0; m < 32; ++m) {
+            s0 += lo16_to_float<BF16>(xp[m]);
+            s1 += hi16_to_float<BF16>(xp[m]);
+        }
+        L.xg[i] = s0 + s1;
+    }
+    __syncthreads();
+
+    // ---- A: v = x W^up for this tile ------------------------------------
+    uint32_t xr_a[XREG ? TB * NG : 1][32];
+    float xg_a[TB][NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const int g = min(go + SEG * gi, G - 1);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            xg_a[tb][gi] = L.xg[tb * G + g];
+            if constexpr (XREG) {
+                const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint4 xx = xv[q];
+                    xr_a[tb * NG + gi][4 * q + 0] = xx.x;
+                    xr_a[tb * NG + gi][4 * q + 1] = xx.y;
+                    xr_a[tb * NG + gi][4 * q + 2] = xx.z;
+                    xr_a[tb * NG + gi][4 * q + 3] = xx.w;
                 }
             }
         }
-
-        // ---- B: compaction of the union mask -------------------------------
-        if (wave == 0) {
-            int n = 0;
-            for (int r0 = 0; r0 < nrows; r0 += 64) {
-                const int r = r0 + lane;
-                int on = 0;
-                if (r < nrows)
-                    for (int tb = 0; tb < nt; ++tb) on |= L.mk[tb * cpw + r];
-                const uint64_t bal = __ballot(on);
-                const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-                if (on) L.list[n + pre] = (uint16_t)r;
-                n += __popcll(bal);
-            }
-            if (lane == 0) L.misc[0] = n;
+    }
+    for (int p0 = 0; p0 < passes; p0 += PR) {
+        if constexpr (TB > 1) {
+            if (p0 + PR < passes) LOAD_BLOCK(p0 + PR, cqn, cszn, okmn)
+        } else {
+            if (p0 > 0) load_block(p0);
         }
-        __syncthreads();
-        const int n_act = L.misc[0];
-
-        // ---- C: gate / down gathers over the active channels -----------------
-        float yacc[TB][NCH][8];
+        // units outside the tile (ok bit clear) get s = 0 when used: the select
+        // is kept away from the loads so that they all issue back to back
+        float part[TB][PR];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int i = 0; i < NCH; ++i)
+            for (int p = 0; p < PR; ++p) part[tb][p] = 0.f;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) yacc[tb][i][q] = 0.f;
+        for (int p = 0; p < PR; ++p) {
+            if (p0 + p >= passes) continue;         // uniform: padding passes of the block
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                uint32_t pw[32];
+                decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
+                const bool ok = (okm >> (p * NG + gi)) & 1u;
+                const float s = ok ? half_bits_to_float(csz[p][gi] & 0xFFFFu) : 0.f;
+                const float z = half_bits_to_float(csz[p][gi] >> 16);
+                const int g = min(go + SEG * gi, G - 1);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    float sp;
+                    if constexpr (XREG) {
+                        sp = group_dot<BF16>(pw, xr_a[tb * NG + gi]);
+                    } else {
+                        uint32_t xp[32];
+                        const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const uint4 xx = xv[q];
+                            xp[4 * q + 0] = xx.x;
+                            xp[4 * q + 1] = xx.y;
+                            xp[4 * q + 2] = xx.z;
+                            xp[4 * q + 3] = xx.w;
+                        }
+                        sp = group_dot<BF16>(pw, xp);
+                    }
+                    part[tb][p] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
+                }
+            }
+        }
+        // reduce the PR passes of each token over the segment's lanes
+        constexpr int LOGPR = Log2<PR>::v;
+        const int psel = go >> (LOGSEG - LOGPR);              // pass this lane ends up with
+        const bool writer = (go & ((SEG / PR) - 1)) == 0;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const float v = transposed_reduce<PR, SEG>(part[tb], lane);
+            const int r = (p0 + psel) * ROWS_PASS + wave * RPW + rs;
+            if (writer && r < nrows && tb < nt && p0 + psel < passes) {
+                L.vs[tb * cpw + r] = v;
+                L.mk[tb * cpw + r] = fabsf(v) > thr ? 1 : 0;
+            }
+        }
+        if constexpr (TB > 1) {
+#pragma unroll
+            for (int p = 0; p < PR; ++p)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    cq[p][gi] = cqn[p][gi];
+                    csz[p][gi] = cszn[p][gi];
+                }
+            okm = okmn;
+        }
+    }
+#undef LOAD_BLOCK
+    __syncthreads();
 
-        if (n_act > 0) {
-            uint4 xr[TB][NCH];
+    // exports
+    if (a.v_out || a.mask_out) {
+        for (int i = tid; i < nt * nrows; i += THREADS) {
+            const int tb = i / nrows, r = i - tb * nrows;
+            const int t = L.tok_t[tb];
+            if (a.layer) {
+                if (a.mask_out)
+                    a.mask_out[((size_t)t * (a.k + a.S) + L.tok_slot[tb]) * f + j0 + r] =
+                        L.mk[tb * cpw + r];
+            } else {
+                if (a.mask_out) a.mask_out[(size_t)t * f + j0 + r] = L.mk[tb * cpw + r];
+                if (a.v_out) a.v_out[(size_t)t * f + j0 + r] = L.vs[tb * cpw + r];
+            }
+        }
+    }
+
+    // ---- B: compaction of the union mask -------------------------------
+    if (wave == 0) {
+        int n = 0;
+        for (int r0 = 0; r0 < nrows; r0 += 64) {
+            const int r = r0 + lane;
+            int on = 0;
+            if (r < nrows)
+                for (int tb = 0; tb < nt; ++tb) on |= L.mk[tb * cpw + r];
+            const uint64_t bal = __ballot(on);
+            const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+            if (on) L.list[n + pre] = (uint16_t)r;
+            n += __popcll(bal);
+        }
+        if (lane == 0) L.misc[0] = n;
+    }
+    __syncthreads();
+    const int n_act = L.misc[0];
+
+    // ---- C: gate / down gathers over the active channels -----------------
+    float yacc[TB][NCH][8];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) yacc[tb][i][q] = 0.f;
+
+    if (n_act > 0) {
+        uint4 xr[TB][NCH];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = min(tid + THREADS * i, CPR - 1);
+                xr[tb][i] = *(const uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8);
+                if (tid + THREADS * i >= CPR) xr[tb][i] = make_uint4(0, 0, 0, 0);
+            }
+        for (int b0 = 0; b0 < n_act; b0 += RB) {
+            uint4 gw[RB][NCH], dw[RB][NCH];
+            int rows[RB];
+#pragma unroll
+            for (int q = 0; q < RB; ++q) {
+                const int ent = min(b0 + q, n_act - 1);
+                rows[q] = (int)L.list[ent];
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    gw[q][i] = make_uint4(0, 0, 0, 0);
+                    dw[q][i] = make_uint4(0, 0, 0, 0);
+                    if (b0 + q < n_act) {                   // uniform: no loads past the list
+                        const int c = min(tid + THREADS * i, CPR - 1);
+                        gw[q][i] = *(const uint4 *)(gate + (size_t)rows[q] * d + (size_t)c * 8);
+                        dw[q][i] = *(const uint4 *)(down + (size_t)rows[q] * d + (size_t)c * 8);
+                    }
+                }
+            }
+            // partial gate dots, reduced over the wave, then over waves in LDS
+            float p[TB * RB];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    const int c = min(tid + THREADS * i, CPR - 1);
-                    xr[tb][i] = *(const uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8);
-                    if (tid + THREADS * i >= CPR) xr[tb][i] = make_uint4(0, 0, 0, 0);
-                }
-            for (int b0 = 0; b0 < n_act; b0 += RB) {
-                uint4 gw[RB][NCH], dw[RB][NCH];
-                int rows[RB];
-#pragma unroll
                 for (int q = 0; q < RB; ++q) {
-                    const int ent = min(b0 + q, n_act - 1);
-                    rows[q] = (int)L.list[ent];
+                    float acc = 0.f;
 #pragma unroll
                     for (int i = 0; i < NCH; ++i) {
-                        gw[q][i] = make_uint4(0, 0, 0, 0);
-                        dw[q][i] = make_uint4(0, 0, 0, 0);
-                        if (b0 + q < n_act) {                   // uniform: no loads past the list
-                            const int c = min(tid + THREADS * i, CPR - 1);
-                            gw[q][i] = *(const uint4 *)(gate + (size_t)rows[q] * d + (size_t)c * 8);
-                            dw[q][i] = *(const uint4 *)(down + (size_t)rows[q] * d + (size_t)c * 8);
-                        }
+                        acc = dot2<BF16>(gw[q][i].x, xr[tb][i].x, acc);
+                        acc = dot2<BF16>(gw[q][i].y, xr[tb][i].y, acc);
+                        acc = dot2<BF16>(gw[q][i].z, xr[tb][i].z, acc);
+                        acc = dot2<BF16>(gw[q][i].w, xr[tb][i].w, acc);
                     }
+                    p[tb * RB + q] = acc;
                 }
-                // partial gate dots, reduced over the wave, then over waves in LDS
-                float p[TB * RB];
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                    for (int q = 0; q < RB; ++q) {
-                        float acc = 0.f;
-#pragma unroll
-                        for (int i = 0; i < NCH; ++i) {
-                            acc = dot2<BF16>(gw[q][i].x, xr[tb][i].x, acc);
-                            acc = dot2<BF16>(gw[q][i].y, xr[tb][i].y, acc);
-                            acc = dot2<BF16>(gw[q][i].z, xr[tb][i].z, acc);
-                            acc = dot2<BF16>(gw[q][i].w, xr[tb][i].w, acc);
-                        }
-                        p[tb * RB + q] = acc;
-                    }
-                {
-                    constexpr int NP = TB * RB;
-                    constexpr int NPR = NP < 64 ? NP : 64;
-                    static_assert(NP <= 64, "too many gate partials per batch");
-                    const float v = transposed_reduce<NPR, 64>(p, lane);
-                    constexpr int LOGNP = Log2<NPR>::v;
-                    const int idx = lane >> (6 - LOGNP);
-                    if ((lane & ((64 / NPR) - 1)) == 0) L.gp[wave * NP + idx] = v;
-                }
-                __syncthreads();
-#pragma unroll
-                for (int q = 0; q < RB; ++q) {
-                    const bool valid = b0 + q < n_act;
-                    const int r = rows[q];
-#pragma unroll
-                    for (int tb = 0; tb < TB; ++tb) {
-                        float g = 0.f;
-#pragma unroll
-                        for (int w = 0; w < W; ++w) g += L.gp[w * TB * RB + tb * RB + q];
-                        const float h = (valid && tb < nt && L.mk[tb * cpw + r])
-                                            ? silu(g) * L.vs[tb * cpw + r] : 0.f;
-#pragma unroll
-                        for (int i = 0; i < NCH; ++i) {
-                            const uint32_t dv[4] = {dw[q][i].x, dw[q][i].y, dw[q][i].z, dw[q][i].w};
-#pragma unroll
-                            for (int m = 0; m < 4; ++m) {
-                                yacc[tb][i][2 * m] += h * lo16_to_float<BF16>(dv[m]);
-                                yacc[tb][i][2 * m + 1] += h * hi16_to_float<BF16>(dv[m]);
-                            }
-                        }
-                    }
-                }
-                __syncthreads();
+            {
+                constexpr int NP = TB * RB;
+                constexpr int NPR = NP < 64 ? NP : 64;
+                static_assert(NP <= 64, "too many gate partials per batch");
+                const float v = transposed_reduce<NPR, 64>(p, lane);
+                constexpr int LOGNP = Log2<NPR>::v;
+                const int idx = lane >> (6 - LOGNP);
+                if ((lane & ((64 / NPR) - 1)) == 0) L.gp[wave * NP + idx] = v;
             }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < RB; ++q) {
+                const bool valid = b0 + q < n_act;
+                const int r = rows[q];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    float g = 0.f;
+#pragma unroll
+                    for (int w = 0; w < W; ++w) g += L.gp[w * TB * RB + tb * RB + q];
+                    const float h = (valid && tb < nt && L.mk[tb * cpw + r])
+                                        ? silu(g) * L.vs[tb * cpw + r] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < NCH; ++i) {
+                        const uint32_t dv[4] = {dw[q][i].x, dw[q][i].y, dw[q][i].z, dw[q][i].w};
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            yacc[tb][i][2 * m] += h * lo16_to_float<BF16>(dv[m]);
+                            yacc[tb][i][2 * m + 1] += h * hi16_to_float<BF16>(dv[m]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
         }
-        // ---- D: this workgroup's scaled partial rows -------------------------
+    }
+    // ---- D: this workgroup's scaled partial rows -------------------------
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            if (tb >= nt) continue;
-            float sc = 1.0f;                            // router weight / caller's scale
-            if (!a.layer) {
-                if (a.token_scale) sc = a.token_scale[t0 + tb];
-            } else if (!shared_slot) {
-                sc = a.topk_w[a.pairs[pair0 + t0 + tb]];
-            }
-            float *dst = a.part + ((size_t)L.tok_row[tb] * a.tiles + tile) * d;
+    for (int tb = 0; tb < TB; ++tb) {
+        if (tb >= nt) continue;
+        const float sc = L.tok_sc[tb];
+        float *dst = a.part + ((size_t)L.tok_row[tb] * a.tiles + tile) * d;
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int c = tid + THREADS * i;
-                if (c >= CPR) continue;
-                float4 lo = make_float4(sc * yacc[tb][i][0], sc * yacc[tb][i][1],
-                                        sc * yacc[tb][i][2], sc * yacc[tb][i][3]);
-                float4 hi = make_float4(sc * yacc[tb][i][4], sc * yacc[tb][i][5],
-                                        sc * yacc[tb][i][6], sc * yacc[tb][i][7]);
-                *(float4 *)(dst + (size_t)c * 8) = lo;
-                *(float4 *)(dst + (size_t)c * 8 + 4) = hi;
-            }
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + THREADS * i;
+            if (c >= CPR) continue;
+            float4 lo = make_float4(sc * yacc[tb][i][0], sc * yacc[tb][i][1],
+                                    sc * yacc[tb][i][2], sc * yacc[tb][i][3]);
+            float4 hi = make_float4(sc * yacc[tb][i][4], sc * yacc[tb][i][5],
+                                    sc * yacc[tb][i][6], sc * yacc[tb][i][7]);
+            *(float4 *)(dst + (size_t)c * 8) = lo;
+            *(float4 *)(dst + (size_t)c * 8 + 4) = hi;
         }
-        __syncthreads();
     }
 }
 

@@ -11,8 +11,8 @@ struct SparseArgs {
     uint32_t dec_mask, dec_one;         // INT2 decode constants (set by the launcher)
     int d, f;
     int cpw;                            // channels per workgroup tile
-    int tiles;                          // workgroups per expert
-    int slots;                          // expert slots in the grid
+    int tiles;                          // workgroups per token chunk
+    int slots;                          // token-chunk slots in the grid
     const uint8_t *up_q;                // expert 0 of a fixed-stride pool
     const uint16_t *up_sz;
     const uint16_t *gate;
@@ -26,8 +26,8 @@ struct SparseArgs {
     const float *token_scale;           // [T] or nullptr
     // layer mode (layer != 0)
     int layer, E, k, S;
-    const int32_t *active;              // [E] ascending ids of experts with tokens
-    const int32_t *n_active;            // [1]
+    const int32_t *chunk_tab;           // routed chunks: expert << 16 | first grouped position
+    const int32_t *n_chunks;            // [1] routed chunks in chunk_tab
     const int32_t *offset;              // [E+1]
     const int32_t *pairs;               // [T*k]
     const float *topk_w;                // [T*k]
@@ -37,7 +37,7 @@ struct SparseArgs {
     float *v_out;                       // single only: [T][f]
 };
 
-// Launch the fused Algorithm-1 kernel; tb = tokens per chunk (1, 2, 4, 8).
+// Launch the fused Algorithm-1 kernel; tb = tokens per chunk (1, 2, 4).
 hipError_t launch_sparse_expert_f16(const SparseArgs &a, int tb, hipStream_t s);
 hipError_t launch_sparse_expert_bf16(const SparseArgs &a, int tb, hipStream_t s);
 
@@ -71,6 +71,8 @@ struct RouteArgs {
     int32_t *count, *offset, *pairs;    // nullable as a group (grouping skipped)
     int32_t *pair_pos;                  // nullable: grouped position of each pair
     int32_t *active, *n_active;         // nullable
+    int chunk;                          // > 0: split each expert's pairs into chunks of this size
+    int32_t *chunk_tab, *n_chunks;      // [<= T*k], [1]: expert << 16 | first grouped position
 };
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 

@@ -6,8 +6,9 @@
 // the top-k with ties going to the lower index, and writes the softmax
 // weights.  A second kernel of one workgroup then groups the T*k (token, slot)
 // pairs by expert: counts, exclusive offsets, the pairs of each expert in
-// ascending order, their grouped positions, and the list of experts that
-// received tokens.  A single token is grouped by its own workgroup.  No
+// ascending order, their grouped positions, the list of experts that received
+// tokens and, for the sparse layer, the table of fixed-size token chunks that
+// sets its grid.  A single token is grouped by its own workgroup.  No
 // host synchronisation, atomics across workgroups or fences are involved.
 #include "device.hpp"
 #include "internal.hpp"
@@ -58,14 +59,17 @@ __device__ __forceinline__ void argmax_pair(float &v, int &i, float ov, int oi)
 
 // Counting sort of the T*k pairs by expert, stable in pair order.  Reads the
 // top-k indices through coherent loads (they were written by this or an
-// earlier kernel).
+// earlier kernel).  With a.chunk > 0 it also lists every expert's pairs in
+// chunks of a.chunk consecutive grouped positions (the last one shorter),
+// experts in ascending order: entry = expert << 16 | first position.
 __device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
 {
     const int tid = threadIdx.x;
     const int E = a.E;
     int *cnt = (int *)smem;                          // [E] counts
     int *run = cnt + E;                              // [E] running placement base
-    int *ce = run + E;                               // [kRouteThreads] chunk experts
+    int *ce = run + E;                               // [kRouteThreads] experts of a batch of pairs
+    int *cst = ce + kRouteThreads;                   // [E+1] first chunk of each expert
     const int P = a.T * a.k;
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
@@ -73,16 +77,35 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
         atomicAdd(&cnt[load_coherent_i32(a.topk_idx + p)], 1);
     __syncthreads();
     if (tid == 0) {
-        int o = 0, na = 0;
+        int o = 0, na = 0, nc = 0;
         for (int e = 0; e < E; ++e) {
             a.offset[e] = o;
             run[e] = o;
+            cst[e] = nc;
             a.count[e] = cnt[e];
             if (a.active && cnt[e] > 0) a.active[na++] = e;
+            if (a.chunk > 0) nc += (cnt[e] + a.chunk - 1) / a.chunk;
             o += cnt[e];
         }
         a.offset[E] = o;
+        cst[E] = nc;
         if (a.n_active) *a.n_active = na;
+        if (a.chunk > 0) *a.n_chunks = nc;
+    }
+    __syncthreads();
+    if (a.chunk > 0) {
+        // chunk ci belongs to the last expert whose first chunk is <= ci
+        // (experts without pairs own no chunk and share the next one's start)
+        const int nc = cst[E];
+        for (int ci = tid; ci < nc; ci += kRouteThreads) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (cst[mid] <= ci) lo = mid;
+                else hi = mid - 1;
+            }
+            a.chunk_tab[ci] = (lo << 16) | (run[lo] + (ci - cst[lo]) * a.chunk);
+        }
     }
     __syncthreads();
     // stable placement, one chunk of pairs at a time
@@ -217,7 +240,7 @@ group_kernel(RouteArgs a)
 hipError_t launch_route(const RouteArgs &a, hipStream_t s)
 {
     size_t lds = (size_t)a.d * 4 + (size_t)a.E * 4 + (size_t)a.k * 4 + 16;
-    const size_t lds_group = (size_t)a.E * 8 + kRouteThreads * 4 + 16;
+    const size_t lds_group = (size_t)a.E * 12 + kRouteThreads * 4 + 32;
     if (lds_group > lds) lds = lds_group;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)route_kernel,
