@@ -1,6 +1,6 @@
 // Sum of per-workgroup partial rows into the output (second kernel of the
-// expert and layer paths; two variants by the number of contributions).  Token t's output row is the sum, in a fixed order,
-// of `tiles` partials of each of its rows: one row per token for a single
+// expert and layer paths; two variants by the number of contributions).
+// Token t's output row is the sum, in a fixed order, of `tiles` partials of each of its rows: one row per token for a single
 // expert; for a layer, one row per routed choice (at the pair's position in the
 // grouped order) and one per shared expert.  Router weights were applied when
 // the partials were written.  The order of the additions is fixed, so the
@@ -13,8 +13,9 @@ namespace moeffn {
 namespace {
 
 constexpr int kRedThreads = 256;
-constexpr int kCols = 16;               // output columns per workgroup (4 threads x float4)
-constexpr int kGroups = kRedThreads / 4;  // contribution groups per workgroup
+constexpr int kCols = 32;               // output columns per workgroup: one 128-byte line of a row
+constexpr int kSeg = kCols / 4;         // threads per line (float4 each)
+constexpr int kGroups = kRedThreads / kSeg;  // contribution groups per workgroup
 constexpr int kBatch = 8;               // loads in flight per thread
 constexpr int kMaxRowsPerTok = kMaxExpertsPerToken;
 
@@ -25,31 +26,38 @@ __device__ __forceinline__ int part_row(const ReduceArgs &a, int t, int ri)
     return a.T * a.k + (ri - a.k) * a.T + t;
 }
 
-// One workgroup per (token, 16 columns): about d/16 * T workgroups, so the
-// partial rows are read by many compute units at once.
+// One workgroup per (token, 32 columns): d/32 * T workgroups, so the partial
+// rows are read by many compute units at once, in whole 128-byte lines.
+// Contribution c = ri * tiles + tile (row ri of the token, tile `tile`); group g
+// of kSeg threads adds contributions g, g + kGroups, ... in that order, then the
+// groups' sums are added in group order: a fixed order.
 __global__ void __launch_bounds__(kRedThreads)
 reduce_kernel(ReduceArgs a)
 {
-    __shared__ float4 sm[kGroups][4];
+    __shared__ float4 sm[kGroups][kSeg];
     __shared__ int rows_s[kMaxRowsPerTok];
     const int cblocks = a.d / kCols;
     const int t = blockIdx.x / cblocks;
     const int cb = blockIdx.x - t * cblocks;
     for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRedThreads) rows_s[ri] = part_row(a, t, ri);
     __syncthreads();
-    const int cq = threadIdx.x & 3, tg = threadIdx.x >> 2;
+    const int cq = threadIdx.x % kSeg, tg = threadIdx.x / kSeg;
     const int col = cb * kCols + cq * 4;
     const int n = a.rows_per_tok * a.tiles;
+    // (row, tile) of this thread's next contribution, advanced by kGroups at a time
+    int ri = tg / a.tiles, tile = tg - ri * a.tiles;
+    const int dri = kGroups / a.tiles, dtile = kGroups - dri * a.tiles;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    // kBatch loads in flight per thread, then added in order
     for (int c0 = tg; c0 < n; c0 += kGroups * kBatch) {
         float4 v[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-            const int ci = c0 + b * kGroups;
-            const int cc = ci < n ? ci : tg;
-            const int ri = cc / a.tiles, tile = cc - ri * a.tiles;
-            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[ri] * a.tiles + tile) * a.d + col);
+            const bool ok = c0 + b * kGroups < n;
+            const int r = ok ? ri : 0, tl = ok ? tile : 0;
+            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[r] * a.tiles + tl) * a.d + col);
+            ri += dri;
+            tile += dtile;
+            if (tile >= a.tiles) { tile -= a.tiles; ++ri; }
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -93,14 +101,16 @@ reduce_rows_kernel(ReduceArgs a)
     __syncthreads();
     if (col >= a.d) return;
     const int n = a.rows_per_tok * a.tiles;
+    int ri = 0, tile = 0;                       // (row, tile) of contribution c0 + b
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = 0; c0 < n; c0 += kRowBatch) {
         float4 v[kRowBatch];
 #pragma unroll
         for (int b = 0; b < kRowBatch; ++b) {
-            const int ci = min(c0 + b, n - 1);
-            const int ri = ci / a.tiles, tile = ci - ri * a.tiles;
-            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[ri] * a.tiles + tile) * a.d + col);
+            const bool ok = c0 + b < n;
+            const int r = ok ? ri : 0, tl = ok ? tile : 0;
+            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[r] * a.tiles + tl) * a.d + col);
+            if (++tile == a.tiles) { tile = 0; ++ri; }
         }
 #pragma unroll
         for (int b = 0; b < kRowBatch; ++b) {
