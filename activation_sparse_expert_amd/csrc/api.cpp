@@ -170,7 +170,8 @@ moe_status check_route_args(const void *x, moe_dtype xdt, int T, int d, const vo
                             moe_dtype rdt, int E, int k)
 {
     if (!x || !rw) return MOE_ERR_INVALID_ARG;
-    if (T < 1 || d < 1 || E < 1 || E > 1024 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (T < 1 || d < 8 || E < 1 || E > 1024 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+    if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;         // rows are read in 16-byte units
     if ((long long)T * k > 65536) return MOE_ERR_UNSUPPORTED;
     if (!valid_out(xdt) || !valid_out(rdt)) return MOE_ERR_UNSUPPORTED;
     if ((size_t)d * 4 + (size_t)E * 4 + (size_t)k * 4 + 16 > 160 * 1024) return MOE_ERR_UNSUPPORTED;

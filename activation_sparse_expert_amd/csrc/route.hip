@@ -17,7 +17,7 @@ namespace moeffn {
 
 namespace {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
 __device__ __forceinline__ float load_any(const void *p, int dt, size_t i)
@@ -62,8 +62,11 @@ __device__ __forceinline__ void argmax_pair(float &v, int &i, float ov, int oi)
 // earlier kernel).  With a.chunk > 0 it also lists every expert's pairs in
 // chunks of a.chunk consecutive grouped positions (the last one shorter),
 // experts in ascending order: entry = expert << 16 | first position.
-__device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
+__device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, int my_e)
 {
+    // reg: every pair is p = tid and this thread's pair chose expert my_e (a
+    // single token with k <= kRouteThreads, known in registers); else the
+    // choices are read from memory
     const int tid = threadIdx.x;
     const int E = a.E;
     int *cnt = (int *)smem;                          // [E] counts
@@ -74,7 +77,7 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
     for (int p = tid; p < P; p += kRouteThreads)
-        atomicAdd(&cnt[load_coherent_i32(a.topk_idx + p)], 1);
+        atomicAdd(&cnt[reg ? my_e : load_coherent_i32(a.topk_idx + p)], 1);
     __syncthreads();
     if (tid == 0) {
         int o = 0, na = 0, nc = 0;
@@ -111,7 +114,7 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
     // stable placement, one chunk of pairs at a time
     for (int b = 0; b < P; b += kRouteThreads) {
         const int p = b + tid;
-        const int e = p < P ? load_coherent_i32(a.topk_idx + p) : -1;
+        const int e = p < P ? (reg ? my_e : load_coherent_i32(a.topk_idx + p)) : -1;
         ce[tid] = e;
         __syncthreads();
         if (e >= 0) {
@@ -129,6 +132,7 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem)
     }
 }
 
+template <int CB, int GE>
 __global__ void __launch_bounds__(kRouteThreads)
 route_kernel(RouteArgs a)
 {
@@ -160,28 +164,64 @@ route_kernel(RouteArgs a)
     }
     __syncthreads();
 
-    // logits: one wave per expert; a lane takes chunks lane, lane + 64, ... of the
-    // router row in a fixed order (4 loads in flight), then a fixed butterfly
-    for (int e = wave; e < E; e += kRouteWaves) {
-        float p = 0.f;
-        for (int c0 = lane; c0 < nch; c0 += 4 * 64) {
-            float w[4][8];
+    // logits: a wave takes GE experts at a time (e = wave, wave + W, ...) and a
+    // lane the 16-byte units lane, lane + 64, ... of their rows, CB units per
+    // expert per round: GE * CB = 16 loads in flight.  Every expert's sum runs
+    // in the same order (units ascending within a lane, then a fixed
+    // butterfly), so identical router rows tie exactly.
+    {
+        const int esz = a.rdt == 2 ? 4 : 2;
+        const int epu = 16 / esz;                       // elements per 16-byte unit
+        const int nu = d / epu;
+        const unsigned char *rw = (const unsigned char *)a.rw;
+        for (int e0 = wave; e0 < E; e0 += kRouteWaves * GE) {
+            float p[GE];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = min(c0 + u * 64, nch - 1);
-                load8(a.rw, a.rdt, (size_t)e * d + (size_t)c * 8, w[u]);
+            for (int g = 0; g < GE; ++g) p[g] = 0.f;
+            for (int u0 = 0; u0 < nu; u0 += 64 * CB) {
+                uint4 w[GE][CB];
+#pragma unroll
+                for (int g = 0; g < GE; ++g)
+#pragma unroll
+                    for (int u = 0; u < CB; ++u) {
+                        const int e = e0 + kRouteWaves * g, uu = u0 + lane + 64 * u;
+                        w[g][u] = make_uint4(0, 0, 0, 0);
+                        if (e < E && uu < nu) w[g][u] = load_nt16(rw + ((size_t)e * d) * esz + (size_t)uu * 16);
+                    }
+#pragma unroll
+                for (int g = 0; g < GE; ++g)
+#pragma unroll
+                    for (int u = 0; u < CB; ++u) {
+                        const int uu = u0 + lane + 64 * u;
+                        if (e0 + kRouteWaves * g < E && uu < nu) {
+                            const float *xp = xs + (size_t)uu * epu;
+                            const uint32_t ww[4] = {w[g][u].x, w[g][u].y, w[g][u].z, w[g][u].w};
+                            if (a.rdt == 2) {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) p[g] += xp[q] * __uint_as_float(ww[q]);
+                            } else if (a.rdt == 1) {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    p[g] += xp[2 * q] * bf16_bits_to_float((uint16_t)(ww[q] & 0xFFFFu));
+                                    p[g] += xp[2 * q + 1] * bf16_bits_to_float((uint16_t)(ww[q] >> 16));
+                                }
+                            } else {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    p[g] += xp[2 * q] * half_bits_to_float((uint16_t)(ww[q] & 0xFFFFu));
+                                    p[g] += xp[2 * q + 1] * half_bits_to_float((uint16_t)(ww[q] >> 16));
+                                }
+                            }
+                        }
+                    }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + u * 64;
-                if (c < nch) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) p += xs[c * 8 + q] * w[u][q];
-                }
+            for (int g = 0; g < GE; ++g) {
+                const int e = e0 + kRouteWaves * g;
+                const float v = seg_sum<64>(p[g]);
+                if (lane == 0 && e < E) lg[e] = v + (a.bias ? a.bias[e] : 0.f);
             }
         }
-        p = seg_sum<64>(p);
-        if (lane == 0) lg[e] = p + (a.bias ? a.bias[e] : 0.f);
     }
     __syncthreads();
 
@@ -224,7 +264,9 @@ route_kernel(RouteArgs a)
 
     if (!a.count || gridDim.x != 1) return;
     __syncthreads();            // one token: its own workgroup groups it
-    group_pairs(a, smem);
+    const int my_e = tid < k ? sel[tid] : 0;      // read before the grouping reuses LDS
+    __syncthreads();
+    group_pairs(a, smem, k <= kRouteThreads, my_e);
 }
 
 // Grouping of all T*k pairs by one workgroup (after the per-token kernel).
@@ -232,7 +274,7 @@ __global__ void __launch_bounds__(kRouteThreads)
 group_kernel(RouteArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    group_pairs(a, smem);
+    group_pairs(a, smem, false, 0);
 }
 
 }  // namespace
@@ -242,13 +284,23 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
     size_t lds = (size_t)a.d * 4 + (size_t)a.E * 4 + (size_t)a.k * 4 + 16;
     const size_t lds_group = (size_t)a.E * 12 + kRouteThreads * 4 + 32;
     if (lds_group > lds) lds = lds_group;
+    // 16-byte units per lane of one router row (64 lanes): CB of them per expert
+    // and round, GE = 16 / CB experts per wave at a time
+    const int nu = a.d * (a.rdt == 2 ? 4 : 2) / 16;
+    const int cpl = (nu + 63) / 64;
+    const void *kern;
+    if (cpl > 8) kern = (const void *)route_kernel<16, 1>;
+    else if (cpl > 4) kern = (const void *)route_kernel<8, 2>;
+    else if (cpl > 2) kern = (const void *)route_kernel<4, 4>;
+    else if (cpl > 1) kern = (const void *)route_kernel<2, 8>;
+    else kern = (const void *)route_kernel<1, 16>;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)route_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(route_kernel, dim3(a.T), dim3(kRouteThreads), lds, s, a);
-    hipError_t e = hipGetLastError();
+    void *args[] = {(void *)&a};
+    hipError_t e = hipLaunchKernel(kern, dim3(a.T), dim3(kRouteThreads), args, lds, s);
+    if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess || !a.count || a.T == 1) return e;
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kRouteThreads), lds_group, s, a);
     return hipGetLastError();
