@@ -79,21 +79,55 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
     for (int p = tid; p < P; p += kRouteThreads)
         atomicAdd(&cnt[reg ? my_e : load_coherent_i32(a.topk_idx + p)], 1);
     __syncthreads();
-    if (tid == 0) {
-        int o = 0, na = 0, nc = 0;
-        for (int e = 0; e < E; ++e) {
-            a.offset[e] = o;
-            run[e] = o;
-            cst[e] = nc;
-            a.count[e] = cnt[e];
-            if (a.active && cnt[e] > 0) a.active[na++] = e;
-            if (a.chunk > 0) nc += (cnt[e] + a.chunk - 1) / a.chunk;
-            o += cnt[e];
+    // one exclusive scan over the experts gives, packed in 64 bits, the pair
+    // offset (bits 0-23), the first chunk (24-47) and the position in the
+    // active list (48-63) of every expert; no field can overflow (at most
+    // 65536 pairs, chunks or experts)
+    {
+        __shared__ unsigned long long wsum[kRouteWaves];
+        const int lane = tid & 63, wave = tid >> 6;
+        auto pack = [&](int e) -> unsigned long long {
+            if (e >= E) return 0ull;
+            const unsigned long long c = (unsigned)cnt[e];
+            const unsigned long long nch = a.chunk > 0 ? (c + a.chunk - 1) / a.chunk : 0ull;
+            return c | (nch << 24) | ((unsigned long long)(c > 0) << 48);
+        };
+        const int e0 = 2 * tid;                      // this thread's experts: e0, e0 + 1 (E <= 1024)
+        const unsigned long long v0 = pack(e0), v1 = pack(e0 + 1);
+        unsigned long long incl = v0 + v1;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const unsigned long long o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
         }
-        a.offset[E] = o;
-        cst[E] = nc;
-        if (a.n_active) *a.n_active = na;
-        if (a.chunk > 0) *a.n_chunks = nc;
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        unsigned long long base = 0ull, total = 0ull;
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            if (w < wave) base += wsum[w];
+            total += wsum[w];
+        }
+        const unsigned long long ex0 = base + incl - v0 - v1, ex1 = ex0 + v0;
+        const unsigned long long ex[2] = {ex0, ex1};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = e0 + i;
+            if (e < E) {
+                const int off = (int)(ex[i] & 0xFFFFFFull);
+                a.offset[e] = off;
+                run[e] = off;
+                cst[e] = (int)((ex[i] >> 24) & 0xFFFFFFull);
+                a.count[e] = cnt[e];
+                if (a.active && cnt[e] > 0) a.active[(int)(ex[i] >> 48)] = e;
+            }
+        }
+        if (tid == 0) {
+            a.offset[E] = (int)(total & 0xFFFFFFull);
+            cst[E] = (int)((total >> 24) & 0xFFFFFFull);
+            if (a.n_active) *a.n_active = (int)(total >> 48);
+            if (a.chunk > 0) *a.n_chunks = cst[E];
+        }
     }
     __syncthreads();
     if (a.chunk > 0) {
@@ -124,10 +158,7 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
             if (a.pair_pos) a.pair_pos[p] = run[e] + rank;
         }
         __syncthreads();
-        if (tid == 0) {
-            const int n = min(kRouteThreads, P - b);
-            for (int q = 0; q < n; ++q) run[ce[q]]++;
-        }
+        if (e >= 0) atomicAdd(&run[e], 1);          // the batch's pairs of e follow these
         __syncthreads();
     }
 }
