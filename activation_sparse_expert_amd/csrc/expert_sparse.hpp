@@ -518,74 +518,91 @@ expert_kernel(SparseArgs a)
                 xr[tb][i] = *(const uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8);
                 if (tid + THREADS * i >= CPR) xr[tb][i] = make_uint4(0, 0, 0, 0);
             }
-        for (int b0 = 0; b0 < n_act; b0 += RB) {
-            uint4 gw[RB][NCH], dw[RB][NCH];
-            int rows[RB];
-#pragma unroll
-            for (int q = 0; q < RB; ++q) {
-                const int ent = min(b0 + q, n_act - 1);
-                rows[q] = (int)L.list[ent];
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    gw[q][i] = make_uint4(0, 0, 0, 0);
-                    dw[q][i] = make_uint4(0, 0, 0, 0);
-                    if (b0 + q < n_act) {                   // uniform: no loads past the list
-                        const int c = min(tid + THREADS * i, CPR - 1);
-                        gw[q][i] = *(const uint4 *)(gate + (size_t)rows[q] * d + (size_t)c * 8);
-                        dw[q][i] = *(const uint4 *)(down + (size_t)rows[q] * d + (size_t)c * 8);
-                    }
-                }
+        // loads of the batch of rows starting at list entry B0 (none past the list)
+#define C_LOAD(B0, GW, DW, ROWS)                                                               \
+    _Pragma("unroll") for (int q = 0; q < RB; ++q) {                                           \
+        const int ent = min((B0) + q, n_act - 1);                                              \
+        ROWS[q] = (int)L.list[ent];                                                            \
+        _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                      \
+            GW[q][i] = make_uint4(0, 0, 0, 0);                                                 \
+            DW[q][i] = make_uint4(0, 0, 0, 0);                                                 \
+            if ((B0) + q < n_act) {                 /* uniform: no loads past the list */      \
+                const int c = min(tid + THREADS * i, CPR - 1);                                 \
+                GW[q][i] = *(const uint4 *)(gate + (size_t)ROWS[q] * d + (size_t)c * 8);       \
+                DW[q][i] = *(const uint4 *)(down + (size_t)ROWS[q] * d + (size_t)c * 8);       \
+            }                                                                                  \
+        }                                                                                      \
+    }
+        // gate dots of the batch, reduced over the wave and then over the waves
+        // in LDS; h = SiLU(g) v per token and row; h * down into the slices of y
+#define C_COMPUTE(B0, GW, DW, ROWS)                                                            \
+    {                                                                                          \
+        float p[TB * RB];                                                                      \
+        _Pragma("unroll") for (int tb = 0; tb < TB; ++tb)                                      \
+            _Pragma("unroll") for (int q = 0; q < RB; ++q) {                                   \
+                float acc = 0.f;                                                               \
+                _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                              \
+                    acc = dot2<BF16>(GW[q][i].x, xr[tb][i].x, acc);                            \
+                    acc = dot2<BF16>(GW[q][i].y, xr[tb][i].y, acc);                            \
+                    acc = dot2<BF16>(GW[q][i].z, xr[tb][i].z, acc);                            \
+                    acc = dot2<BF16>(GW[q][i].w, xr[tb][i].w, acc);                            \
+                }                                                                              \
+                p[tb * RB + q] = acc;                                                          \
+            }                                                                                  \
+        {                                                                                      \
+            constexpr int NP = TB * RB;                                                        \
+            constexpr int NPR = NP < 64 ? NP : 64;                                             \
+            static_assert(NP <= 64, "too many gate partials per batch");                       \
+            const float v = transposed_reduce<NPR, 64>(p, lane);                               \
+            constexpr int LOGNP = Log2<NPR>::v;                                                \
+            const int idx = lane >> (6 - LOGNP);                                               \
+            if ((lane & ((64 / NPR) - 1)) == 0) L.gp[wave * NP + idx] = v;                     \
+        }                                                                                      \
+        __syncthreads();                                                                       \
+        _Pragma("unroll") for (int q = 0; q < RB; ++q) {                                       \
+            const bool valid = (B0) + q < n_act;                                               \
+            const int r = ROWS[q];                                                             \
+            _Pragma("unroll") for (int tb = 0; tb < TB; ++tb) {                                \
+                float g = 0.f;                                                                 \
+                _Pragma("unroll") for (int w = 0; w < W; ++w) g += L.gp[w * TB * RB + tb * RB + q]; \
+                const float h = (valid && tb < nt && L.mk[tb * cpw + r])                       \
+                                    ? silu(g) * L.vs[tb * cpw + r] : 0.f;                      \
+                _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                              \
+                    const uint32_t dv[4] = {DW[q][i].x, DW[q][i].y, DW[q][i].z, DW[q][i].w};   \
+                    _Pragma("unroll") for (int m = 0; m < 4; ++m) {                            \
+                        yacc[tb][i][2 * m] += h * lo16_to_float<BF16>(dv[m]);                  \
+                        yacc[tb][i][2 * m + 1] += h * hi16_to_float<BF16>(dv[m]);              \
+                    }                                                                          \
+                }                                                                              \
+            }                                                                                  \
+        }                                                                                      \
+        __syncthreads();                                                                       \
+    }
+        uint4 gw[RB][NCH], dw[RB][NCH];
+        int rows[RB];
+        // bf16 at 512 threads has no room for a second set of rows (it spills)
+        constexpr bool PIPE = TB > 1 && !(BF16 && THREADS >= 512);
+        if constexpr (PIPE) {
+            // two batches in flight: the next batch's rows load while this one
+            // is multiplied (sets a and b alternate)
+            uint4 gb[RB][NCH], db[RB][NCH];
+            int rowsb[RB];
+            C_LOAD(0, gw, dw, rows)
+            for (int b0 = 0; b0 < n_act; b0 += 2 * RB) {
+                if (b0 + RB < n_act) C_LOAD(b0 + RB, gb, db, rowsb)
+                C_COMPUTE(b0, gw, dw, rows)
+                if (b0 + RB >= n_act) break;
+                if (b0 + 2 * RB < n_act) C_LOAD(b0 + 2 * RB, gw, dw, rows)
+                C_COMPUTE(b0 + RB, gb, db, rowsb)
             }
-            // partial gate dots, reduced over the wave, then over waves in LDS
-            float p[TB * RB];
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                for (int q = 0; q < RB; ++q) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int i = 0; i < NCH; ++i) {
-                        acc = dot2<BF16>(gw[q][i].x, xr[tb][i].x, acc);
-                        acc = dot2<BF16>(gw[q][i].y, xr[tb][i].y, acc);
-                        acc = dot2<BF16>(gw[q][i].z, xr[tb][i].z, acc);
-                        acc = dot2<BF16>(gw[q][i].w, xr[tb][i].w, acc);
-                    }
-                    p[tb * RB + q] = acc;
-                }
-            {
-                constexpr int NP = TB * RB;
-                constexpr int NPR = NP < 64 ? NP : 64;
-                static_assert(NP <= 64, "too many gate partials per batch");
-                const float v = transposed_reduce<NPR, 64>(p, lane);
-                constexpr int LOGNP = Log2<NPR>::v;
-                const int idx = lane >> (6 - LOGNP);
-                if ((lane & ((64 / NPR) - 1)) == 0) L.gp[wave * NP + idx] = v;
+        } else {
+            for (int b0 = 0; b0 < n_act; b0 += RB) {
+                C_LOAD(b0, gw, dw, rows)
+                C_COMPUTE(b0, gw, dw, rows)
             }
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < RB; ++q) {
-                const bool valid = b0 + q < n_act;
-                const int r = rows[q];
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    float g = 0.f;
-#pragma unroll
-                    for (int w = 0; w < W; ++w) g += L.gp[w * TB * RB + tb * RB + q];
-                    const float h = (valid && tb < nt && L.mk[tb * cpw + r])
-                                        ? silu(g) * L.vs[tb * cpw + r] : 0.f;
-#pragma unroll
-                    for (int i = 0; i < NCH; ++i) {
-                        const uint32_t dv[4] = {dw[q][i].x, dw[q][i].y, dw[q][i].z, dw[q][i].w};
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            yacc[tb][i][2 * m] += h * lo16_to_float<BF16>(dv[m]);
-                            yacc[tb][i][2 * m + 1] += h * hi16_to_float<BF16>(dv[m]);
-                        }
-                    }
-                }
-            }
-            __syncthreads();
         }
+#undef C_LOAD
+#undef C_COMPUTE
     }
     // ---- D: this workgroup's scaled partial rows -------------------------
 #pragma unroll
