@@ -126,6 +126,7 @@ def _route(x=FAKE, xdt=0, T=4, d=4096, rw=FAKE, rdt=0, E=8, k=2, outs=True, ws=F
     (dict(E=0), -1), (dict(E=2000, k=2), -1), (dict(outs=False), -1), (dict(ws=None), -4),
     (dict(ws_bytes=0), -4), (dict(xdt=5), -2), (dict(x=FAKE + 1), -3), (dict(T=40000, k=2), -2),
     (dict(d=60000), -2),
+    (dict(d=4), -1), (dict(d=4100), -2),    # rows are read in 16-byte units: d % 8 == 0
 ])
 def test_route_rejects(kw, code):
     assert _route(**kw) == code

@@ -153,6 +153,30 @@ def test_small_layer_dense(T, E, S, k, d, f):
                        f"dense layer T={T} E={E}+{S} k={k} d={d} f={f}")
 
 
+def test_layer_hot_expert_many_chunks():
+    """A router bias sends nearly every token to expert 3, which then holds
+    about T/tb chunks of the sparse grid with a ragged last one, while the
+    other experts hold one or two each and the shared expert's T tokens split
+    into chunks as well; sampled tokens from the first, middle and last chunks
+    are checked against the oracle."""
+    T, E, S, k, d, f = 150, 6, 1, 2, 512, 256
+    experts, thr = build_host_layer(66, E, S, d, f, "f16", 0.7, 1.0, layer=d)
+    R_bits = synth.to_f16_bits(synth.router_f32(66, d, E, d))
+    bias = np.zeros(E, dtype=np.float32)
+    bias[3] = 2.0
+    x_bits = synth.to_f16_bits(synth.tokens_f32(67, T, d, 1.0, layer=d))
+    L = device_layer(experts, thr, R_bits, "f16", E, S, k, bias=bias)
+    y, tr = run_layer(L, to_dev_bits(x_bits, "f16"), moe.PATH_SPARSE)
+    hist = np.bincount(tr["topk_idx"].ravel(), minlength=E)
+    say(f"hot expert: tokens per expert {hist.tolist()}")
+    assert hist[3] >= 140
+    hot = np.flatnonzero((tr["topk_idx"] == 3).any(axis=1))
+    cold = np.flatnonzero(~(tr["topk_idx"] == 3).any(axis=1))
+    tokens = np.unique(np.concatenate([hot[:5], hot[len(hot) // 2:len(hot) // 2 + 2], hot[-3:], cold[:2]]))
+    oracle_layer_check(experts, thr, R_bits, "f16", bias, E, S, k, x_bits, y, tr, tokens, False,
+                       f"hot expert layer T={T} E={E}+{S} k={k}")
+
+
 def test_layer_repeatable_and_workspace_clean():
     T, E, S, k, d, f = 7, 8, 1, 2, 512, 128
     experts, thr = build_host_layer(64, E, S, d, f, "f16", 0.6, 1.0)
