@@ -174,7 +174,7 @@ moe_status check_route_args(const void *x, moe_dtype xdt, int T, int d, const vo
     if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;         // rows are read in 16-byte units
     if ((long long)T * k > 65536) return MOE_ERR_UNSUPPORTED;
     if (!valid_out(xdt) || !valid_out(rdt)) return MOE_ERR_UNSUPPORTED;
-    if ((size_t)d * 4 + (size_t)E * 4 + (size_t)k * 4 + 16 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if ((size_t)d * 4 + (size_t)E * 8 + (size_t)k * 4 + 16 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
     if (!aligned(x, xdt == MOE_F32 ? 4 : 2) || !aligned(rw, rdt == MOE_F32 ? 4 : 2))
         return MOE_ERR_ALIGNMENT;
     return MOE_OK;

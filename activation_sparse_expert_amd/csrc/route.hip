@@ -20,41 +20,127 @@ namespace {
 constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-__device__ __forceinline__ float load_any(const void *p, int dt, size_t i)
+// 16-bit float bits to float (bf16 or fp16), chosen at compile time
+template <bool BF>
+__device__ __forceinline__ float f16bits(uint32_t b)
 {
-    if (dt == 2) return ((const float *)p)[i];
-    const uint16_t b = ((const uint16_t *)p)[i];
-    return dt == 1 ? bf16_bits_to_float(b) : half_bits_to_float(b);
+    return BF ? bf16_bits_to_float((uint16_t)b) : half_bits_to_float((uint16_t)b);
 }
 
-// Eight consecutive elements starting at element i (i % 8 == 0) as floats.
-__device__ __forceinline__ void load8(const void *p, int dt, size_t i, float (&v)[8])
+// x of one token into LDS as fp32, 8 elements per 16-byte unit (32 for fp32
+// input), four loads in flight per thread; one copy per input type, so that no
+// type test sits between the loads
+template <int XT>
+__device__ __forceinline__ void stage_x(const void *x, int t, int d, float *xs, int tid)
 {
-    if (dt == 2) {
-        const float4 a = *(const float4 *)((const float *)p + i);
-        const float4 b = *(const float4 *)((const float *)p + i + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        return;
-    }
-    const uint4 r = *(const uint4 *)((const uint16_t *)p + i);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    const int nch = d / 8;
+    if constexpr (XT == 2) {
+        const float *xf = (const float *)x + (size_t)t * d;
+        for (int c0 = tid; c0 < nch; c0 += 2 * kRouteThreads) {
+            float4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (dt == 1) {
-            v[2 * q] = bf16_bits_to_float((uint16_t)(w[q] & 0xFFFFu));
-            v[2 * q + 1] = bf16_bits_to_float((uint16_t)(w[q] >> 16));
-        } else {
-            v[2 * q] = half_bits_to_float((uint16_t)(w[q] & 0xFFFFu));
-            v[2 * q + 1] = half_bits_to_float((uint16_t)(w[q] >> 16));
+            for (int u = 0; u < 2; ++u) {
+                const int c = min(c0 + u * kRouteThreads, nch - 1);
+                v[2 * u] = *(const float4 *)(xf + (size_t)c * 8);
+                v[2 * u + 1] = *(const float4 *)(xf + (size_t)c * 8 + 4);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int c = c0 + u * kRouteThreads;
+                if (c < nch) {
+                    *(float4 *)&xs[c * 8] = v[2 * u];
+                    *(float4 *)&xs[c * 8 + 4] = v[2 * u + 1];
+                }
+            }
+        }
+    } else {
+        const uint16_t *xh = (const uint16_t *)x + (size_t)t * d;
+        for (int c0 = tid; c0 < nch; c0 += 4 * kRouteThreads) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = min(c0 + u * kRouteThreads, nch - 1);
+                v[u] = *(const uint4 *)(xh + (size_t)c * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + u * kRouteThreads;
+                if (c < nch) {
+                    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    *(float4 *)&xs[c * 8] = make_float4(f16bits<XT == 1>(w[0] & 0xFFFFu), f16bits<XT == 1>(w[0] >> 16),
+                                                        f16bits<XT == 1>(w[1] & 0xFFFFu), f16bits<XT == 1>(w[1] >> 16));
+                    *(float4 *)&xs[c * 8 + 4] = make_float4(f16bits<XT == 1>(w[2] & 0xFFFFu), f16bits<XT == 1>(w[2] >> 16),
+                                                            f16bits<XT == 1>(w[3] & 0xFFFFu), f16bits<XT == 1>(w[3] >> 16));
+                }
+            }
         }
     }
 }
 
-// argmax over (value, index) with the lower index winning ties
-__device__ __forceinline__ void argmax_pair(float &v, int &i, float ov, int oi)
+// Logits of one token: a wave takes GE experts at a time (e = wave, wave + W,
+// ...) and a lane the 16-byte units lane, lane + 64, ... of their rows, CB
+// units per expert per round: GE * CB loads in flight, all issued (rows and
+// units clamped to valid ones) before the products, which drop units and
+// experts past the end.  Every expert's sum runs in the same order (units
+// ascending within a lane, then a fixed butterfly), so identical router rows
+// tie exactly.  WT: router weight type (0 fp16, 1 bf16, 2 fp32).
+template <int CB, int GE, int WT>
+__device__ __forceinline__ void logits(const RouteArgs &a, const float *xs, const float *bs, float *lg,
+                                       int wave, int lane)
 {
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+    const int d = a.d, E = a.E;
+    constexpr int esz = WT == 2 ? 4 : 2;
+    constexpr int epu = 16 / esz;                       // elements per 16-byte unit
+    const int nu = d / epu;
+    const unsigned char *rw = (const unsigned char *)a.rw;
+    for (int e0 = wave; e0 < E; e0 += kRouteWaves * GE) {
+        float p[GE];
+#pragma unroll
+        for (int g = 0; g < GE; ++g) p[g] = 0.f;
+        for (int u0 = 0; u0 < nu; u0 += 64 * CB) {
+            uint4 w[GE][CB];
+#pragma unroll
+            for (int g = 0; g < GE; ++g)
+#pragma unroll
+                for (int u = 0; u < CB; ++u) {
+                    const int e = min(e0 + kRouteWaves * g, E - 1);
+                    const int uu = min(u0 + lane + 64 * u, nu - 1);
+                    w[g][u] = load_nt16(rw + ((size_t)e * d) * esz + (size_t)uu * 16);
+                }
+#pragma unroll
+            for (int g = 0; g < GE; ++g)
+#pragma unroll
+                for (int u = 0; u < CB; ++u) {
+                    const int uu = u0 + lane + 64 * u;
+                    const float *xp = xs + (size_t)min(uu, nu - 1) * epu;
+                    float q = p[g];
+                    if constexpr (WT == 2) {
+                        const float4 xv = *(const float4 *)xp;
+                        q += xv.x * __uint_as_float(w[g][u].x);
+                        q += xv.y * __uint_as_float(w[g][u].y);
+                        q += xv.z * __uint_as_float(w[g][u].z);
+                        q += xv.w * __uint_as_float(w[g][u].w);
+                    } else {
+                        const float4 x0 = *(const float4 *)xp, x1 = *(const float4 *)(xp + 4);
+                        q += x0.x * f16bits<WT == 1>(w[g][u].x & 0xFFFFu);
+                        q += x0.y * f16bits<WT == 1>(w[g][u].x >> 16);
+                        q += x0.z * f16bits<WT == 1>(w[g][u].y & 0xFFFFu);
+                        q += x0.w * f16bits<WT == 1>(w[g][u].y >> 16);
+                        q += x1.x * f16bits<WT == 1>(w[g][u].z & 0xFFFFu);
+                        q += x1.y * f16bits<WT == 1>(w[g][u].z >> 16);
+                        q += x1.z * f16bits<WT == 1>(w[g][u].w & 0xFFFFu);
+                        q += x1.w * f16bits<WT == 1>(w[g][u].w >> 16);
+                    }
+                    if (e0 + kRouteWaves * g < E && uu < nu) p[g] = q;
+                }
+        }
+#pragma unroll
+        for (int g = 0; g < GE; ++g) {
+            const int e = e0 + kRouteWaves * g;
+            const float v = seg_sum<64>(p[g]);
+            if (lane == 0 && e < E) lg[e] = v + bs[e];
+        }
+    }
 }
 
 // Counting sort of the T*k pairs by expert, stable in pair order.  Reads the
@@ -169,113 +255,51 @@ route_kernel(RouteArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     float *xs = (float *)smem;                        // [d]
-    float *lg = xs + a.d;                             // [E]
-    int *sel = (int *)(lg + a.E);                     // [k]
+    float *lg = xs + a.d;                             // [E rounded up to 4]
+    float *bs = lg + ((a.E + 3) & ~3);                // [E] router bias (0 without one)
+    int *sel = (int *)(bs + a.E);                     // [k]
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, E = a.E, k = a.k;
 
-    // x in 8-element chunks (16 or 32 bytes per load), all of a thread's loads in flight
-    const int nch = d / 8;
-    for (int c0 = tid; c0 < nch; c0 += 4 * kRouteThreads) {
-        float v[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = min(c0 + u * kRouteThreads, nch - 1);
-            load8(a.x, a.xdt, (size_t)t * d + (size_t)c * 8, v[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = c0 + u * kRouteThreads;
-            if (c < nch) {
-                *(float4 *)&xs[c * 8] = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
-                *(float4 *)&xs[c * 8 + 4] = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
-            }
-        }
-    }
+    if (a.xdt == 2) stage_x<2>(a.x, t, d, xs, tid);
+    else if (a.xdt == 1) stage_x<1>(a.x, t, d, xs, tid);
+    else stage_x<0>(a.x, t, d, xs, tid);
+    for (int e = tid; e < E; e += kRouteThreads) bs[e] = a.bias ? a.bias[e] : 0.f;
     __syncthreads();
 
-    // logits: a wave takes GE experts at a time (e = wave, wave + W, ...) and a
-    // lane the 16-byte units lane, lane + 64, ... of their rows, CB units per
-    // expert per round: GE * CB = 16 loads in flight.  Every expert's sum runs
-    // in the same order (units ascending within a lane, then a fixed
-    // butterfly), so identical router rows tie exactly.
+    if (a.rdt == 2) logits<CB, GE, 2>(a, xs, bs, lg, wave, lane);
+    else if (a.rdt == 1) logits<CB, GE, 1>(a, xs, bs, lg, wave, lane);
+    else logits<CB, GE, 0>(a, xs, bs, lg, wave, lane);
+    __syncthreads();
+
+    // top-k in one ranking pass: the rank of expert e is the number of experts
+    // ahead of it in the order (larger logit, then lower index; a NaN logit
+    // counts as -inf), and the experts of rank < k are the choices in rank
+    // order.  The logits are padded to a multiple of 4 with -inf, which never
+    // ranks ahead of a real expert.
     {
-        const int esz = a.rdt == 2 ? 4 : 2;
-        const int epu = 16 / esz;                       // elements per 16-byte unit
-        const int nu = d / epu;
-        const unsigned char *rw = (const unsigned char *)a.rw;
-        for (int e0 = wave; e0 < E; e0 += kRouteWaves * GE) {
-            float p[GE];
+        const int E4 = (E + 3) & ~3;
+        for (int e = E + tid; e < E4; e += kRouteThreads) lg[e] = -INFINITY;
+        __syncthreads();
+        for (int e = tid; e < E; e += kRouteThreads) {
+            const float le = lg[e] != lg[e] ? -INFINITY : lg[e];
+            int r = 0;
+            for (int e2 = 0; e2 < E4; e2 += 4) {
+                const float4 l4 = *(const float4 *)&lg[e2];
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-            for (int g = 0; g < GE; ++g) p[g] = 0.f;
-            for (int u0 = 0; u0 < nu; u0 += 64 * CB) {
-                uint4 w[GE][CB];
-#pragma unroll
-                for (int g = 0; g < GE; ++g)
-#pragma unroll
-                    for (int u = 0; u < CB; ++u) {
-                        const int e = e0 + kRouteWaves * g, uu = u0 + lane + 64 * u;
-                        w[g][u] = make_uint4(0, 0, 0, 0);
-                        if (e < E && uu < nu) w[g][u] = load_nt16(rw + ((size_t)e * d) * esz + (size_t)uu * 16);
-                    }
-#pragma unroll
-                for (int g = 0; g < GE; ++g)
-#pragma unroll
-                    for (int u = 0; u < CB; ++u) {
-                        const int uu = u0 + lane + 64 * u;
-                        if (e0 + kRouteWaves * g < E && uu < nu) {
-                            const float *xp = xs + (size_t)uu * epu;
-                            const uint32_t ww[4] = {w[g][u].x, w[g][u].y, w[g][u].z, w[g][u].w};
-                            if (a.rdt == 2) {
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) p[g] += xp[q] * __uint_as_float(ww[q]);
-                            } else if (a.rdt == 1) {
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) {
-                                    p[g] += xp[2 * q] * bf16_bits_to_float((uint16_t)(ww[q] & 0xFFFFu));
-                                    p[g] += xp[2 * q + 1] * bf16_bits_to_float((uint16_t)(ww[q] >> 16));
-                                }
-                            } else {
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) {
-                                    p[g] += xp[2 * q] * half_bits_to_float((uint16_t)(ww[q] & 0xFFFFu));
-                                    p[g] += xp[2 * q + 1] * half_bits_to_float((uint16_t)(ww[q] >> 16));
-                                }
-                            }
-                        }
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const float l2 = lv[j] != lv[j] ? -INFINITY : lv[j];
+                    r += (l2 > le) || (l2 == le && e2 + j < e);
+                }
             }
-#pragma unroll
-            for (int g = 0; g < GE; ++g) {
-                const int e = e0 + kRouteWaves * g;
-                const float v = seg_sum<64>(p[g]);
-                if (lane == 0 && e < E) lg[e] = v + (a.bias ? a.bias[e] : 0.f);
-            }
+            if (r < k) sel[r] = e;
         }
+        __syncthreads();
     }
-    __syncthreads();
-
     if (wave == 0) {
-        // top-k by repeated wave argmax; chosen experts are knocked out
-        float m_sel = -INFINITY;
-        for (int s = 0; s < k; ++s) {
-            float bv = -INFINITY;
-            int bi = 0x7FFFFFFF;
-            for (int e = lane; e < E; e += 64) {
-                bool taken = false;
-                for (int q = 0; q < s; ++q) taken |= (sel[q] == e);
-                if (!taken) argmax_pair(bv, bi, lg[e], e);
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oi = __shfl_xor(bi, off, 64);
-                argmax_pair(bv, bi, ov, oi);
-            }
-            sel[s] = bi;              // every lane stores the same value and reads its own
-            if (s == 0) m_sel = bv;
-        }
+        const float m_sel = lg[sel[0]];
         // weights
         float m = m_sel, den = 0.f;
         if (a.renorm) {
@@ -312,16 +336,15 @@ group_kernel(RouteArgs a)
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s)
 {
-    size_t lds = (size_t)a.d * 4 + (size_t)a.E * 4 + (size_t)a.k * 4 + 16;
+    size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 4 + 32;
     const size_t lds_group = (size_t)a.E * 12 + kRouteThreads * 4 + 32;
     if (lds_group > lds) lds = lds_group;
-    // 16-byte units per lane of one router row (64 lanes): CB of them per expert
-    // and round, GE = 16 / CB experts per wave at a time
+    // 16-byte units per lane of one router row (64 lanes): CB (<= 8) of them per
+    // expert and round, GE = 16 / CB experts per wave at a time
     const int nu = a.d * (a.rdt == 2 ? 4 : 2) / 16;
     const int cpl = (nu + 63) / 64;
     const void *kern;
-    if (cpl > 8) kern = (const void *)route_kernel<16, 1>;
-    else if (cpl > 4) kern = (const void *)route_kernel<8, 2>;
+    if (cpl > 4) kern = (const void *)route_kernel<8, 2>;
     else if (cpl > 2) kern = (const void *)route_kernel<4, 4>;
     else if (cpl > 1) kern = (const void *)route_kernel<2, 8>;
     else kern = (const void *)route_kernel<1, 16>;
