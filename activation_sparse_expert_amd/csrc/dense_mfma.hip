@@ -6,13 +6,13 @@
 // and the layer adds each token's rows with its router weight (shared experts
 // with weight 1).
 //
-// Kernel 1 (gate/up): a workgroup of 4 waves owns 64 intermediate channels of
+// Kernel 1 (gate/up): a workgroup of 8 waves owns 128 intermediate channels of
 // one expert and loops over the expert's tokens in 64-row chunks; wave w takes
-// token half w & 1 and channel half w >> 1.  v_mfma_f32_32x32x16_bf16 runs
+// token half w & 1 and channel quarter w >> 1.  v_mfma_f32_32x32x16_bf16 runs
 // with the tokens as rows (A) and the weight rows as columns (B).  Each
 // 128-wide k block of the gate, up and x tiles is copied straight from global
-// memory into LDS (whole 256-byte row pieces, four rows per instruction), two
-// blocks ahead of the one being multiplied, in a three-stage ring; weights are
+// memory into LDS (whole 256-byte row pieces, four rows per instruction), one
+// block ahead of the one being multiplied, in two 80 KB stages; weights are
 // read from HBM once.  The reduction index k is permuted inside
 // every 64-wide block (lane half h takes k = 32h + 8s + 0..7 at step s); A and
 // B use the same permutation, which leaves the sum unchanged.  Epilogue:
@@ -94,16 +94,18 @@ constexpr int kXP = 72;         // halves per LDS row of a 64-wide k block (16-b
 // serves far better than 128-byte pieces).  A row's sixteen 16-byte chunks are
 // stored with the low three bits of the chunk index XOR-swizzled by (row & 7),
 // so a fragment read (32 rows, one chunk each) is free of bank conflicts.
-constexpr int kGuBN = 64;                                           // channels per workgroup
-constexpr int kGuStages = 3;
-constexpr int kGuRows = 3 * 64;
+constexpr int kGuThreads = 512;
+constexpr int kGuWaves = kGuThreads / 64;
+constexpr int kGuBN = 128;                                          // channels per workgroup
+constexpr int kGuStages = 2;
+constexpr int kGuRows = 2 * kGuBN + 64;                             // gate, up and x rows of a stage
 constexpr size_t kGuStage = (size_t)kGuRows * 256;                  // bytes
-constexpr size_t kGuLds = kGuStages * kGuStage;
-constexpr int kGuCopies = kGuRows * 16 / 64 / 4;                   // 16-byte copies per lane per stage (12)
+constexpr size_t kGuLds = kGuStages * kGuStage;                     // 160 KB
+constexpr int kGuCopies = kGuRows * 16 / 64 / kGuWaves;            // 16-byte copies per lane per stage (10)
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + 16 * (chunk ^ (row & 7)); }
 
-__global__ void __launch_bounds__(kDenseThreads)
+__global__ void __launch_bounds__(kGuThreads)
 gateup_kernel(DenseArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -115,7 +117,7 @@ gateup_kernel(DenseArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, li = lane & 31;
-    const int mt = wave & 1, nt = wave >> 1;                        // token half, channel half
+    const int mt = wave & 1, nt = wave >> 1;                        // token half, channel quarter
     const int d = a.d;
     const int j = nb * kGuBN + nt * 32 + li;                        // this lane's B column
     const size_t wbase = (size_t)si.e * a.f * d + (size_t)nb * kGuBN * d;
@@ -129,12 +131,12 @@ gateup_kernel(DenseArgs a)
             const int p = (wave * kGuCopies + q) * 64 + lane;           // 16-byte position in the stage
             const int row = p >> 4, c = (p & 15) ^ (row & 7);           // tile row, source chunk
             const uint16_t *rp;
-            if (row < 64) {
+            if (row < kGuBN) {
                 rp = a.gate + wbase + (size_t)row * d;
-            } else if (row < 128) {
-                rp = a.up + wbase + (size_t)(row - 64) * d;
+            } else if (row < 2 * kGuBN) {
+                rp = a.up + wbase + (size_t)(row - kGuBN) * d;
             } else {
-                const int m = m0 + row - 128;                           // rows past the chunk read
+                const int m = m0 + row - 2 * kGuBN;                     // rows past the chunk read
                 rp = a.x + (size_t)(m < si.ntok ? token_of(a, si, m) : 0) * d;   // a valid token
             }
             src[q] = rp + 8 * c;
@@ -151,17 +153,15 @@ gateup_kernel(DenseArgs a)
         const bool mine = m0 + 32 * mt < si.ntok;                   // this wave's token half has tokens
 
         issue(0, 0);
-        if (nkb > 1) issue(1, 1);
         for (int kb = 0; kb < nkb; ++kb) {
-            // block kb has landed once at most one stage of copies is younger
-            if (kb + 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGuCopies) : "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // block kb's copies are the only ones in flight
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             // the stage written next held block kb - 1, which every wave has finished
-            if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % kGuStages);
+            if (kb + 1 < nkb) issue(kb + 1, (kb + 1) % kGuStages);
             if (mine) {
                 const unsigned char *st = smem + (size_t)(kb % kGuStages) * kGuStage;
-                const int gr = nt * 32 + li, ur = 64 + nt * 32 + li, xr = 128 + mt * 32 + li;
+                const int gr = nt * 32 + li, ur = kGuBN + nt * 32 + li, xr = 2 * kGuBN + mt * 32 + li;
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) {
                     const int c = 8 * h + s8;                       // k = 64h + 8 s8 + 0..7
@@ -339,7 +339,7 @@ hipError_t launch_dense_layer(const DenseArgs &a, hipStream_t s)
     hipError_t e = hipFuncSetAttribute((const void *)gateup_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGuLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kGuBN)), dim3(kDenseThreads), kGuLds, s, a);
+    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kGuBN)), dim3(kGuThreads), kGuLds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void *)down_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
