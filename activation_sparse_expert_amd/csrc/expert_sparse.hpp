@@ -5,13 +5,18 @@
 // One workgroup owns a tile of `cpw` intermediate channels of one expert and a
 // chunk of up to TB tokens, and runs the whole algorithm for them:
 //   A  v = x W^up over its channels.  A lane takes 16 bytes of codes (one
-//      group of 64 inputs of one channel), turns every pair of codes into a
-//      packed 16-bit pair (1 + q/4) with one mask-and-or and accumulates
-//      x . (1 + q/4) with packed dot products in fp32.  Per group,
-//      sum x q = 4 (S' - X_g), so the group's share of v is
-//      s (4 S' - (4 + z) X_g) with X_g the group sum of x.  SEG lanes share one
-//      channel; the per-channel sums of up to 8 passes are reduced together by
-//      a transposed butterfly (each step halves the values a lane carries).
+//      group of 64 inputs of one channel).  fp16 activations: masking a code
+//      pair in place gives an fp16 subnormal pair q 2^(p-24), so one AND per
+//      pair (and one shift per word) feeds a packed dot product with fp32
+//      accumulation, one accumulator per code position.  bf16 activations:
+//      one mask-and-or per pair makes the bf16 pair (1 + q/4), and per group
+//      sum x q = 4 (S' - X_g).  The group's share of v is s (sum x q - z X_g),
+//      X_g being the group sum of x.  SEG lanes share one channel; the
+//      per-channel sums of up to 8 passes are reduced together by a transposed
+//      butterfly (each step halves the values a lane carries).  A single-token
+//      tile issues its code loads a few passes ahead of the decode (buffer
+//      loads over the tile; passes past its end read zeros), so the VALU work
+//      overlaps the stream instead of following it.
 //   B  mask = |v| > t (fp32), union over the chunk's tokens, compacted into an
 //      ascending list of active channels with a wave ballot.
 //   C  for each active channel j: every thread reads its 16-byte chunk(s) of
@@ -33,6 +38,7 @@ namespace sparse {
 
 constexpr int kXPad = 72;               // halves per 64-element group slot in LDS (16 B pad)
 constexpr int kPB = 8;                  // channel passes loaded and reduced together
+constexpr int kAhead = 3;               // single-token tiles: passes of codes in flight
 
 template <int N>
 struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
@@ -109,6 +115,45 @@ __device__ __forceinline__ float group_dot(const uint32_t (&pw)[32], const uint3
         a3 = dot2<BF16>(pw[m + 3], xp[m + 3], a3);
     }
     return (a0 + a1) + (a2 + a3);
+}
+
+// sum_k x_k q_k over one 64-input group, fp16 activations.  Masking a code
+// pair in place leaves an fp16 subnormal pair q 2^(p-24) (p = bit position of
+// the code in its half-word, 0..8): one v_and_b32 per pair for code slots 0-4,
+// and one shift of the word by 6 brings slots 5-7 to positions 4, 6, 8.  Pairs
+// with the same position share an accumulator, and the positions are
+// recombined by exact powers of two.  Measured on gfx950 with activations of
+// the N(0,1)/64 scale: the packed dot product keeps a relative error of about
+// 1e-6 on the position-0 chain and 1e-8 on positions 4-8 (the latter carry
+// 16-256x the weight), and it does not flush fp16 subnormal inputs; there is
+// no cancellation against a constant term as in the (1 + q/4) decode.
+__device__ __forceinline__ float group_xq_f16(const uint4 &c, const uint32_t (&xp)[32])
+{
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    float a0 = 0.f, a2 = 0.f, a4 = 0.f, a6 = 0.f, a8 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t wi = w[i], ws = wi >> 6;
+        a0 = dot2<false>(wi & 0x00030003u, xp[8 * i + 0], a0);
+        a2 = dot2<false>(wi & 0x000C000Cu, xp[8 * i + 1], a2);
+        a4 = dot2<false>(wi & 0x00300030u, xp[8 * i + 2], a4);
+        a6 = dot2<false>(wi & 0x00C000C0u, xp[8 * i + 3], a6);
+        a8 = dot2<false>(wi & 0x03000300u, xp[8 * i + 4], a8);
+        a4 = dot2<false>(ws & 0x00300030u, xp[8 * i + 5], a4);
+        a6 = dot2<false>(ws & 0x00C000C0u, xp[8 * i + 6], a6);
+        a8 = dot2<false>(ws & 0x03000300u, xp[8 * i + 7], a8);
+    }
+    return 65536.0f * ((((a0 * 4.0f + a2) * 4.0f + a4) * 4.0f + a6) * 4.0f + a8);
+}
+
+// The activation pairs of one group: from registers (XREG) or from the copy
+// just read out of LDS.
+template <bool XREG, int N>
+__device__ __forceinline__ const uint32_t (&pick_x(const uint32_t (&reg)[32],
+                                                   const uint32_t (&lds)[N]))[32]
+{
+    if constexpr (XREG) return reg;
+    else return lds;
 }
 
 // Transposed butterfly over the SEG lanes of a segment: on entry every lane
@@ -203,7 +248,46 @@ __host__ __device__ constexpr int rows_per_batch()
     return (8 / NCH) < 1 ? 1 : 8 / NCH;
 }
 
-template <bool BF16, int TB, class GEO>
+// Raw buffer access to one tile's codes or scales: offsets at or past
+// `bytes` (kOob) return zeros without a memory access, so the loads of a
+// block of passes can be issued unconditionally.
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 bload_nt16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2 /* nt */);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload_nt4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2 /* nt */);
+}
+
+// Gate/down row chunk of phase C.  A single-token chunk reads each active row
+// once, so the rows are streamed (nontemporal); chunks of several tokens keep
+// ordinary loads, because other chunks of the same expert read the same rows
+// and find them in cache.
+template <int TB>
+__device__ __forceinline__ uint4 row_load(const uint16_t *p)
+{
+    if constexpr (TB == 1) return load_nt16(p);
+    else return *(const uint4 *)p;
+}
+
+// passes of channels per phase-A block (host and device)
+template <int TB, class GEO>
+__host__ __device__ constexpr int pass_block()
+{
+    constexpr int pb = (kPB / (TB * GEO::NG)) < 1 ? 1 : (kPB / (TB * GEO::NG));
+    return pb < GEO::SEG ? pb : GEO::SEG;
+}
+
+template <bool BF16, int TB, class GEO, bool ONE>
 __global__ void __launch_bounds__(GEO::THREADS)
 expert_kernel(SparseArgs a)
 {
@@ -215,8 +299,7 @@ expert_kernel(SparseArgs a)
     constexpr int LOGSEG = Log2<SEG>::v;
     // channel passes loaded and reduced together (<= SEG; fewer when a lane
     // carries several tokens or groups, to bound registers)
-    constexpr int PB = (kPB / (TB * NG)) < 1 ? 1 : (kPB / (TB * NG));
-    constexpr int PR = PB < SEG ? PB : SEG;
+    constexpr int PR = pass_block<TB, GEO>();
     constexpr bool XREG = (TB * NG) <= 2;           // x pairs of the lane's groups kept in registers
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -307,6 +390,28 @@ expert_kernel(SparseArgs a)
         }                                                                                   \
     }
     auto load_block = [&](int p0) { LOAD_BLOCK(p0, cq, csz, okm) };
+    // Single-token tiles: the passes of a block are issued kAhead at a time
+    // (buffer loads over the tile; passes past the tile read zeros), so that
+    // the decode of early passes overlaps the rest of the stream.
+    constexpr bool LAZY = TB == 1;
+    constexpr int AH = kAhead < PR ? kAhead : PR;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(upq, (uint32_t)nrows * (d / 4));
+    const __amdgpu_buffer_rsrc_t rz = tile_rsrc(upsz, (uint32_t)nrows * G * 4);
+    const int r_lane = wave * RPW + rs;             // channel of this lane in pass 0
+    const uint32_t q_lane = (uint32_t)(r_lane * (d / 4) + go * 16);
+    const uint32_t z_lane = (uint32_t)((r_lane * G + go) * 4);
+#define LOAD_PASS(P0, p)                                                                    \
+    {                                                                                       \
+        const int pp = (P0) + (p);                                                          \
+        const bool rok = r_lane + pp * ROWS_PASS < nrows;                                   \
+        _Pragma("unroll") for (int gi = 0; gi < NG; ++gi) {                                 \
+            const bool ok = rok && go + SEG * gi < G;                                       \
+            const uint32_t oq = q_lane + (uint32_t)(pp * ROWS_PASS * (d / 4) + gi * SEG * 16); \
+            const uint32_t oz = z_lane + (uint32_t)((pp * ROWS_PASS * G + gi * SEG) * 4);   \
+            cq[p][gi] = bload_nt16(rq, ok ? oq : kOob);                                     \
+            csz[p][gi] = bload_nt4(rz, ok ? oz : kOob);                                     \
+        }                                                                                   \
+    }
 
     // 16-byte x chunks each thread stages per token chunk
     constexpr int XL = (TB * 8 * SEG * NG + THREADS - 1) / THREADS;
@@ -342,14 +447,38 @@ expert_kernel(SparseArgs a)
 
     // ---- x loads, then the up-code loads; only x is waited for here -------
     uint4 xl[XL];
+    if constexpr (TB == 1) {
+        // one token: a buffer over its row, so that no branch separates the
+        // x load from the code loads issued after it
+        const int t0 = __builtin_amdgcn_readfirstlane(L.tok_t[0]);
+        const __amdgpu_buffer_rsrc_t rx = tile_rsrc(a.x + (size_t)t0 * d, (uint32_t)d * 2);
 #pragma unroll
-    for (int u = 0; u < XL; ++u) {
-        const int i = tid + u * THREADS;
-        const int tb = i / CPR, c = i - tb * CPR;
-        xl[u] = make_uint4(0, 0, 0, 0);
-        if (i < TB * CPR && tb < nt) xl[u] = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
+        for (int u = 0; u < XL; ++u) {
+            const int i = tid + u * THREADS;
+            typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, i < CPR ? i * 16 : (int)kOob, 0, 0);
+            xl[u] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < XL; ++u) {
+            const int i = tid + u * THREADS;
+            const int tb = i / CPR, c = i - tb * CPR;
+            xl[u] = make_uint4(0, 0, 0, 0);
+            if (i < TB * CPR && tb < nt) xl[u] = *(const uint4 *)(a.x + (size_t)L.tok_t[tb] * d + (size_t)c * 8);
+        }
     }
-    load_block(0);          // up codes do not depend on x: in flight while x is staged
+    // up codes do not depend on x: in flight while x is staged (x first)
+    if constexpr (LAZY) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < AH; ++p) {
+            LOAD_PASS(0, p)
+            __builtin_amdgcn_sched_barrier(0);      // keep the passes in order
+        }
+    } else {
+        load_block(0);
+    }
 #pragma unroll
     for (int u = 0; u < XL; ++u) {
         const int i = tid + u * THREADS;
@@ -392,11 +521,15 @@ expert_kernel(SparseArgs a)
             }
         }
     }
-    for (int p0 = 0; p0 < passes; p0 += PR) {
+    // ONE: the tile is a single block of passes (straight-line code)
+    for (int p0 = 0; p0 < (ONE ? 1 : passes); p0 += PR) {
         if constexpr (TB > 1) {
             if (p0 + PR < passes) LOAD_BLOCK(p0 + PR, cqn, cszn, okmn)
-        } else {
-            if (p0 > 0) load_block(p0);
+        } else if constexpr (!ONE) {
+            if (p0 > 0) {
+#pragma unroll
+                for (int p = 0; p < AH; ++p) LOAD_PASS(p0, p)
+            }
         }
         // units outside the tile (ok bit clear) get s = 0 when used: the select
         // is kept away from the loads so that they all issue back to back
@@ -407,34 +540,43 @@ expert_kernel(SparseArgs a)
             for (int p = 0; p < PR; ++p) part[tb][p] = 0.f;
 #pragma unroll
         for (int p = 0; p < PR; ++p) {
+            if constexpr (LAZY) {
+                if (p + AH < PR) LOAD_PASS(p0, p + AH)
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (p0 + p >= passes) continue;         // uniform: padding passes of the block
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
-                uint32_t pw[32];
-                decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
-                const bool ok = (okm >> (p * NG + gi)) & 1u;
+                // fp16: subnormal-pair decode (group_xq_f16); bf16: (1 + q/4) pairs
+                uint32_t pw[BF16 ? 32 : 1];
+                if constexpr (BF16) decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
+                // units outside the tile: s = 0 (zeros from the buffer loads, or
+                // the ok bit of the block loads)
+                const bool ok = LAZY || ((okm >> (p * NG + gi)) & 1u);
                 const float s = ok ? half_bits_to_float(csz[p][gi] & 0xFFFFu) : 0.f;
                 const float z = half_bits_to_float(csz[p][gi] >> 16);
                 const int g = min(go + SEG * gi, G - 1);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
-                    float sp;
-                    if constexpr (XREG) {
-                        sp = group_dot<BF16>(pw, xr_a[tb * NG + gi]);
-                    } else {
-                        uint32_t xp[32];
+                    uint32_t xl_[XREG ? 1 : 32];
+                    if constexpr (!XREG) {
                         const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             const uint4 xx = xv[q];
-                            xp[4 * q + 0] = xx.x;
-                            xp[4 * q + 1] = xx.y;
-                            xp[4 * q + 2] = xx.z;
-                            xp[4 * q + 3] = xx.w;
+                            xl_[4 * q + 0] = xx.x;
+                            xl_[4 * q + 1] = xx.y;
+                            xl_[4 * q + 2] = xx.z;
+                            xl_[4 * q + 3] = xx.w;
                         }
-                        sp = group_dot<BF16>(pw, xp);
                     }
-                    part[tb][p] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
+                    const uint32_t(&xp)[32] = pick_x<XREG>(xr_a[XREG ? tb * NG + gi : 0], xl_);
+                    if constexpr (BF16) {
+                        const float sp = group_dot<BF16>(pw, xp);
+                        part[tb][p] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
+                    } else {
+                        part[tb][p] += s * (group_xq_f16(cq[p][gi], xp) - z * xg_a[tb][gi]);
+                    }
                 }
             }
         }
@@ -463,6 +605,7 @@ expert_kernel(SparseArgs a)
         }
     }
 #undef LOAD_BLOCK
+#undef LOAD_PASS
     __syncthreads();
 
     // exports
@@ -528,8 +671,8 @@ expert_kernel(SparseArgs a)
             DW[q][i] = make_uint4(0, 0, 0, 0);                                                 \
             if ((B0) + q < n_act) {                 /* uniform: no loads past the list */      \
                 const int c = min(tid + THREADS * i, CPR - 1);                                 \
-                GW[q][i] = *(const uint4 *)(gate + (size_t)ROWS[q] * d + (size_t)c * 8);       \
-                DW[q][i] = *(const uint4 *)(down + (size_t)ROWS[q] * d + (size_t)c * 8);       \
+                GW[q][i] = row_load<TB>(gate + (size_t)ROWS[q] * d + (size_t)c * 8);           \
+                DW[q][i] = row_load<TB>(down + (size_t)ROWS[q] * d + (size_t)c * 8);           \
             }                                                                                  \
         }                                                                                      \
     }
@@ -629,7 +772,9 @@ hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
 {
     size_t off[11];
     const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off);
-    auto kern = expert_kernel<BF16, TB, GEO>;
+    constexpr int rows_pass = GEO::W * (64 / GEO::SEG);
+    const bool one = (a.cpw + rows_pass - 1) / rows_pass <= pass_block<TB, GEO>();
+    auto kern = one ? expert_kernel<BF16, TB, GEO, true> : expert_kernel<BF16, TB, GEO, false>;
     SparseArgs args = a;
     args.dec_mask = decode_const<BF16>().mask;
     args.dec_one = decode_const<BF16>().one;
