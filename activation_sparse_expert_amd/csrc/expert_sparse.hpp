@@ -661,6 +661,25 @@ expert_kernel(SparseArgs a)
                 xr[tb][i] = *(const uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8);
                 if (tid + THREADS * i >= CPR) xr[tb][i] = make_uint4(0, 0, 0, 0);
             }
+        // h = SiLU(g) v of (token tb, list entry B0 + q) for lane tb * RB + q: the
+        // wave partials of the gate dot are added in wave order
+        auto lane_h = [&](int b0, int ln, const Lds &Ls, int nact, int ntok, int cp) -> float {
+            float h = 0.f;
+            if (ln < TB * RB) {
+                const int tb = ln / RB, q = ln - tb * RB;
+                const int ent = b0 + q;
+                if (ent < nact && tb < ntok) {
+                    const int r = (int)Ls.list[ent];
+                    if (Ls.mk[tb * cp + r]) {
+                        float g = 0.f;
+#pragma unroll
+                        for (int w = 0; w < W; ++w) g += Ls.gp[w * TB * RB + tb * RB + q];
+                        h = silu(g) * Ls.vs[tb * cp + r];
+                    }
+                }
+            }
+            return h;
+        };
         // loads of the batch of rows starting at list entry B0 (none past the list)
 #define C_LOAD(B0, GW, DW, ROWS)                                                               \
     _Pragma("unroll") for (int q = 0; q < RB; ++q) {                                           \
@@ -702,14 +721,13 @@ expert_kernel(SparseArgs a)
             if ((lane & ((64 / NPR) - 1)) == 0) L.gp[wave * NP + idx] = v;                     \
         }                                                                                      \
         __syncthreads();                                                                       \
+        /* h of (token tb, row q) is computed once, by lane tb * RB + q of every     */        \
+        /* wave, and read from that lane by all (one v_readlane per row and token)    */        \
+        const float hl = lane_h((B0), lane, L, n_act, nt, cpw);                                \
         _Pragma("unroll") for (int q = 0; q < RB; ++q) {                                       \
-            const bool valid = (B0) + q < n_act;                                               \
-            const int r = ROWS[q];                                                             \
             _Pragma("unroll") for (int tb = 0; tb < TB; ++tb) {                                \
-                float g = 0.f;                                                                 \
-                _Pragma("unroll") for (int w = 0; w < W; ++w) g += L.gp[w * TB * RB + tb * RB + q]; \
-                const float h = (valid && tb < nt && L.mk[tb * cpw + r])                       \
-                                    ? silu(g) * L.vs[tb * cpw + r] : 0.f;                      \
+                const float h = __int_as_float(                                                \
+                    __builtin_amdgcn_readlane(__float_as_int(hl), tb * RB + q));               \
                 _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                              \
                     const uint32_t dv[4] = {DW[q][i].x, DW[q][i].y, DW[q][i].z, DW[q][i].w};   \
                     _Pragma("unroll") for (int m = 0; m < 4; ++m) {                            \
@@ -774,7 +792,11 @@ hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
     const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off);
     constexpr int rows_pass = GEO::W * (64 / GEO::SEG);
     const bool one = (a.cpw + rows_pass - 1) / rows_pass <= pass_block<TB, GEO>();
-    auto kern = one ? expert_kernel<BF16, TB, GEO, true> : expert_kernel<BF16, TB, GEO, false>;
+    auto kern = expert_kernel<BF16, TB, GEO, false>;
+    // (the widest geometry keeps the loop form: its straight-line version spills)
+    if constexpr (GEO::NG < 4) {
+        if (one) kern = expert_kernel<BF16, TB, GEO, true>;
+    }
     SparseArgs args = a;
     args.dec_mask = decode_const<BF16>().mask;
     args.dec_one = decode_const<BF16>().one;
