@@ -186,6 +186,33 @@ def batched_measure(reps=10, T=256):
                                                / MFMA_BF16_PEAK_TFLOPS)
     out["workload"] = (f"Mixtral-8x22B-shaped layer, 8 experts d={d} f={f} bf16, top-2, "
                        f"{T} tokens; dense = threshold off on bf16 MFMA, sparse = 70% thresholds")
+    # extra point: the same layer at a micro-batch of 2048 tokens (about 512 per
+    # expert, 512 flop per weight byte, above the 312.5 flop/B ridge), where the
+    # dense path is a real contraction and MFMA utilisation is the measure
+    T2 = 2048
+    x2 = torch.from_numpy(synth.tokens_f32(cfg, T2, d, c["x_scale"])).to(bf).to(dev)
+    y2 = torch.empty((T2, d), dtype=torch.float32, device=dev)
+    ws2 = moe.new_workspace(L.workspace_bytes(T2), dev)
+    for _ in range(2):
+        moe.layer_forward(L, x2, path=moe.PATH_DENSE, y=y2, ws=ws2, trace={"expert_count": cnt})
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        moe.layer_forward(L, x2, path=moe.PATH_DENSE, y=y2, ws=ws2)
+    e1.record()
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / 5
+    flops = 2.0 * 3 * T2 * k * d * f
+    wbytes = int((cnt.cpu().numpy() > 0).sum()) * 3 * d * f * 2
+    out["dense_mfma_T2048"] = {
+        "workload": f"same layer, micro-batch {T2} tokens, dense bf16 MFMA path",
+        "ms_per_layer": sec * 1e3, "tokens_per_s": T2 / sec, "tflops": flops / sec / 1e12,
+        "mfma_util": flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "flop_per_weight_byte": flops / wbytes,
+        "mfma_attainable": min(1.0, flops / wbytes * HBM_PEAK_GBS / 1e3 / MFMA_BF16_PEAK_TFLOPS)}
+    del x2, y2, ws2
     del L, gate, down, up_q, up_sz, up_dense
     torch.cuda.empty_cache()
     return out
