@@ -119,6 +119,7 @@ struct LayerWs {
     int32_t *chunk_tab, *n_chunks;
     float *part;
     float *h;
+    float *lg;              // [T][E] router logits (wide-router split)
 };
 
 size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, void *base)
@@ -127,7 +128,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     const TilePlan tp = layer_plan(T, d, f, E, k, S).tp;
     const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
     size_t o = 0;
-    size_t off[13];
+    size_t off[14];
     off[0] = o; o += up(4);
     off[1] = o; o += up((size_t)T * k * 4);
     off[2] = o; o += up((size_t)T * k * 4);
@@ -141,6 +142,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     off[10] = o; o += up(dense_h_bytes(T, f, k, S));
     off[11] = o; o += up((size_t)T * k * 4);           // every chunk holds at least one pair
     off[12] = o; o += up(4);
+    off[13] = o; o += up((size_t)T * E * 4);
     if (out) {
         char *p = (char *)base;
         out->topk_idx = (int32_t *)(p + off[1]);
@@ -155,6 +157,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->h = (float *)(p + off[10]);
         out->chunk_tab = (int32_t *)(p + off[11]);
         out->n_chunks = (int32_t *)(p + off[12]);
+        out->lg = (float *)(p + off[13]);
     }
     return o;
 }
@@ -219,7 +222,9 @@ size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S)
     if (T < 1 || d < 1) return 0;
     switch (op) {
     case MOE_OP_EXPERT: return f < 1 ? 0 : expert_ws_bytes(T, d, f);
-    case MOE_OP_ROUTE: return up(4);
+    case MOE_OP_ROUTE:
+        if (E < 1) return 0;
+        return up(4) + up((size_t)T * E * 4);          // logits of the wide-router split
     case MOE_OP_LAYER:
         if (E < 1 || k < 1 || k > E || S < 0 || f < 1) return 0;
         return layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr);
@@ -254,6 +259,7 @@ moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void
     a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits = logits_out;
     a.count = expert_count; a.offset = expert_offset; a.pairs = pair_by_expert;
     a.pair_pos = nullptr; a.active = nullptr; a.n_active = nullptr;
+    a.lg_buf = route_split(d, E, rdt) ? (float *)((char *)ws + up(4)) : nullptr;
     return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -342,6 +348,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.count = (trace && trace->expert_count) ? trace->expert_count : w.count;
     r.offset = w.offset; r.pairs = w.pairs; r.pair_pos = w.pair_pos;
     r.active = w.active; r.n_active = w.n_active;
+    r.lg_buf = route_split(d, E, L->rdt) ? w.lg : nullptr;
     const SparsePlan sp = layer_plan(T, d, f, E, k, S);
     if (path == MOE_PATH_SPARSE) {
         r.chunk = sp.tb; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;

@@ -143,6 +143,67 @@ __device__ __forceinline__ void logits(const RouteArgs &a, const float *xs, cons
     }
 }
 
+// 8 elements of a 16-bit (XT/WT 0 fp16, 1 bf16) or fp32 (2) array at element
+// offset 8 g, as floats (one or two 16-byte loads)
+template <int T_>
+__device__ __forceinline__ void load8(const void *base, size_t g, float (&v)[8])
+{
+    if constexpr (T_ == 2) {
+        const float4 a = *((const float4 *)base + 2 * g), b = *((const float4 *)base + 2 * g + 1);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 u = *((const uint4 *)base + g);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = f16bits<T_ == 1>(w[i] & 0xFFFFu);
+            v[2 * i + 1] = f16bits<T_ == 1>(w[i] >> 16);
+        }
+    }
+}
+
+// Wide routers: logits only, one wave per (token, expert), eight experts per
+// workgroup, so the router rows of a token are read by many compute units at
+// once.  Lane l takes the 8-element groups l, l + 64, ... of the row and of x
+// (4 of each in flight), in ascending order, and the lanes' sums are
+// added by a fixed butterfly: every expert's logit is formed the same way, so
+// identical router rows tie exactly.  route_kernel then ranks them.
+template <int XT, int WT>
+__global__ void __launch_bounds__(kRouteThreads)
+route_logits_kernel(RouteArgs a)
+{
+    const int nblk = (a.E + kRouteWaves - 1) / kRouteWaves;
+    const int t = blockIdx.x / nblk;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = (blockIdx.x - t * nblk) * kRouteWaves + wave;
+    if (e >= a.E) return;                               // no barriers in this kernel
+    constexpr int xsz = XT == 2 ? 4 : 2, wsz = WT == 2 ? 4 : 2;
+    const unsigned char *xr = (const unsigned char *)a.x + (size_t)t * a.d * xsz;
+    const unsigned char *wr = (const unsigned char *)a.rw + (size_t)e * a.d * wsz;
+    const int ng = a.d / 8;
+    constexpr int CB = 4;                               // groups per lane per round
+    float acc = 0.f;
+    for (int g0 = 0; g0 < ng; g0 += 64 * CB) {
+        float xv[CB][8], wv[CB][8];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int g = min(g0 + lane + 64 * i, ng - 1);
+            load8<XT>(xr, g, xv[i]);
+            load8<WT>(wr, g, wv[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            float q = acc;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q += xv[i][j] * wv[i][j];
+            if (g0 + lane + 64 * i < ng) acc = q;
+        }
+    }
+    acc = seg_sum<64>(acc);
+    if (lane == 0) a.lg_buf[(size_t)t * a.E + e] = acc + (a.bias ? a.bias[e] : 0.f);
+}
+
 // Counting sort of the T*k pairs by expert, stable in pair order.  Reads the
 // top-k indices through coherent loads (they were written by this or an
 // earlier kernel).  With a.chunk > 0 it also lists every expert's pairs in
@@ -262,16 +323,22 @@ route_kernel(RouteArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, E = a.E, k = a.k;
 
-    if (a.xdt == 2) stage_x<2>(a.x, t, d, xs, tid);
-    else if (a.xdt == 1) stage_x<1>(a.x, t, d, xs, tid);
-    else stage_x<0>(a.x, t, d, xs, tid);
-    for (int e = tid; e < E; e += kRouteThreads) bs[e] = a.bias ? a.bias[e] : 0.f;
-    __syncthreads();
+    if (a.lg_buf) {
+        // logits (bias included) from route_logits_kernel
+        for (int e = tid; e < E; e += kRouteThreads) lg[e] = a.lg_buf[(size_t)t * E + e];
+        __syncthreads();
+    } else {
+        if (a.xdt == 2) stage_x<2>(a.x, t, d, xs, tid);
+        else if (a.xdt == 1) stage_x<1>(a.x, t, d, xs, tid);
+        else stage_x<0>(a.x, t, d, xs, tid);
+        for (int e = tid; e < E; e += kRouteThreads) bs[e] = a.bias ? a.bias[e] : 0.f;
+        __syncthreads();
 
-    if (a.rdt == 2) logits<CB, GE, 2>(a, xs, bs, lg, wave, lane);
-    else if (a.rdt == 1) logits<CB, GE, 1>(a, xs, bs, lg, wave, lane);
-    else logits<CB, GE, 0>(a, xs, bs, lg, wave, lane);
-    __syncthreads();
+        if (a.rdt == 2) logits<CB, GE, 2>(a, xs, bs, lg, wave, lane);
+        else if (a.rdt == 1) logits<CB, GE, 1>(a, xs, bs, lg, wave, lane);
+        else logits<CB, GE, 0>(a, xs, bs, lg, wave, lane);
+        __syncthreads();
+    }
 
     // top-k in one ranking pass: the rank of expert e is the number of experts
     // ahead of it in the order (larger logit, then lower index; a NaN logit
@@ -334,8 +401,32 @@ group_kernel(RouteArgs a)
 
 }  // namespace
 
+bool route_split(int d, int E, int rdt)
+{
+    return (size_t)E * d * (rdt == 2 ? 4 : 2) > (128u << 10);
+}
+
+namespace {
+template <int XT>
+const void *logits_kernel_for(int rdt)
+{
+    if (rdt == 2) return (const void *)route_logits_kernel<XT, 2>;
+    if (rdt == 1) return (const void *)route_logits_kernel<XT, 1>;
+    return (const void *)route_logits_kernel<XT, 0>;
+}
+}  // namespace
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t s)
 {
+    if (a.lg_buf) {
+        const void *lk = a.xdt == 2 ? logits_kernel_for<2>(a.rdt)
+                       : a.xdt == 1 ? logits_kernel_for<1>(a.rdt) : logits_kernel_for<0>(a.rdt);
+        const int nblk = (a.E + kRouteWaves - 1) / kRouteWaves;
+        void *largs[] = {(void *)&a};
+        hipError_t e = hipLaunchKernel(lk, dim3((unsigned)a.T * nblk), dim3(kRouteThreads), largs, 0, s);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 4 + 32;
     const size_t lds_group = (size_t)a.E * 12 + kRouteThreads * 4 + 32;
     if (lds_group > lds) lds = lds_group;

@@ -48,8 +48,11 @@ def test_router(T, d, E, k, renorm, xdt, zipf, xscale):
     check_route(x_bits, xdt, R_bits, rdt, E, k, renorm, bias, out, f"router T={T} E={E} k={k}")
 
 
-def test_router_exact_ties_lowest_index():
-    T, d, E, k = 9, 512, 8, 3
+@pytest.mark.parametrize("T,d,E,k", [
+    (9, 512, 8, 3),         # one workgroup per token computes the logits
+    (3, 2048, 64, 6),       # 256 KB of router rows per token: logits kernel over many workgroups
+])
+def test_router_exact_ties_lowest_index(T, d, E, k):
     Rf = synth.router_f32(51, 0, E, d)
     Rf[5] = Rf[2]
     Rf[7] = Rf[0]
