@@ -403,7 +403,7 @@ group_kernel(RouteArgs a)
 
 bool route_split(int d, int E, int rdt)
 {
-    return (size_t)E * d * (rdt == 2 ? 4 : 2) > (128u << 10);
+    return (size_t)E * d * (rdt == 2 ? 4 : 2) > (32u << 10);
 }
 
 namespace {
