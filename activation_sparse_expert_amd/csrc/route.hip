@@ -4,7 +4,9 @@
 // One workgroup per token computes the E logits (every expert with the same
 // code path and reduction order, so identical router rows tie exactly), picks
 // the top-k with ties going to the lower index, and writes the softmax
-// weights.  A second kernel of one workgroup then groups the T*k (token, slot)
+// weights.  When a token's router rows exceed 32 KB, a first kernel computes
+// the logits instead, one wave per (token, expert) over many workgroups, and
+// the per-token kernel only ranks them.  A second kernel of one workgroup then groups the T*k (token, slot)
 // pairs by expert: counts, exclusive offsets, the pairs of each expert in
 // ascending order, their grouped positions, the list of experts that received
 // tokens and, for the sparse layer, the table of fixed-size token chunks that
