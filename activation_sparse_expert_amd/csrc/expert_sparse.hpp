@@ -300,7 +300,7 @@ expert_kernel(SparseArgs a)
     // channel passes loaded and reduced together (<= SEG; fewer when a lane
     // carries several tokens or groups, to bound registers)
     constexpr int PR = pass_block<TB, GEO>();
-    constexpr bool XREG = (TB * NG) <= 2;           // x pairs of the lane's groups kept in registers
+    constexpr bool XREG = (TB * NG) <= 4;            // x pairs of the lane's groups kept in registers
 
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -487,19 +487,23 @@ expert_kernel(SparseArgs a)
             *(uint4 *)(L.xs + ((size_t)tb * G + (c >> 3)) * kXPad + (c & 7) * 8) = xl[u];
     }
     __syncthreads();
-    for (int i = tid; i < TB * G; i += THREADS) {
-        const uint32_t *xp = (const uint32_t *)(L.xs + (size_t)i * kXPad);
-        float s0 = 0.f, s1 = 0.f;
+    if constexpr (!XREG) {
+        for (int i = tid; i < TB * G; i += THREADS) {
+            const uint32_t *xp = (const uint32_t *)(L.xs + (size_t)i * kXPad);
+            float s0 = 0.f, s1 = 0.f;
 #pragma unroll 8
-        for (int m = 0; m < 32; ++m) {
-            s0 += lo16_to_float<BF16>(xp[m]);
-            s1 += hi16_to_float<BF16>(xp[m]);
+            for (int m = 0; m < 32; ++m) {
+                s0 += lo16_to_float<BF16>(xp[m]);
+                s1 += hi16_to_float<BF16>(xp[m]);
+            }
+            L.xg[i] = s0 + s1;
         }
-        L.xg[i] = s0 + s1;
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- A: v = x W^up for this tile ------------------------------------
+    // With the lane's x pairs in registers (XREG) the group sums come from
+    // them (packed dot with ones, no further barrier); otherwise from LDS.
     uint32_t xr_a[XREG ? TB * NG : 1][32];
     float xg_a[TB][NG];
 #pragma unroll
@@ -507,7 +511,6 @@ expert_kernel(SparseArgs a)
         const int g = min(go + SEG * gi, G - 1);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            xg_a[tb][gi] = L.xg[tb * G + g];
             if constexpr (XREG) {
                 const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
 #pragma unroll
@@ -518,6 +521,17 @@ expert_kernel(SparseArgs a)
                     xr_a[tb * NG + gi][4 * q + 2] = xx.z;
                     xr_a[tb * NG + gi][4 * q + 3] = xx.w;
                 }
+                float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+                for (int m = 0; m < 32; m += 4) {
+                    s0 = dot2<BF16>(xr_a[tb * NG + gi][m], a.dec_one, s0);
+                    s1 = dot2<BF16>(xr_a[tb * NG + gi][m + 1], a.dec_one, s1);
+                    s2 = dot2<BF16>(xr_a[tb * NG + gi][m + 2], a.dec_one, s2);
+                    s3 = dot2<BF16>(xr_a[tb * NG + gi][m + 3], a.dec_one, s3);
+                }
+                xg_a[tb][gi] = (s0 + s1) + (s2 + s3);
+            } else {
+                xg_a[tb][gi] = L.xg[tb * G + g];
             }
         }
     }
