@@ -16,7 +16,10 @@
 // read from HBM once.  The reduction index k is permuted inside
 // every 64-wide block (lane half h takes k = 32h + 8s + 0..7 at step s); A and
 // B use the same permutation, which leaves the sum unchanged.  Epilogue:
-// h = SiLU(g) * u in fp32 to the workspace.
+// h = SiLU(g) * u in fp32 to the workspace.  When experts average more than
+// 64 tokens, gateup128_kernel takes 128 tokens per pass instead (64-wide k
+// blocks in three 48 KB stages, two in flight), so each staged weight block
+// feeds twice the products and the weights stream half as often.
 // Kernel 2 (down): a workgroup owns 128 output columns and one quarter of the
 // intermediate channels (split-K); A = H split into bf16 hi + lo parts (so H
 // keeps ~16 significant bits), B = W^down.  W^down is stored channel-major
@@ -187,6 +190,111 @@ gateup_kernel(DenseArgs a)
     }
 }
 
+// gate/up for experts with many tokens: 128 tokens per pass, so each weight
+// block staged in LDS feeds twice the products.  Stage = one 64-wide k block:
+// 128 gate, 128 up and 128 x rows of 128 bytes (48 KB), three stages, two
+// blocks in flight.  Wave w owns channel quarter w >> 1 and token quarters
+// 2 (w & 1) and 2 (w & 1) + 1.  Chunks are XOR-swizzled by (row & 7) as above.
+constexpr int kG2Rows = 2 * kGuBN + 128;
+constexpr size_t kG2Stage = (size_t)kG2Rows * 128;                 // 48 KB
+constexpr int kG2Stages = 3;
+constexpr size_t kG2Lds = kG2Stages * kG2Stage;                    // 144 KB
+constexpr int kG2Copies = kG2Rows * 8 / 64 / kGuWaves;            // 16-byte copies per lane per stage (6)
+
+__device__ __forceinline__ int swz2(int row, int chunk) { return row * 128 + 16 * (chunk ^ (row & 7)); }
+
+__global__ void __launch_bounds__(kGuThreads)
+gateup128_kernel(DenseArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int nblk = a.f / kGuBN;
+    const int slot = blockIdx.x / nblk;
+    const int nb = blockIdx.x - slot * nblk;
+    const SlotInfo si = slot_info(a, slot);
+    if (!si.valid) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, li = lane & 31;
+    const int mp = wave & 1, nt = wave >> 1;                        // token-quarter pair, channel quarter
+    const int d = a.d;
+    const int j = nb * kGuBN + nt * 32 + li;                        // this lane's B column
+    const size_t wbase = (size_t)si.e * a.f * d + (size_t)nb * kGuBN * d;
+    const int nkb = d / 64;
+
+    for (int m0 = 0; m0 < si.ntok; m0 += 128) {
+        // copy q of wave w covers tile rows 8 (w kG2Copies + q) .. + 7
+        const uint16_t *src[kG2Copies];
+#pragma unroll
+        for (int q = 0; q < kG2Copies; ++q) {
+            const int p = (wave * kG2Copies + q) * 64 + lane;           // 16-byte position in the stage
+            const int row = p >> 3, c = (p & 7) ^ (row & 7);            // tile row, source chunk
+            const uint16_t *rp;
+            if (row < kGuBN) {
+                rp = a.gate + wbase + (size_t)row * d;
+            } else if (row < 2 * kGuBN) {
+                rp = a.up + wbase + (size_t)(row - kGuBN) * d;
+            } else {
+                const int m = m0 + row - 2 * kGuBN;                     // rows past the chunk read
+                rp = a.x + (size_t)(m < si.ntok ? token_of(a, si, m) : 0) * d;   // a valid token
+            }
+            src[q] = rp + 8 * c;
+        }
+        auto issue = [&](int kb, int stage) {
+            unsigned char *base = smem + (size_t)stage * kG2Stage;
+#pragma unroll
+            for (int q = 0; q < kG2Copies; ++q)
+                copy16_to_lds(src[q] + (size_t)kb * 64, base + (size_t)(wave * kG2Copies + q) * 1024);
+        };
+
+        floatx16 ag[2], au[2];
+        for (int i = 0; i < 2; ++i)
+            for (int r = 0; r < 16; ++r) { ag[i][r] = 0.f; au[i][r] = 0.f; }
+        bool mine[2];
+        for (int i = 0; i < 2; ++i) mine[i] = m0 + 32 * (2 * mp + i) < si.ntok;
+
+        issue(0, 0);
+        if (nkb > 1) issue(1, 1);
+        for (int kb = 0; kb < nkb; ++kb) {
+            // this wave's copies of block kb are done once at most the next
+            // block's remain in flight
+            if (kb + 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2Copies) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            // the stage written next held block kb - 1, which every wave has finished
+            if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % kG2Stages);
+            const unsigned char *st = smem + (size_t)(kb % kG2Stages) * kG2Stage;
+            const int gr = nt * 32 + li, ur = kGuBN + nt * 32 + li;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int c = 4 * h + s4;                           // k = 32h + 8 s4 + 0..7
+                const uint4 bg = *(const uint4 *)(st + swz2(gr, c));
+                const uint4 bu = *(const uint4 *)(st + swz2(ur, c));
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    if (mine[i]) {
+                        const int xr = 2 * kGuBN + 32 * (2 * mp + i) + li;
+                        const uint4 ax = *(const uint4 *)(st + swz2(xr, c));
+                        ag[i] = mfma(ax, bg, ag[i]);
+                        au[i] = mfma(ax, bu, au[i]);
+                    }
+                }
+            }
+        }
+        __syncthreads();        // the stages are reused by the next pass
+        // D layout: value r of lane l is row 8(r/4) + 4h + r%4, column l%32
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (!mine[i]) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + 32 * (2 * mp + i) + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < si.ntok)
+                    a.h[(size_t)(si.hrow0 + m) * a.f + j] = silu(ag[i][r]) * au[i][r];
+            }
+        }
+    }
+}
+
 constexpr int kBP = 136;        // halves per LDS row of a down-weight tile (128 columns + pad)
 constexpr size_t kDownHs = (size_t)2 * 64 * kXP;                  // hi + lo H tiles (halves)
 constexpr size_t kDownBs = (size_t)64 * kBP;                      // one weight tile (halves)
@@ -336,10 +444,16 @@ hipError_t launch_dense_layer(const DenseArgs &a, hipStream_t s)
     if (a.f % kNB != 0 || a.d % kNB != 0 || (a.f / kKSplit) % 64 != 0 || a.f % kGuBN != 0)
         return hipErrorInvalidValue;
     const int slots = a.S + (a.E < a.T * a.k ? a.E : a.T * a.k);
-    hipError_t e = hipFuncSetAttribute((const void *)gateup_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGuLds);
+    // experts averaging more than 64 tokens take the 128-token passes
+    const bool wide = (long long)a.T * a.k > 64ll * a.E;
+    const void *gk = wide ? (const void *)gateup128_kernel : (const void *)gateup_kernel;
+    const size_t glds = wide ? kG2Lds : kGuLds;
+    hipError_t e = hipFuncSetAttribute(gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)glds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kGuBN)), dim3(kGuThreads), kGuLds, s, a);
+    if (wide)
+        hipLaunchKernelGGL(gateup128_kernel, dim3(slots * (a.f / kGuBN)), dim3(kGuThreads), glds, s, a);
+    else
+        hipLaunchKernelGGL(gateup_kernel, dim3(slots * (a.f / kGuBN)), dim3(kGuThreads), glds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void *)down_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -144,7 +144,11 @@ def test_small_layer_sparse(T, E, S, k, d, f):
                        False, f"sparse layer T={T} E={E}+{S} k={k} d={d} f={f}")
 
 
-@pytest.mark.parametrize("T,E,S,k,d,f", [(150, 4, 0, 2, 512, 512), (9, 6, 1, 2, 1024, 256)])
+@pytest.mark.parametrize("T,E,S,k,d,f", [
+    (150, 4, 0, 2, 512, 512),    # ~75 tokens per expert: 128-token gate/up passes, one partial
+    (9, 6, 1, 2, 1024, 256),     # 64-token passes
+    (300, 4, 1, 2, 512, 512),    # ~150 per routed expert, 300 for the shared one: several passes
+])
 def test_small_layer_dense(T, E, S, k, d, f):
     experts, thr = build_host_layer(62, E, S, d, f, "bf16", 0.7, 1 / 16, layer=d)
     R_bits = synth.to_bf16_bits(synth.router_f32(62, d, E, d))
@@ -152,6 +156,8 @@ def test_small_layer_dense(T, E, S, k, d, f):
     L = device_layer(experts, thr, R_bits, "bf16", E, S, k, dense=True)
     y, tr = run_layer(L, to_dev_bits(x_bits, "bf16"), moe.PATH_DENSE)
     tokens = np.arange(T) if T <= 16 else np.array([0, 1, 63, 64, 100, T - 1])
+    if T > 200:
+        tokens = np.concatenate([tokens, [150, 200, 250, 280]])
     oracle_layer_check(experts, thr, R_bits, "bf16", None, E, S, k, x_bits, y, tr, tokens, True,
                        f"dense layer T={T} E={E}+{S} k={k} d={d} f={f}")
 
