@@ -75,8 +75,9 @@ struct RouteArgs {
     int32_t *chunk_tab, *n_chunks;      // [<= T*k], [1]: expert << 16 | first grouped position
     float *lg_buf;                      // [T][E] workspace for the wide-router split (route_split)
 };
-// Routers whose rows are large per token (E d element bytes above 32 KB)
-// compute their logits in a separate kernel spread over many workgroups.
+// Routers with more than 8 experts whose rows are large per token (E d
+// element bytes above 32 KB) compute their logits in a separate kernel spread
+// over many workgroups.
 bool route_split(int d, int E, int rdt);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 

@@ -4,9 +4,11 @@
 // One workgroup per token computes the E logits (every expert with the same
 // code path and reduction order, so identical router rows tie exactly), picks
 // the top-k with ties going to the lower index, and writes the softmax
-// weights.  When a token's router rows exceed 32 KB, a first kernel computes
-// the logits instead, one wave per (token, expert) over many workgroups, and
-// the per-token kernel only ranks them.  A second kernel of one workgroup then groups the T*k (token, slot)
+// weights.  With at most 8 experts, wave e forms logit e from x and router
+// row e read straight from global memory.  When a token's router rows exceed
+// 32 KB with more experts, a first kernel computes the logits that way, one
+// wave per (token, expert) over many workgroups, and the per-token kernel only
+// ranks them.  A second kernel of one workgroup then groups the T*k (token, slot)
 // pairs by expert: counts, exclusive offsets, the pairs of each expert in
 // ascending order, their grouped positions, the list of experts that received
 // tokens and, for the sparse layer, the table of fixed-size token chunks that
@@ -172,14 +174,8 @@ __device__ __forceinline__ void load8(const void *base, size_t g, float (&v)[8])
 // added by a fixed butterfly: every expert's logit is formed the same way, so
 // identical router rows tie exactly.  route_kernel then ranks them.
 template <int XT, int WT>
-__global__ void __launch_bounds__(kRouteThreads)
-route_logits_kernel(RouteArgs a)
+__device__ __forceinline__ float wave_logit(const RouteArgs &a, int t, int e, int lane)
 {
-    const int nblk = (a.E + kRouteWaves - 1) / kRouteWaves;
-    const int t = blockIdx.x / nblk;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = (blockIdx.x - t * nblk) * kRouteWaves + wave;
-    if (e >= a.E) return;                               // no barriers in this kernel
     constexpr int xsz = XT == 2 ? 4 : 2, wsz = WT == 2 ? 4 : 2;
     const unsigned char *xr = (const unsigned char *)a.x + (size_t)t * a.d * xsz;
     const unsigned char *wr = (const unsigned char *)a.rw + (size_t)e * a.d * wsz;
@@ -202,8 +198,28 @@ route_logits_kernel(RouteArgs a)
             if (g0 + lane + 64 * i < ng) acc = q;
         }
     }
-    acc = seg_sum<64>(acc);
-    if (lane == 0) a.lg_buf[(size_t)t * a.E + e] = acc + (a.bias ? a.bias[e] : 0.f);
+    return seg_sum<64>(acc) + (a.bias ? a.bias[e] : 0.f);
+}
+
+template <int XT>
+__device__ __forceinline__ float wave_logit_x(const RouteArgs &a, int t, int e, int lane)
+{
+    if (a.rdt == 2) return wave_logit<XT, 2>(a, t, e, lane);
+    if (a.rdt == 1) return wave_logit<XT, 1>(a, t, e, lane);
+    return wave_logit<XT, 0>(a, t, e, lane);
+}
+
+template <int XT, int WT>
+__global__ void __launch_bounds__(kRouteThreads)
+route_logits_kernel(RouteArgs a)
+{
+    const int nblk = (a.E + kRouteWaves - 1) / kRouteWaves;
+    const int t = blockIdx.x / nblk;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = (blockIdx.x - t * nblk) * kRouteWaves + wave;
+    if (e >= a.E) return;                               // no barriers in this kernel
+    const float v = wave_logit<XT, WT>(a, t, e, lane);
+    if (lane == 0) a.lg_buf[(size_t)t * a.E + e] = v;
 }
 
 // Counting sort of the T*k pairs by expert, stable in pair order.  Reads the
@@ -329,6 +345,15 @@ route_kernel(RouteArgs a)
         // logits (bias included) from route_logits_kernel
         for (int e = tid; e < E; e += kRouteThreads) lg[e] = a.lg_buf[(size_t)t * E + e];
         __syncthreads();
+    } else if (E <= kRouteWaves) {
+        // few experts: wave e forms logit e as the logits kernel does
+        if (wave < E) {
+            const float v = a.xdt == 2 ? wave_logit_x<2>(a, t, wave, lane)
+                          : a.xdt == 1 ? wave_logit_x<1>(a, t, wave, lane)
+                                       : wave_logit_x<0>(a, t, wave, lane);
+            if (lane == 0) lg[wave] = v;
+        }
+        __syncthreads();
     } else {
         if (a.xdt == 2) stage_x<2>(a.x, t, d, xs, tid);
         else if (a.xdt == 1) stage_x<1>(a.x, t, d, xs, tid);
@@ -405,7 +430,8 @@ group_kernel(RouteArgs a)
 
 bool route_split(int d, int E, int rdt)
 {
-    return (size_t)E * d * (rdt == 2 ? 4 : 2) > (32u << 10);
+    // up to kRouteWaves experts the per-token kernel forms the logits the same way itself
+    return E > kRouteWaves && (size_t)E * d * (rdt == 2 ? 4 : 2) > (32u << 10);
 }
 
 namespace {
