@@ -287,7 +287,10 @@ __host__ __device__ constexpr int pass_block()
     return pb < GEO::SEG ? pb : GEO::SEG;
 }
 
-template <bool BF16, int TB, class GEO, bool ONE>
+// ONE: the tile is a single block of passes (straight-line code).  PBX: the
+// block is PBX times the usual pass block (2 for single-token tiles of 9-16
+// passes, so that they too run straight-line with a continuous lookahead).
+template <bool BF16, int TB, class GEO, bool ONE, int PBX = 1>
 __global__ void __launch_bounds__(GEO::THREADS)
 expert_kernel(SparseArgs a)
 {
@@ -299,7 +302,8 @@ expert_kernel(SparseArgs a)
     constexpr int LOGSEG = Log2<SEG>::v;
     // channel passes loaded and reduced together (<= SEG; fewer when a lane
     // carries several tokens or groups, to bound registers)
-    constexpr int PR = pass_block<TB, GEO>();
+    constexpr int PR = pass_block<TB, GEO>() * PBX;
+    static_assert(PR <= GEO::SEG, "passes of a block exceed the segment");
     constexpr bool XREG = (TB * NG) <= 4;            // x pairs of the lane's groups kept in registers
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -810,6 +814,10 @@ hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
     // (the widest geometry keeps the loop form: its straight-line version spills)
     if constexpr (GEO::NG < 4) {
         if (one) kern = expert_kernel<BF16, TB, GEO, true>;
+    }
+    if constexpr (TB == 1 && GEO::NG == 1 && 2 * pass_block<TB, GEO>() <= GEO::SEG) {
+        const int passes = (a.cpw + rows_pass - 1) / rows_pass;
+        if (!one && passes <= 2 * pass_block<TB, GEO>()) kern = expert_kernel<BF16, TB, GEO, true, 2>;
     }
     SparseArgs args = a;
     args.dec_mask = decode_const<BF16>().mask;
