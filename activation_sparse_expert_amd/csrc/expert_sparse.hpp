@@ -447,14 +447,16 @@ expert_kernel(SparseArgs a)
         L.tok_row[tid] = row;
         L.tok_sc[tid] = sc;
     }
-    __syncthreads();
+    // a single expert's token needs no table: its x load need not wait for
+    // the bookkeeping (the x-staging barrier publishes it before any use)
+    if (a.layer || TB > 1) __syncthreads();
 
     // ---- x loads, then the up-code loads; only x is waited for here -------
     uint4 xl[XL];
     if constexpr (TB == 1) {
         // one token: a buffer over its row, so that no branch separates the
         // x load from the code loads issued after it
-        const int t0 = __builtin_amdgcn_readfirstlane(L.tok_t[0]);
+        const int t0 = a.layer ? __builtin_amdgcn_readfirstlane(L.tok_t[0]) : tbase;
         const __amdgpu_buffer_rsrc_t rx = tile_rsrc(a.x + (size_t)t0 * d, (uint32_t)d * 2);
 #pragma unroll
         for (int u = 0; u < XL; ++u) {
@@ -797,8 +799,10 @@ expert_kernel(SparseArgs a)
                                     sc * yacc[tb][i][2], sc * yacc[tb][i][3]);
             float4 hi = make_float4(sc * yacc[tb][i][4], sc * yacc[tb][i][5],
                                     sc * yacc[tb][i][6], sc * yacc[tb][i][7]);
-            *(float4 *)(dst + (size_t)c * 8) = lo;
-            *(float4 *)(dst + (size_t)c * 8 + 4) = hi;
+            // streamed: the reduce kernel reads each partial row once
+            typedef float v4f __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(v4f{lo.x, lo.y, lo.z, lo.w}, (v4f *)(dst + (size_t)c * 8));
+            __builtin_nontemporal_store(v4f{hi.x, hi.y, hi.z, hi.w}, (v4f *)(dst + (size_t)c * 8 + 4));
         }
     }
 }
