@@ -42,7 +42,8 @@
  *   16-byte aligned up_q/gate_t/down/x and 4-byte aligned up_sz.
  *
  * Workspace: every forward call takes a device workspace of at least
- * moe_workspace_size(...) bytes (fp32 partial rows and routing tables).  It
+ * moe_workspace_size(...) bytes (fp32 partial rows, routing tables and, for
+ * routers with more than 8 experts, the [T][E] fp32 router logits).  It
  * needs no initialisation and holds nothing from one call to the next.  Calls
  * that share a workspace must be ordered (same stream); overlapping calls need
  * distinct workspaces.
