@@ -120,6 +120,7 @@ struct LayerWs {
     float *part;
     float *h;
     float *lg;              // [T][E] router logits (wide-router split)
+    int32_t *chunk_rec;     // [T*k][4] single-token chunk records
 };
 
 size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, void *base)
@@ -128,7 +129,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     const TilePlan tp = layer_plan(T, d, f, E, k, S).tp;
     const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
     size_t o = 0;
-    size_t off[14];
+    size_t off[15];
     off[0] = o; o += up(4);
     off[1] = o; o += up((size_t)T * k * 4);
     off[2] = o; o += up((size_t)T * k * 4);
@@ -143,6 +144,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     off[11] = o; o += up((size_t)T * k * 4);           // every chunk holds at least one pair
     off[12] = o; o += up(4);
     off[13] = o; o += up((size_t)T * E * 4);
+    off[14] = o; o += up((size_t)T * k * 16);
     if (out) {
         char *p = (char *)base;
         out->topk_idx = (int32_t *)(p + off[1]);
@@ -158,6 +160,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->chunk_tab = (int32_t *)(p + off[11]);
         out->n_chunks = (int32_t *)(p + off[12]);
         out->lg = (float *)(p + off[13]);
+        out->chunk_rec = (int32_t *)(p + off[14]);
     }
     return o;
 }
@@ -177,7 +180,7 @@ moe_status check_route_args(const void *x, moe_dtype xdt, int T, int d, const vo
     if (d % 8 != 0) return MOE_ERR_UNSUPPORTED;         // rows are read in 16-byte units
     if ((long long)T * k > 65536) return MOE_ERR_UNSUPPORTED;
     if (!valid_out(xdt) || !valid_out(rdt)) return MOE_ERR_UNSUPPORTED;
-    if ((size_t)d * 4 + (size_t)E * 8 + (size_t)k * 4 + 16 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
+    if ((size_t)d * 4 + (size_t)E * 8 + (size_t)k * 8 + 32 > 160 * 1024) return MOE_ERR_UNSUPPORTED;
     if (!aligned(x, xdt == MOE_F32 ? 4 : 2) || !aligned(rw, rdt == MOE_F32 ? 4 : 2))
         return MOE_ERR_ALIGNMENT;
     return MOE_OK;
@@ -352,6 +355,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     const SparsePlan sp = layer_plan(T, d, f, E, k, S);
     if (path == MOE_PATH_SPARSE) {
         r.chunk = sp.tb; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;
+        if (sp.tb == 1) r.chunk_rec = w.chunk_rec;
     }
     hipError_t he = launch_route(r, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
@@ -389,6 +393,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     a.token_scale = nullptr;
     a.layer = 1; a.E = E; a.k = k; a.S = S;
     a.chunk_tab = w.chunk_tab; a.n_chunks = w.n_chunks;
+    a.chunk_rec = sp.tb == 1 ? w.chunk_rec : nullptr;
     a.offset = w.offset; a.pairs = w.pairs;
     a.topk_w = r.topk_w;
     a.part = w.part;

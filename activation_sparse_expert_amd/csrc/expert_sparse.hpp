@@ -335,6 +335,8 @@ expert_kernel(SparseArgs a)
     const int chunk = blockIdx.x / a.tiles;
     const int tile = blockIdx.x - chunk * a.tiles;
     int e = 0, nt = 0, pos0 = 0, tbase = 0, sh = 0;
+    int rec_p = -1;                                 // single-token chunk record: pair, weight
+    float rec_w = 1.0f;
     bool shared_slot = false;
     if (!a.layer) {
         tbase = chunk * TB;
@@ -349,11 +351,21 @@ expert_kernel(SparseArgs a)
             shared_slot = true;
         } else {
             const int ci = chunk - a.S * nsc;
-            if (ci >= *a.n_chunks) return;          // beyond this call's chunks
-            const int ent = a.chunk_tab[ci];
-            e = ent >> 16;
-            pos0 = ent & 0xFFFF;
-            nt = min(TB, a.offset[e + 1] - pos0);
+            if (TB == 1 && a.chunk_rec) {
+                // one pair per chunk: the grid holds exactly T k routed chunks
+                const int4 rec = *(const int4 *)(a.chunk_rec + 4 * (size_t)ci);
+                e = rec.x;
+                rec_p = rec.y;
+                rec_w = __int_as_float(rec.z);
+                pos0 = rec.w;
+                nt = 1;
+            } else {
+                if (ci >= *a.n_chunks) return;      // beyond this call's chunks
+                const int ent = a.chunk_tab[ci];
+                e = ent >> 16;
+                pos0 = ent & 0xFFFF;
+                nt = min(TB, a.offset[e + 1] - pos0);
+            }
         }
     }
     if (nt <= 0) return;
@@ -435,11 +447,11 @@ expert_kernel(SparseArgs a)
                 row = a.T * a.k + sh * a.T + t;
             } else {
                 const int pos = pos0 + tid;
-                const int p = a.pairs[pos];
+                const int p = rec_p >= 0 ? rec_p : a.pairs[pos];
                 t = p / a.k;
                 sl = p - t * a.k;
                 row = pos;
-                sc = a.topk_w[p];
+                sc = rec_p >= 0 ? rec_w : a.topk_w[p];
             }
         }
         L.tok_t[tid] = t;
@@ -447,16 +459,19 @@ expert_kernel(SparseArgs a)
         L.tok_row[tid] = row;
         L.tok_sc[tid] = sc;
     }
-    // a single expert's token needs no table: its x load need not wait for
-    // the bookkeeping (the x-staging barrier publishes it before any use)
-    if (a.layer || TB > 1) __syncthreads();
+    // a single token known without the table (single expert, shared expert,
+    // chunk record): its x load need not wait for the bookkeeping (the
+    // x-staging barrier publishes it before any use)
+    const int t0u = TB > 1 ? -1
+                  : (!a.layer || shared_slot) ? tbase : (rec_p >= 0 ? rec_p / a.k : -1);
+    if (t0u < 0) __syncthreads();
 
     // ---- x loads, then the up-code loads; only x is waited for here -------
     uint4 xl[XL];
     if constexpr (TB == 1) {
         // one token: a buffer over its row, so that no branch separates the
         // x load from the code loads issued after it
-        const int t0 = a.layer ? __builtin_amdgcn_readfirstlane(L.tok_t[0]) : tbase;
+        const int t0 = t0u >= 0 ? t0u : __builtin_amdgcn_readfirstlane(L.tok_t[0]);
         const __amdgpu_buffer_rsrc_t rx = tile_rsrc(a.x + (size_t)t0 * d, (uint32_t)d * 2);
 #pragma unroll
         for (int u = 0; u < XL; ++u) {

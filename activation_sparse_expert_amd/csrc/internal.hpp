@@ -27,6 +27,7 @@ struct SparseArgs {
     // layer mode (layer != 0)
     int layer, E, k, S;
     const int32_t *chunk_tab;           // routed chunks: expert << 16 | first grouped position
+    const int32_t *chunk_rec;           // single-token chunks: [chunk] {expert, pair, weight bits, position}
     const int32_t *n_chunks;            // [1] routed chunks in chunk_tab
     const int32_t *offset;              // [E+1]
     const int32_t *pairs;               // [T*k]
@@ -74,6 +75,7 @@ struct RouteArgs {
     int chunk;                          // > 0: split each expert's pairs into chunks of this size
     int32_t *chunk_tab, *n_chunks;      // [<= T*k], [1]: expert << 16 | first grouped position
     float *lg_buf;                      // [T][E] workspace for the wide-router split (route_split)
+    int32_t *chunk_rec;                 // nullable, with chunk == 1: [T*k][4] per-chunk records
 };
 // Routers with more than 8 experts whose rows are large per token (E d
 // element bytes above 32 KB) compute their logits in a separate kernel spread

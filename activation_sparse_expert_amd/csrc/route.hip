@@ -227,11 +227,11 @@ route_logits_kernel(RouteArgs a)
 // earlier kernel).  With a.chunk > 0 it also lists every expert's pairs in
 // chunks of a.chunk consecutive grouped positions (the last one shorter),
 // experts in ascending order: entry = expert << 16 | first position.
-__device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, int my_e)
+__device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, int my_e, float my_w)
 {
-    // reg: every pair is p = tid and this thread's pair chose expert my_e (a
-    // single token with k <= kRouteThreads, known in registers); else the
-    // choices are read from memory
+    // reg: every pair is p = tid and this thread's pair chose expert my_e with
+    // weight my_w (a single token with k <= kRouteThreads, known in
+    // registers); else the choices are read from memory
     const int tid = threadIdx.x;
     const int E = a.E;
     int *cnt = (int *)smem;                          // [E] counts
@@ -319,8 +319,15 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
         if (e >= 0) {
             int rank = 0;
             for (int q = 0; q < tid; ++q) rank += (ce[q] == e);
-            a.pairs[run[e] + rank] = p;
-            if (a.pair_pos) a.pair_pos[p] = run[e] + rank;
+            const int pos = run[e] + rank;
+            a.pairs[pos] = p;
+            if (a.pair_pos) a.pair_pos[p] = pos;
+            if (a.chunk_rec) {
+                // single-token chunks: chunk pos holds pair p; its record lets
+                // the expert kernel start from one load
+                const float w = reg ? my_w : a.topk_w[p];
+                *(int4 *)(a.chunk_rec + 4 * (size_t)pos) = make_int4(e, p, __float_as_int(w), pos);
+            }
         }
         __syncthreads();
         if (e >= 0) atomicAdd(&run[e], 1);          // the batch's pairs of e follow these
@@ -337,6 +344,7 @@ route_kernel(RouteArgs a)
     float *lg = xs + a.d;                             // [E rounded up to 4]
     float *bs = lg + ((a.E + 3) & ~3);                // [E] router bias (0 without one)
     int *sel = (int *)(bs + a.E);                     // [k]
+    float *wsel = (float *)(sel + a.k);               // [k] weights of the choices
     const int t = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = a.d, E = a.E, k = a.k;
@@ -404,8 +412,10 @@ route_kernel(RouteArgs a)
         den = seg_sum<64>(den);
         for (int s = lane; s < k; s += 64) {
             const int e = sel[s];
+            const float w = __expf(lg[e] - m) / den;
             a.topk_idx[(size_t)t * k + s] = e;
-            a.topk_w[(size_t)t * k + s] = __expf(lg[e] - m) / den;
+            a.topk_w[(size_t)t * k + s] = w;
+            wsel[s] = w;
         }
         if (a.logits)
             for (int e = lane; e < E; e += 64) a.logits[(size_t)t * E + e] = lg[e];
@@ -414,8 +424,9 @@ route_kernel(RouteArgs a)
     if (!a.count || gridDim.x != 1) return;
     __syncthreads();            // one token: its own workgroup groups it
     const int my_e = tid < k ? sel[tid] : 0;      // read before the grouping reuses LDS
+    const float my_w = tid < k ? wsel[tid] : 0.f;
     __syncthreads();
-    group_pairs(a, smem, k <= kRouteThreads, my_e);
+    group_pairs(a, smem, k <= kRouteThreads, my_e, my_w);
 }
 
 // Grouping of all T*k pairs by one workgroup (after the per-token kernel).
@@ -423,7 +434,7 @@ __global__ void __launch_bounds__(kRouteThreads)
 group_kernel(RouteArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    group_pairs(a, smem, false, 0);
+    group_pairs(a, smem, false, 0, 0.f);
 }
 
 }  // namespace
@@ -455,7 +466,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
         if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 4 + 32;
+    size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 8 + 32;
     const size_t lds_group = (size_t)a.E * 12 + kRouteThreads * 4 + 32;
     if (lds_group > lds) lds = lds_group;
     // 16-byte units per lane of one router row (64 lanes): CB (<= 8) of them per
