@@ -387,13 +387,15 @@ route_kernel(RouteArgs a)
         for (int e = tid; e < E; e += kRouteThreads) {
             const float le = lg[e] != lg[e] ? -INFINITY : lg[e];
             int r = 0;
+#pragma unroll 4
             for (int e2 = 0; e2 < E4; e2 += 4) {
                 const float4 l4 = *(const float4 *)&lg[e2];
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float l2 = lv[j] != lv[j] ? -INFINITY : lv[j];
-                    r += (l2 > le) || (l2 == le && e2 + j < e);
+                    // branch-free: ahead if larger, or equal with a lower index
+                    r += (int)(l2 > le) | ((int)(l2 == le) & (int)(e2 + j < e));
                 }
             }
             if (r < k) sel[r] = e;
