@@ -30,13 +30,13 @@ __device__ __forceinline__ int part_row(const ReduceArgs &a, int t, int ri)
 // rows are read by many compute units at once, in whole 128-byte lines.
 // Contribution c = ri * tiles + tile (row ri of the token, tile `tile`); group g
 // of kSeg threads adds contributions g, g + kGroups, ... in that order, then the
-// groups' sums are added in group order: a fixed order.  A single expert's
+// groups' sums are added by a butterfly within each wave and then wave by wave: a fixed order.  A single expert's
 // token has one row (row t), so that case skips the row table.
 template <bool LAYER>
 __global__ void __launch_bounds__(kRedThreads)
 reduce_kernel(ReduceArgs a)
 {
-    __shared__ float4 sm[kGroups][kSeg];
+    __shared__ float4 sm[kRedThreads / 64][kSeg];
     __shared__ int rows_s[LAYER ? kMaxRowsPerTok : 1];
     const int cblocks = a.d / kCols;
     const int t = blockIdx.x / cblocks;
@@ -71,12 +71,22 @@ reduce_kernel(ReduceArgs a)
             }
         }
     }
-    sm[tg][cq] = s;
+    // groups of one wave by butterfly (lanes with the same column slot), then
+    // the waves in order through LDS: a fixed order
+#pragma unroll
+    for (int off = kSeg; off < 64; off <<= 1) {
+        s.x += __shfl_xor(s.x, off, 64);
+        s.y += __shfl_xor(s.y, off, 64);
+        s.z += __shfl_xor(s.z, off, 64);
+        s.w += __shfl_xor(s.w, off, 64);
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) < kSeg) sm[wave][cq] = s;
     __syncthreads();
     if (tg == 0) {
         float4 r = sm[0][cq];
-        for (int g = 1; g < kGroups; ++g) {
-            const float4 v = sm[g][cq];
+        for (int w = 1; w < kRedThreads / 64; ++w) {
+            const float4 v = sm[w][cq];
             r.x += v.x; r.y += v.y; r.z += v.z; r.w += v.w;
         }
         const size_t base = (size_t)t * a.d + col;
