@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
 MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
-PATH_SPARSE, PATH_DENSE = 0, 1
+PATH_SPARSE, PATH_DENSE, PATH_AUTO = 0, 1, 2
 OP_EXPERT, OP_ROUTE, OP_LAYER = 0, 1, 2
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",

@@ -326,7 +326,13 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     if (!L->thresholds) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) || !aligned(L->thresholds, 4))
         return MOE_ERR_ALIGNMENT;
-    if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE) return MOE_ERR_INVALID_ARG;
+    if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE && path != MOE_PATH_AUTO)
+        return MOE_ERR_INVALID_ARG;
+    if (path == MOE_PATH_AUTO) {
+        const bool dense_ok = L->wdt == MOE_BF16 && L->up_dense && aligned(L->up_dense, 16) &&
+                              !(trace && trace->masks) && f % 256 == 0 && d % 128 == 0;
+        path = dense_ok && (long long)T * k >= 8ll * E ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+    }
     if (path == MOE_PATH_DENSE) {
         if (L->wdt != MOE_BF16 || !L->up_dense) return MOE_ERR_UNSUPPORTED;
         if (!aligned(L->up_dense, 16)) return MOE_ERR_ALIGNMENT;

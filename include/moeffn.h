@@ -84,7 +84,8 @@ typedef enum { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
 
 typedef enum {
     MOE_PATH_SPARSE = 0,        /* Algorithm 1: INT2 up, threshold mask, row gathers */
-    MOE_PATH_DENSE = 1          /* bf16 MFMA grouped GEMM, threshold off            */
+    MOE_PATH_DENSE = 1,         /* bf16 MFMA grouped GEMM, threshold off            */
+    MOE_PATH_AUTO = 2           /* dense when it moves fewer bytes, else sparse     */
 } moe_path;
 
 typedef enum {
@@ -178,6 +179,14 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
  *   y_t = sum_s w_{t,s} a_{e(t,s)}(x_t) + sum_i a_{E+i}(x_t)
  * where a_e is Algorithm 1 (MOE_PATH_SPARSE) or the dense SwiGLU with the bf16
  * up weights in L->up_dense (MOE_PATH_DENSE, which needs wdt == MOE_BF16).
+ * MOE_PATH_AUTO picks per call, on the host, from the batch size (MoE-Lightning
+ * review, "层次化屋顶模型": the expert FFN's operational intensity grows with the
+ * tokens per expert): the dense path when it is available (bf16 weights,
+ * up_dense set, its shape limits met, no mask export requested) and the routed
+ * tokens average at least 8 per expert (T k >= 8 E), else the sparse path.  At
+ * that size a sparse chunk of 4 tokens reads the union of 4 masks' rows (about
+ * 76% of the rows at 70% sparsity) again for every chunk, more than one pass
+ * over the dense weights.
  *   x [T][d] in xdt (== L->wdt), y [T][d] in ydt (overwritten).
  * trace (host struct, NULL allowed) receives the optional exports.
  */

@@ -148,6 +148,7 @@ def _layer(desc=None, x=FAKE, xdt=0, T=4, y=FAKE, ydt=2, path=0, ws=FAKE, ws_byt
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), -1), (dict(T=0), -1), (dict(path=3), -1), (dict(ws=None), -4),
+    (dict(path=2, ws_bytes=4096), -4),      # MOE_PATH_AUTO is a valid path: the workspace check follows
     (dict(ws_bytes=4096), -4), (dict(xdt=1), -2), (dict(path=1), -2),   # dense needs bf16 + up_dense
 ])
 def test_layer_rejects(kw, code):

@@ -162,6 +162,28 @@ def test_small_layer_dense(T, E, S, k, d, f):
                        f"dense layer T={T} E={E}+{S} k={k} d={d} f={f}")
 
 
+@pytest.mark.parametrize("T,E,S,k,d,f,expect", [
+    (9, 6, 1, 2, 1024, 256, "sparse"),       # 18 routed pairs < 8 per expert
+    (150, 4, 0, 2, 512, 512, "dense"),       # 75 per expert
+])
+def test_layer_auto_path(T, E, S, k, d, f, expect):
+    """MOE_PATH_AUTO takes the dense path from 8 routed tokens per expert on
+    average (bf16 layer with dense up weights), else the sparse path: its
+    output is bit-identical to the path it names."""
+    experts, thr = build_host_layer(64, E, S, d, f, "bf16", 0.7, 1 / 16, layer=d)
+    R_bits = synth.to_bf16_bits(synth.router_f32(64, d, E, d))
+    x_bits = synth.to_bf16_bits(synth.tokens_f32(65, T, d, 1 / 16, layer=d))
+    L = device_layer(experts, thr, R_bits, "bf16", E, S, k, dense=True)
+    x = to_dev_bits(x_bits, "bf16")
+    y_auto, _ = run_layer(L, x, moe.PATH_AUTO, want_masks=False)
+    named = moe.PATH_DENSE if expect == "dense" else moe.PATH_SPARSE
+    y_named, _ = run_layer(L, x, named, want_masks=False)
+    other = moe.PATH_SPARSE if expect == "dense" else moe.PATH_DENSE
+    y_other, _ = run_layer(L, x, other, want_masks=False)
+    assert np.array_equal(y_auto, y_named), f"AUTO at T={T} is not the {expect} path"
+    assert not np.array_equal(y_auto, y_other)
+
+
 def test_layer_hot_expert_many_chunks():
     """A router bias sends nearly every token to expert 3, which then holds
     about T/tb chunks of the sparse grid with a ragged last one, while the
