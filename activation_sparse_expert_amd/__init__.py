@@ -16,14 +16,14 @@ LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
 MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
 PATH_SPARSE, PATH_DENSE, PATH_AUTO = 0, 1, 2
-OP_EXPERT, OP_ROUTE, OP_LAYER = 0, 1, 2
+OP_EXPERT, OP_ROUTE, OP_LAYER, OP_CALIBRATE = 0, 1, 2, 3
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 
 EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_workspace_size", "moe_workspace_init", "moe_pack_up_int2",
-            "moe_materialize_up_bf16", "moe_status_string"]
+            "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold"]
 
 
 class MoeError(RuntimeError):
@@ -79,6 +79,8 @@ def lib():
         L.moe_materialize_up_bf16.argtypes = [P, P, I, I, P, P]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [I]
+        L.moe_calibrate_threshold.restype = I
+        L.moe_calibrate_threshold.argtypes = [P, C.c_longlong, C.c_double, P, P, Z, P]
         _lib = L
     return _lib
 
@@ -240,6 +242,23 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
                                  _stream())
     _check(st, "moe_layer_forward")
     return y
+
+
+def calibrate_threshold(v, q: float, *, out=None, ws=None):
+    """Threshold t = linear-interpolation q-quantile of |v| over all of the
+    fp32 device tensor v, computed on the GPU; returns a one-element fp32
+    device tensor."""
+    import torch
+    if v.dtype != torch.float32 or not v.is_contiguous():
+        raise ValueError("v must be a contiguous fp32 tensor")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=v.device)
+    if ws is None:
+        ws = new_workspace(workspace_size(OP_CALIBRATE, 1, 1), v.device)
+    st = lib().moe_calibrate_threshold(_ptr(v), v.numel(), float(q), _ptr(out), _ptr(ws),
+                                       ws.numel(), _stream())
+    _check(st, "moe_calibrate_threshold")
+    return out
 
 
 def pack_up_int2(w_up_t, *, up_q=None, up_sz=None):

@@ -3,6 +3,7 @@
 // for an invalid request, so the error paths can be exercised without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <new>
 
 #include "../../include/moeffn.h"
@@ -231,8 +232,27 @@ size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S)
     case MOE_OP_LAYER:
         if (E < 1 || k < 1 || k > E || S < 0 || f < 1) return 0;
         return layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr);
+    case MOE_OP_CALIBRATE:
+        return up(calibrate_ws_bytes());
     }
     return 0;
+}
+
+moe_status moe_calibrate_threshold(const float *v, long long n, double q, float *t_out,
+                                   void *ws, size_t ws_bytes, void *stream)
+{
+    if (!v || !t_out || n < 1 || n >= (1ll << 31) || !(q >= 0.0 && q <= 1.0))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(v, 4) || !aligned(t_out, 4)) return MOE_ERR_ALIGNMENT;
+    if (!ws || ws_bytes < up(calibrate_ws_bytes())) return MOE_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
+    // virtual index and neighbours as numpy's linear quantile forms them
+    const double h = (double)(n - 1) * q;
+    long long lo = (long long)std::floor(h), hi = lo + 1;
+    const double gamma = h - std::floor(h);
+    if (h >= (double)(n - 1)) lo = hi = n - 1;
+    if (h < 0.0) lo = hi = 0;
+    return hip_status(launch_calibrate(v, n, lo, hi, gamma, t_out, ws, (hipStream_t)stream));
 }
 
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream)

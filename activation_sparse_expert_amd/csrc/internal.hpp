@@ -102,4 +102,10 @@ hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, 
                                    uint16_t *out, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
+// Threshold calibration: out = linear-interpolation quantile of |v| between
+// order statistics r_lo and r_hi with weight gamma (computed on the host).
+size_t calibrate_ws_bytes();
+hipError_t launch_calibrate(const float *v, long long n, long long r_lo, long long r_hi,
+                            double gamma, float *out, void *ws, hipStream_t s);
+
 }  // namespace moeffn

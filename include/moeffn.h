@@ -91,7 +91,8 @@ typedef enum {
 typedef enum {
     MOE_OP_EXPERT = 0,          /* moe_expert_forward_sparse */
     MOE_OP_ROUTE = 1,           /* moe_route_topk           */
-    MOE_OP_LAYER = 2            /* moe_layer_forward        */
+    MOE_OP_LAYER = 2,           /* moe_layer_forward        */
+    MOE_OP_CALIBRATE = 3        /* moe_calibrate_threshold  */
 } moe_op;
 
 /* One compressed expert (FloE review, "混合压缩策略": {W^S(gate), W^S(down),
@@ -194,6 +195,22 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
                              void *y, moe_dtype ydt, moe_path path,
                              const moe_layer_trace *trace,
                              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Threshold calibration (FloE review, "高效稀疏 GEMV 内核": t_ij sets the
+ * activation sparsity; the pages leave its placement open).  t_out[0] (fp32,
+ * device) = the q-quantile of |v| over the n values of v (fp32, device; e.g.
+ * the v_out export of moe_expert_forward_sparse on calibration tokens), with
+ * linear interpolation between order statistics: h = (n - 1) q,
+ * a = |v|_(floor h), b = |v|_(floor h + 1) (both the largest when h >= n - 1),
+ * g = h - floor h, t = a + (b - a) g (b - (b - a)(1 - g) when g >= 1/2) in
+ * fp64, rounded to fp32 (the interpolation numpy's quantile uses).  The order
+ * statistics are found on the GPU by a radix select on the bit patterns of
+ * |v|: no host synchronisation.  v must be finite; 1 <= n < 2^31, 0 <= q <= 1.
+ * Workspace: moe_workspace_size(MOE_OP_CALIBRATE, ...) bytes (sizes unused).
+ */
+moe_status moe_calibrate_threshold(const float *v, long long n, double q, float *t_out,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes needed by `op` at these sizes (0 when the sizes are invalid). */
 size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S);

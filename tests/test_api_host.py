@@ -183,6 +183,20 @@ def test_pack_and_materialize_reject():
     assert L.moe_workspace_init(FAKE + 2, 256, None) == -3
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), -1), (dict(n=0), -1), (dict(n=1 << 31), -1), (dict(q=-0.01), -1),
+    (dict(q=1.5), -1), (dict(q=float("nan")), -1), (dict(out=None), -1),
+    (dict(v=FAKE + 2), -3), (dict(ws=None), -4), (dict(ws_bytes=64), -4),
+])
+def test_calibrate_rejects(kw, code):
+    L = _lib_or_skip()
+    a = dict(v=FAKE, n=1000, q=0.9, out=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    assert L.moe_calibrate_threshold(a["v"], a["n"], a["q"], a["out"], a["ws"], a["ws_bytes"],
+                                     None) == code
+    assert L.moe_workspace_size(moe.OP_CALIBRATE, 1, 1, 0, 1, 1, 0) > 0
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(moe, "_lib", None)
     monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoeffn.so")
