@@ -116,7 +116,7 @@ size_t expert_ws_bytes(int T, int d, int f)
 struct LayerWs {
     int32_t *topk_idx;
     float *topk_w;
-    int32_t *count, *offset, *pairs, *pair_pos, *active, *n_active;
+    int32_t *count, *offset, *pairs, *active, *n_active;
     int32_t *chunk_tab, *n_chunks;
     float *part;
     float *h;
@@ -130,22 +130,21 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     const TilePlan tp = layer_plan(T, d, f, E, k, S).tp;
     const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
     size_t o = 0;
-    size_t off[15];
+    size_t off[14];
     off[0] = o; o += up(4);
     off[1] = o; o += up((size_t)T * k * 4);
     off[2] = o; o += up((size_t)T * k * 4);
     off[3] = o; o += up((size_t)E * 4);
     off[4] = o; o += up((size_t)(E + 1) * 4);
     off[5] = o; o += up((size_t)T * k * 4);
-    off[6] = o; o += up((size_t)T * k * 4);
-    off[7] = o; o += up((size_t)E * 4);
-    off[8] = o; o += up(4);
-    off[9] = o; o += up((size_t)rows * part_tiles * d * 4);
-    off[10] = o; o += up(dense_h_bytes(T, f, k, S));
-    off[11] = o; o += up((size_t)T * k * 4);           // every chunk holds at least one pair
-    off[12] = o; o += up(4);
-    off[13] = o; o += up((size_t)T * E * 4);
-    off[14] = o; o += up((size_t)T * k * 16);
+    off[6] = o; o += up((size_t)E * 4);
+    off[7] = o; o += up(4);
+    off[8] = o; o += up((size_t)rows * part_tiles * d * 4);
+    off[9] = o; o += up(dense_h_bytes(T, f, k, S));
+    off[10] = o; o += up((size_t)T * k * 4);           // every chunk holds at least one pair
+    off[11] = o; o += up(4);
+    off[12] = o; o += up((size_t)T * E * 4);
+    off[13] = o; o += up((size_t)T * k * 16);
     if (out) {
         char *p = (char *)base;
         out->topk_idx = (int32_t *)(p + off[1]);
@@ -153,15 +152,14 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->count = (int32_t *)(p + off[3]);
         out->offset = (int32_t *)(p + off[4]);
         out->pairs = (int32_t *)(p + off[5]);
-        out->pair_pos = (int32_t *)(p + off[6]);
-        out->active = (int32_t *)(p + off[7]);
-        out->n_active = (int32_t *)(p + off[8]);
-        out->part = (float *)(p + off[9]);
-        out->h = (float *)(p + off[10]);
-        out->chunk_tab = (int32_t *)(p + off[11]);
-        out->n_chunks = (int32_t *)(p + off[12]);
-        out->lg = (float *)(p + off[13]);
-        out->chunk_rec = (int32_t *)(p + off[14]);
+        out->active = (int32_t *)(p + off[6]);
+        out->n_active = (int32_t *)(p + off[7]);
+        out->part = (float *)(p + off[8]);
+        out->h = (float *)(p + off[9]);
+        out->chunk_tab = (int32_t *)(p + off[10]);
+        out->n_chunks = (int32_t *)(p + off[11]);
+        out->lg = (float *)(p + off[12]);
+        out->chunk_rec = (int32_t *)(p + off[13]);
     }
     return o;
 }
@@ -281,7 +279,7 @@ moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void
     a.E = E; a.k = k; a.renorm = renormalize ? 1 : 0;
     a.topk_idx = topk_idx; a.topk_w = topk_w; a.logits = logits_out;
     a.count = expert_count; a.offset = expert_offset; a.pairs = pair_by_expert;
-    a.pair_pos = nullptr; a.active = nullptr; a.n_active = nullptr;
+    a.active = nullptr; a.n_active = nullptr;
     a.lg_buf = route_split(d, E, rdt) ? (float *)((char *)ws + up(4)) : nullptr;
     return hip_status(launch_route(a, (hipStream_t)stream));
 }
@@ -324,7 +322,7 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     if (he != hipSuccess) return MOE_ERR_HIP;
     ReduceArgs r{};
     r.part = (const float *)ws; r.tiles = tp.tiles; r.d = d; r.T = T;
-    r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0; r.pair_pos = nullptr;
+    r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0;
     r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
     return hip_status(launch_reduce(r, s));
 }
@@ -375,7 +373,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.topk_w = (trace && trace->topk_w) ? trace->topk_w : w.topk_w;
     r.logits = trace ? trace->logits : nullptr;
     r.count = (trace && trace->expert_count) ? trace->expert_count : w.count;
-    r.offset = w.offset; r.pairs = w.pairs; r.pair_pos = w.pair_pos;
+    r.offset = w.offset; r.pairs = w.pairs;
     r.active = w.active; r.n_active = w.n_active;
     r.lg_buf = route_split(d, E, L->rdt) ? w.lg : nullptr;
     const SparsePlan sp = layer_plan(T, d, f, E, k, S);
@@ -389,7 +387,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     const size_t qs = (size_t)f * (d / 4), szs = (size_t)f * (d / 64) * 2, wst = (size_t)f * d;
     ReduceArgs red{};
     red.d = d; red.T = T; red.layer = 1; red.rows_per_tok = k + S; red.k = k; red.S = S;
-    red.pair_pos = w.pair_pos; red.part = w.part;
+    red.part = w.part;
     red.y = y; red.ydt = (int)ydt; red.accumulate = 0;
     if (path == MOE_PATH_DENSE) {
         DenseArgs a{};

@@ -334,8 +334,15 @@ down_kernel(DenseArgs a)
             int row = 0;
             float sc = 0.f;
             if (tid < nm) {
-                row = si.hrow0 + m0 + tid;
-                sc = si.shared ? 1.f : a.topk_w[a.pairs[si.pair0 + m0 + tid]];
+                // partial rows: routed ones by pair t k + s, shared ones after them
+                if (si.shared) {
+                    row = si.hrow0 + m0 + tid;
+                    sc = 1.f;
+                } else {
+                    const int p = a.pairs[si.pair0 + m0 + tid];
+                    row = p;
+                    sc = a.topk_w[p];
+                }
             }
             row_s[tid] = row;
             sc_s[tid] = sc;

@@ -450,7 +450,7 @@ expert_kernel(SparseArgs a)
                 const int p = rec_p >= 0 ? rec_p : a.pairs[pos];
                 t = p / a.k;
                 sl = p - t * a.k;
-                row = pos;
+                row = p;                            // routed partial rows are indexed by pair
                 sc = rec_p >= 0 ? rec_w : a.topk_w[p];
             }
         }

@@ -51,7 +51,6 @@ struct ReduceArgs {
     int layer;                          // 0: row of token t is t; 1: routed + shared rows
     int rows_per_tok;                   // 1 or k + S
     int k, S;
-    const int32_t *pair_pos;            // [T*k] grouped position of pair t*k + s
     void *y;
     int ydt;
     int accumulate;
@@ -70,7 +69,6 @@ struct RouteArgs {
     float *topk_w;
     float *logits;                      // nullable
     int32_t *count, *offset, *pairs;    // nullable as a group (grouping skipped)
-    int32_t *pair_pos;                  // nullable: grouped position of each pair
     int32_t *active, *n_active;         // nullable
     int chunk;                          // > 0: split each expert's pairs into chunks of this size
     int32_t *chunk_tab, *n_chunks;      // [<= T*k], [1]: expert << 16 | first grouped position

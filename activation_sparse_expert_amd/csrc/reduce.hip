@@ -1,8 +1,8 @@
 // Sum of per-workgroup partial rows into the output (second kernel of the
 // expert and layer paths; two variants by the number of contributions).
-// Token t's output row is the sum, in a fixed order, of `tiles` partials of each of its rows: one row per token for a single
-// expert; for a layer, one row per routed choice (at the pair's position in the
-// grouped order) and one per shared expert.  Router weights were applied when
+// Token t's output row is the sum, in a fixed order, of `tiles` partials of
+// each of its rows: one row per token for a single expert; for a layer, one row
+// per routed choice (row t k + s for choice s) and one per shared expert.  Router weights were applied when
 // the partials were written.  The order of the additions is fixed, so the
 // output is bit-reproducible.
 #include "device.hpp"
@@ -22,7 +22,7 @@ constexpr int kMaxRowsPerTok = kMaxExpertsPerToken;
 __device__ __forceinline__ int part_row(const ReduceArgs &a, int t, int ri)
 {
     if (!a.layer) return t;
-    if (ri < a.k) return a.pair_pos[t * a.k + ri];
+    if (ri < a.k) return t * a.k + ri;            // routed: the pair's own row
     return a.T * a.k + (ri - a.k) * a.T + t;
 }
 

@@ -321,7 +321,6 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
             for (int q = 0; q < tid; ++q) rank += (ce[q] == e);
             const int pos = run[e] + rank;
             a.pairs[pos] = p;
-            if (a.pair_pos) a.pair_pos[p] = pos;
             if (a.chunk_rec) {
                 // single-token chunks: chunk pos holds pair p; its record lets
                 // the expert kernel start from one load
