@@ -12,6 +12,9 @@ What each function follows is stated in ``oracle.c``; in short:
                               MoE-Lightning review "MoE 模型架构") and the
                               per-expert token counts (MoE-Infinity review "4.3")
   layer_forward               routed + shared experts combined, sparse or dense
+  ream_add / eamc_match       request-level EAM accumulation and the cosine-
+                              distance nearest stored EAM (MoE-Infinity review
+                              "4.3", "4.5")
 """
 from __future__ import annotations
 
@@ -61,6 +64,9 @@ def lib():
         L.oracle_route_topk.argtypes = [P, I, I, I, P, I, P, I, I, I, P, P, P, P, P, P]
         L.oracle_layer_forward.argtypes = [P, I, I, I, I, P, I, P, I, I, I, I, P, P, P, P, I,
                                            P, I, P, P, P, P, P, P]
+        L.oracle_ream_add.argtypes = [P, I, I, P]
+        L.oracle_eamc_match.restype = I
+        L.oracle_eamc_match.argtypes = [P, I, I, P, P]
         _lib = L
     return _lib
 
@@ -218,3 +224,25 @@ def calibrate_threshold(v_abs: np.ndarray, sparsity: float) -> np.float32:
     it: the linear-interpolation quantile of |v| over the calibration tokens
     (the pages give t_ij as an input and do not say how it is placed)."""
     return np.float32(np.quantile(np.asarray(v_abs, dtype=np.float64).ravel(), sparsity))
+
+
+# ------------------------------------------------------------------ EAM
+
+def ream_add(ream: np.ndarray, layer: int, count) -> None:
+    """Add one iteration's per-expert counts of ``layer`` into the request-level
+    EAM ``ream`` [L][E] int32 (in place)."""
+    assert ream.dtype == np.int32 and ream.flags.c_contiguous
+    c = _c(count, np.int32)
+    assert c.shape == (ream.shape[1],)
+    lib().oracle_ream_add(_p(ream), ream.shape[1], int(layer), _p(c))
+
+
+def eamc_match(eamc, query):
+    """(index of the nearest stored EAM or -1, distances [n] f64)."""
+    b = _c(eamc, np.int32)
+    q = _c(query, np.int32).ravel()
+    n, ln = b.shape
+    assert q.shape == (ln,)
+    dist = np.empty(n, dtype=np.float64)
+    i = lib().oracle_eamc_match(_p(b), n, ln, _p(q), _p(dist))
+    return int(i), dist

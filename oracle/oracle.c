@@ -25,6 +25,9 @@
  *                experts of each token (Mixtral: 8 experts, top-2).
  *   [MoEInf-4.3] MoE-Infinity review, "4.3": the iteration-level expert
  *                activation matrix counts the tokens routed to each expert.
+ *   [MoEInf-4.5] MoE-Infinity review, "4.5": the collection of past request-
+ *                level EAMs is searched for the one closest to the current
+ *                EAM, both flattened, by cosine distance.
  *   [MoEL-arch]  MoE-Lightning review, "三、技术架构 / MoE 模型架构": a gating
  *                network selects the top-k expert FFNs of each token.
  *
@@ -50,6 +53,13 @@
  *   R8  Layer: y_t = sum_s w_{t,s} a_{e(t,s)}(x_t) + sum_shared a_sh(x_t).
  *   R9  Dense grouped-GEMM path: the same layer at t < 0 with the up weights
  *       materialised once as bf16_rne(dequant(INT2)) next to bf16 gate/down.
+ *   R21 EAM matching: the cosine distance of two flattened count vectors is
+ *       1 - <a, b> / sqrt(|a|^2 |b|^2); it is 1 when either vector is zero (no
+ *       direction).  Counts outside [0, 2^22) make a stored EAM unusable (NaN,
+ *       never the match); a query with one matches nothing (index -1).  The
+ *       smallest distance wins, the lowest index among equal ones.
+ *   R22 Request-level EAM: after each iteration the iteration's per-layer
+ *       counts are added into the request's matrix, row = layer.
  *
  * Everything below is straight loops in double precision.
  */
@@ -503,4 +513,46 @@ void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
         }
     }
     free(idx); free(w); free(l); free(mbuf); free(ytok); free(ubf);
+}
+
+/* ------------------------------------------------------ EAM / EAMC */
+
+/*
+ * [MoEInf-4.3], reading R22: ream [L][E] += this iteration's counts of layer
+ * `layer` (count [E], e.g. the expert_count of oracle_route_topk).
+ */
+void oracle_ream_add(int32_t *ream, int E, int layer, const int32_t *count)
+{
+    for (int e = 0; e < E; ++e) ream[(size_t)layer * E + e] += count[e];
+}
+
+/*
+ * [MoEInf-4.5], reading R21: dist[i] = cosine distance between query [len]
+ * and stored EAM i (eamc [n][len]); returns the index of the smallest.
+ * The dot product and squared norms are integer sums (exact: entries are
+ * below 2^22 and len is small), the rest is double precision.
+ */
+int oracle_eamc_match(const int32_t *eamc, int n, int len, const int32_t *query, double *dist)
+{
+    const long long lim = 1ll << 22;
+    int query_ok = 1;
+    for (int c = 0; c < len; ++c)
+        if (query[c] < 0 || query[c] >= lim) query_ok = 0;
+    int best = -1;
+    for (int i = 0; i < n; ++i) {
+        const int32_t *b = eamc + (size_t)i * len;
+        int ok = query_ok;
+        long long ab = 0, aa = 0, bb = 0;
+        for (int c = 0; c < len; ++c) {
+            if (b[c] < 0 || b[c] >= lim) ok = 0;
+            ab += (long long)query[c] * b[c];
+            aa += (long long)query[c] * query[c];
+            bb += (long long)b[c] * b[c];
+        }
+        if (!ok) dist[i] = NAN;
+        else if (aa == 0 || bb == 0) dist[i] = 1.0;
+        else dist[i] = 1.0 - (double)ab / sqrt((double)aa * (double)bb);
+        if (ok && (best < 0 || dist[i] < dist[best])) best = i;   /* strict: lowest index on ties */
+    }
+    return best;
 }

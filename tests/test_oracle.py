@@ -496,3 +496,105 @@ def test_calibrated_threshold_realises_sparsity():
     t50 = oracle.calibrate_threshold(np.abs(v), 0.5)
     _, m, _ = oracle.expert_forward(xc, "f16", up_q, up_sz, gb, db, "f16", thr=t50)
     assert abs(1 - m.mean() - 0.5) < 0.01
+
+
+# ------------------------------------------------------------------ EAM / EAMC
+# MoE-Infinity review, "4.3" (EAM: tokens routed to each of the L x E experts;
+# the request-level EAM adds up the iterations) and "4.5" (nearest past EAM by
+# cosine distance of the flattened matrices).
+
+def test_ream_add_is_bincount_of_routed_experts():
+    rng = np.random.default_rng(41)
+    L, E, k, T = 4, 8, 2, 37
+    ream = rng.integers(0, 50, size=(L, E)).astype(np.int32)
+    want = ream.astype(np.int64).copy()
+    for layer in (0, 3, 3, 1):
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        cnt = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+        oracle.ream_add(ream, layer, cnt)
+        want[layer] += cnt
+        assert cnt.sum() == T * k
+    np.testing.assert_array_equal(ream, want)
+
+
+def test_ream_add_from_router_counts():
+    # the count the oracle's router reports is the routed tokens per expert
+    rng = np.random.default_rng(42)
+    T, d, E, k = 9, 64, 6, 2
+    x = oracle_f32_bits(rng.standard_normal((T, d)))
+    R = oracle_f32_bits(rng.standard_normal((E, d)) * 0.1)
+    r = oracle.route_topk(x, "f32", R, "f32", E, k)
+    idx, cnt = r["topk_idx"], r["expert_count"]
+    ream = np.zeros((3, E), dtype=np.int32)
+    oracle.ream_add(ream, 2, cnt)
+    np.testing.assert_array_equal(ream[2], np.bincount(idx.ravel(), minlength=E))
+    assert ream[:2].sum() == 0
+
+
+def oracle_f32_bits(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def test_eamc_distance_matches_scipy_cosine():
+    from scipy.spatial.distance import cosine
+    rng = np.random.default_rng(43)
+    for n, ln in ((1, 7), (13, 256), (40, 1728)):
+        b = rng.integers(0, 300, size=(n, ln)).astype(np.int32)
+        b[:, rng.random(ln) < 0.5] = 0                    # sparse activation
+        q = rng.integers(0, 300, size=ln).astype(np.int32)
+        i, dist = oracle.eamc_match(b, q)
+        ref = np.array([cosine(q.astype(np.float64), r.astype(np.float64)) for r in b])
+        np.testing.assert_allclose(dist, ref, rtol=0, atol=1e-13)
+        assert i == int(np.argmin(ref))
+
+
+def test_eamc_closed_forms():
+    q = np.array([3, 0, 4, 0], dtype=np.int32)
+    b = np.array([[3, 0, 4, 0],          # same: 0
+                  [6, 0, 8, 0],          # same direction: 0
+                  [0, 5, 0, 0],          # orthogonal: 1
+                  [0, 0, 0, 0],          # zero vector: 1
+                  [3, 4, 0, 0],          # cos = 9/25
+                  [1, 0, 0, 0]],         # cos = 3/5
+                 dtype=np.int32)
+    i, dist = oracle.eamc_match(b, q)
+    assert abs(dist[0]) < 1e-15 and abs(dist[1]) < 1e-15
+    assert dist[2] == 1.0 and dist[3] == 1.0
+    assert abs(dist[4] - (1 - 9 / 25)) < 1e-15
+    assert abs(dist[5] - (1 - 3 / 5)) < 1e-15
+    assert i in (0, 1) and dist[i] == dist[:2].min()
+    i, dist = oracle.eamc_match(b, np.zeros(4, dtype=np.int32))
+    assert i == 0 and np.all(dist == 1.0)                 # all equal: lowest index
+
+
+def test_eamc_argmin_bruteforce_ties_and_invalid():
+    rng = np.random.default_rng(44)
+    for trial in range(30):
+        n, ln = int(rng.integers(1, 12)), int(rng.integers(1, 9))
+        b = rng.integers(0, 4, size=(n, ln)).astype(np.int32)
+        b[rng.integers(0, n)] = b[rng.integers(0, n)]       # a duplicate: exact tie
+        q = rng.integers(0, 4, size=ln).astype(np.int32)
+        if trial % 5 == 0:
+            b[rng.integers(0, n), rng.integers(0, ln)] = 1 << 22    # out of range
+        if trial % 7 == 0:
+            b[rng.integers(0, n), rng.integers(0, ln)] = -1
+        i, dist = oracle.eamc_match(b, q)
+        best, bd = -1, None
+        for r in range(n):
+            row = [int(v) for v in b[r]]
+            if any(v < 0 or v >= 1 << 22 for v in row):
+                assert math.isnan(dist[r])
+                continue
+            qq = [int(v) for v in q]
+            ab = sum(x * y for x, y in zip(qq, row))
+            aa = sum(x * x for x in qq)
+            bb = sum(y * y for y in row)
+            dd = 1.0 if aa == 0 or bb == 0 else 1.0 - ab / math.sqrt(aa * bb)
+            assert abs(dist[r] - dd) < 1e-15
+            if best < 0 or dd < bd:
+                best, bd = r, dd
+        assert i == best
+    b = np.ones((3, 4), dtype=np.int32)
+    q = np.array([1, 2, 3, 1 << 22], dtype=np.int32)
+    i, dist = oracle.eamc_match(b, q)
+    assert i == -1 and np.all(np.isnan(dist))
