@@ -16,14 +16,15 @@ LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
 MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
 PATH_SPARSE, PATH_DENSE, PATH_AUTO = 0, 1, 2
-OP_EXPERT, OP_ROUTE, OP_LAYER, OP_CALIBRATE = 0, 1, 2, 3
+OP_EXPERT, OP_ROUTE, OP_LAYER, OP_CALIBRATE, OP_EAMC = 0, 1, 2, 3, 4
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 
 EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_workspace_size", "moe_workspace_init", "moe_pack_up_int2",
-            "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold"]
+            "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold",
+            "moe_eamc_match"]
 
 
 class MoeError(RuntimeError):
@@ -47,7 +48,7 @@ class LayerDesc(C.Structure):
 
 class LayerTrace(C.Structure):
     _fields_ = [("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("logits", C.c_void_p),
-                ("expert_count", C.c_void_p), ("masks", C.c_void_p)]
+                ("expert_count", C.c_void_p), ("masks", C.c_void_p), ("eam_row", C.c_void_p)]
 
 
 _lib = None
@@ -81,6 +82,8 @@ def lib():
         L.moe_status_string.argtypes = [I]
         L.moe_calibrate_threshold.restype = I
         L.moe_calibrate_threshold.argtypes = [P, C.c_longlong, C.c_double, P, P, Z, P]
+        L.moe_eamc_match.restype = I
+        L.moe_eamc_match.argtypes = [P, I, I, P, P, P, P, Z, P]
         _lib = L
     return _lib
 
@@ -224,7 +227,8 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
     """Route and combine one layer on x [T][d]; returns y [T][d].
 
     ``trace`` may map any of topk_idx, topk_w, logits, expert_count, masks to
-    preallocated device tensors that receive those exports."""
+    preallocated device tensors that receive those exports, and eam_row to an
+    int32 [E] device tensor that the call's per-expert counts are added into."""
     import torch
     T, d = x.shape
     if y is None:
@@ -235,7 +239,7 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
     if trace:
         tr = LayerTrace(_ptr(trace.get("topk_idx")), _ptr(trace.get("topk_w")),
                         _ptr(trace.get("logits")), _ptr(trace.get("expert_count")),
-                        _ptr(trace.get("masks")))
+                        _ptr(trace.get("masks")), _ptr(trace.get("eam_row")))
     desc = layer.desc()
     st = lib().moe_layer_forward(C.byref(desc), _ptr(x), _dt(x), T, _ptr(y), _dt(y), path,
                                  C.byref(tr) if tr is not None else None, _ptr(ws), ws.numel(),
@@ -259,6 +263,30 @@ def calibrate_threshold(v, q: float, *, out=None, ws=None):
                                        ws.numel(), _stream())
     _check(st, "moe_calibrate_threshold")
     return out
+
+
+def eamc_match(eamc, query, *, idx=None, dist=None, ws=None):
+    """Cosine-distance nearest match of the int32 query [len] among the stored
+    EAMs eamc [n][len] (both contiguous int32 device tensors, flattened L x E
+    counts).  Returns (idx, dist): a one-element int32 tensor with the index
+    (-1 when no stored EAM is valid) and, if ``dist`` was given or ``ws`` is
+    None, the fp64 distances [n]."""
+    import torch
+    if eamc.dtype != torch.int32 or query.dtype != torch.int32:
+        raise TypeError("eamc and query must be int32")
+    if eamc.dim() != 2 or not eamc.is_contiguous() or not query.is_contiguous():
+        raise ValueError("eamc must be a contiguous [n][len] tensor, query contiguous")
+    n, ln = eamc.shape
+    if query.numel() != ln:
+        raise ValueError("query must have len entries")
+    if idx is None:
+        idx = torch.empty(1, dtype=torch.int32, device=eamc.device)
+    if dist is None and ws is None:
+        dist = torch.empty(n, dtype=torch.float64, device=eamc.device)
+    st = lib().moe_eamc_match(_ptr(eamc), n, ln, _ptr(query), _ptr(idx), _ptr(dist), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream())
+    _check(st, "moe_eamc_match")
+    return idx, dist
 
 
 def pack_up_int2(w_up_t, *, up_q=None, up_sz=None):

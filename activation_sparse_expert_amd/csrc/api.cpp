@@ -14,6 +14,7 @@ using namespace moeffn;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kEamcMaxLen = 1 << 17;         // entries of one flattened EAM
 
 size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -232,8 +233,29 @@ size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S)
         return layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr);
     case MOE_OP_CALIBRATE:
         return up(calibrate_ws_bytes());
+    case MOE_OP_EAMC:
+        return d > kEamcMaxLen ? 0 : up((size_t)T * 8);   // T stored EAMs of d entries
     }
     return 0;
+}
+
+moe_status moe_eamc_match(const int32_t *eamc, int n, int len, const int32_t *query,
+                          int32_t *idx_out, double *dist_out, void *ws, size_t ws_bytes,
+                          void *stream)
+{
+    if (!eamc || !query || !idx_out || n < 1 || len < 1 || len > kEamcMaxLen)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(eamc, 4) || !aligned(query, 4) || !aligned(idx_out, 4) ||
+        (dist_out && !aligned(dist_out, 8)))
+        return MOE_ERR_ALIGNMENT;
+    double *dist = dist_out;
+    if (!dist) {
+        if (!ws || ws_bytes < moe_workspace_size(MOE_OP_EAMC, n, len, 0, 0, 0, 0))
+            return MOE_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
+        dist = (double *)ws;
+    }
+    return hip_status(launch_eamc_match(eamc, n, len, query, idx_out, dist, (hipStream_t)stream));
 }
 
 moe_status moe_calibrate_threshold(const float *v, long long n, double q, float *t_out,
@@ -373,6 +395,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.topk_w = (trace && trace->topk_w) ? trace->topk_w : w.topk_w;
     r.logits = trace ? trace->logits : nullptr;
     r.count = (trace && trace->expert_count) ? trace->expert_count : w.count;
+    r.eam_row = trace ? trace->eam_row : nullptr;
     r.offset = w.offset; r.pairs = w.pairs;
     r.active = w.active; r.n_active = w.n_active;
     r.lg_buf = route_split(d, E, L->rdt) ? w.lg : nullptr;

@@ -74,6 +74,7 @@ struct RouteArgs {
     int32_t *chunk_tab, *n_chunks;      // [<= T*k], [1]: expert << 16 | first grouped position
     float *lg_buf;                      // [T][E] workspace for the wide-router split (route_split)
     int32_t *chunk_rec;                 // nullable, with chunk == 1: [T*k][4] per-chunk records
+    int32_t *eam_row;                   // nullable: [E] per-expert counts are added into it
 };
 // Routers with more than 8 experts whose rows are large per token (E d
 // element bytes above 32 KB) compute their logits in a separate kernel spread
@@ -102,6 +103,10 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 // Threshold calibration: out = linear-interpolation quantile of |v| between
 // order statistics r_lo and r_hi with weight gamma (computed on the host).
+// Cosine-distance nearest stored EAM: dist [n] fp64 (written), idx_out [1].
+hipError_t launch_eamc_match(const int32_t *eamc, int n, int len, const int32_t *query,
+                             int32_t *idx_out, double *dist, hipStream_t s);
+
 size_t calibrate_ws_bytes();
 hipError_t launch_calibrate(const float *v, long long n, long long r_lo, long long r_hi,
                             double gamma, float *out, void *ws, hipStream_t s);

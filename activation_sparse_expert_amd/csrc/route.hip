@@ -284,6 +284,7 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
                 run[e] = off;
                 cst[e] = (int)((ex[i] >> 24) & 0xFFFFFFull);
                 a.count[e] = cnt[e];
+                if (a.eam_row) a.eam_row[e] += cnt[e];   // request-level EAM row
                 if (a.active && cnt[e] > 0) a.active[(int)(ex[i] >> 48)] = e;
             }
         }

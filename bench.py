@@ -356,6 +356,28 @@ def layers_measure():
     return out
 
 
+def eamc_measure():
+    """Nearest stored request-level EAM (cosine distance) over a collection:
+    per call n stored EAMs of L x E int32 counts are read once."""
+    import torch
+    import activation_sparse_expert_amd as moe
+    import synth
+    res = {}
+    for name, n, L, E, k in (("mixtral_32x8_n1000", 1000, 32, 8, 2),
+                             ("arctic_35x128_n4096", 4096, 35, 128, 2)):
+        a = torch.from_numpy(synth.eam_collection(7, n, L, E, k)).cuda()
+        b, q = a[:n].contiguous(), a[n].contiguous()
+        idx = torch.empty(1, dtype=torch.int32, device=a.device)
+        dist = torch.empty(n, dtype=torch.float64, device=a.device)
+        sec = time_graph(lambda: moe.eamc_match(b, q, idx=idx, dist=dist), reps=20, inner=50)
+        nbytes = n * L * E * 4 + L * E * 4 + n * 8
+        res[name] = {"workload": f"{n} stored EAMs of {L} layers x {E} experts, one query",
+                     "us_per_call": sec * 1e6, "bytes_per_call": nbytes,
+                     "achieved_gbs": nbytes / sec / 1e9,
+                     "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def cpu_baseline(sparsity, budget_s):
     """The fp64 oracle, as it stands, on instance 0 and the same tokens."""
     import oracle
@@ -525,6 +547,8 @@ def main():
     if not args.no_layers:
         log("measuring the layer workloads")
         out["more"].update(layers_measure())
+        log("measuring the EAMC match")
+        out["more"]["eamc_match"] = eamc_measure()
     if not args.no_batched:
         log("measuring the batched layer (dense MFMA and sparse paths)")
         out["batched"] = batched_measure()

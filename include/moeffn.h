@@ -92,7 +92,8 @@ typedef enum {
     MOE_OP_EXPERT = 0,          /* moe_expert_forward_sparse */
     MOE_OP_ROUTE = 1,           /* moe_route_topk           */
     MOE_OP_LAYER = 2,           /* moe_layer_forward        */
-    MOE_OP_CALIBRATE = 3        /* moe_calibrate_threshold  */
+    MOE_OP_CALIBRATE = 3,       /* moe_calibrate_threshold  */
+    MOE_OP_EAMC = 4             /* moe_eamc_match (T = n, d = len) */
 } moe_op;
 
 /* One compressed expert (FloE review, "混合压缩策略": {W^S(gate), W^S(down),
@@ -136,6 +137,11 @@ typedef struct {
     uint8_t *masks;             /* [T][k+S][f] 0/1, sparse path only: slot s<k is
                                    the token's s-th routed expert, slot k+i its
                                    i-th shared expert                        */
+    int32_t *eam_row;           /* [E] int32: this call's tokens per routed expert
+                                   (the layer's row of the iteration-level EAM)
+                                   are ADDED into it, so a row kept across the
+                                   calls of a request accumulates the request-
+                                   level EAM (MoE-Infinity review, "4.3")     */
 } moe_layer_trace;
 
 /*
@@ -211,6 +217,26 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
  */
 moe_status moe_calibrate_threshold(const float *v, long long n, double q, float *t_out,
                                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Nearest stored request-level EAM (MoE-Infinity review, "4.5": the EAMs are
+ * compared flattened, by cosine distance, and the smallest distance is the
+ * match; "4.3": an EAM counts the tokens routed to each of the L x E experts).
+ *   eamc [n][len] int32 (device): n stored EAMs, each flattened (len = L E);
+ *   query [len] int32 (device).
+ *   dist_i = 1 - <q, b_i> / sqrt(|q|^2 |b_i|^2), the dot product and squared
+ *   norms exact in 64-bit integers, the rest in fp64 (not clipped, so it may be
+ *   a rounding step below 0); dist_i = 1 when q or b_i is all zeros.
+ *   Entries must lie in [0, 2^22): a stored EAM with an entry outside gets NaN
+ *   and is never chosen; a query with one gets NaN everywhere.
+ * Outputs: idx_out[0] int32 = the i of the smallest dist_i (the lowest i among
+ * equal ones; -1 when every dist_i is NaN); dist_out [n] fp64 or NULL.
+ * Limits: 1 <= n, 1 <= len <= 2^17.  Workspace (only when dist_out is NULL):
+ * moe_workspace_size(MOE_OP_EAMC, n, len, ...) bytes.
+ */
+moe_status moe_eamc_match(const int32_t *eamc, int n, int len, const int32_t *query,
+                          int32_t *idx_out, double *dist_out,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes needed by `op` at these sizes (0 when the sizes are invalid). */
 size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S);

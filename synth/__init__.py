@@ -20,13 +20,17 @@ fine   DeepSeek-V2-Lite shape, 64 routed (top-6) + 2 shared, d=2048, f=1408,
        router bias -1.1 ln(rank) (Zipf, s=1.1), x N(0,1)
 =====  ====================================================================
 
+Request-level expert activation matrices (MoE-Infinity review, "4.3"-"4.4":
+L x E token counts per request that fall into 10-30 groups of similar
+matrices, each skewed within the request) are drawn by ``eam_collection``.
+
 Seeds: ``seed = 1_000_000*cfg + 10_000*layer + 100*expert + tensor_id``.
 """
 from __future__ import annotations
 
 import numpy as np
 
-T_GATE, T_UP, T_DOWN, T_ROUTER, T_X, T_CALIB, T_NOISE, T_RANK = range(8)
+T_GATE, T_UP, T_DOWN, T_ROUTER, T_X, T_CALIB, T_NOISE, T_RANK, T_EAM = range(9)
 
 CFG_TINY, CFG_MIXTRAL, CFG_STACK, CFG_WIDE, CFG_FINE = 1, 2, 3, 4, 5
 
@@ -112,6 +116,24 @@ def zipf_bias(cfg: int, layer: int, E: int, s: float) -> np.ndarray:
     permutation of the ranks 1..E (float32)."""
     ranks = rng(seed_of(cfg, layer, 0, T_RANK)).permutation(E) + 1
     return (-s * np.log(ranks.astype(np.float64))).astype(np.float32)
+
+
+def eam_collection(cfg: int, n: int, L: int, E: int, k: int, groups: int = 20,
+                   max_tokens: int = 512, alpha: float = 0.3):
+    """n + 1 flattened request-level EAMs [n + 1][L * E] int32 (the last row a
+    query).  Every group has, per layer, expert preferences ~ Dirichlet(alpha)
+    (small alpha: few experts take most tokens); a request picks a group and a
+    token count uniform in [1, max_tokens], and each layer's k * tokens choices
+    are drawn multinomially from the group's preferences."""
+    r = rng(seed_of(cfg, 0, 0, T_EAM))
+    pref = r.dirichlet(np.full(E, alpha), size=(groups, L))
+    g = r.integers(0, groups, size=n + 1)
+    tok = r.integers(1, max_tokens + 1, size=n + 1)
+    out = np.empty((n + 1, L, E), dtype=np.int32)
+    for i in range(n + 1):
+        for l in range(L):
+            out[i, l] = r.multinomial(int(tok[i]) * k, pref[g[i], l])
+    return out.reshape(n + 1, L * E)
 
 
 def hidden_stream_f32(cfg: int, L: int, T: int, d: int, scale: float = 1.0 / 64, mix: float = 0.2):

@@ -197,6 +197,22 @@ def test_calibrate_rejects(kw, code):
     assert L.moe_workspace_size(moe.OP_CALIBRATE, 1, 1, 0, 1, 1, 0) > 0
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), -1), (dict(q=None), -1), (dict(idx=None), -1), (dict(n=0), -1),
+    (dict(ln=0), -1), (dict(ln=(1 << 17) + 1), -1), (dict(b=FAKE + 2), -3),
+    (dict(idx=FAKE + 1), -3), (dict(dist=FAKE + 4), -3), (dict(dist=None, ws=None), -4),
+    (dict(dist=None, ws_bytes=8 * 99), -4), (dict(dist=None, ws=FAKE + 8), -3),
+])
+def test_eamc_match_rejects(kw, code):
+    L = _lib_or_skip()
+    a = dict(b=FAKE, n=100, ln=256, q=FAKE, idx=FAKE, dist=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    assert L.moe_eamc_match(a["b"], a["n"], a["ln"], a["q"], a["idx"], a["dist"], a["ws"],
+                            a["ws_bytes"], None) == code
+    assert L.moe_workspace_size(moe.OP_EAMC, 100, 256, 0, 0, 0, 0) >= 800
+    assert L.moe_workspace_size(moe.OP_EAMC, 100, (1 << 17) + 1, 0, 0, 0, 0) == 0
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(moe, "_lib", None)
     monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoeffn.so")
