@@ -65,6 +65,10 @@ def lib():
         L.oracle_layer_forward.argtypes = [P, I, I, I, I, P, I, P, I, I, I, I, P, P, P, P, I,
                                            P, I, P, P, P, P, P, P]
         L.oracle_ream_add.argtypes = [P, I, I, P]
+        L.oracle_pack_up_bits.argtypes = [P, I, I, I, P, P]
+        L.oracle_dequant_up_bits.argtypes = [P, P, I, I, I, P]
+        L.oracle_expert_forward_bits.argtypes = [I, P, I, I, I, I, P, P, P, P, I, C.c_float, P,
+                                                 P, P, P, P, I]
         L.oracle_eamc_match.restype = I
         L.oracle_eamc_match.argtypes = [P, I, I, P, P]
         _lib = L
@@ -121,6 +125,27 @@ def dequant_up(up_q: np.ndarray, up_sz: np.ndarray, d: int) -> np.ndarray:
     return out
 
 
+def pack_up_bits(w_t: np.ndarray, bits: int):
+    """Up weights at 8, 4, 2 or 1 bits per code -> (up_q [f][d*bits/8] u8,
+    up_sz [f][d/64][2] fp16 bits); 2 is the INT2 format above."""
+    w_t = _c(w_t, np.float32)
+    f, d = w_t.shape
+    assert d % 64 == 0 and bits in (1, 2, 4, 8)
+    q = np.zeros((f, d * bits // 8), dtype=np.uint8)
+    sz = np.zeros((f, d // 64, 2), dtype=np.uint16)
+    lib().oracle_pack_up_bits(_p(w_t), d, f, bits, _p(q), _p(sz))
+    return q, sz
+
+
+def dequant_up_bits(up_q, up_sz, d: int, bits: int) -> np.ndarray:
+    up_q = _c(up_q, np.uint8)
+    up_sz = _c(up_sz, np.uint16)
+    f = up_q.shape[0]
+    out = np.empty((f, d), dtype=np.float64)
+    lib().oracle_dequant_up_bits(_p(up_q), _p(up_sz), d, f, bits, _p(out))
+    return out
+
+
 def materialize_up_bf16(up_q, up_sz, d):
     up_q = _c(up_q, np.uint8)
     up_sz = _c(up_sz, np.uint16)
@@ -133,9 +158,9 @@ def materialize_up_bf16(up_q, up_sz, d):
 # ------------------------------------------------------------------ expert
 
 def expert_forward(x_bits, xdt, up_q, up_sz, gate_bits, down_bits, wdt, thr,
-                   scale=None, mask_in=None, y_init=None):
+                   scale=None, mask_in=None, y_init=None, bits=2):
     """Algorithm 1 on T tokens.  x_bits [T][d] (uint16 bits for f16/bf16 or
-    float32), weights per the INT2 format.  Returns (v [T][f] f64,
+    float32), up weights in the format of ``bits`` (2: INT2).  Returns (v [T][f] f64,
     mask [T][f] u8, y [T][d] f64)."""
     xa = _c(x_bits, np.float32 if xdt == "f32" else np.uint16)
     T, d = xa.shape
@@ -156,9 +181,9 @@ def expert_forward(x_bits, xdt, up_q, up_sz, gate_bits, down_bits, wdt, thr,
         acc = 1
     sc = None if scale is None else _c(scale, np.float64)
     mi = None if mask_in is None else _c(mask_in, np.uint8)
-    lib().oracle_expert_forward(_p(xa), DT[xdt], T, d, f, _p(up_q), _p(up_sz), _p(g), _p(dn),
-                                DT[wdt], C.c_float(thr), _p(sc), _p(mi), _p(v), _p(m), _p(y),
-                                acc)
+    lib().oracle_expert_forward_bits(int(bits), _p(xa), DT[xdt], T, d, f, _p(up_q), _p(up_sz),
+                                     _p(g), _p(dn), DT[wdt], C.c_float(thr), _p(sc), _p(mi),
+                                     _p(v), _p(m), _p(y), acc)
     return v, m, y
 
 

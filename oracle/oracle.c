@@ -60,6 +60,8 @@
  *       smallest distance wins, the lowest index among equal ones.
  *   R22 Request-level EAM: after each iteration the iteration's per-layer
  *       counts are added into the request's matrix, row = layer.
+ *   R23 Other up widths (8, 4, 1 bits): the INT2 group-64 min-max scheme with
+ *       2^bits - 1 levels, codes packed plainly at bit k*bits of the row.
  *
  * Everything below is straight loops in double precision.
  */
@@ -247,6 +249,81 @@ static double up_weight(const uint8_t *up_q, const uint16_t *up_sz, int d, int j
     return s * ((double)code_at(up_q, d, j, k) - z);
 }
 
+/*
+ * Other up widths (FloE review, "三、技术架构 / 敏感度分析": the up projection
+ * is also quantised to 8, 4 and 1 bits; reading R23).  The same per-channel,
+ * per-64-input-group asymmetric min-max scheme as the INT2 format with
+ * L = 2^bits - 1 levels: s = fp16((mx - mn) / L) (1 when 0), z = fp16(-mn / s),
+ * q = clamp(round_half_even(w / s + z), 0, L).  Codes are packed plainly:
+ * input k of channel j sits at bit k*bits of row j (rows of d*bits/8 bytes,
+ * least significant bits first within a byte).
+ */
+static int code_at_bits(const uint8_t *up_q, int d, int bits, int j, int k)
+{
+    size_t bit = (size_t)k * bits;
+    const uint8_t *row = up_q + (size_t)j * ((size_t)d * bits / 8);
+    return (row[bit / 8] >> (bit % 8)) & ((1 << bits) - 1);
+}
+
+void oracle_pack_up_bits(const float *w_t, int d, int f, int bits, uint8_t *up_q, uint16_t *up_sz)
+{
+    if (bits == 2) { oracle_pack_up_int2(w_t, d, f, up_q, up_sz); return; }
+    const int G = d / 64, L = (1 << bits) - 1;
+    const size_t rb = (size_t)d * bits / 8;
+    memset(up_q, 0, rb * (size_t)f);
+    for (int j = 0; j < f; ++j) {
+        for (int g = 0; g < G; ++g) {
+            const float *w = w_t + (size_t)j * d + (size_t)g * 64;
+            float mn = w[0], mx = w[0];
+            for (int i = 1; i < 64; ++i) {
+                if (w[i] < mn) mn = w[i];
+                if (w[i] > mx) mx = w[i];
+            }
+            volatile float range = mx - mn;
+            volatile float step = range / (float)L;
+            uint16_t sb = oracle_double_to_half_rne((double)step);
+            float s = (float)oracle_half_to_double(sb);
+            if (s == 0.0f) { sb = 0x3C00; s = 1.0f; }
+            volatile float negmn = -mn;
+            volatile float zq = negmn / s;
+            uint16_t zb = oracle_double_to_half_rne((double)zq);
+            float z = (float)oracle_half_to_double(zb);
+            up_sz[((size_t)j * G + g) * 2 + 0] = sb;
+            up_sz[((size_t)j * G + g) * 2 + 1] = zb;
+            for (int i = 0; i < 64; ++i) {
+                volatile float a = w[i] / s;
+                volatile float b = a + z;
+                float r = rintf(b);
+                int q = (int)r;
+                if (r < 0.0f) q = 0;
+                if (r > (float)L) q = L;
+                size_t bit = ((size_t)g * 64 + i) * bits;
+                up_q[(size_t)j * rb + bit / 8] |= (uint8_t)(q << (bit % 8));
+            }
+        }
+    }
+}
+
+/* w'_{k,j} = s (q - z) for any supported width (exact in double). */
+static double up_weight_bits(const uint8_t *up_q, const uint16_t *up_sz, int d, int bits,
+                             int j, int k)
+{
+    if (bits == 2) return up_weight(up_q, up_sz, d, j, k);
+    int G = d / 64;
+    int g = k / 64;
+    double s = oracle_half_to_double(up_sz[((size_t)j * G + g) * 2 + 0]);
+    double z = oracle_half_to_double(up_sz[((size_t)j * G + g) * 2 + 1]);
+    return s * ((double)code_at_bits(up_q, d, bits, j, k) - z);
+}
+
+void oracle_dequant_up_bits(const uint8_t *up_q, const uint16_t *up_sz, int d, int f, int bits,
+                            double *out)
+{
+    for (int j = 0; j < f; ++j)
+        for (int k = 0; k < d; ++k)
+            out[(size_t)j * d + k] = up_weight_bits(up_q, up_sz, d, bits, j, k);
+}
+
 /* Full dequantisation into double, out[j][k] = w'_{k,j}. */
 void oracle_dequant_up(const uint8_t *up_q, const uint16_t *up_sz, int d, int f, double *out)
 {
@@ -283,11 +360,11 @@ static double silu(double g) { return g / (1.0 + exp(-g)); }
  * Outputs (all optional): v_out [T][f], mask_out [T][f], y_out [T][d]
  *         (y_out is accumulated into when accumulate != 0).
  */
-void oracle_expert_forward(const void *x, int xdt, int T, int d, int f,
-                           const uint8_t *up_q, const uint16_t *up_sz,
-                           const void *gate_t, const void *down, int wdt,
-                           float thr, const double *scale, const uint8_t *mask_in,
-                           double *v_out, uint8_t *mask_out, double *y_out, int accumulate)
+void oracle_expert_forward_bits(int bits, const void *x, int xdt, int T, int d, int f,
+                                const uint8_t *up_q, const uint16_t *up_sz,
+                                const void *gate_t, const void *down, int wdt,
+                                float thr, const double *scale, const uint8_t *mask_in,
+                                double *v_out, uint8_t *mask_out, double *y_out, int accumulate)
 {
     double *xr = (double *)malloc(sizeof(double) * (size_t)T * d);
     double *yr = (double *)calloc((size_t)T * d, sizeof(double));
@@ -298,7 +375,7 @@ void oracle_expert_forward(const void *x, int xdt, int T, int d, int f,
     /* channel by channel; each token's arithmetic is independent of the others */
     for (int j = 0; j < f; ++j) {
         for (int k = 0; k < d; ++k) {
-            wu[k] = up_weight(up_q, up_sz, d, j, k);
+            wu[k] = up_weight_bits(up_q, up_sz, d, bits, j, k);
             wg[k] = load_typed(gate_t, wdt, (size_t)j * d + k);
             wd[k] = load_typed(down, wdt, (size_t)j * d + k);
         }
@@ -326,6 +403,17 @@ void oracle_expert_forward(const void *x, int xdt, int T, int d, int f,
             }
     }
     free(xr); free(yr); free(wu); free(wg); free(wd);
+}
+
+/* The INT2 expert (C0 format). */
+void oracle_expert_forward(const void *x, int xdt, int T, int d, int f,
+                           const uint8_t *up_q, const uint16_t *up_sz,
+                           const void *gate_t, const void *down, int wdt,
+                           float thr, const double *scale, const uint8_t *mask_in,
+                           double *v_out, uint8_t *mask_out, double *y_out, int accumulate)
+{
+    oracle_expert_forward_bits(2, x, xdt, T, d, f, up_q, up_sz, gate_t, down, wdt, thr, scale,
+                               mask_in, v_out, mask_out, y_out, accumulate);
 }
 
 /* ------------------------------------------------------ C2: router */

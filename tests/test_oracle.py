@@ -598,3 +598,111 @@ def test_eamc_argmin_bruteforce_ties_and_invalid():
     q = np.array([1, 2, 3, 1 << 22], dtype=np.int32)
     i, dist = oracle.eamc_match(b, q)
     assert i == -1 and np.all(np.isnan(dist))
+
+
+# ------------------------------------------------------------------ other up widths
+# FloE review, "敏感度分析": the up projection quantised to 8, 4 and 1 bits as
+# well as 2; the same group-64 min-max scheme with 2^bits - 1 levels.
+
+def unpack_plain(up_q, d, bits):
+    """Codes [f][d] from rows that hold input k at bit k*bits (LSB first)."""
+    b = np.unpackbits(np.ascontiguousarray(up_q), axis=1, bitorder="little").astype(np.int64)
+    b = b.reshape(up_q.shape[0], d, bits)
+    return (b << np.arange(bits)).sum(-1)
+
+
+def exact_bits_expert(rng, d, f, bits, s_pow=-9):
+    L = (1 << bits) - 1
+    G = d // 64
+    q = rng.integers(0, L + 1, size=(f, d))
+    q[:, ::64] = 0
+    q[:, 1::64] = L
+    z = rng.integers(0, L + 1, size=(f, G)).astype(np.float64)   # integer zeros: exact
+    if bits == 1:
+        z[:] = 0.0
+    s = 2.0 ** s_pow
+    w = s * (q - np.repeat(z, 64, axis=1))
+    w32 = w.astype(np.float32)
+    assert np.all(w32.astype(np.float64) == w)
+    return w32, q, s, z
+
+
+@pytest.mark.parametrize("bits", [1, 4, 8])
+def test_pack_bits_exact_round_trip_and_layout(bits):
+    rng = np.random.default_rng(70 + bits)
+    d, f = 256, 7
+    w, q, s, z = exact_bits_expert(rng, d, f, bits)
+    up_q, up_sz = oracle.pack_up_bits(w, bits)
+    assert up_q.shape == (f, d * bits // 8)
+    assert np.all(up_sz[..., 0] == bits16(f16(np.full((f, d // 64), s))))
+    zb = up_sz[..., 1]
+    assert np.all((zb == bits16(f16(z))) | ((z == 0) & np.isin(zb, (0, 0x8000))))
+    assert np.array_equal(unpack_plain(up_q, d, bits), q)
+    assert np.array_equal(oracle.dequant_up_bits(up_q, up_sz, d, bits), w.astype(np.float64))
+
+
+def test_pack_bits_single_code_positions():
+    d = 64
+    for bits in (1, 4, 8):
+        L = (1 << bits) - 1
+        for k in (0, 1, 5, 33, 63):
+            w = np.zeros((1, d), dtype=np.float32)
+            w[0, k] = float(L)          # min 0, max L -> s = 1, z = 0, code L at k
+            up_q, _ = oracle.pack_up_bits(w, bits)
+            bit = k * bits
+            expect = np.zeros(d * bits // 8, dtype=np.uint8)
+            expect[bit // 8] = L << (bit % 8)
+            assert np.array_equal(up_q[0], expect), (bits, k)
+
+
+@pytest.mark.parametrize("bits", [1, 4, 8])
+def test_pack_bits_error_bound(bits):
+    w = synth.normal_f32(5000 + bits, (32, 512), 0.02)
+    up_q, up_sz = oracle.pack_up_bits(w, bits)
+    deq = oracle.dequant_up_bits(up_q, up_sz, 512, bits)
+    s = np.repeat(np.asarray([[oracle.half_to_double(b) for b in row] for row in up_sz[..., 0]]), 64, 1)
+    z = np.repeat(np.asarray([[oracle.half_to_double(b) for b in row] for row in up_sz[..., 1]]), 64, 1)
+    err = np.abs(deq - w.astype(np.float64))
+    L = (1 << bits) - 1
+    # half a step, plus the fp16 rounding of z (< 2^-11 relative, times s)
+    assert np.all(err <= 0.5 * s + np.abs(z) * s * 2.0 ** -10 + 1e-12)
+    # more bits, smaller error
+    if bits > 1:
+        lo_q, lo_sz = oracle.pack_up_bits(w, 1 if bits == 4 else 4)
+        lo = oracle.dequant_up_bits(lo_q, lo_sz, 512, 1 if bits == 4 else 4)
+        assert np.abs(deq - w).mean() < np.abs(lo - w).mean()
+    codes = unpack_plain(up_q, 512, bits).reshape(32, 8, 64)
+    g = w.reshape(32, 8, 64)
+    assert np.all(np.take_along_axis(codes, g.argmin(-1)[..., None], -1) == 0)
+    assert np.all(np.take_along_axis(codes, g.argmax(-1)[..., None], -1) == L)
+
+
+def test_pack_bits_two_is_the_int2_format():
+    w = synth.normal_f32(5100, (16, 256), 0.02)
+    a = oracle.pack_up_bits(w, 2)
+    b = oracle.pack_up_int2(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("bits", [1, 4, 8])
+def test_expert_bits_dense_threshold_is_textbook_swiglu(bits):
+    d, f, T = 256, 128, 2
+    rng = np.random.default_rng(80 + bits)
+    w_up, _, _, _ = exact_bits_expert(rng, d, f, bits)
+    up_q, up_sz = oracle.pack_up_bits(w_up, bits)
+    gb = synth.to_bits(synth.normal_f32(81, (f, d), 0.02), "f16")
+    db = synth.to_bits(synth.normal_f32(82, (f, d), 0.02), "f16")
+    x = synth.to_bits(synth.normal_f32(83, (T, d), 1 / 16), "f16")
+    v, m, y = oracle.expert_forward(x, "f16", up_q, up_sz, gb, db, "f16", thr=-1.0, bits=bits)
+    X = _bits_to_f64(x, "f16")
+    Wg = _bits_to_f64(gb, "f16").T
+    Wd = _bits_to_f64(db, "f16")
+    Wu = w_up.astype(np.float64).T
+    ref = (X @ Wg * expit(X @ Wg) * (X @ Wu)) @ Wd
+    assert np.all(m == 1)
+    np.testing.assert_allclose(v, X @ Wu, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-14)
+    # a threshold keeps exactly the channels with |v| > t
+    t = float(np.median(np.abs(v)))
+    v2, m2, _ = oracle.expert_forward(x, "f16", up_q, up_sz, gb, db, "f16", thr=t, bits=bits)
+    assert np.array_equal(m2, (np.abs(v2) > np.float32(t)).astype(np.uint8))
