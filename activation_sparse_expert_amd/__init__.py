@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
 MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
 PATH_SPARSE, PATH_DENSE, PATH_AUTO = 0, 1, 2
-OP_EXPERT, OP_ROUTE, OP_LAYER, OP_CALIBRATE, OP_EAMC = 0, 1, 2, 3, 4
+OP_EXPERT, OP_ROUTE, OP_LAYER, OP_CALIBRATE, OP_EAMC, OP_EXPERT_BITS = 0, 1, 2, 3, 4, 5
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_ALIGNMENT", -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_workspace_size", "moe_workspace_init", "moe_pack_up_int2",
             "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold",
-            "moe_eamc_match"]
+            "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits"]
 
 
 class MoeError(RuntimeError):
@@ -82,6 +82,11 @@ def lib():
         L.moe_status_string.argtypes = [I]
         L.moe_calibrate_threshold.restype = I
         L.moe_calibrate_threshold.argtypes = [P, C.c_longlong, C.c_double, P, P, Z, P]
+        L.moe_expert_forward_sparse_bits.restype = I
+        L.moe_expert_forward_sparse_bits.argtypes = [C.POINTER(ExpertView), I, I, I, I, P, I, I,
+                                                     P, I, P, I, P, P, P, Z, P]
+        L.moe_pack_up_bits.restype = I
+        L.moe_pack_up_bits.argtypes = [P, I, I, I, I, P, P, P]
         L.moe_eamc_match.restype = I
         L.moe_eamc_match.argtypes = [P, I, I, P, P, P, P, Z, P]
         _lib = L
@@ -166,6 +171,25 @@ def expert_forward_sparse(expert: Expert, x, *, y=None, out_dtype=None, token_sc
         int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_out), _ptr(v_out), _ptr(ws),
         ws.numel(), _stream())
     _check(st, "moe_expert_forward_sparse")
+    return y
+
+
+def expert_forward_sparse_bits(expert: Expert, bits: int, x, *, y=None, out_dtype=None,
+                               token_scale=None, accumulate: bool = False, mask_out=None,
+                               v_out=None, ws=None):
+    """Algorithm 1 with the up codes at ``bits`` (8, 4, 2 or 1) bits; y [T][d]."""
+    import torch
+    T, d = x.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=out_dtype or torch.float32, device=x.device)
+    if ws is None:
+        ws = new_workspace(workspace_size(OP_EXPERT_BITS, T, d, expert.f), x.device)
+    v = expert.view()
+    st = lib().moe_expert_forward_sparse_bits(
+        C.byref(v), int(bits), d, expert.f, _dt(expert.gate_t), _ptr(x), _dt(x), T,
+        _ptr(token_scale), int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_out), _ptr(v_out),
+        _ptr(ws), ws.numel(), _stream())
+    _check(st, "moe_expert_forward_sparse_bits")
     return y
 
 
@@ -300,6 +324,21 @@ def pack_up_int2(w_up_t, *, up_q=None, up_sz=None):
     st = lib().moe_pack_up_int2(_ptr(w_up_t), _dt(w_up_t), d, f, _ptr(up_q), _ptr(up_sz),
                                 _stream())
     _check(st, "moe_pack_up_int2")
+    return up_q, up_sz
+
+
+def pack_up_bits(w_up_t, bits: int, *, up_q=None, up_sz=None):
+    """Group-64 quantisation of up weights [f][d] to 8, 4, 2 or 1 bits on the
+    device; returns (up_q [f][d*bits/8] uint8, up_sz [f][d/64][2])."""
+    import torch
+    f, d = w_up_t.shape
+    if up_q is None:
+        up_q = torch.empty((f, d * bits // 8), dtype=torch.uint8, device=w_up_t.device)
+    if up_sz is None:
+        up_sz = torch.empty((f, d // 64, 2), dtype=torch.int16, device=w_up_t.device)
+    st = lib().moe_pack_up_bits(_ptr(w_up_t), _dt(w_up_t), d, f, int(bits), _ptr(up_q),
+                                _ptr(up_sz), _stream())
+    _check(st, "moe_pack_up_bits")
     return up_q, up_sz
 
 

@@ -12,7 +12,7 @@ BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "expert_sparse_f16.hip", "expert_sparse_bf16.hip", "reduce.hip", "route.hip",
            "pack.hip", "dense_mfma.hip", "calibrate.hip",
-           "eamc.hip"]
+           "eamc.hip", "expert_bits.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -108,6 +108,12 @@ SparsePlan layer_plan(int T, int d, int f, int E, int k, int S)
     return SparsePlan{tb, (int)bound, plan_tiles(f, (int)expect, (long long)T * (k + S), d)};
 }
 
+size_t bits_ws_bytes(int T, int d, int f)
+{
+    const size_t tiles = (size_t)(f + kBitsTile - 1) / kBitsTile;
+    return up((size_t)T * f * 4) + up((size_t)T * tiles * d * 4);
+}
+
 size_t expert_ws_bytes(int T, int d, int f)
 {
     const TilePlan tp = expert_plan(T, d, f).tp;
@@ -233,6 +239,11 @@ size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S)
         return layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr);
     case MOE_OP_CALIBRATE:
         return up(calibrate_ws_bytes());
+    case MOE_OP_EXPERT_BITS: {
+        if (f < 1) return 0;
+        const size_t a = expert_ws_bytes(T, d, f), b = bits_ws_bytes(T, d, f);
+        return a > b ? a : b;
+    }
     case MOE_OP_EAMC:
         return d > kEamcMaxLen ? 0 : up((size_t)T * 8);   // T stored EAMs of d entries
     }
@@ -349,6 +360,49 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     return hip_status(launch_reduce(r, s));
 }
 
+moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, int d, int f,
+                                          moe_dtype wdt, const void *x, moe_dtype xdt, int T,
+                                          const float *token_scale, int accumulate, void *y,
+                                          moe_dtype ydt, uint8_t *mask_out, float *v_out,
+                                          void *ws, size_t ws_bytes, void *stream)
+{
+    if (bits == 2)
+        return moe_expert_forward_sparse(e, d, f, wdt, x, xdt, T, token_scale, accumulate, y, ydt,
+                                         mask_out, v_out, ws, ws_bytes, stream);
+    if (bits != 1 && bits != 4 && bits != 8) return MOE_ERR_INVALID_ARG;
+    if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
+    if (st != MOE_OK) return st;
+    if ((d != 512 && d != 1024 && d != 2048 && d != 4096) || T > kBitsMaxT ||
+        bits_lds_up(T, d) > kBitsMaxLds)
+        return MOE_ERR_UNSUPPORTED;
+    st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
+    if (st != MOE_OK) return st;
+    if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||
+        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)))
+        return MOE_ERR_ALIGNMENT;
+    if (!ws || ws_bytes < bits_ws_bytes(T, d, f)) return MOE_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    BitsArgs a{};
+    a.up_q = e->up_q; a.up_sz = e->up_sz;
+    a.gate = (const uint16_t *)e->gate_t; a.down = (const uint16_t *)e->down;
+    a.bits = bits; a.d = d; a.f = f; a.T = T; a.bf16 = wdt == MOE_BF16 ? 1 : 0;
+    a.thr = e->threshold;
+    a.x = (const uint16_t *)x; a.token_scale = token_scale;
+    a.v = v_out ? v_out : (float *)ws;
+    a.mask_out = mask_out;
+    a.part = (float *)((char *)ws + up((size_t)T * f * 4));
+    a.tiles = (f + kBitsTile - 1) / kBitsTile;
+    hipError_t he = launch_expert_bits(a, s);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+    ReduceArgs r{};
+    r.part = a.part; r.tiles = a.tiles; r.d = d; r.T = T;
+    r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0;
+    r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
+    return hip_status(launch_reduce(r, s));
+}
+
 moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, int T, void *y,
                              moe_dtype ydt, moe_path path, const moe_layer_trace *trace, void *ws,
                              size_t ws_bytes, void *stream)
@@ -460,6 +514,20 @@ moe_status moe_pack_up_int2(const void *w_up_t, moe_dtype dt, int d, int f, uint
     if (!aligned(up_q, 16) || !aligned(up_sz, 4) || !aligned(w_up_t, dt == MOE_F32 ? 4 : 2))
         return MOE_ERR_ALIGNMENT;
     return hip_status(launch_pack_int2(w_up_t, (int)dt, d, f, up_q, up_sz, (hipStream_t)stream));
+}
+
+moe_status moe_pack_up_bits(const void *w_up_t, moe_dtype dt, int d, int f, int bits,
+                            uint8_t *up_q, uint16_t *up_sz, void *stream)
+{
+    if (bits == 2) return moe_pack_up_int2(w_up_t, dt, d, f, up_q, up_sz, stream);
+    if (bits != 1 && bits != 4 && bits != 8) return MOE_ERR_INVALID_ARG;
+    if (!w_up_t || !up_q || !up_sz) return MOE_ERR_INVALID_ARG;
+    if (d < 64 || d % 64 != 0 || f < 1) return MOE_ERR_INVALID_ARG;
+    if (!valid_out(dt)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(up_q, 16) || !aligned(up_sz, 4) || !aligned(w_up_t, dt == MOE_F32 ? 4 : 2))
+        return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_pack_bits(w_up_t, (int)dt, d, f, bits, up_q, up_sz,
+                                       (hipStream_t)stream));
 }
 
 moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,

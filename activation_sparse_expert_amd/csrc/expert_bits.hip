@@ -1,0 +1,247 @@
+// The sparse expert with the up projection at 8, 4 or 1 bits per code (FloE
+// review, "敏感度分析": the up projection is also quantised to INT8, INT4 and
+// INT1; the expert itself is Algorithm 1 of "高效稀疏 GEMV 内核").  The codes
+// use the same group-64 scale and zero point as the INT2 format, packed plainly:
+// input k of channel j at bit k*bits of row j.
+//
+// Two kernels and the shared reduce:
+//  * upb_kernel: v = x W^up and the mask |v| > t.  The tokens' x is staged in
+//    LDS as fp32 with per-16-input sums; every wave streams 8 rows of codes,
+//    a lane taking 16 codes (2*bits bytes) per step, and adds
+//    s (sum q x - z sum x) per 16-code chunk.  v goes to memory.
+//  * gatherb_kernel: one workgroup per 128 channels.  For each token the
+//    active channels of the tile are ranked (ballots in channel order) and
+//    shared out by rank over the 4 waves; a wave forms the gate dot product of
+//    its channel, h = SiLU(g) v (times the token scale), and adds h times the
+//    down row into per-lane column sums.  The waves' sums are added in LDS in
+//    wave order and written as the tile's partial row; the reduce kernel adds
+//    the tiles in a fixed order.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace moeffn {
+
+namespace {
+
+constexpr int kUThreads = 256;
+constexpr int kURows = 8;               // rows per wave
+constexpr int kUMaxSteps = 4;           // 16-code chunks per lane per row: d <= 4096
+constexpr int kGThreads = 256;
+
+template <int BITS>
+struct Chunk;                           // 16 codes of one lane
+template <> struct Chunk<8> {
+    uint4 w;
+    __device__ void load(const uint8_t *p) { w = load_nt16(p); }
+    __device__ int code(int u) const
+    {
+        const uint32_t x = u < 4 ? w.x : u < 8 ? w.y : u < 12 ? w.z : w.w;
+        return (x >> (8 * (u & 3))) & 0xFF;
+    }
+};
+template <> struct Chunk<4> {
+    uint2 w;
+    __device__ void load(const uint8_t *p)
+    {
+        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+        const v2u v = __builtin_nontemporal_load((const v2u *)p);
+        w = make_uint2(v.x, v.y);
+    }
+    __device__ int code(int u) const
+    {
+        const uint32_t x = u < 8 ? w.x : w.y;
+        return (x >> (4 * (u & 7))) & 0xF;
+    }
+};
+template <> struct Chunk<1> {
+    uint32_t w;
+    __device__ void load(const uint8_t *p) { w = __builtin_nontemporal_load((const uint16_t *)p); }
+    __device__ int code(int u) const { return (w >> u) & 1; }
+};
+
+template <int BITS, bool BF16>
+__global__ void __launch_bounds__(kUThreads)
+upb_kernel(BitsArgs a)
+{
+    extern __shared__ __align__(16) float xs[];      // [T][d] x, then [T][d/16] chunk sums
+    const int d = a.d, T = a.T, nchunk = d / 16;
+    float *xc = xs + (size_t)T * d;
+    for (int i = threadIdx.x; i < T * d; i += kUThreads) {
+        const uint16_t b = a.x[i];
+        xs[i] = BF16 ? bf16_bits_to_float(b) : half_bits_to_float(b);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < T * nchunk; i += kUThreads) {
+        const float *p = xs + (size_t)i * 16;     // chunk i of the flattened [T][d]
+        float s = 0.f;
+        for (int u = 0; u < 16; ++u) s += p[u];
+        xc[i] = s;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int G = d / 64;
+    const size_t row_bytes = (size_t)d * BITS / 8;
+    const int j0 = (blockIdx.x * (kUThreads / 64) + wave) * kURows;
+    for (int r = 0; r < kURows; ++r) {
+        const int j = j0 + r;
+        if (j >= a.f) break;                      // wave-uniform
+        Chunk<BITS> ch[kUMaxSteps];
+        uint32_t sz[kUMaxSteps];
+#pragma unroll
+        for (int st = 0; st < kUMaxSteps; ++st) {
+            const int c = lane + 64 * st;
+            if (c < nchunk) {
+                ch[st].load(a.up_q + (size_t)j * row_bytes + (size_t)c * 2 * BITS);
+                sz[st] = load_nt4(a.up_sz + ((size_t)j * G + c / 4) * 2);
+            }
+        }
+        for (int t = 0; t < T; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int st = 0; st < kUMaxSteps; ++st) {
+                const int c = lane + 64 * st;
+                if (c < nchunk) {
+                    const float *xp = xs + (size_t)t * d + (size_t)c * 16;
+                    float dq = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) dq += (float)ch[st].code(u) * xp[u];
+                    const float s = half_bits_to_float(sz[st] & 0xFFFFu);
+                    const float z = half_bits_to_float(sz[st] >> 16);
+                    acc += s * (dq - z * xc[t * nchunk + c]);
+                }
+            }
+            acc = seg_sum<64>(acc);
+            if (lane == 0) {
+                a.v[(size_t)t * a.f + j] = acc;
+                if (a.mask_out) a.mask_out[(size_t)t * a.f + j] = fabsf(acc) > a.thr ? 1 : 0;
+            }
+        }
+    }
+}
+
+// NC = d / 512: lane l owns columns 8 l + 512 i, i < NC
+template <bool BF16, int NC>
+__global__ void __launch_bounds__(kGThreads)
+gatherb_kernel(BitsArgs a)
+{
+    extern __shared__ __align__(16) float red[];     // [d]
+    const int d = a.d;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tile = blockIdx.x;
+    const int jt = tile * kBitsTile;
+    for (int t = 0; t < a.T; ++t) {
+        uint4 xr[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) xr[i] = *(const uint4 *)(a.x + (size_t)t * d + 8 * lane + 512 * i);
+        float acc[NC][8];
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[i][u] = 0.f;
+        const float sc = a.token_scale ? a.token_scale[t] : 1.f;
+        int rank = 0;
+        for (int half = 0; half < kBitsTile / 64; ++half) {
+            const int jl = jt + half * 64 + lane;
+            const bool act = jl < a.f && fabsf(a.v[(size_t)t * a.f + jl]) > a.thr;
+            unsigned long long m = __ballot(act);
+            while (m) {
+                const int b = __builtin_ctzll(m);
+                m &= m - 1;
+                if ((rank++ & 3) != wave) continue;
+                const int j = jt + half * 64 + b;
+                const float vj = a.v[(size_t)t * a.f + j];
+                const uint16_t *grow = a.gate + (size_t)j * d;
+                const uint16_t *drow = a.down + (size_t)j * d;
+                uint4 gw[NC];
+#pragma unroll
+                for (int i = 0; i < NC; ++i) gw[i] = load_nt16(grow + 8 * lane + 512 * i);
+                float g = 0.f;
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    g = dot2<BF16>(gw[i].x, xr[i].x, g);
+                    g = dot2<BF16>(gw[i].y, xr[i].y, g);
+                    g = dot2<BF16>(gw[i].z, xr[i].z, g);
+                    g = dot2<BF16>(gw[i].w, xr[i].w, g);
+                }
+                uint4 dw[NC];
+#pragma unroll
+                for (int i = 0; i < NC; ++i) dw[i] = load_nt16(drow + 8 * lane + 512 * i);
+                g = seg_sum<64>(g);
+                const float h = silu(g) * vj * sc;
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    const uint32_t w4[4] = {dw[i].x, dw[i].y, dw[i].z, dw[i].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[i][2 * q] += h * lo16_to_float<BF16>(w4[q]);
+                        acc[i][2 * q + 1] += h * hi16_to_float<BF16>(w4[q]);
+                    }
+                }
+            }
+        }
+        // the waves' column sums, added in wave order
+        for (int w = 0; w < kGThreads / 64; ++w) {
+            if (wave == w) {
+#pragma unroll
+                for (int i = 0; i < NC; ++i)
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        float *p = red + 8 * lane + 512 * i + u;
+                        *p = w == 0 ? acc[i][u] : *p + acc[i][u];
+                    }
+            }
+            __syncthreads();
+        }
+        float *dst = a.part + ((size_t)t * a.tiles + tile) * d;
+        for (int c = threadIdx.x * 4; c < d; c += kGThreads * 4) {
+            const float4 v4 = *(const float4 *)(red + c);
+            typedef float v4f __attribute__((ext_vector_type(4)));
+            v4f o = {v4.x, v4.y, v4.z, v4.w};
+            __builtin_nontemporal_store(o, (v4f *)(dst + c));
+        }
+        __syncthreads();                               // red is reused by the next token
+    }
+}
+
+template <int BITS>
+const void *upb_for(bool bf16)
+{
+    return bf16 ? (const void *)upb_kernel<BITS, true> : (const void *)upb_kernel<BITS, false>;
+}
+
+template <int NC>
+const void *gatherb_for(bool bf16)
+{
+    return bf16 ? (const void *)gatherb_kernel<true, NC> : (const void *)gatherb_kernel<false, NC>;
+}
+
+}  // namespace
+
+size_t bits_lds_up(int T, int d) { return (size_t)T * d * 4 + (size_t)T * (d / 16) * 4; }
+
+hipError_t launch_expert_bits(const BitsArgs &a, hipStream_t s)
+{
+    const void *up = a.bits == 8 ? upb_for<8>(a.bf16) : a.bits == 4 ? upb_for<4>(a.bf16)
+                   : a.bits == 1 ? upb_for<1>(a.bf16) : nullptr;
+    const int nc = a.d / 512;
+    const void *ga = nc == 1 ? gatherb_for<1>(a.bf16) : nc == 2 ? gatherb_for<2>(a.bf16)
+                   : nc == 4 ? gatherb_for<4>(a.bf16) : nc == 8 ? gatherb_for<8>(a.bf16) : nullptr;
+    if (!up || !ga || a.d % 512 != 0 || a.d / 16 > 64 * kUMaxSteps) return hipErrorInvalidValue;
+    const size_t lds_up = bits_lds_up(a.T, a.d);
+    if (lds_up > kBitsMaxLds) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(up, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_up);
+    if (e != hipSuccess) return e;
+    const int rows_per_block = (kUThreads / 64) * kURows;
+    void *args[] = {(void *)&a};
+    e = hipLaunchKernel(up, dim3((a.f + rows_per_block - 1) / rows_per_block), dim3(kUThreads),
+                        args, lds_up, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(ga, dim3(a.tiles), dim3(kGThreads), args, (size_t)a.d * 4, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e;
+}
+
+}  // namespace moeffn

@@ -57,6 +57,48 @@ pack_int2_kernel(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz)
     *(uint4 *)(q + j * (d / 4) + g * 16) = make_uint4(words[0], words[1], words[2], words[3]);
 }
 
+// The same quantiser with L = 2^BITS - 1 levels (8, 4 or 1 bits): the codes
+// of a group are packed plainly, input k at bit k*BITS of the row, least
+// significant bits first; a group takes 8*BITS bytes.
+template <int BITS>
+__global__ void __launch_bounds__(256)
+pack_bits_kernel(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz)
+{
+    constexpr int L = (1 << BITS) - 1;
+    constexpr int NW = 2 * BITS;                // 32-bit words per group
+    const int G = d / 64;
+    const size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= (size_t)f * G) return;
+    const size_t j = u / G, g = u - j * G;
+    const size_t base = j * d + g * 64;
+    float mn = load_w(w, dt, base), mx = mn;
+    for (int i = 1; i < 64; ++i) {
+        const float v = load_w(w, dt, base + i);
+        if (v < mn) mn = v;
+        if (v > mx) mx = v;
+    }
+    uint16_t sb = float_to_half_bits(__fdiv_rn(mx - mn, (float)L));
+    float s = half_bits_to_float(sb);
+    if (s == 0.0f) { sb = 0x3C00; s = 1.0f; }
+    const uint16_t zb = float_to_half_bits(__fdiv_rn(-mn, s));
+    const float z = half_bits_to_float(zb);
+    sz[u * 2 + 0] = sb;
+    sz[u * 2 + 1] = zb;
+    uint32_t words[NW];
+    for (int i = 0; i < NW; ++i) words[i] = 0;
+    for (int i = 0; i < 64; ++i) {
+        const float a = __fdiv_rn(load_w(w, dt, base + i), s);
+        const float r = rintf(__fadd_rn(a, z));
+        int c = (int)r;
+        if (r < 0.0f) c = 0;
+        if (r > (float)L) c = L;
+        const int bit = i * BITS;
+        words[bit / 32] |= (uint32_t)c << (bit % 32);
+    }
+    uint32_t *dst = (uint32_t *)(q + j * ((size_t)d * BITS / 8) + g * 8 * BITS);
+    for (int i = 0; i < NW; ++i) dst[i] = words[i];
+}
+
 // Round a double to bfloat16, nearest-even, from its bits (finite inputs).
 __device__ __forceinline__ uint16_t double_to_bf16_bits(double v)
 {
@@ -120,6 +162,18 @@ hipError_t launch_pack_int2(const void *w, int dt, int d, int f, uint8_t *q, uin
     const size_t n = (size_t)f * (d / 64);
     const unsigned blocks = (unsigned)((n + 255) / 256);
     hipLaunchKernelGGL(pack_int2_kernel, dim3(blocks), dim3(256), 0, s, w, dt, d, f, q, sz);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_bits(const void *w, int dt, int d, int f, int bits, uint8_t *q,
+                            uint16_t *sz, hipStream_t s)
+{
+    const size_t n = (size_t)f * (d / 64);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    if (bits == 8) hipLaunchKernelGGL(pack_bits_kernel<8>, dim3(blocks), dim3(256), 0, s, w, dt, d, f, q, sz);
+    else if (bits == 4) hipLaunchKernelGGL(pack_bits_kernel<4>, dim3(blocks), dim3(256), 0, s, w, dt, d, f, q, sz);
+    else if (bits == 1) hipLaunchKernelGGL(pack_bits_kernel<1>, dim3(blocks), dim3(256), 0, s, w, dt, d, f, q, sz);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

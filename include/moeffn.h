@@ -93,7 +93,8 @@ typedef enum {
     MOE_OP_ROUTE = 1,           /* moe_route_topk           */
     MOE_OP_LAYER = 2,           /* moe_layer_forward        */
     MOE_OP_CALIBRATE = 3,       /* moe_calibrate_threshold  */
-    MOE_OP_EAMC = 4             /* moe_eamc_match (T = n, d = len) */
+    MOE_OP_EAMC = 4,            /* moe_eamc_match (T = n, d = len) */
+    MOE_OP_EXPERT_BITS = 5      /* moe_expert_forward_sparse_bits, any width */
 } moe_op;
 
 /* One compressed expert (FloE review, "混合压缩策略": {W^S(gate), W^S(down),
@@ -182,6 +183,25 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
                                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The same expert with the up projection at 8, 4, 2 or 1 bits per code (FloE
+ * review, "敏感度分析": the up projection quantised to INT8/INT4/INT2/INT1).
+ * bits == 2 is moe_expert_forward_sparse with the INT2 format above.  For 8, 4
+ * and 1: up_q [f][d*bits/8], input k of channel j at bit k*bits of row j
+ * (least significant bits first), up_sz [f][d/64][2] as for INT2 with
+ * 2^bits - 1 levels (moe_pack_up_bits).  Other arguments, outputs and the
+ * mask rule as moe_expert_forward_sparse; the output is bit-reproducible.
+ * Limits for 8, 4, 1 bits: d in {512, 1024, 2048, 4096}, T <= 8 with
+ * T*d*4.25 bytes <= 144 KiB (else MOE_ERR_UNSUPPORTED).
+ * Workspace: moe_workspace_size(MOE_OP_EXPERT_BITS, T, d, f) bytes.
+ */
+moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, int d, int f,
+                                          moe_dtype wdt, const void *x, moe_dtype xdt, int T,
+                                          const float *token_scale, int accumulate,
+                                          void *y, moe_dtype ydt,
+                                          uint8_t *mask_out, float *v_out,
+                                          void *ws, size_t ws_bytes, void *stream);
+
+/*
  * One MoE layer: route (as moe_route_topk) and combine
  *   y_t = sum_s w_{t,s} a_{e(t,s)}(x_t) + sum_i a_{E+i}(x_t)
  * where a_e is Algorithm 1 (MOE_PATH_SPARSE) or the dense SwiGLU with the bf16
@@ -254,6 +274,16 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * Inputs are expected finite with |w| small enough that (mx - mn) / 3 fits fp16.
  */
 moe_status moe_pack_up_int2(const void *w_up_t, moe_dtype dt, int d, int f,
+                            uint8_t *up_q, uint16_t *up_sz, void *stream);
+
+/*
+ * Quantise up weights to 8, 4, 2 or 1 bits: the scheme of moe_pack_up_int2
+ * with L = 2^bits - 1 levels, s = fp16_rne((mx - mn) / L) (1 if 0),
+ * q = clamp(round_half_even(w / s + z), 0, L); codes packed plainly (input k at
+ * bit k*bits of its row); bits == 2 gives the INT2 format.  Outputs up_q
+ * [f][d*bits/8] (16-byte aligned), up_sz [f][d/64][2].  d % 64 == 0, f >= 1.
+ */
+moe_status moe_pack_up_bits(const void *w_up_t, moe_dtype dt, int d, int f, int bits,
                             uint8_t *up_q, uint16_t *up_sz, void *stream);
 
 /*

@@ -213,6 +213,26 @@ def test_eamc_match_rejects(kw, code):
     assert L.moe_workspace_size(moe.OP_EAMC, 100, (1 << 17) + 1, 0, 0, 0, 0) == 0
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=3), -1), (dict(bits=0), -1), (dict(d=6144), -2), (dict(d=8192), -2),
+    (dict(T=9), -2), (dict(T=0), -1), (dict(f=100), -1), (dict(x=None), -1),
+    (dict(x=FAKE + 8), -3), (dict(ws=None), -4), (dict(ws_bytes=1024), -4), (dict(wdt=2), -2),
+])
+def test_expert_bits_rejects(kw, code):
+    L = _lib_or_skip()
+    a = dict(bits=4, d=4096, f=14336, wdt=0, x=FAKE, T=1, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    v = _view()
+    assert L.moe_expert_forward_sparse_bits(C.byref(v), a["bits"], a["d"], a["f"], a["wdt"],
+                                            a["x"], a["wdt"], a["T"], None, 0, FAKE, 2, None,
+                                            None, a["ws"], a["ws_bytes"], None) == code
+    assert L.moe_pack_up_bits(FAKE, 2, 4096, 8, 3, FAKE, FAKE, None) == -1
+    assert L.moe_pack_up_bits(FAKE, 2, 100, 8, 4, FAKE, FAKE, None) == -1
+    assert L.moe_pack_up_bits(FAKE, 2, 4096, 8, 4, FAKE + 8, FAKE, None) == -3
+    assert moe.workspace_size(moe.OP_EXPERT_BITS, 4, 4096, 14336) >= \
+        moe.workspace_size(moe.OP_EXPERT, 4, 4096, 14336)
+
+
 def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(moe, "_lib", None)
     monkeypatch.setattr(moe, "LIB_PATH", "/nonexistent/libmoeffn.so")
