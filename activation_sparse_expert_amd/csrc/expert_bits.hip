@@ -6,14 +6,16 @@
 //
 // Two kernels and the shared reduce:
 //  * upb_kernel: v = x W^up and the mask |v| > t.  The tokens' x is staged in
-//    LDS as fp32 with per-16-input sums; every wave streams 8 rows of codes,
-//    a lane taking 16 codes (2*bits bytes) per step, and adds
+//    LDS as fp32 with per-16-input sums (one token: then moved to the lanes'
+//    registers, as a lane always takes the same chunks); every wave streams 8
+//    rows of codes, the next row's loads in flight while one is computed, a
+//    lane taking 16 codes (2*bits bytes) per step and adding
 //    s (sum q x - z sum x) per 16-code chunk.  v goes to memory.
-//  * gatherb_kernel: one workgroup per 128 channels.  For each token the
+//  * gatherb_kernel: one workgroup per 64 channels.  For each token the
 //    active channels of the tile are ranked (ballots in channel order) and
-//    shared out by rank over the 4 waves; a wave forms the gate dot product of
-//    its channel, h = SiLU(g) v (times the token scale), and adds h times the
-//    down row into per-lane column sums.  The waves' sums are added in LDS in
+//    shared out by rank over the 4 waves; a wave loads its channel's gate and
+//    down rows together, forms the gate dot product, h = SiLU(g) v (times the
+//    token scale), and adds h times the down row into per-lane column sums.  The waves' sums are added in LDS in
 //    wave order and written as the tile's partial row; the reduce kernel adds
 //    the tiles in a fixed order.
 #include "device.hpp"
@@ -59,16 +61,24 @@ template <> struct Chunk<1> {
     __device__ int code(int u) const { return (w >> u) & 1; }
 };
 
-template <int BITS, bool BF16>
+// ONE: a single token, whose x chunks stay in the lane's registers (the
+// lane always takes the same chunks); otherwise they are read from LDS per row
+template <int BITS, bool BF16, bool ONE>
 __global__ void __launch_bounds__(kUThreads)
 upb_kernel(BitsArgs a)
 {
     extern __shared__ __align__(16) float xs[];      // [T][d] x, then [T][d/16] chunk sums
     const int d = a.d, T = a.T, nchunk = d / 16;
     float *xc = xs + (size_t)T * d;
-    for (int i = threadIdx.x; i < T * d; i += kUThreads) {
-        const uint16_t b = a.x[i];
-        xs[i] = BF16 ? bf16_bits_to_float(b) : half_bits_to_float(b);
+    // 8 inputs per 16-byte load (d % 512 == 0, x 16-byte aligned)
+    for (int i = threadIdx.x; i < T * d / 8; i += kUThreads) {
+        const uint4 w = *(const uint4 *)(a.x + 8 * (size_t)i);
+        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+        float4 *o = (float4 *)(xs + 8 * (size_t)i);
+        o[0] = make_float4(lo16_to_float<BF16>(w4[0]), hi16_to_float<BF16>(w4[0]),
+                           lo16_to_float<BF16>(w4[1]), hi16_to_float<BF16>(w4[1]));
+        o[1] = make_float4(lo16_to_float<BF16>(w4[2]), hi16_to_float<BF16>(w4[2]),
+                           lo16_to_float<BF16>(w4[3]), hi16_to_float<BF16>(w4[3]));
     }
     __syncthreads();
     for (int i = threadIdx.x; i < T * nchunk; i += kUThreads) {
@@ -82,20 +92,37 @@ upb_kernel(BitsArgs a)
     const int wave = threadIdx.x >> 6;
     const int G = d / 64;
     const size_t row_bytes = (size_t)d * BITS / 8;
+    float xreg[ONE ? kUMaxSteps : 1][16], xcr[ONE ? kUMaxSteps : 1];
+    if constexpr (ONE) {
+#pragma unroll
+        for (int st = 0; st < kUMaxSteps; ++st) {
+            const int c = lane + 64 * st;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) xreg[st][u] = c < nchunk ? xs[c * 16 + u] : 0.f;
+            xcr[st] = c < nchunk ? xc[c] : 0.f;
+        }
+    }
     const int j0 = (blockIdx.x * (kUThreads / 64) + wave) * kURows;
-    for (int r = 0; r < kURows; ++r) {
-        const int j = j0 + r;
-        if (j >= a.f) break;                      // wave-uniform
-        Chunk<BITS> ch[kUMaxSteps];
-        uint32_t sz[kUMaxSteps];
+    // the next row's codes are loaded while the current one is computed
+    Chunk<BITS> ch[kUMaxSteps], chn[kUMaxSteps];
+    uint32_t sz[kUMaxSteps], szn[kUMaxSteps];
+    auto load_row = [&](int j, Chunk<BITS> (&c_)[kUMaxSteps], uint32_t (&s_)[kUMaxSteps]) {
 #pragma unroll
         for (int st = 0; st < kUMaxSteps; ++st) {
             const int c = lane + 64 * st;
             if (c < nchunk) {
-                ch[st].load(a.up_q + (size_t)j * row_bytes + (size_t)c * 2 * BITS);
-                sz[st] = load_nt4(a.up_sz + ((size_t)j * G + c / 4) * 2);
+                c_[st].load(a.up_q + (size_t)j * row_bytes + (size_t)c * 2 * BITS);
+                s_[st] = load_nt4(a.up_sz + ((size_t)j * G + c / 4) * 2);
             }
         }
+    };
+    if (j0 < a.f) load_row(j0, chn, szn);
+    for (int r = 0; r < kURows; ++r) {
+        const int j = j0 + r;
+        if (j >= a.f) break;                      // wave-uniform
+#pragma unroll
+        for (int st = 0; st < kUMaxSteps; ++st) { ch[st] = chn[st]; sz[st] = szn[st]; }
+        if (r + 1 < kURows && j + 1 < a.f) load_row(j + 1, chn, szn);
         for (int t = 0; t < T; ++t) {
             float acc = 0.f;
 #pragma unroll
@@ -105,10 +132,11 @@ upb_kernel(BitsArgs a)
                     const float *xp = xs + (size_t)t * d + (size_t)c * 16;
                     float dq = 0.f;
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) dq += (float)ch[st].code(u) * xp[u];
+                    for (int u = 0; u < 16; ++u)
+                        dq += (float)ch[st].code(u) * (ONE ? xreg[ONE ? st : 0][u] : xp[u]);
                     const float s = half_bits_to_float(sz[st] & 0xFFFFu);
                     const float z = half_bits_to_float(sz[st] >> 16);
-                    acc += s * (dq - z * xc[t * nchunk + c]);
+                    acc += s * (dq - z * (ONE ? xcr[ONE ? st : 0] : xc[t * nchunk + c]));
                 }
             }
             acc = seg_sum<64>(acc);
@@ -154,9 +182,11 @@ gatherb_kernel(BitsArgs a)
                 const float vj = a.v[(size_t)t * a.f + j];
                 const uint16_t *grow = a.gate + (size_t)j * d;
                 const uint16_t *drow = a.down + (size_t)j * d;
-                uint4 gw[NC];
+                uint4 gw[NC], dw[NC];
 #pragma unroll
                 for (int i = 0; i < NC; ++i) gw[i] = load_nt16(grow + 8 * lane + 512 * i);
+#pragma unroll
+                for (int i = 0; i < NC; ++i) dw[i] = load_nt16(drow + 8 * lane + 512 * i);
                 float g = 0.f;
 #pragma unroll
                 for (int i = 0; i < NC; ++i) {
@@ -165,9 +195,6 @@ gatherb_kernel(BitsArgs a)
                     g = dot2<BF16>(gw[i].z, xr[i].z, g);
                     g = dot2<BF16>(gw[i].w, xr[i].w, g);
                 }
-                uint4 dw[NC];
-#pragma unroll
-                for (int i = 0; i < NC; ++i) dw[i] = load_nt16(drow + 8 * lane + 512 * i);
                 g = seg_sum<64>(g);
                 const float h = silu(g) * vj * sc;
 #pragma unroll
@@ -206,9 +233,11 @@ gatherb_kernel(BitsArgs a)
 }
 
 template <int BITS>
-const void *upb_for(bool bf16)
+const void *upb_for(bool bf16, bool one)
 {
-    return bf16 ? (const void *)upb_kernel<BITS, true> : (const void *)upb_kernel<BITS, false>;
+    if (one) return bf16 ? (const void *)upb_kernel<BITS, true, true>
+                         : (const void *)upb_kernel<BITS, false, true>;
+    return bf16 ? (const void *)upb_kernel<BITS, true, false> : (const void *)upb_kernel<BITS, false, false>;
 }
 
 template <int NC>
@@ -223,8 +252,9 @@ size_t bits_lds_up(int T, int d) { return (size_t)T * d * 4 + (size_t)T * (d / 1
 
 hipError_t launch_expert_bits(const BitsArgs &a, hipStream_t s)
 {
-    const void *up = a.bits == 8 ? upb_for<8>(a.bf16) : a.bits == 4 ? upb_for<4>(a.bf16)
-                   : a.bits == 1 ? upb_for<1>(a.bf16) : nullptr;
+    const bool one = a.T == 1;
+    const void *up = a.bits == 8 ? upb_for<8>(a.bf16, one) : a.bits == 4 ? upb_for<4>(a.bf16, one)
+                   : a.bits == 1 ? upb_for<1>(a.bf16, one) : nullptr;
     const int nc = a.d / 512;
     const void *ga = nc == 1 ? gatherb_for<1>(a.bf16) : nc == 2 ? gatherb_for<2>(a.bf16)
                    : nc == 4 ? gatherb_for<4>(a.bf16) : nc == 8 ? gatherb_for<8>(a.bf16) : nullptr;

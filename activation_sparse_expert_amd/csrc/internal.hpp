@@ -104,7 +104,7 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 // Threshold calibration: out = linear-interpolation quantile of |v| between
 // order statistics r_lo and r_hi with weight gamma (computed on the host).
 // The sparse expert with 8-, 4- or 1-bit up codes (plain packing, same scales).
-constexpr int kBitsTile = 128;                  // channels per gather workgroup
+constexpr int kBitsTile = 64;                   // channels per gather workgroup
 constexpr size_t kBitsMaxLds = 144u << 10;      // x staging of the up kernel
 constexpr int kBitsMaxT = 8;                    // tokens per call
 struct BitsArgs {

@@ -356,6 +356,56 @@ def layers_measure():
     return out
 
 
+def bits_measure(sparsity=0.9):
+    """One Mixtral-8x7B-shaped expert with the up codes at 8, 4 and 1 bits,
+    one token per call, 90% sparsity: time per call and algorithmic bytes
+    (codes d f bits/8, scales f d/16, gate + down rows of the active channels,
+    x) per call."""
+    import torch
+    import activation_sparse_expert_amd as moe
+    import synth
+    d, f = D, F
+    dev = torch.device("cuda:0")
+    g = synth.device_normal(synth.seed_of(2, 0, 0, synth.T_GATE), (f, d), 0.02, dev, torch.float16)
+    dn = synth.device_normal(synth.seed_of(2, 0, 0, synth.T_DOWN), (f, d), 0.02, dev, torch.float16)
+    u = synth.device_normal(synth.seed_of(2, 0, 0, synth.T_UP), (f, d), 0.02, dev)
+    xs = synth.device_normal(synth.seed_of(2, 0, 0, synth.T_X), (64, d), 1 / 64, dev, torch.float16)
+    res = {}
+    for bits in (8, 4, 1):
+        up_q, up_sz = moe.pack_up_bits(u, bits)
+        ex = moe.Expert(up_q, up_sz, g, dn, 0.0)
+        v = torch.empty((64, f), dtype=torch.float32, device=dev)
+        ws = moe.new_workspace(moe.workspace_size(moe.OP_EXPERT_BITS, 1, d, f), dev)
+        y = torch.empty((1, d), dtype=torch.float32, device=dev)
+        ex.threshold = -1.0
+        for t in range(64):
+            moe.expert_forward_sparse_bits(ex, bits, xs[t:t + 1], y=y, v_out=v[t:t + 1], ws=ws)
+        torch.cuda.synchronize()
+        ex.threshold = float(torch.quantile(v.abs().flatten()[:1 << 24].float(), sparsity))
+        m = torch.empty((1, f), dtype=torch.uint8, device=dev)
+        act = 0
+        for t in range(64):
+            moe.expert_forward_sparse_bits(ex, bits, xs[t:t + 1], y=y, mask_out=m, ws=ws)
+            act += int(m.sum().item())
+        act /= 64
+        ci = [0]
+
+        def call():
+            t = ci[0] % 64
+            ci[0] += 1
+            moe.expert_forward_sparse_bits(ex, bits, xs[t:t + 1], y=y, ws=ws)
+        sec = time_graph(call, reps=10, inner=64)
+        nbytes = d * f * bits / 8 + f * (d // 64) * 4 + 2 * act * d * 2 + d * 2
+        res[f"int{bits}"] = {"us_per_call": sec * 1e6, "tokens_per_s": 1 / sec,
+                             "active_channels": act, "bytes_per_call": nbytes,
+                             "achieved_gbs": nbytes / sec / 1e9,
+                             "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS}
+        del up_q, up_sz, ex
+    res["workload"] = ("one Mixtral-8x7B-shaped expert (d=4096, f=14336), up codes at 8/4/1 bits, "
+                       "90% sparsity, batch 1")
+    return res
+
+
 def eamc_measure():
     """Nearest stored request-level EAM (cosine distance) over a collection:
     per call n stored EAMs of L x E int32 counts are read once."""
@@ -547,6 +597,8 @@ def main():
     if not args.no_layers:
         log("measuring the layer workloads")
         out["more"].update(layers_measure())
+        log("measuring the 8/4/1-bit up variants")
+        out["more"]["expert_up_bits"] = bits_measure()
         log("measuring the EAMC match")
         out["more"]["eamc_match"] = eamc_measure()
     if not args.no_batched:
