@@ -14,8 +14,9 @@
 //  * gatherb_kernel: one workgroup per 64 channels.  For each token the
 //    active channels of the tile are ranked (ballots in channel order) and
 //    shared out by rank over the 4 waves; a wave loads its channel's gate and
-//    down rows together, forms the gate dot product, h = SiLU(g) v (times the
-//    token scale), and adds h times the down row into per-lane column sums.  The waves' sums are added in LDS in
+//    down rows together (the next channel's while one is computed), forms the
+//    gate dot product, h = SiLU(g) v (times the token scale), and adds h times
+//    the down row into per-lane column sums.  The waves' sums are added in LDS in
 //    wave order and written as the tile's partial row; the reduce kernel adds
 //    the tiles in a fixed order.
 #include "device.hpp"
@@ -169,44 +170,66 @@ gatherb_kernel(BitsArgs a)
 #pragma unroll
             for (int u = 0; u < 8; ++u) acc[i][u] = 0.f;
         const float sc = a.token_scale ? a.token_scale[t] : 1.f;
-        int rank = 0;
-        for (int half = 0; half < kBitsTile / 64; ++half) {
-            const int jl = jt + half * 64 + lane;
-            const bool act = jl < a.f && fabsf(a.v[(size_t)t * a.f + jl]) > a.thr;
-            unsigned long long m = __ballot(act);
-            while (m) {
-                const int b = __builtin_ctzll(m);
-                m &= m - 1;
-                if ((rank++ & 3) != wave) continue;
-                const int j = jt + half * 64 + b;
-                const float vj = a.v[(size_t)t * a.f + j];
-                const uint16_t *grow = a.gate + (size_t)j * d;
-                const uint16_t *drow = a.down + (size_t)j * d;
-                uint4 gw[NC], dw[NC];
+        static_assert(kBitsTile == 64, "one ballot per tile");
+        const int jl = jt + lane;
+        const bool act = jl < a.f && fabsf(a.v[(size_t)t * a.f + jl]) > a.thr;
+        unsigned long long m = __ballot(act);
+        // this wave's channels: the active ones whose rank in channel order is
+        // the wave's index mod 4, taken in channel order
+        unsigned long long mine = 0;
+        for (int rank = 0; m; ++rank) {
+            if ((rank & 3) == wave) mine |= m & (~m + 1);
+            m &= m - 1;
+        }
+        auto load_ch = [&](int j, uint4 (&g_)[NC], uint4 (&d_)[NC]) {
+            const uint16_t *grow = a.gate + (size_t)j * d;
+            const uint16_t *drow = a.down + (size_t)j * d;
 #pragma unroll
-                for (int i = 0; i < NC; ++i) gw[i] = load_nt16(grow + 8 * lane + 512 * i);
+            for (int i = 0; i < NC; ++i) g_[i] = load_nt16(grow + 8 * lane + 512 * i);
 #pragma unroll
-                for (int i = 0; i < NC; ++i) dw[i] = load_nt16(drow + 8 * lane + 512 * i);
-                float g = 0.f;
+            for (int i = 0; i < NC; ++i) d_[i] = load_nt16(drow + 8 * lane + 512 * i);
+        };
+        // the next channel's rows are loaded while one is computed
+        uint4 gw[NC], dw[NC];
+        int jc = -1;
+        if (mine) {
+            jc = jt + __builtin_ctzll(mine);
+            mine &= mine - 1;
+            load_ch(jc, gw, dw);
+        }
+        while (jc >= 0) {
+            int jn = -1;
+            uint4 gn[NC], dn[NC];
+            if (mine) {
+                jn = jt + __builtin_ctzll(mine);
+                mine &= mine - 1;
+                load_ch(jn, gn, dn);
+            }
+            const float vj = a.v[(size_t)t * a.f + jc];
+            float g = 0.f;
 #pragma unroll
-                for (int i = 0; i < NC; ++i) {
-                    g = dot2<BF16>(gw[i].x, xr[i].x, g);
-                    g = dot2<BF16>(gw[i].y, xr[i].y, g);
-                    g = dot2<BF16>(gw[i].z, xr[i].z, g);
-                    g = dot2<BF16>(gw[i].w, xr[i].w, g);
-                }
-                g = seg_sum<64>(g);
-                const float h = silu(g) * vj * sc;
+            for (int i = 0; i < NC; ++i) {
+                g = dot2<BF16>(gw[i].x, xr[i].x, g);
+                g = dot2<BF16>(gw[i].y, xr[i].y, g);
+                g = dot2<BF16>(gw[i].z, xr[i].z, g);
+                g = dot2<BF16>(gw[i].w, xr[i].w, g);
+            }
+            g = seg_sum<64>(g);
+            const float h = silu(g) * vj * sc;
 #pragma unroll
-                for (int i = 0; i < NC; ++i) {
-                    const uint32_t w4[4] = {dw[i].x, dw[i].y, dw[i].z, dw[i].w};
+            for (int i = 0; i < NC; ++i) {
+                const uint32_t w4[4] = {dw[i].x, dw[i].y, dw[i].z, dw[i].w};
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[i][2 * q] += h * lo16_to_float<BF16>(w4[q]);
-                        acc[i][2 * q + 1] += h * hi16_to_float<BF16>(w4[q]);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    acc[i][2 * q] += h * lo16_to_float<BF16>(w4[q]);
+                    acc[i][2 * q + 1] += h * hi16_to_float<BF16>(w4[q]);
                 }
             }
+            if (jn >= 0) {
+#pragma unroll
+                for (int i = 0; i < NC; ++i) { gw[i] = gn[i]; dw[i] = dn[i]; }
+            }
+            jc = jn;
         }
         // the waves' column sums, added in wave order
         for (int w = 0; w < kGThreads / 64; ++w) {
