@@ -6,11 +6,12 @@
 //
 // Two kernels and the shared reduce:
 //  * upb_kernel: v = x W^up and the mask |v| > t.  The tokens' x is staged in
-//    LDS as fp32 with per-16-input sums (one token: then moved to the lanes'
-//    registers, as a lane always takes the same chunks); every wave streams 8
-//    rows of codes, the next row's loads in flight while one is computed, a
-//    lane taking 16 codes (2*bits bytes) per step and adding
-//    s (sum q x - z sum x) per 16-code chunk.  v goes to memory.
+//    LDS as fp32 with per-16-input sums (one token: each lane reads its own
+//    chunks into registers instead, as it always takes the same ones, and no
+//    LDS is used); every wave streams 8 rows of codes (4 below 8 bits), the
+//    next row's loads in flight while one is computed, a lane taking 16 codes
+//    (2*bits bytes) per step and adding s (sum q x - z sum x) per 16-code
+//    chunk.  v goes to memory.
 //  * gatherb_kernel: one workgroup per 64 channels.  For each token the
 //    active channels of the tile are ranked (ballots in channel order) and
 //    shared out by rank over the 4 waves; a wave loads its channel's gate and
@@ -27,7 +28,9 @@ namespace moeffn {
 namespace {
 
 constexpr int kUThreads = 256;
-constexpr int kURows = 8;               // rows per wave
+// rows per wave: 8 at 8 bits, 4 below (measured best on the Mixtral shape)
+template <int BITS>
+__host__ __device__ constexpr int urows() { return BITS == 8 ? 8 : 4; }
 constexpr int kUMaxSteps = 4;           // 16-code chunks per lane per row: d <= 4096
 constexpr int kGThreads = 256;
 
@@ -71,8 +74,9 @@ upb_kernel(BitsArgs a)
     extern __shared__ __align__(16) float xs[];      // [T][d] x, then [T][d/16] chunk sums
     const int d = a.d, T = a.T, nchunk = d / 16;
     float *xc = xs + (size_t)T * d;
-    // 8 inputs per 16-byte load (d % 512 == 0, x 16-byte aligned)
-    for (int i = threadIdx.x; i < T * d / 8; i += kUThreads) {
+    // 8 inputs per 16-byte load (d % 512 == 0, x 16-byte aligned); one token
+    // needs no staging: each lane reads its own chunks below
+    for (int i = threadIdx.x; !ONE && i < T * d / 8; i += kUThreads) {
         const uint4 w = *(const uint4 *)(a.x + 8 * (size_t)i);
         const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
         float4 *o = (float4 *)(xs + 8 * (size_t)i);
@@ -81,28 +85,46 @@ upb_kernel(BitsArgs a)
         o[1] = make_float4(lo16_to_float<BF16>(w4[2]), hi16_to_float<BF16>(w4[2]),
                            lo16_to_float<BF16>(w4[3]), hi16_to_float<BF16>(w4[3]));
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < T * nchunk; i += kUThreads) {
-        const float *p = xs + (size_t)i * 16;     // chunk i of the flattened [T][d]
-        float s = 0.f;
-        for (int u = 0; u < 16; ++u) s += p[u];
-        xc[i] = s;
+    if constexpr (!ONE) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < T * nchunk; i += kUThreads) {
+            const float *p = xs + (size_t)i * 16;     // chunk i of the flattened [T][d]
+            float s = 0.f;
+            for (int u = 0; u < 16; ++u) s += p[u];
+            xc[i] = s;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int G = d / 64;
     const size_t row_bytes = (size_t)d * BITS / 8;
     float xreg[ONE ? kUMaxSteps : 1][16], xcr[ONE ? kUMaxSteps : 1];
     if constexpr (ONE) {
+        // the lane's chunks straight from x (two 16-byte loads each), their
+        // sums in the same order as the staged form
 #pragma unroll
         for (int st = 0; st < kUMaxSteps; ++st) {
             const int c = lane + 64 * st;
+            uint32_t w8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (c < nchunk) {
+                const uint4 p0 = *(const uint4 *)(a.x + (size_t)c * 16);
+                const uint4 p1 = *(const uint4 *)(a.x + (size_t)c * 16 + 8);
+                w8[0] = p0.x; w8[1] = p0.y; w8[2] = p0.z; w8[3] = p0.w;
+                w8[4] = p1.x; w8[5] = p1.y; w8[6] = p1.z; w8[7] = p1.w;
+            }
+            float sum = 0.f;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) xreg[st][u] = c < nchunk ? xs[c * 16 + u] : 0.f;
-            xcr[st] = c < nchunk ? xc[c] : 0.f;
+            for (int u = 0; u < 8; ++u) {
+                xreg[st][2 * u] = lo16_to_float<BF16>(w8[u]);
+                xreg[st][2 * u + 1] = hi16_to_float<BF16>(w8[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sum += xreg[st][u];
+            xcr[st] = sum;
         }
     }
+    constexpr int kURows = urows<BITS>();
     const int j0 = (blockIdx.x * (kUThreads / 64) + wave) * kURows;
     // the next row's codes are loaded while the current one is computed
     Chunk<BITS> ch[kUMaxSteps], chn[kUMaxSteps];
@@ -282,11 +304,15 @@ hipError_t launch_expert_bits(const BitsArgs &a, hipStream_t s)
     const void *ga = nc == 1 ? gatherb_for<1>(a.bf16) : nc == 2 ? gatherb_for<2>(a.bf16)
                    : nc == 4 ? gatherb_for<4>(a.bf16) : nc == 8 ? gatherb_for<8>(a.bf16) : nullptr;
     if (!up || !ga || a.d % 512 != 0 || a.d / 16 > 64 * kUMaxSteps) return hipErrorInvalidValue;
-    const size_t lds_up = bits_lds_up(a.T, a.d);
+    const size_t lds_up = one ? 0 : bits_lds_up(a.T, a.d);
     if (lds_up > kBitsMaxLds) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute(up, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_up);
-    if (e != hipSuccess) return e;
-    const int rows_per_block = (kUThreads / 64) * kURows;
+    hipError_t e = hipSuccess;
+    if (lds_up > 0) {
+        e = hipFuncSetAttribute(up, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_up);
+        if (e != hipSuccess) return e;
+    }
+    const int rows_per_block =
+        (kUThreads / 64) * (a.bits == 8 ? urows<8>() : a.bits == 4 ? urows<4>() : urows<1>());
     void *args[] = {(void *)&a};
     e = hipLaunchKernel(up, dim3((a.f + rows_per_block - 1) / rows_per_block), dim3(kUThreads),
                         args, lds_up, s);
