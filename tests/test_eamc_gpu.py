@@ -175,3 +175,27 @@ def test_layer_eam_row_accumulates_request_counts():
         oracle.ream_add(acc, 1, oracle.route_topk(x_bits, "f16", R_bits, "f16", E, k)["expert_count"])
     assert np.array_equal(acc[1], row.cpu().numpy())
     say(f"rEAM row after the request: {row.cpu().numpy().tolist()}")
+
+
+def test_layer_eam_row_on_dense_and_auto_paths():
+    """The row is added by the grouping step, which every path shares: a bf16
+    layer run on the dense MFMA path and then through AUTO (which picks dense
+    here) accumulates the routed counts of both calls."""
+    from test_parity_layer_gpu import build_host_layer, device_layer
+    T, E, S, k, d, f = 40, 4, 1, 2, 512, 256
+    experts, thr = build_host_layer(72, E, S, d, f, "bf16", 0.7, 1 / 16, layer=1)
+    R_bits = synth.to_bf16_bits(synth.router_f32(72, 1, E, d, std=0.5))
+    L = device_layer(experts, thr, R_bits, "bf16", E, S, k, dense=True)
+    row = torch.full((E,), 5, dtype=torch.int32, device=DEV)
+    want = np.full(E, 5, dtype=np.int64)
+    for step, path in enumerate([moe.PATH_DENSE, moe.PATH_AUTO]):
+        x_bits = synth.to_bf16_bits(synth.tokens_f32(73 + step, T, d, 1.0, layer=1))
+        tr = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=DEV), eam_row=row)
+        moe.layer_forward(L, to_dev_bits(x_bits, "bf16"), path=path, trace=tr)
+        torch.cuda.synchronize()
+        idx = tr["topk_idx"].cpu().numpy()
+        ref = oracle.route_topk(x_bits, "bf16", R_bits, "bf16", E, k)
+        assert np.array_equal(idx, ref["topk_idx"]), f"path {path}: routing"
+        want += np.bincount(idx.ravel(), minlength=E)
+        got = row.cpu().numpy()
+        assert np.array_equal(got, want), f"path {path}: {got} != {want}"
