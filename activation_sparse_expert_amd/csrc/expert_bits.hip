@@ -6,12 +6,12 @@
 //
 // Two kernels and the shared reduce:
 //  * upb_kernel: v = x W^up and the mask |v| > t.  The tokens' x is staged in
-//    LDS as fp32 with per-16-input sums (one token: each lane reads its own
-//    chunks into registers instead, as it always takes the same ones, and no
-//    LDS is used); every wave streams 8 rows of codes (4 below 8 bits), the
-//    next row's loads in flight while one is computed, a lane taking 16 codes
-//    (2*bits bytes) per step and adding s (sum q x - z sum x) per 16-code
-//    chunk.  v goes to memory.
+//    LDS as fp32, input 16 c + u at row u, column c, with per-16-input sums
+//    (one token: each lane reads its own chunks into registers instead, as it
+//    always takes the same ones, and no LDS is used); every wave streams 8
+//    rows of codes (4 below 8 bits), the next row's loads in flight while one
+//    is computed, a lane taking 16 codes (2*bits bytes) per step and adding
+//    s (sum q x - z sum x) per 16-code chunk.  v goes to memory.
 //  * gatherb_kernel: one workgroup per 64 channels.  For each token the
 //    active channels of the tile are ranked (ballots in channel order) and
 //    shared out by rank over the 4 waves; a wave loads its channel's gate and
@@ -71,26 +71,33 @@ template <int BITS, bool BF16, bool ONE>
 __global__ void __launch_bounds__(kUThreads)
 upb_kernel(BitsArgs a)
 {
-    extern __shared__ __align__(16) float xs[];      // [T][d] x, then [T][d/16] chunk sums
+    // several tokens: x staged as xs[t][u][c] = x[t][16 c + u] (fp32), so that
+    // consecutive lanes (consecutive chunks c) read consecutive words, then
+    // the chunk sums xc[t][c]; one token needs no staging: each lane reads its
+    // own chunks below
+    extern __shared__ __align__(16) float xs[];
     const int d = a.d, T = a.T, nchunk = d / 16;
     float *xc = xs + (size_t)T * d;
-    // 8 inputs per 16-byte load (d % 512 == 0, x 16-byte aligned); one token
-    // needs no staging: each lane reads its own chunks below
     for (int i = threadIdx.x; !ONE && i < T * d / 8; i += kUThreads) {
+        // 8 inputs per 16-byte load (d % 512 == 0, x 16-byte aligned)
         const uint4 w = *(const uint4 *)(a.x + 8 * (size_t)i);
         const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
-        float4 *o = (float4 *)(xs + 8 * (size_t)i);
-        o[0] = make_float4(lo16_to_float<BF16>(w4[0]), hi16_to_float<BF16>(w4[0]),
-                           lo16_to_float<BF16>(w4[1]), hi16_to_float<BF16>(w4[1]));
-        o[1] = make_float4(lo16_to_float<BF16>(w4[2]), hi16_to_float<BF16>(w4[2]),
-                           lo16_to_float<BF16>(w4[3]), hi16_to_float<BF16>(w4[3]));
+        const int t = (8 * i) / d, k0 = 8 * i - t * d;
+        const int c = k0 / 16, u0 = k0 % 16;
+        float *o = xs + (size_t)t * d + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o[(size_t)(u0 + 2 * q) * nchunk] = lo16_to_float<BF16>(w4[q]);
+            o[(size_t)(u0 + 2 * q + 1) * nchunk] = hi16_to_float<BF16>(w4[q]);
+        }
     }
     if constexpr (!ONE) {
         __syncthreads();
         for (int i = threadIdx.x; i < T * nchunk; i += kUThreads) {
-            const float *p = xs + (size_t)i * 16;     // chunk i of the flattened [T][d]
+            const int t = i / nchunk, c = i - t * nchunk;
+            const float *p = xs + (size_t)t * d + c;
             float s = 0.f;
-            for (int u = 0; u < 16; ++u) s += p[u];
+            for (int u = 0; u < 16; ++u) s += p[(size_t)u * nchunk];
             xc[i] = s;
         }
         __syncthreads();
@@ -152,11 +159,12 @@ upb_kernel(BitsArgs a)
             for (int st = 0; st < kUMaxSteps; ++st) {
                 const int c = lane + 64 * st;
                 if (c < nchunk) {
-                    const float *xp = xs + (size_t)t * d + (size_t)c * 16;
+                    const float *xp = xs + (size_t)t * d + c;
                     float dq = 0.f;
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
-                        dq += (float)ch[st].code(u) * (ONE ? xreg[ONE ? st : 0][u] : xp[u]);
+                        dq += (float)ch[st].code(u) *
+                              (ONE ? xreg[ONE ? st : 0][u] : xp[(size_t)u * nchunk]);
                     const float s = half_bits_to_float(sz[st] & 0xFFFFu);
                     const float z = half_bits_to_float(sz[st] >> 16);
                     acc += s * (dq - z * (ONE ? xcr[ONE ? st : 0] : xc[t * nchunk + c]));
