@@ -9,9 +9,10 @@
 //    LDS as fp32, input 16 c + u at row u, column c, with per-16-input sums
 //    (one token: each lane reads its own chunks into registers instead, as it
 //    always takes the same ones, and no LDS is used); every wave streams 8
-//    rows of codes (4 below 8 bits), the next row's loads in flight while one
-//    is computed, a lane taking 16 codes (2*bits bytes) per step and adding
-//    s (sum q x - z sum x) per 16-code chunk.  v goes to memory.
+//    rows of codes (4 below 8 bits for one token), the next row's loads in
+//    flight while one is computed, a lane taking 16 codes (2*bits bytes) per
+//    step and adding s (sum q x - z sum x) per 16-code chunk.  v goes to
+//    memory.
 //  * gatherb_kernel: one workgroup per 64 channels.  For each token the
 //    active channels of the tile are ranked (ballots in channel order) and
 //    shared out by rank over the 4 waves; a wave loads its channel's gate and
@@ -28,9 +29,10 @@ namespace moeffn {
 namespace {
 
 constexpr int kUThreads = 256;
-// rows per wave: 8 at 8 bits, 4 below (measured best on the Mixtral shape)
-template <int BITS>
-__host__ __device__ constexpr int urows() { return BITS == 8 ? 8 : 4; }
+// rows per wave: 8 at 8 bits or with several tokens (each workgroup stages
+// their x), 4 for one token below 8 bits (measured on the Mixtral shape)
+template <int BITS, bool ONE>
+__host__ __device__ constexpr int urows() { return BITS == 8 || !ONE ? 8 : 4; }
 constexpr int kUMaxSteps = 4;           // 16-code chunks per lane per row: d <= 4096
 constexpr int kGThreads = 256;
 
@@ -131,7 +133,7 @@ upb_kernel(BitsArgs a)
             xcr[st] = sum;
         }
     }
-    constexpr int kURows = urows<BITS>();
+    constexpr int kURows = urows<BITS, ONE>();
     const int j0 = (blockIdx.x * (kUThreads / 64) + wave) * kURows;
     // the next row's codes are loaded while the current one is computed
     Chunk<BITS> ch[kUMaxSteps], chn[kUMaxSteps];
@@ -319,8 +321,8 @@ hipError_t launch_expert_bits(const BitsArgs &a, hipStream_t s)
         e = hipFuncSetAttribute(up, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_up);
         if (e != hipSuccess) return e;
     }
-    const int rows_per_block =
-        (kUThreads / 64) * (a.bits == 8 ? urows<8>() : a.bits == 4 ? urows<4>() : urows<1>());
+    const int urows_run = !one ? urows<8, false>() : a.bits == 8 ? urows<8, true>() : urows<4, true>();
+    const int rows_per_block = (kUThreads / 64) * urows_run;   // urows<1, .> equals urows<4, .>
     void *args[] = {(void *)&a};
     e = hipLaunchKernel(up, dim3((a.f + rows_per_block - 1) / rows_per_block), dim3(kUThreads),
                         args, lds_up, s);
