@@ -396,10 +396,28 @@ def bits_measure(sparsity=0.9):
             moe.expert_forward_sparse_bits(ex, bits, xs[t:t + 1], y=y, ws=ws)
         sec = time_graph(call, reps=10, inner=64)
         nbytes = d * f * bits / 8 + f * (d // 64) * 4 + 2 * act * d * 2 + d * 2
+        # four tokens per call (x staged in LDS); rows of the union of the masks
+        y4 = torch.empty((4, d), dtype=torch.float32, device=dev)
+        ws4 = moe.new_workspace(moe.workspace_size(moe.OP_EXPERT_BITS, 4, d, f), dev)
+        m4 = torch.empty((4, f), dtype=torch.uint8, device=dev)
+        uni = 0
+        for t in range(0, 64, 4):
+            moe.expert_forward_sparse_bits(ex, bits, xs[t:t + 4], y=y4, mask_out=m4, ws=ws4)
+            uni += int(m4.any(dim=0).sum().item())
+        uni /= 16
+
+        def call4():
+            t = (ci[0] % 16) * 4
+            ci[0] += 1
+            moe.expert_forward_sparse_bits(ex, bits, xs[t:t + 4], y=y4, ws=ws4)
+        sec4 = time_graph(call4, reps=10, inner=32)
         res[f"int{bits}"] = {"us_per_call": sec * 1e6, "tokens_per_s": 1 / sec,
                              "active_channels": act, "bytes_per_call": nbytes,
                              "achieved_gbs": nbytes / sec / 1e9,
-                             "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS}
+                             "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                             "batch4_us_per_call": sec4 * 1e6,
+                             "batch4_tokens_per_s": 4 / sec4,
+                             "batch4_union_channels": uni}
         del up_q, up_sz, ex
     res["workload"] = ("one Mixtral-8x7B-shaped expert (d=4096, f=14336), up codes at 8/4/1 bits, "
                        "90% sparsity, batch 1")
