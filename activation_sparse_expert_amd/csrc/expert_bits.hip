@@ -9,10 +9,10 @@
 //    LDS as fp32, input 16 c + u at row u, column c, with per-16-input sums
 //    (one token: each lane reads its own chunks into registers instead, as it
 //    always takes the same ones, and no LDS is used); every wave streams 8
-//    rows of codes (4 below 8 bits for one token), the next row's loads in
-//    flight while one is computed, a lane taking 16 codes (2*bits bytes) per
-//    step and adding s (sum q x - z sum x) per 16-code chunk.  v goes to
-//    memory.
+//    rows of codes (4 below 8 bits for one token), the loads of the rows up to
+//    3 ahead in flight while one is computed, a lane taking 16 codes
+//    (2*bits bytes) per step and adding s (sum q x - z sum x) per 16-code
+//    chunk.  v goes to memory.
 //  * gatherb_kernel: one workgroup per 64 channels.  For each token the
 //    active channels of the tile are ranked (ballots in channel order) and
 //    shared out by rank over the 4 waves; a wave loads its channel's gate and
@@ -35,6 +35,7 @@ template <int BITS, bool ONE>
 __host__ __device__ constexpr int urows() { return BITS == 8 || !ONE ? 8 : 4; }
 constexpr int kUMaxSteps = 4;           // 16-code chunks per lane per row: d <= 4096
 constexpr int kGThreads = 256;
+constexpr int kUAhead = 3;              // rows of codes in flight ahead of the one computed
 
 template <int BITS>
 struct Chunk;                           // 16 codes of one lane
@@ -135,26 +136,29 @@ upb_kernel(BitsArgs a)
     }
     constexpr int kURows = urows<BITS, ONE>();
     const int j0 = (blockIdx.x * (kUThreads / 64) + wave) * kURows;
-    // the next row's codes are loaded while the current one is computed
-    Chunk<BITS> ch[kUMaxSteps], chn[kUMaxSteps];
-    uint32_t sz[kUMaxSteps], szn[kUMaxSteps];
-    auto load_row = [&](int j, Chunk<BITS> (&c_)[kUMaxSteps], uint32_t (&s_)[kUMaxSteps]) {
+    // f % 64 == 0 and a workgroup takes 16 or 32 rows: all of a wave's rows
+    // exist once its first does (no barrier follows)
+    if (j0 >= a.f) return;
+    // the row loop is unrolled; row r + kUAhead's codes are loaded while row r
+    // is computed (the buffers of a row live from its load to its use)
+    Chunk<BITS> ch[kURows][kUMaxSteps];
+    uint32_t sz[kURows][kUMaxSteps];
+    auto load_row = [&](int r) {
 #pragma unroll
         for (int st = 0; st < kUMaxSteps; ++st) {
             const int c = lane + 64 * st;
             if (c < nchunk) {
-                c_[st].load(a.up_q + (size_t)j * row_bytes + (size_t)c * 2 * BITS);
-                s_[st] = load_nt4(a.up_sz + ((size_t)j * G + c / 4) * 2);
+                ch[r][st].load(a.up_q + (size_t)(j0 + r) * row_bytes + (size_t)c * 2 * BITS);
+                sz[r][st] = load_nt4(a.up_sz + ((size_t)(j0 + r) * G + c / 4) * 2);
             }
         }
     };
-    if (j0 < a.f) load_row(j0, chn, szn);
+#pragma unroll
+    for (int r = 0; r < kUAhead && r < kURows; ++r) load_row(r);
+#pragma unroll
     for (int r = 0; r < kURows; ++r) {
         const int j = j0 + r;
-        if (j >= a.f) break;                      // wave-uniform
-#pragma unroll
-        for (int st = 0; st < kUMaxSteps; ++st) { ch[st] = chn[st]; sz[st] = szn[st]; }
-        if (r + 1 < kURows && j + 1 < a.f) load_row(j + 1, chn, szn);
+        if (r + kUAhead < kURows) load_row(r + kUAhead);
         for (int t = 0; t < T; ++t) {
             float acc = 0.f;
 #pragma unroll
@@ -165,10 +169,10 @@ upb_kernel(BitsArgs a)
                     float dq = 0.f;
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
-                        dq += (float)ch[st].code(u) *
+                        dq += (float)ch[r][st].code(u) *
                               (ONE ? xreg[ONE ? st : 0][u] : xp[(size_t)u * nchunk]);
-                    const float s = half_bits_to_float(sz[st] & 0xFFFFu);
-                    const float z = half_bits_to_float(sz[st] >> 16);
+                    const float s = half_bits_to_float(sz[r][st] & 0xFFFFu);
+                    const float z = half_bits_to_float(sz[r][st] >> 16);
                     acc += s * (dq - z * (ONE ? xcr[ONE ? st : 0] : xc[t * nchunk + c]));
                 }
             }
