@@ -488,6 +488,8 @@ def main():
                     help="skip the layer workloads (32-layer stack, fine-grained layer)")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched-layer (dense MFMA vs sparse) measurement")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="only the 8/4/1-bit expert and EAMC measurements (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run the known-size elementwise kernel (counter scaling)")
     args = ap.parse_args()
@@ -501,6 +503,10 @@ def main():
         return
     if args.batched_only:
         print(json.dumps({"batched": batched_measure()}), flush=True)
+        return
+    if args.variants_only:
+        print(json.dumps({"expert_up_bits": bits_measure(), "eamc_match": eamc_measure()}),
+              flush=True)
         return
 
     import torch
