@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_workspace_size", "moe_workspace_init", "moe_pack_up_int2",
             "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold",
-            "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits"]
+            "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits",
+            "moe_build_sources_sha256"]
 
 
 class MoeError(RuntimeError):
@@ -48,25 +49,35 @@ class LayerDesc(C.Structure):
 
 class LayerTrace(C.Structure):
     _fields_ = [("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("logits", C.c_void_p),
-                ("expert_count", C.c_void_p), ("masks", C.c_void_p), ("eam_row", C.c_void_p)]
+                ("expert_count", C.c_void_p), ("masks", C.c_void_p), ("eam_row", C.c_void_p),
+                ("mask_bits", C.c_void_p), ("nnz", C.c_void_p)]
 
 
 _lib = None
 
 
 def lib():
-    """The loaded libmoeffn (raises if it has not been built)."""
+    """The loaded libmoeffn.  Raises if it has not been built, or if it was
+    built from other sources than the ones in csrc/ (a stale binary)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libmoeffn.so not built ({LIB_PATH}); run __graft_entry__.build()")
+        from .build import sources_sha256
         L = C.CDLL(LIB_PATH)
+        L.moe_build_sources_sha256.restype = C.c_char_p
+        L.moe_build_sources_sha256.argtypes = []
+        built = L.moe_build_sources_sha256().decode()
+        want = sources_sha256()
+        if built != want:
+            raise RuntimeError(f"libmoeffn.so is stale: built from sources {built[:16]}..., "
+                               f"csrc/ now hashes to {want[:16]}...; run __graft_entry__.build()")
         P, I, Z = C.c_void_p, C.c_int, C.c_size_t
         L.moe_route_topk.restype = I
         L.moe_route_topk.argtypes = [P, I, I, I, P, I, P, I, I, I, P, P, P, P, P, P, P, Z, P]
         L.moe_expert_forward_sparse.restype = I
         L.moe_expert_forward_sparse.argtypes = [C.POINTER(ExpertView), I, I, I, P, I, I, P, I,
-                                                P, I, P, P, P, Z, P]
+                                                P, I, P, P, P, P, P, Z, P]
         L.moe_layer_forward.restype = I
         L.moe_layer_forward.argtypes = [C.POINTER(LayerDesc), P, I, I, P, I, I,
                                         C.POINTER(LayerTrace), P, Z, P]
@@ -84,7 +95,7 @@ def lib():
         L.moe_calibrate_threshold.argtypes = [P, C.c_longlong, C.c_double, P, P, Z, P]
         L.moe_expert_forward_sparse_bits.restype = I
         L.moe_expert_forward_sparse_bits.argtypes = [C.POINTER(ExpertView), I, I, I, I, P, I, I,
-                                                     P, I, P, I, P, P, P, Z, P]
+                                                     P, I, P, I, P, P, P, P, P, Z, P]
         L.moe_pack_up_bits.restype = I
         L.moe_pack_up_bits.argtypes = [P, I, I, I, I, P, P, P]
         L.moe_eamc_match.restype = I
@@ -157,8 +168,12 @@ class Expert:
 
 
 def expert_forward_sparse(expert: Expert, x, *, y=None, out_dtype=None, token_scale=None,
-                          accumulate: bool = False, mask_out=None, v_out=None, ws=None):
-    """Algorithm 1 of the FloE review on x [T][d]; returns y [T][d]."""
+                          accumulate: bool = False, mask_out=None, v_out=None, mask_bits=None,
+                          nnz=None, ws=None):
+    """Algorithm 1 of the FloE review on x [T][d]; returns y [T][d].
+
+    Optional exports: mask_out [T][f] uint8, v_out [T][f] fp32, mask_bits
+    [T][f/64] int64 (bit l of word i = channel 64 i + l), nnz [T] int32."""
     import torch
     T, d = x.shape
     if y is None:
@@ -168,15 +183,15 @@ def expert_forward_sparse(expert: Expert, x, *, y=None, out_dtype=None, token_sc
     v = expert.view()
     st = lib().moe_expert_forward_sparse(
         C.byref(v), d, expert.f, _dt(expert.gate_t), _ptr(x), _dt(x), T, _ptr(token_scale),
-        int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_out), _ptr(v_out), _ptr(ws),
-        ws.numel(), _stream())
+        int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_bits), _ptr(nnz), _ptr(mask_out),
+        _ptr(v_out), _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_expert_forward_sparse")
     return y
 
 
 def expert_forward_sparse_bits(expert: Expert, bits: int, x, *, y=None, out_dtype=None,
                                token_scale=None, accumulate: bool = False, mask_out=None,
-                               v_out=None, ws=None):
+                               v_out=None, mask_bits=None, nnz=None, ws=None):
     """Algorithm 1 with the up codes at ``bits`` (8, 4, 2 or 1) bits; y [T][d]."""
     import torch
     T, d = x.shape
@@ -187,8 +202,8 @@ def expert_forward_sparse_bits(expert: Expert, bits: int, x, *, y=None, out_dtyp
     v = expert.view()
     st = lib().moe_expert_forward_sparse_bits(
         C.byref(v), int(bits), d, expert.f, _dt(expert.gate_t), _ptr(x), _dt(x), T,
-        _ptr(token_scale), int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_out), _ptr(v_out),
-        _ptr(ws), ws.numel(), _stream())
+        _ptr(token_scale), int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_bits), _ptr(nnz),
+        _ptr(mask_out), _ptr(v_out), _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_expert_forward_sparse_bits")
     return y
 
@@ -250,9 +265,10 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
                   trace: Optional[dict] = None, ws=None):
     """Route and combine one layer on x [T][d]; returns y [T][d].
 
-    ``trace`` may map any of topk_idx, topk_w, logits, expert_count, masks to
-    preallocated device tensors that receive those exports, and eam_row to an
-    int32 [E] device tensor that the call's per-expert counts are added into."""
+    ``trace`` may map any of topk_idx, topk_w, logits, expert_count, masks,
+    mask_bits, nnz to preallocated device tensors that receive those exports,
+    and eam_row to an int32 [E] device tensor that the call's per-expert counts
+    are added into."""
     import torch
     T, d = x.shape
     if y is None:
@@ -263,7 +279,8 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
     if trace:
         tr = LayerTrace(_ptr(trace.get("topk_idx")), _ptr(trace.get("topk_w")),
                         _ptr(trace.get("logits")), _ptr(trace.get("expert_count")),
-                        _ptr(trace.get("masks")), _ptr(trace.get("eam_row")))
+                        _ptr(trace.get("masks")), _ptr(trace.get("eam_row")),
+                        _ptr(trace.get("mask_bits")), _ptr(trace.get("nnz")))
     desc = layer.desc()
     st = lib().moe_layer_forward(C.byref(desc), _ptr(x), _dt(x), T, _ptr(y), _dt(y), path,
                                  C.byref(tr) if tr is not None else None, _ptr(ws), ws.numel(),

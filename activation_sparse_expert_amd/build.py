@@ -1,6 +1,7 @@
 """Build libmoeffn.so (hipcc, gfx950) in-tree."""
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -14,6 +15,8 @@ SOURCES = ["api.cpp", "expert_sparse_f16.hip", "expert_sparse_bf16.hip", "reduce
            "pack.hip", "dense_mfma.hip", "calibrate.hip",
            "eamc.hip", "expert_bits.hip"]
 
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moeffn.h")
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
@@ -23,9 +26,25 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def sources_sha256() -> str:
+    """SHA-256 over every file of csrc/ and the public header, in name order.
+    The library carries it (moe_build_sources_sha256) so that the binding can
+    refuse a binary built from other sources."""
+    h = hashlib.sha256()
+    names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".hpp", ".cpp", ".h")))
+    for n in names:
+        h.update(n.encode())
+        with open(os.path.join(CSRC, n), "rb") as fh:
+            h.update(fh.read())
+    with open(HEADER, "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()
+
+
+def _compile(src: str, sha: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, f'-DMOE_SOURCES_SHA256="{sha}"', "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -34,8 +53,9 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    sha = sources_sha256()
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, sha), SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -108,17 +108,23 @@ SparsePlan layer_plan(int T, int d, int f, int E, int k, int S)
     return SparsePlan{tb, (int)bound, plan_tiles(f, (int)expect, (long long)T * (k + S), d)};
 }
 
-size_t bits_ws_bytes(int T, int d, int f)
+// Byte masks staged for the bitmask / nnz exports when the caller asks for
+// those but not for the byte masks themselves: T f bytes after the rest.
+size_t bits_ws_core(int T, int d, int f)
 {
     const size_t tiles = (size_t)(f + kBitsTile - 1) / kBitsTile;
     return up((size_t)T * f * 4) + up((size_t)T * tiles * d * 4);
 }
 
-size_t expert_ws_bytes(int T, int d, int f)
+size_t bits_ws_bytes(int T, int d, int f) { return bits_ws_core(T, d, f) + up((size_t)T * f); }
+
+size_t expert_ws_core(int T, int d, int f)
 {
     const TilePlan tp = expert_plan(T, d, f).tp;
     return up((size_t)T * tp.tiles * d * 4);
 }
+
+size_t expert_ws_bytes(int T, int d, int f) { return expert_ws_core(T, d, f) + up((size_t)T * f); }
 
 struct LayerWs {
     int32_t *topk_idx;
@@ -129,6 +135,7 @@ struct LayerWs {
     float *h;
     float *lg;              // [T][E] router logits (wide-router split)
     int32_t *chunk_rec;     // [T*k][4] single-token chunk records
+    uint8_t *masks;         // [T][k+S][f] byte masks staged for the bitmask / nnz exports
 };
 
 size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, void *base)
@@ -137,7 +144,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     const TilePlan tp = layer_plan(T, d, f, E, k, S).tp;
     const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
     size_t o = 0;
-    size_t off[14];
+    size_t off[15];
     off[0] = o; o += up(4);
     off[1] = o; o += up((size_t)T * k * 4);
     off[2] = o; o += up((size_t)T * k * 4);
@@ -152,6 +159,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     off[11] = o; o += up(4);
     off[12] = o; o += up((size_t)T * E * 4);
     off[13] = o; o += up((size_t)T * k * 16);
+    off[14] = o; o += up((size_t)rows * f);
     if (out) {
         char *p = (char *)base;
         out->topk_idx = (int32_t *)(p + off[1]);
@@ -167,6 +175,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->n_chunks = (int32_t *)(p + off[11]);
         out->lg = (float *)(p + off[12]);
         out->chunk_rec = (int32_t *)(p + off[13]);
+        out->masks = (uint8_t *)(p + off[14]);
     }
     return o;
 }
@@ -212,6 +221,12 @@ moe_status check_weight_ptrs(const uint8_t *q, const uint16_t *sz, const void *g
 }  // namespace
 
 extern "C" {
+
+#ifndef MOE_SOURCES_SHA256
+#define MOE_SOURCES_SHA256 "unknown"
+#endif
+
+const char *moe_build_sources_sha256(void) { return MOE_SOURCES_SHA256; }
 
 const char *moe_status_string(moe_status s)
 {
@@ -320,7 +335,8 @@ moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void
 moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe_dtype wdt,
                                      const void *x, moe_dtype xdt, int T,
                                      const float *token_scale, int accumulate, void *y,
-                                     moe_dtype ydt, uint8_t *mask_out, float *v_out, void *ws,
+                                     moe_dtype ydt, uint64_t *mask_bits, int32_t *nnz_out,
+                                     uint8_t *mask_out, float *v_out, void *ws,
                                      size_t ws_bytes, void *stream)
 {
     if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
@@ -329,12 +345,15 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
     if (st != MOE_OK) return st;
     if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||
-        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)))
+        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)) ||
+        (mask_bits && !aligned(mask_bits, 8)) || (nnz_out && !aligned(nnz_out, 4)))
         return MOE_ERR_ALIGNMENT;
     if (!ws || ws_bytes < expert_ws_bytes(T, d, f)) return MOE_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
 
     hipStream_t s = (hipStream_t)stream;
+    const bool want_bits = mask_bits || nnz_out;
+    if (want_bits && !mask_out) mask_out = (uint8_t *)ws + expert_ws_core(T, d, f);
     const SparsePlan sp = expert_plan(T, d, f);
     const TilePlan tp = sp.tp;
     SparseArgs a{};
@@ -357,18 +376,21 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     r.part = (const float *)ws; r.tiles = tp.tiles; r.d = d; r.T = T;
     r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0;
     r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
-    return hip_status(launch_reduce(r, s));
+    he = launch_reduce(r, s);
+    if (he == hipSuccess && want_bits) he = launch_mask_bits(mask_out, T, f, mask_bits, nnz_out, s);
+    return hip_status(he);
 }
 
 moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, int d, int f,
                                           moe_dtype wdt, const void *x, moe_dtype xdt, int T,
                                           const float *token_scale, int accumulate, void *y,
-                                          moe_dtype ydt, uint8_t *mask_out, float *v_out,
+                                          moe_dtype ydt, uint64_t *mask_bits, int32_t *nnz_out,
+                                          uint8_t *mask_out, float *v_out,
                                           void *ws, size_t ws_bytes, void *stream)
 {
     if (bits == 2)
         return moe_expert_forward_sparse(e, d, f, wdt, x, xdt, T, token_scale, accumulate, y, ydt,
-                                         mask_out, v_out, ws, ws_bytes, stream);
+                                         mask_bits, nnz_out, mask_out, v_out, ws, ws_bytes, stream);
     if (bits != 1 && bits != 4 && bits != 8) return MOE_ERR_INVALID_ARG;
     if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
     moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
@@ -379,11 +401,14 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
     st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
     if (st != MOE_OK) return st;
     if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||
-        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)))
+        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)) ||
+        (mask_bits && !aligned(mask_bits, 8)) || (nnz_out && !aligned(nnz_out, 4)))
         return MOE_ERR_ALIGNMENT;
     if (!ws || ws_bytes < bits_ws_bytes(T, d, f)) return MOE_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
+    const bool want_bits = mask_bits || nnz_out;
+    if (want_bits && !mask_out) mask_out = (uint8_t *)ws + bits_ws_core(T, d, f);
     BitsArgs a{};
     a.up_q = e->up_q; a.up_sz = e->up_sz;
     a.gate = (const uint16_t *)e->gate_t; a.down = (const uint16_t *)e->down;
@@ -400,7 +425,9 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
     r.part = a.part; r.tiles = a.tiles; r.d = d; r.T = T;
     r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0;
     r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
-    return hip_status(launch_reduce(r, s));
+    he = launch_reduce(r, s);
+    if (he == hipSuccess && want_bits) he = launch_mask_bits(mask_out, T, f, mask_bits, nnz_out, s);
+    return hip_status(he);
 }
 
 moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, int T, void *y,
@@ -424,15 +451,19 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         return MOE_ERR_INVALID_ARG;
     if (path == MOE_PATH_AUTO) {
         const bool dense_ok = L->wdt == MOE_BF16 && L->up_dense && aligned(L->up_dense, 16) &&
-                              !(trace && trace->masks) && f % 256 == 0 && d % 128 == 0;
+                              !(trace && (trace->masks || trace->mask_bits || trace->nnz)) &&
+                              f % 256 == 0 && d % 128 == 0;
         path = dense_ok && (long long)T * k >= 8ll * E ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
     }
     if (path == MOE_PATH_DENSE) {
         if (L->wdt != MOE_BF16 || !L->up_dense) return MOE_ERR_UNSUPPORTED;
         if (!aligned(L->up_dense, 16)) return MOE_ERR_ALIGNMENT;
-        if (trace && trace->masks) return MOE_ERR_UNSUPPORTED;
+        if (trace && (trace->masks || trace->mask_bits || trace->nnz)) return MOE_ERR_UNSUPPORTED;
         if (f % 256 != 0 || d % 128 != 0) return MOE_ERR_UNSUPPORTED;
     }
+    if (trace && ((trace->mask_bits && !aligned(trace->mask_bits, 8)) ||
+                  (trace->nnz && !aligned(trace->nnz, 4))))
+        return MOE_ERR_ALIGNMENT;
     if (!ws || ws_bytes < layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr))
         return MOE_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
@@ -498,11 +529,16 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     a.offset = w.offset; a.pairs = w.pairs;
     a.topk_w = r.topk_w;
     a.part = w.part;
+    const bool want_bits = trace && (trace->mask_bits || trace->nnz);
     a.mask_out = trace ? trace->masks : nullptr; a.v_out = nullptr;
+    if (want_bits && !a.mask_out) a.mask_out = w.masks;
     he = launch_sparse(a, L->wdt == MOE_BF16, sp.tb, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
     red.tiles = tp.tiles;
-    return hip_status(launch_reduce(red, s));
+    he = launch_reduce(red, s);
+    if (he == hipSuccess && want_bits)
+        he = launch_mask_bits(a.mask_out, T * (k + S), f, trace->mask_bits, trace->nnz, s);
+    return hip_status(he);
 }
 
 moe_status moe_pack_up_int2(const void *w_up_t, moe_dtype dt, int d, int f, uint8_t *up_q,

@@ -100,6 +100,11 @@ hipError_t launch_pack_int2(const void *w, int dt, int d, int f, uint8_t *q, uin
 hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, int f,
                                    uint16_t *out, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+// Bitmask and population count of `rows` 0/1 byte masks of f channels (f % 64
+// == 0): bits [rows][f/64] (channel 64 i + l at bit l of word i) and nnz [rows];
+// either may be null.
+hipError_t launch_mask_bits(const uint8_t *m, int rows, int f, uint64_t *bits, int32_t *nnz,
+                            hipStream_t s);
 
 // Threshold calibration: out = linear-interpolation quantile of |v| between
 // order statistics r_lo and r_hi with weight gamma (computed on the host).

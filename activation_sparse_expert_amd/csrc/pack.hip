@@ -186,6 +186,48 @@ hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, 
     return hipGetLastError();
 }
 
+namespace {
+
+// Bit form of 0/1 channel masks (FloE review, "高效稀疏 GEMV 内核": the mask of
+// Algorithm 1 as a bitmask, and its population count).  One workgroup per row
+// of f channels: wave w packs the 64-channel words w, w + 4, ... by a ballot
+// (channel 64 i + l at bit l of word i) and counts them; the four wave counts
+// are added in LDS.  Integer work, no atomics.
+constexpr int kPackThreads = 256;
+
+__global__ void __launch_bounds__(kPackThreads)
+mask_bits_kernel(const uint8_t *m, int f, uint64_t *bits, int32_t *nnz)
+{
+    __shared__ int cnt[kPackThreads / 64];
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int words = f / 64;
+    const uint8_t *src = m + (size_t)row * f;
+    int n = 0;
+    for (int wi = wave; wi < words; wi += kPackThreads / 64) {
+        const uint64_t b = __ballot(src[(size_t)wi * 64 + lane] != 0);
+        if (bits && lane == 0) bits[(size_t)row * words + wi] = b;
+        n += __popcll(b);
+    }
+    if (lane == 0) cnt[wave] = n;
+    __syncthreads();
+    if (threadIdx.x == 0 && nnz) {
+        int t = 0;
+        for (int w = 0; w < kPackThreads / 64; ++w) t += cnt[w];
+        nnz[row] = t;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mask_bits(const uint8_t *m, int rows, int f, uint64_t *bits, int32_t *nnz,
+                            hipStream_t s)
+{
+    if (rows < 1 || f % 64 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mask_bits_kernel, dim3(rows), dim3(kPackThreads), 0, s, m, f, bits, nnz);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s)
 {
     const size_t n = bytes / 4;

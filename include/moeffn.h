@@ -143,6 +143,11 @@ typedef struct {
                                    are ADDED into it, so a row kept across the
                                    calls of a request accumulates the request-
                                    level EAM (MoE-Infinity review, "4.3")     */
+    uint64_t *mask_bits;        /* [T][k+S][f/64] the masks of `masks` as bits:
+                                   channel 64 i + l at bit l of word i (sparse
+                                   path only)                                */
+    int32_t *nnz;               /* [T][k+S] active channels per mask (sparse
+                                   path only)                                */
 } moe_layer_trace;
 
 /*
@@ -173,12 +178,20 @@ moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d,
  *   h = SiLU(x gate_t[mask]^T) * v[mask], y_t = token_scale_t * h W^down[mask].
  *   x [T][d] in xdt (must equal wdt), y [T][d] in ydt (f16/bf16/f32);
  *   token_scale [T] fp32 or NULL (= 1); accumulate != 0 adds into y.
- * Optional exports: mask_out [T][f] uint8 0/1, v_out [T][f] fp32.
+ * Optional exports (NULL = not wanted):
+ *   mask_bits [T][f/64] uint64, 8-byte aligned: the mask of line 2 of
+ *             Algorithm 1 as bits, channel 64 i + l at bit l of word i;
+ *   nnz_out   [T] int32: active channels per token;
+ *   mask_out  [T][f] uint8 0/1: the same mask, one byte per channel;
+ *   v_out     [T][f] fp32: v.
+ * The bitmask and nnz are formed from the byte mask by one more small kernel
+ * (staged in the workspace when mask_out is NULL).
  */
 moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe_dtype wdt,
                                      const void *x, moe_dtype xdt, int T,
                                      const float *token_scale, int accumulate,
                                      void *y, moe_dtype ydt,
+                                     uint64_t *mask_bits, int32_t *nnz_out,
                                      uint8_t *mask_out, float *v_out,
                                      void *ws, size_t ws_bytes, void *stream);
 
@@ -198,6 +211,7 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
                                           moe_dtype wdt, const void *x, moe_dtype xdt, int T,
                                           const float *token_scale, int accumulate,
                                           void *y, moe_dtype ydt,
+                                          uint64_t *mask_bits, int32_t *nnz_out,
                                           uint8_t *mask_out, float *v_out,
                                           void *ws, size_t ws_bytes, void *stream);
 
@@ -295,6 +309,11 @@ moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, i
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status s);
+
+/* Static string: SHA-256 (64 hex digits) of the sources this binary was built
+ * from (every file of csrc/ and this header, in name order), so that a binding
+ * can refuse a library that is older than its sources. */
+const char *moe_build_sources_sha256(void);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,54 @@ def say(*a):
     sys.stdout.flush()
 
 
+# ---------------------------------------------------------------------------
+# Canary-guarded device buffers: every output and workspace handed to the
+# library sits between two runs of canary bytes, checked after the call, so a
+# write past either end of a buffer fails the test.
+# ---------------------------------------------------------------------------
+CANARY = 0xA5
+GUARD = 4096            # bytes on each side (keeps every alignment the library asks for)
+
+
+class Guarded:
+    """A device tensor of `shape` and `dtype` inside a canary-filled buffer."""
+
+    def __init__(self, shape, dtype, fill=None):
+        shape = tuple(int(s) for s in shape)
+        esz = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) * esz
+        self.n = n
+        self.buf = torch.full((GUARD + n + GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+        self.t = self.buf[GUARD:GUARD + n].view(dtype).view(shape)
+        if fill is not None:
+            self.t.copy_(fill)
+
+    def check(self, what=""):
+        b = self.buf.cpu().numpy()
+        lo, hi = b[:GUARD], b[GUARD + self.n:]
+        assert (lo == CANARY).all(), f"{what}: {int((lo != CANARY).sum())} bytes written before the buffer"
+        assert (hi == CANARY).all(), f"{what}: {int((hi != CANARY).sum())} bytes written past the buffer"
+
+
+def guarded_workspace(nbytes):
+    """A workspace of exactly `nbytes` (the library's stated size) between canaries."""
+    return Guarded((nbytes,), torch.uint8, fill=None)
+
+
+def bits_of(mask_u8: np.ndarray) -> np.ndarray:
+    """[..][f] 0/1 bytes -> [..][f/64] uint64 words, channel 64 i + l at bit l of word i."""
+    m = np.ascontiguousarray(mask_u8 != 0)
+    packed = np.packbits(m, axis=-1, bitorder="little")          # 8 channels per byte
+    return packed.view(np.uint64) if packed.shape[-1] % 8 == 0 else None
+
+
+def check_bits_exports(mask_u8, bits_dev, nnz_dev, what=""):
+    """The bitmask and nnz exports are the byte mask in another form, bit for bit."""
+    b = bits_dev.cpu().numpy().view(np.uint64)
+    assert np.array_equal(b, bits_of(mask_u8)), f"{what}: bitmask differs from the byte mask"
+    assert np.array_equal(nnz_dev.cpu().numpy(), (mask_u8 != 0).sum(-1)), f"{what}: nnz"
+
+
 def to_dev_bits(bits: np.ndarray, dt: str):
     """uint16 bit patterns -> device tensor of dtype dt (same bytes)."""
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy())
@@ -138,16 +186,30 @@ def check_route(x_bits, xdt, R_bits, rdt, E, k, renorm, bias, out, what):
 
 
 def run_layer(L, x, path, want_masks=True):
+    """One layer call with every output, export and the workspace canary-
+    guarded; the bitmask and nnz exports are checked against the byte masks."""
     T = x.shape[0]
-    tr = dict(topk_idx=torch.empty((T, L.k), dtype=torch.int32, device=DEV),
-              topk_w=torch.empty((T, L.k), dtype=torch.float32, device=DEV),
-              logits=torch.empty((T, L.E), dtype=torch.float32, device=DEV),
-              expert_count=torch.empty(L.E, dtype=torch.int32, device=DEV))
-    if want_masks and path == moe.PATH_SPARSE:
-        tr["masks"] = torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=DEV)
-    y = moe.layer_forward(L, x, path=path, trace=tr)
+    g = dict(topk_idx=Guarded((T, L.k), torch.int32),
+             topk_w=Guarded((T, L.k), torch.float32),
+             logits=Guarded((T, L.E), torch.float32),
+             expert_count=Guarded((L.E,), torch.int32))
+    sparse = want_masks and path == moe.PATH_SPARSE
+    if sparse:
+        g["masks"] = Guarded((T, L.k + L.S, L.f), torch.uint8)
+        g["mask_bits"] = Guarded((T, L.k + L.S, L.f // 64), torch.int64)
+        g["nnz"] = Guarded((T, L.k + L.S), torch.int32)
+    y = Guarded((T, L.d), torch.float32)
+    ws = guarded_workspace(L.workspace_bytes(T))
+    moe.layer_forward(L, x, path=path, y=y.t, ws=ws.t, trace={k: v.t for k, v in g.items()})
     torch.cuda.synchronize()
-    return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in tr.items()}
+    for k, v in g.items():
+        v.check(f"layer export {k}")
+    y.check("layer y")
+    ws.check("layer workspace")
+    tr = {k: v.t.cpu().numpy() for k, v in g.items()}
+    if sparse:
+        check_bits_exports(tr["masks"], g["mask_bits"].t, g["nnz"].t, "layer masks")
+    return y.t.cpu().numpy(), tr
 
 
 # ---------------------------------------------------------------------------

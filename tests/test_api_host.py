@@ -73,11 +73,11 @@ def _view(**kw):
 
 
 def _expert(view=None, d=4096, f=14336, wdt=0, x=FAKE, xdt=0, T=1, y=FAKE, ydt=2, ws=FAKE,
-            ws_bytes=1 << 26, scale=None, v_out=None):
+            ws_bytes=1 << 26, scale=None, v_out=None, mask_bits=None, nnz=None):
     L = _lib_or_skip()
     v = view if view is not None else _view()
-    return L.moe_expert_forward_sparse(C.byref(v), d, f, wdt, x, xdt, T, scale, 0, y, ydt, None,
-                                       v_out, ws, ws_bytes, None)
+    return L.moe_expert_forward_sparse(C.byref(v), d, f, wdt, x, xdt, T, scale, 0, y, ydt,
+                                       mask_bits, nnz, None, v_out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -95,6 +95,9 @@ def _expert(view=None, d=4096, f=14336, wdt=0, x=FAKE, xdt=0, T=1, y=FAKE, ydt=2
     (dict(ws=None), -4),
     (dict(ws_bytes=1024), -4),
     (dict(ws=FAKE + 4), -3),
+    (dict(mask_bits=FAKE + 4), -3),     # the bitmask is 64-bit words
+    (dict(nnz=FAKE + 2), -3),
+    (dict(ws_bytes=4 * 4096 * 256), -4),    # partial rows only: no room for staged masks
 ])
 def test_expert_rejects(kw, code):
     assert _expert(**kw) == code
@@ -111,7 +114,7 @@ def test_expert_rejects_weight_pointers(field, val, code):
 def test_expert_null_view():
     L = _lib_or_skip()
     assert L.moe_expert_forward_sparse(None, 4096, 14336, 0, FAKE, 0, 1, None, 0, FAKE, 2, None,
-                                       None, FAKE, 1 << 20, None) == -1
+                                       None, None, None, FAKE, 1 << 20, None) == -1
 
 
 def _route(x=FAKE, xdt=0, T=4, d=4096, rw=FAKE, rdt=0, E=8, k=2, outs=True, ws=FAKE, ws_bytes=256):
@@ -170,6 +173,29 @@ def test_layer_dense_shape_limits():
     assert _layer(desc=d, xdt=1, path=1) == -2
 
 
+@pytest.mark.parametrize("field,val,path,code", [
+    ("mask_bits", FAKE, 1, -2),         # the dense path has no masks to export
+    ("nnz", FAKE, 1, -2),
+    ("masks", FAKE, 1, -2),
+    ("mask_bits", FAKE + 4, 0, -3),
+    ("nnz", FAKE + 2, 0, -3),
+])
+def test_layer_trace_exports_rejected(field, val, path, code):
+    L = _lib_or_skip()
+    dsc = _layer_desc(wdt=1, up_dense=FAKE)
+    tr = moe.LayerTrace(**{field: val})
+    assert L.moe_layer_forward(C.byref(dsc), FAKE, 1, 4, FAKE, 2, path, C.byref(tr), FAKE,
+                               1 << 30, None) == code
+
+
+def test_expert_workspace_holds_mask_staging():
+    _lib_or_skip()
+    # T f bytes of staged byte masks (for the bitmask / nnz exports) follow the
+    # partial rows
+    a = moe.workspace_size(moe.OP_EXPERT, 1, 4096, 14336)
+    assert a >= 4 * 4096 * 256 + 14336
+
+
 def test_pack_and_materialize_reject():
     L = _lib_or_skip()
     assert L.moe_pack_up_int2(None, 2, 4096, 8, FAKE, FAKE, None) == -1
@@ -225,12 +251,28 @@ def test_expert_bits_rejects(kw, code):
     v = _view()
     assert L.moe_expert_forward_sparse_bits(C.byref(v), a["bits"], a["d"], a["f"], a["wdt"],
                                             a["x"], a["wdt"], a["T"], None, 0, FAKE, 2, None,
-                                            None, a["ws"], a["ws_bytes"], None) == code
+                                            None, None, None, a["ws"], a["ws_bytes"],
+                                            None) == code
     assert L.moe_pack_up_bits(FAKE, 2, 4096, 8, 3, FAKE, FAKE, None) == -1
     assert L.moe_pack_up_bits(FAKE, 2, 100, 8, 4, FAKE, FAKE, None) == -1
     assert L.moe_pack_up_bits(FAKE, 2, 4096, 8, 4, FAKE + 8, FAKE, None) == -3
     assert moe.workspace_size(moe.OP_EXPERT_BITS, 4, 4096, 14336) >= \
         moe.workspace_size(moe.OP_EXPERT, 4, 4096, 14336)
+
+
+def test_binding_refuses_a_stale_library(monkeypatch):
+    _lib_or_skip()
+    import activation_sparse_expert_amd.build as b
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(b, "sources_sha256", lambda: "0" * 64)
+    with pytest.raises(RuntimeError, match="stale"):
+        moe.lib()
+
+
+def test_library_matches_its_sources():
+    L = _lib_or_skip()
+    import activation_sparse_expert_amd.build as b
+    assert L.moe_build_sources_sha256().decode() == b.sources_sha256()
 
 
 def test_binding_raises_without_library(monkeypatch):

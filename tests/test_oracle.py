@@ -488,6 +488,45 @@ def test_layer_fed_topk_and_masks():
     np.testing.assert_allclose(w3, w[:, ::-1], rtol=1e-14)
 
 
+# Closed forms of the linear-interpolation quantile (the threshold calibration
+# reading): for sorted values x_(0) <= ... <= x_(n-1) and h = q (n - 1), the
+# quantile is x_(floor h) + (h - floor h) (x_(floor h + 1) - x_(floor h)).  Each
+# expected value below is worked out by hand; the cases are chosen so that a
+# swapped q (q <-> 1 - q), another interpolation rule (lower, higher, nearest,
+# midpoint) or an off-by-one order statistic gives a different number.
+@pytest.mark.parametrize("vals,q,want", [
+    (np.arange(11.0), 0.9, 9.0),                    # h = 9 exactly
+    (np.arange(0.0, 50.0, 10.0), 0.8, 32.0),        # h = 3.2: 30 + 0.2 * 10 (lower 30, midpoint 35)
+    (np.arange(0.0, 50.0, 10.0), 0.2, 8.0),         # h = 0.8: 0 + 0.8 * 10 (swapped q gives 32)
+    (np.array([16.0, 1.0, 8.0, 2.0, 4.0]), 0.3, 2.4),   # unsorted; h = 1.2: 2 + 0.2 * 2
+    (np.array([16.0, 1.0, 8.0, 2.0, 4.0]), 0.7, 7.2),   # h = 2.8: 4 + 0.8 * 4
+    (np.array([5.0, 1.0, 5.0, 3.0, 5.0, 0.0]), 0.5, 4.0),   # ties; h = 2.5: 3 + 0.5 * 2
+    (np.array([5.0, 1.0, 5.0, 3.0, 5.0, 0.0]), 0.1, 0.5),   # h = 0.5: 0 + 0.5 * 1
+    (np.array([5.0, 1.0, 5.0, 3.0, 5.0, 0.0]), 0.95, 5.0),  # h = 4.75 between equal values
+    (np.array([5.0, 1.0, 5.0, 3.0, 5.0, 0.0]), 1.0, 5.0),   # q = 1: the largest
+    (np.array([5.0, 1.0, 5.0, 3.0, 5.0, 0.0]), 0.0, 0.0),   # q = 0: the smallest
+    (np.array([0.25]), 0.37, 0.25),                  # one value
+    (np.arange(1001.0) * 0.5, 0.9, 450.0),          # h = 900: the 901st value, 900 * 0.5
+    (np.arange(1001.0) * 0.5, 0.1234, 61.7),        # h = 123.4: 61.5 + 0.4 * 0.5
+])
+def test_calibrate_threshold_closed_forms(vals, q, want):
+    t = oracle.calibrate_threshold(vals, q)
+    assert t.dtype == np.float32
+    assert t == np.float32(want), (t, want)
+
+
+def test_calibrate_threshold_order_statistics_brute_force():
+    """At every q = i / (n - 1) the quantile is the i-th smallest value itself,
+    found here by counting (no sort): the value with exactly i values below it."""
+    rng = np.random.default_rng(5)
+    n = 41
+    vals = rng.permutation(np.arange(n) * 0.75 + 0.125)        # distinct, exact in fp32
+    for i in range(n):
+        below = np.array([(vals < v).sum() for v in vals])
+        want = vals[below == i][0]
+        assert oracle.calibrate_threshold(vals, i / (n - 1)) == np.float32(want)
+
+
 def test_calibrated_threshold_realises_sparsity():
     d, f = 256, 704
     _, up_q, up_sz, gb, db = _tiny_expert(100, d, f)
@@ -706,3 +745,21 @@ def test_expert_bits_dense_threshold_is_textbook_swiglu(bits):
     t = float(np.median(np.abs(v)))
     v2, m2, _ = oracle.expert_forward(x, "f16", up_q, up_sz, gb, db, "f16", thr=t, bits=bits)
     assert np.array_equal(m2, (np.abs(v2) > np.float32(t)).astype(np.uint8))
+
+
+# ------------------------------------------------------------------ input recipe
+# FloE review, "双稀疏预测器", observation 3: the hidden states of consecutive
+# MoE layers have cosine similarity above 0.95.  The 32-layer stack's hidden
+# stream is built to respect that; this holds it to it, in fp32 and after the
+# fp16 cast the layers are fed.
+
+def test_stack_hidden_stream_keeps_cosine_above_095():
+    c = synth.CONFIGS[synth.CFG_STACK]
+    for T in (1, 16):
+        xs = synth.hidden_stream_f32(synth.CFG_STACK, c["L"], T, c["d"], c["x_scale"])
+        for arr in (xs.astype(np.float64),
+                    synth.to_f16_bits(xs).view(np.float16).astype(np.float64)):
+            a, b = arr[:-1], arr[1:]
+            cos = (a * b).sum(-1) / (np.linalg.norm(a, axis=-1) * np.linalg.norm(b, axis=-1))
+            assert cos.shape == (c["L"] - 1, T)
+            assert cos.min() >= 0.95, cos.min()

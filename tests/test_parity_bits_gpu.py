@@ -9,7 +9,8 @@ import torch
 import activation_sparse_expert_amd as moe
 import oracle
 import synth
-from gpu_helpers import (DEV, TORCH_DT, bits_to_f64, check_mask, check_y, dev_bits, say,
+from gpu_helpers import (DEV, TORCH_DT, Guarded, bits_to_f64, check_bits_exports, check_mask,
+                         check_y, dev_bits, guarded_workspace, say,
                          to_dev_bits)
 
 pytestmark = pytest.mark.gpu
@@ -45,11 +46,21 @@ def threshold_for(h, x_bits, sparsity):
 def run_and_check(h, ex, x_bits, thr, what, scale=None):
     T, d, f = x_bits.shape[0], h["d"], h["f"]
     x = to_dev_bits(x_bits, h["wdt"])
-    m = torch.empty((T, f), dtype=torch.uint8, device=DEV)
-    v = torch.empty((T, f), dtype=torch.float32, device=DEV)
+    gm = Guarded((T, f), torch.uint8)
+    gv = Guarded((T, f), torch.float32)
+    gb = Guarded((T, f // 64), torch.int64)
+    gn = Guarded((T,), torch.int32)
+    gy = Guarded((T, d), torch.float32)
+    gw = guarded_workspace(moe.workspace_size(moe.OP_EXPERT_BITS, T, d, f))
     sc = None if scale is None else torch.from_numpy(scale.astype(np.float32)).to(DEV)
-    y = moe.expert_forward_sparse_bits(ex, h["bits"], x, mask_out=m, v_out=v, token_scale=sc)
+    moe.expert_forward_sparse_bits(ex, h["bits"], x, y=gy.t, mask_out=gm.t, v_out=gv.t,
+                                   mask_bits=gb.t, nnz=gn.t, token_scale=sc, ws=gw.t)
     torch.cuda.synchronize()
+    for g, n in ((gm, "mask"), (gv, "v"), (gb, "mask_bits"), (gn, "nnz"), (gy, "y"),
+                 (gw, "workspace")):
+        g.check(f"{what} {n}")
+    m, v, y = gm.t, gv.t, gy.t
+    check_bits_exports(m.cpu().numpy(), gb.t, gn.t, what)
     v_ref, _, _ = oracle.expert_forward(x_bits, h["wdt"], h["up_q"], h["up_sz"], h["gate"],
                                         h["down"], h["wdt"], thr, bits=h["bits"])
     vg = v.cpu().numpy().astype(np.float64)

@@ -7,7 +7,8 @@ import torch
 import activation_sparse_expert_amd as moe
 import oracle
 import synth
-from gpu_helpers import (DEV, HostExpert, check_mask, check_y, dev_bits, say, to_dev_bits)
+from gpu_helpers import (DEV, Guarded, HostExpert, check_bits_exports, check_mask, check_y,
+                         dev_bits, guarded_workspace, say, to_dev_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,17 +22,27 @@ def _gpu():
 
 def run_expert(hx: HostExpert, thr, x_bits, *, T=None, scale=None, ydt=torch.float32,
                y_init=None, accumulate=False):
+    """One expert call with y, every export and the workspace canary-guarded;
+    the bitmask and nnz exports are checked against the byte mask."""
     ex = hx.to_device(thr)
     x = to_dev_bits(x_bits, hx.wdt)
     T = x.shape[0]
-    mask = torch.empty((T, hx.f), dtype=torch.uint8, device=DEV)
-    v = torch.empty((T, hx.f), dtype=torch.float32, device=DEV)
-    y = y_init.clone() if y_init is not None else torch.empty((T, hx.d), dtype=ydt, device=DEV)
+    mask = Guarded((T, hx.f), torch.uint8)
+    v = Guarded((T, hx.f), torch.float32)
+    bits = Guarded((T, hx.f // 64), torch.int64)
+    nnz = Guarded((T,), torch.int32)
+    y = Guarded((T, hx.d), y_init.dtype if y_init is not None else ydt, fill=y_init)
+    ws = guarded_workspace(moe.workspace_size(moe.OP_EXPERT, T, hx.d, hx.f))
     ts = None if scale is None else torch.tensor(scale, dtype=torch.float32, device=DEV)
-    moe.expert_forward_sparse(ex, x, y=y, token_scale=ts, accumulate=accumulate, mask_out=mask,
-                              v_out=v)
+    moe.expert_forward_sparse(ex, x, y=y.t, token_scale=ts, accumulate=accumulate,
+                              mask_out=mask.t, v_out=v.t, mask_bits=bits.t, nnz=nnz.t, ws=ws.t)
     torch.cuda.synchronize()
-    return y.float().cpu().numpy(), mask.cpu().numpy(), v.cpu().numpy()
+    for g, n in ((mask, "mask"), (v, "v"), (bits, "mask_bits"), (nnz, "nnz"), (y, "y"),
+                 (ws, "workspace")):
+        g.check(f"expert d={hx.d} f={hx.f} T={T} {n}")
+    m = mask.t.cpu().numpy()
+    check_bits_exports(m, bits.t, nnz.t, f"expert d={hx.d} f={hx.f} T={T}")
+    return y.t.float().cpu().numpy(), m, v.t.cpu().numpy()
 
 
 def check_case(hx, thr, x_bits, what, **kw):
@@ -139,11 +150,15 @@ def test_mixtral_expert_batch1(mixtral, sp):
         assert abs((1 - m.mean()) - sp) < 0.05
 
 
-@pytest.mark.parametrize("sp", [0.5, 0.9])
+@pytest.mark.parametrize("sp", [0.0, 0.5, 0.7, 0.9])
 def test_mixtral_expert_batch4(mixtral, sp):
+    """Batch 4 at every sparsity of the workload, 0% (t < 0: every channel of
+    every tile active, the heaviest multi-token gather) included."""
     hx, thr, c = mixtral
     x = synth.to_f16_bits(synth.tokens_f32(synth.CFG_MIXTRAL, 4, c["d"], c["x_scale"]))
-    check_case(hx, thr[sp], x, f"d=4096 f=14336 T=4 sparsity {sp}")
+    _, m, _ = check_case(hx, thr[sp], x, f"d=4096 f=14336 T=4 sparsity {sp}")
+    if sp == 0.0:
+        assert m.all()
 
 
 def test_mixtral_expert_infinite_threshold(mixtral):
@@ -158,6 +173,8 @@ def test_mixtral_expert_infinite_threshold(mixtral):
 @pytest.mark.parametrize("d,f,T,wdt", [
     (64, 128, 1, "f16"), (128, 64, 3, "f16"), (512, 192, 2, "f16"), (1024, 256, 5, "bf16"),
     (2048, 1408, 9, "f16"), (6144, 256, 3, "bf16"), (4096, 320, 17, "f16"), (8192, 128, 2, "bf16"),
+    # the widest geometry (4 groups of 64 inputs per lane): d in (8192, 16384]
+    (12288, 128, 1, "f16"), (16384, 64, 2, "bf16"), (9216, 192, 3, "f16"),
 ])
 def test_expert_shapes(d, f, T, wdt):
     hx = HostExpert(90, d, T, d, f, wdt=wdt)
