@@ -25,7 +25,8 @@ EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_workspace_size", "moe_workspace_init", "moe_pack_up_int2",
             "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold",
             "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits",
-            "moe_build_sources_sha256"]
+            "moe_build_sources_sha256", "moe_expert_forward_sparse_noalloc",
+            "moe_noalloc_scratch_bytes"]
 
 
 class MoeError(RuntimeError):
@@ -93,6 +94,11 @@ def lib():
         L.moe_status_string.argtypes = [I]
         L.moe_calibrate_threshold.restype = I
         L.moe_calibrate_threshold.argtypes = [P, C.c_longlong, C.c_double, P, P, Z, P]
+        L.moe_expert_forward_sparse_noalloc.restype = I
+        L.moe_expert_forward_sparse_noalloc.argtypes = [C.POINTER(ExpertView), I, I, I, P, I, I,
+                                                        P, I, P, I, P, P, P, P, P]
+        L.moe_noalloc_scratch_bytes.restype = Z
+        L.moe_noalloc_scratch_bytes.argtypes = []
         L.moe_expert_forward_sparse_bits.restype = I
         L.moe_expert_forward_sparse_bits.argtypes = [C.POINTER(ExpertView), I, I, I, I, P, I, I,
                                                      P, I, P, I, P, P, P, P, P, Z, P]
@@ -186,6 +192,22 @@ def expert_forward_sparse(expert: Expert, x, *, y=None, out_dtype=None, token_sc
         int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_bits), _ptr(nnz), _ptr(mask_out),
         _ptr(v_out), _ptr(ws), ws.numel(), _stream())
     _check(st, "moe_expert_forward_sparse")
+    return y
+
+
+def expert_forward_sparse_noalloc(expert: Expert, x, *, y, token_scale=None,
+                                  accumulate: bool = False, mask_out=None, v_out=None,
+                                  mask_bits=None, nnz=None):
+    """expert_forward_sparse through the allocation-free entry point: the
+    library's static device scratch serves as the workspace, and the caller
+    passes every output (y included), so nothing is allocated."""
+    T, d = x.shape
+    v = expert.view()
+    st = lib().moe_expert_forward_sparse_noalloc(
+        C.byref(v), d, expert.f, _dt(expert.gate_t), _ptr(x), _dt(x), T, _ptr(token_scale),
+        int(bool(accumulate)), _ptr(y), _dt(y), _ptr(mask_bits), _ptr(nnz), _ptr(mask_out),
+        _ptr(v_out), _stream())
+    _check(st, "moe_expert_forward_sparse_noalloc")
     return y
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "../../include/moeffn.h"
@@ -178,6 +179,33 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->masks = (uint8_t *)(p + off[14]);
     }
     return o;
+}
+
+// ---- scratch of the allocation-free entry point ------------------------------
+// A file-scope device array serves as the workspace of
+// moe_expert_forward_sparse_noalloc.  Each GPU holds its own copy at its own
+// address, looked up once per device with hipGetSymbolAddress; host code uses
+// only that address (the array's name is a host-side stand-in, not a device
+// pointer).  Every call on one GPU shares its copy.
+constexpr size_t kScratchBytes = 32u << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the calling thread's current device (null on error).
+void *scratch_for_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
 }
 
 hipError_t launch_sparse(const SparseArgs &a, bool bf16, int tb, hipStream_t s)
@@ -379,6 +407,25 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     he = launch_reduce(r, s);
     if (he == hipSuccess && want_bits) he = launch_mask_bits(mask_out, T, f, mask_bits, nnz_out, s);
     return hip_status(he);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status moe_expert_forward_sparse_noalloc(const moe_expert_view *e, int d, int f,
+                                             moe_dtype wdt, const void *x, moe_dtype xdt, int T,
+                                             const float *token_scale, int accumulate, void *y,
+                                             moe_dtype ydt, uint64_t *mask_bits, int32_t *nnz_out,
+                                             uint8_t *mask_out, float *v_out, void *stream)
+{
+    if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
+    moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
+    if (st != MOE_OK) return st;
+    if (expert_ws_bytes(T, d, f) > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+    void *ws = scratch_for_current_device();
+    if (!ws) return MOE_ERR_HIP;
+    return moe_expert_forward_sparse(e, d, f, wdt, x, xdt, T, token_scale, accumulate, y, ydt,
+                                     mask_bits, nnz_out, mask_out, v_out, ws, kScratchBytes,
+                                     stream);
 }
 
 moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, int d, int f,

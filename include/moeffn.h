@@ -196,6 +196,31 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
                                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_forward_sparse for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, outputs and errors, with no workspace
+ * argument.  Its workspace is a static device array of
+ * moe_noalloc_scratch_bytes() bytes (32 MiB) that each GPU the library runs on
+ * holds until the process ends; the array of the device current on the calling
+ * thread is used.  Nothing is allocated and nothing is freed.  Shapes whose
+ * workspace (moe_workspace_size(MOE_OP_EXPERT, T, d, f)) exceeds the array
+ * return MOE_ERR_UNSUPPORTED (T = 1..8 at d = 4096, f = 14336 fit).  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap on one GPU (other
+ * streams, other threads) race and give wrong results; order them on one
+ * stream.  MOE_ERR_HIP if the array's device address cannot be found.
+ */
+moe_status moe_expert_forward_sparse_noalloc(const moe_expert_view *e, int d, int f,
+                                             moe_dtype wdt, const void *x, moe_dtype xdt, int T,
+                                             const float *token_scale, int accumulate,
+                                             void *y, moe_dtype ydt,
+                                             uint64_t *mask_bits, int32_t *nnz_out,
+                                             uint8_t *mask_out, float *v_out, void *stream);
+
+/* Size in bytes of the static scratch array of moe_expert_forward_sparse_noalloc. */
+size_t moe_noalloc_scratch_bytes(void);
+
+/*
  * The same expert with the up projection at 8, 4, 2 or 1 bits per code (FloE
  * review, "敏感度分析": the up projection quantised to INT8/INT4/INT2/INT1).
  * bits == 2 is moe_expert_forward_sparse with the INT2 format above.  For 8, 4
