@@ -26,7 +26,7 @@ EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold",
             "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits",
             "moe_build_sources_sha256", "moe_expert_forward_sparse_noalloc",
-            "moe_noalloc_scratch_bytes"]
+            "moe_noalloc_scratch_bytes", "moe_materialize_up", "moe_transpose_down"]
 
 
 class MoeError(RuntimeError):
@@ -45,7 +45,8 @@ class LayerDesc(C.Structure):
                 ("top_k", C.c_int), ("renormalize", C.c_int), ("wdt", C.c_int),
                 ("router_w", C.c_void_p), ("rdt", C.c_int), ("router_bias", C.c_void_p),
                 ("up_q", C.c_void_p), ("up_sz", C.c_void_p), ("gate_t", C.c_void_p),
-                ("down", C.c_void_p), ("thresholds", C.c_void_p), ("up_dense", C.c_void_p)]
+                ("down", C.c_void_p), ("thresholds", C.c_void_p), ("up_dense", C.c_void_p),
+                ("down_dense", C.c_void_p)]
 
 
 class LayerTrace(C.Structure):
@@ -90,6 +91,10 @@ def lib():
         L.moe_pack_up_int2.argtypes = [P, I, I, I, P, P, P]
         L.moe_materialize_up_bf16.restype = I
         L.moe_materialize_up_bf16.argtypes = [P, P, I, I, P, P]
+        L.moe_materialize_up.restype = I
+        L.moe_materialize_up.argtypes = [P, P, I, I, I, P, P]
+        L.moe_transpose_down.restype = I
+        L.moe_transpose_down.argtypes = [P, I, I, I, P, P]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [I]
         L.moe_calibrate_threshold.restype = I
@@ -270,14 +275,15 @@ class Layer:
     down: "torch.Tensor"          # [E+S][f][d]
     thresholds: "torch.Tensor"    # [E+S] fp32
     router_bias: Optional["torch.Tensor"] = None
-    up_dense: Optional["torch.Tensor"] = None   # [E+S][f][d] bf16
+    up_dense: Optional["torch.Tensor"] = None   # [E+S][f][d] in the weight type
+    down_dense: Optional["torch.Tensor"] = None  # [E+S][d][f] W^down transposed
 
     def desc(self) -> LayerDesc:
         return LayerDesc(self.d, self.f, self.E, self.S, self.k, int(bool(self.renormalize)),
                          _dt(self.gate_t), _ptr(self.router_w), _dt(self.router_w),
                          _ptr(self.router_bias), _ptr(self.up_q), _ptr(self.up_sz),
                          _ptr(self.gate_t), _ptr(self.down), _ptr(self.thresholds),
-                         _ptr(self.up_dense))
+                         _ptr(self.up_dense), _ptr(self.down_dense))
 
     def workspace_bytes(self, T: int) -> int:
         return workspace_size(OP_LAYER, T, self.d, self.f, self.E, self.k, self.S)
@@ -379,6 +385,32 @@ def pack_up_bits(w_up_t, bits: int, *, up_q=None, up_sz=None):
                                 _ptr(up_sz), _stream())
     _check(st, "moe_pack_up_bits")
     return up_q, up_sz
+
+
+def materialize_up(up_q, up_sz, d: int, dtype, *, out=None):
+    """Dense-path up weights [f][d] = rne(s (q - z)) in dtype (torch.bfloat16
+    or torch.float16)."""
+    import torch
+    f = up_q.shape[0]
+    if out is None:
+        out = torch.empty((f, d), dtype=dtype, device=up_q.device)
+    st = lib().moe_materialize_up(_ptr(up_q), _ptr(up_sz), d, f, _dt(out), _ptr(out), _stream())
+    _check(st, "moe_materialize_up")
+    return out
+
+
+def transpose_down(down, *, out=None):
+    """Dense-path down weights: [n][d][f] (or [d][f]) = the transpose of each
+    expert's down [f][d]."""
+    import torch
+    squeeze = down.dim() == 2
+    dn = down.unsqueeze(0) if squeeze else down
+    n, f, d = dn.shape
+    if out is None:
+        out = torch.empty((n, d, f), dtype=down.dtype, device=down.device)
+    st = lib().moe_transpose_down(_ptr(dn), n, d, f, _ptr(out), _stream())
+    _check(st, "moe_transpose_down")
+    return out[0] if squeeze else out
 
 
 def materialize_up_bf16(up_q, up_sz, d: int, *, out=None):

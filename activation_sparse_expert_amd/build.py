@@ -12,7 +12,7 @@ OUT = os.path.join(HERE, "libmoeffn.so")
 BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "expert_sparse_f16.hip", "expert_sparse_bf16.hip", "reduce.hip", "route.hip",
-           "pack.hip", "dense_mfma.hip", "calibrate.hip",
+           "pack.hip", "dense_mfma.hip", "dense_gemm.hip", "calibrate.hip",
            "eamc.hip", "expert_bits.hip"]
 
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moeffn.h")

@@ -208,6 +208,20 @@ void *scratch_for_current_device()
     return g_scratch_ptr[dev];
 }
 
+// Split of f in the dense down product: enough workgroups (d / 256 column
+// tiles per chunk of tokens) for about two per compute unit, at most 4 (the
+// partial-row region holds 4 slices per row).
+int gemm_ksplit(int T, int k, int E, int S, int d, int f)
+{
+    const long long tk = (long long)T * k;
+    const long long act = E < tk ? E : tk;
+    const long long expect = (long long)S * ((T + kGemmChunk - 1) / kGemmChunk) +
+                             (tk + kGemmChunk - 1) / kGemmChunk + act / 2;
+    int ks = 1;
+    while (ks < kDenseKSplit && expect * (d / 256) * ks < 512 && f % (32 * ks * 2) == 0) ks *= 2;
+    return ks;
+}
+
 hipError_t launch_sparse(const SparseArgs &a, bool bf16, int tb, hipStream_t s)
 {
     return bf16 ? launch_sparse_expert_bf16(a, tb, s) : launch_sparse_expert_f16(a, tb, s);
@@ -401,7 +415,7 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     hipError_t he = launch_sparse(a, wdt == MOE_BF16, sp.tb, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
     ReduceArgs r{};
-    r.part = (const float *)ws; r.tiles = tp.tiles; r.d = d; r.T = T;
+    r.part = a.part; r.tiles = tp.tiles; r.d = d; r.T = T;
     r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0;
     r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
     he = launch_reduce(r, s);
@@ -496,17 +510,21 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         return MOE_ERR_ALIGNMENT;
     if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE && path != MOE_PATH_AUTO)
         return MOE_ERR_INVALID_ARG;
+    // dense kernels: the 256 x 256-tile GEMM (bf16 or fp16; needs the
+    // transposed down weights) or the older bf16 kernels (row-major down)
+    const bool want_masks = trace && (trace->masks || trace->mask_bits || trace->nnz);
+    const bool gemm_ok = L->up_dense && L->down_dense && d % 256 == 0 && f % 128 == 0;
+    const bool old_ok = L->wdt == MOE_BF16 && L->up_dense && f % 256 == 0 && d % 128 == 0;
     if (path == MOE_PATH_AUTO) {
-        const bool dense_ok = L->wdt == MOE_BF16 && L->up_dense && aligned(L->up_dense, 16) &&
-                              !(trace && (trace->masks || trace->mask_bits || trace->nnz)) &&
-                              f % 256 == 0 && d % 128 == 0;
+        const bool dense_ok = (gemm_ok || old_ok) && aligned(L->up_dense, 16) &&
+                              (!L->down_dense || aligned(L->down_dense, 16)) && !want_masks;
         path = dense_ok && (long long)T * k >= 8ll * E ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
     }
     if (path == MOE_PATH_DENSE) {
-        if (L->wdt != MOE_BF16 || !L->up_dense) return MOE_ERR_UNSUPPORTED;
-        if (!aligned(L->up_dense, 16)) return MOE_ERR_ALIGNMENT;
-        if (trace && (trace->masks || trace->mask_bits || trace->nnz)) return MOE_ERR_UNSUPPORTED;
-        if (f % 256 != 0 || d % 128 != 0) return MOE_ERR_UNSUPPORTED;
+        if (!gemm_ok && !old_ok) return MOE_ERR_UNSUPPORTED;
+        if (!aligned(L->up_dense, 16) || (L->down_dense && !aligned(L->down_dense, 16)))
+            return MOE_ERR_ALIGNMENT;
+        if (want_masks) return MOE_ERR_UNSUPPORTED;
     }
     if (trace && ((trace->mask_bits && !aligned(trace->mask_bits, 8)) ||
                   (trace->nnz && !aligned(trace->nnz, 4))))
@@ -532,9 +550,12 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.active = w.active; r.n_active = w.n_active;
     r.lg_buf = route_split(d, E, L->rdt) ? w.lg : nullptr;
     const SparsePlan sp = layer_plan(T, d, f, E, k, S);
+    const bool use_gemm = path == MOE_PATH_DENSE && gemm_ok;
     if (path == MOE_PATH_SPARSE) {
         r.chunk = sp.tb; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;
         if (sp.tb == 1) r.chunk_rec = w.chunk_rec;
+    } else if (use_gemm) {
+        r.chunk = kGemmChunk; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;
     }
     hipError_t he = launch_route(r, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
@@ -544,6 +565,23 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     red.d = d; red.T = T; red.layer = 1; red.rows_per_tok = k + S; red.k = k; red.S = S;
     red.part = w.part;
     red.y = y; red.ydt = (int)ydt; red.accumulate = 0;
+    if (use_gemm) {
+        GemmArgs g{};
+        g.d = d; g.f = f; g.E = E; g.k = k; g.S = S; g.T = T;
+        g.bf16 = L->wdt == MOE_BF16 ? 1 : 0;
+        g.x = (const uint16_t *)x;
+        g.gate = (const uint16_t *)L->gate_t; g.up = L->up_dense;
+        g.down_t = (const uint16_t *)L->down_dense;
+        g.h16 = (uint16_t *)w.h; g.part = w.part;
+        g.chunk_tab = w.chunk_tab; g.n_chunks = w.n_chunks; g.offset = w.offset; g.pairs = w.pairs;
+        g.topk_w = r.topk_w;
+        g.grid_chunks = gemm_grid_chunks(T, k, E, S);
+        g.ksplit = gemm_ksplit(T, k, E, S, d, f);
+        he = launch_gemm_layer(g, s);
+        if (he != hipSuccess) return MOE_ERR_HIP;
+        red.tiles = g.ksplit;
+        return hip_status(launch_reduce(red, s));
+    }
     if (path == MOE_PATH_DENSE) {
         DenseArgs a{};
         a.d = d; a.f = f; a.E = E; a.k = k; a.S = S; a.T = T;
@@ -613,13 +651,29 @@ moe_status moe_pack_up_bits(const void *w_up_t, moe_dtype dt, int d, int f, int 
                                        (hipStream_t)stream));
 }
 
-moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
-                                   uint16_t *out, void *stream)
+moe_status moe_materialize_up(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
+                              moe_dtype dt, uint16_t *out, void *stream)
 {
     if (!up_q || !up_sz || !out) return MOE_ERR_INVALID_ARG;
     if (d < 64 || d % 64 != 0 || f < 1) return MOE_ERR_INVALID_ARG;
+    if (!is16(dt)) return MOE_ERR_UNSUPPORTED;
     if (!aligned(up_sz, 4) || !aligned(out, 2)) return MOE_ERR_ALIGNMENT;
-    return hip_status(launch_materialize_bf16(up_q, up_sz, d, f, out, (hipStream_t)stream));
+    return hip_status(launch_materialize16(up_q, up_sz, d, f, dt == MOE_BF16, out,
+                                           (hipStream_t)stream));
+}
+
+moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
+                                   uint16_t *out, void *stream)
+{
+    return moe_materialize_up(up_q, up_sz, d, f, MOE_BF16, out, stream);
+}
+
+moe_status moe_transpose_down(const void *down, int n, int d, int f, void *out, void *stream)
+{
+    if (!down || !out || n < 1 || d < 1 || f < 1) return MOE_ERR_INVALID_ARG;
+    if (!aligned(down, 2) || !aligned(out, 2)) return MOE_ERR_ALIGNMENT;
+    return hip_status(launch_transpose16((const uint16_t *)down, n, f, d, (uint16_t *)out,
+                                         (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@ struct SparseArgs {
     float *v_out;                       // single only: [T][f]
 };
 
+
 // Launch the fused Algorithm-1 kernel; tb = tokens per chunk (1, 2, 4).
 hipError_t launch_sparse_expert_f16(const SparseArgs &a, int tb, hipStream_t s);
 hipError_t launch_sparse_expert_bf16(const SparseArgs &a, int tb, hipStream_t s);
@@ -97,8 +98,31 @@ size_t dense_h_bytes(int T, int f, int k, int S);
 
 hipError_t launch_pack_int2(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz,
                             hipStream_t s);
-hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, int f,
-                                   uint16_t *out, hipStream_t s);
+hipError_t launch_materialize16(const uint8_t *q, const uint16_t *sz, int d, int f, bool bf16,
+                                uint16_t *out, hipStream_t s);
+
+// Dense grouped GEMM (dense_gemm.hip): gate/up then down for a layer, token
+// rows in chunks of at most 256 of one expert (the grouping kernel's chunk
+// table), W^down transposed ([d][f]) for the down product.
+struct GemmArgs {
+    int d, f, E, k, S, T;
+    int bf16;                           // 1: bf16 MFMA, 0: fp16
+    const uint16_t *x;                  // [T][d]
+    const uint16_t *gate, *up;          // [E+S][f][d]
+    const uint16_t *down_t;             // [E+S][d][f]
+    uint16_t *h16;                      // [T (k + S)][f] workspace, 16-bit
+    float *part;                        // [T (k + S)][ksplit][d] partial rows
+    const int32_t *chunk_tab, *n_chunks, *offset, *pairs;
+    const float *topk_w;
+    int ksplit;                         // split of f in the down product
+    int grid_chunks;                    // chunk slots in the grid (an upper bound)
+};
+constexpr int kGemmChunk = 256;         // token rows per chunk
+int gemm_grid_chunks(int T, int k, int E, int S);
+hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s);
+// out [mats][cols][rows] = in [mats][rows][cols], 16-bit elements
+hipError_t launch_transpose16(const uint16_t *in, int mats, int rows, int cols, uint16_t *out,
+                              hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 // Bitmask and population count of `rows` 0/1 byte masks of f channels (f % 64
 // == 0): bits [rows][f/64] (channel 64 i + l at bit l of word i) and nnz [rows];

@@ -132,8 +132,13 @@ __device__ __forceinline__ uint16_t double_to_bf16_bits(double v)
     return (uint16_t)((sign << 15) | bits);
 }
 
+// Dense-path up weights: out = s (q - z) from the INT2 format, rounded once to
+// bf16 (BF16) or fp16.  The product is exact in double (and in fp32: q - z has
+// at most 13 significant bits and s 11); fp16 rounding is v_cvt_f16_f32's
+// round to nearest even of that exact fp32 value.
+template <bool BF16>
 __global__ void __launch_bounds__(256)
-materialize_bf16_kernel(const uint8_t *q, const uint16_t *sz, int d, int f, uint16_t *out)
+materialize_kernel(const uint8_t *q, const uint16_t *sz, int d, int f, uint16_t *out)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)f * d) return;
@@ -143,7 +148,8 @@ materialize_bf16_kernel(const uint8_t *q, const uint16_t *sz, int d, int f, uint
     const int c = (q[j * (d / 4) + bit / 8] >> (bit % 8)) & 3;
     const double s = (double)half_bits_to_float(sz[(j * G + k / 64) * 2 + 0]);
     const double z = (double)half_bits_to_float(sz[(j * G + k / 64) * 2 + 1]);
-    out[i] = double_to_bf16_bits(s * ((double)c - z));         // exact product in double
+    if constexpr (BF16) out[i] = double_to_bf16_bits(s * ((double)c - z));
+    else out[i] = float_to_half_bits((float)(s * ((double)c - z)));
 }
 
 __global__ void __launch_bounds__(256)
@@ -177,12 +183,15 @@ hipError_t launch_pack_bits(const void *w, int dt, int d, int f, int bits, uint8
     return hipGetLastError();
 }
 
-hipError_t launch_materialize_bf16(const uint8_t *q, const uint16_t *sz, int d, int f,
-                                   uint16_t *out, hipStream_t s)
+hipError_t launch_materialize16(const uint8_t *q, const uint16_t *sz, int d, int f, bool bf16,
+                                uint16_t *out, hipStream_t s)
 {
     const size_t n = (size_t)f * d;
     const unsigned blocks = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(materialize_bf16_kernel, dim3(blocks), dim3(256), 0, s, q, sz, d, f, out);
+    if (bf16)
+        hipLaunchKernelGGL(materialize_kernel<true>, dim3(blocks), dim3(256), 0, s, q, sz, d, f, out);
+    else
+        hipLaunchKernelGGL(materialize_kernel<false>, dim3(blocks), dim3(256), 0, s, q, sz, d, f, out);
     return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@ sparsity, one token per call (decode).  A step is one call of
 moe_expert_forward_sparse on one token: the fused kernel (INT2 up GEMV, mask,
 compaction, gate/down row gathers, fused SiLU, partial rows) and the small
 kernel that sums the partial rows into y.  Steps rotate over R distinct expert
-instances (R * 253 MB far exceeds the 256 MB Infinity Cache) and 16 tokens, so
-the weights come from HBM, as they would when 32 layers x 8 experts are
+instances (32 by default: between two visits to one instance the other 31
+calls touch about 1.3 GB, five times the 256 MB Infinity Cache) and 16 tokens,
+so the weights come from HBM, as they would when 32 layers x 8 experts are
 resident.  Inputs are resident in HBM before the timed region starts; the K
 launches are captured once in a HIP graph and replayed, so the host's launch
 overhead is not what is measured.
@@ -121,10 +122,11 @@ def copy_probe(mib):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def batched_measure(reps=10, T=256):
+def batched_measure(reps=10, T=256, dense_only=False):
     """The batched layer: 8 experts (d=6144, f=16384, bf16), top-2, T tokens.
     Times moe_layer_forward on the dense bf16 MFMA path and on the 70%-sparse
-    path (HIP events around `reps` calls each, after warm-up)."""
+    path (HIP events around `reps` calls each, after warm-up).  dense_only:
+    the new dense path alone, 3 calls at T and at 2048 tokens (for profiling)."""
     import torch
     import activation_sparse_expert_amd as moe
     import synth
@@ -153,22 +155,30 @@ def batched_measure(reps=10, T=256):
         torch.cuda.synchronize()
         thr[e] = float(np.quantile(np.abs(v.cpu().numpy()).ravel(), c["sparsity"]))
     R = torch.from_numpy(synth.router_f32(cfg, 0, E, d)).to(bf).to(dev)
+    down_dense = moe.transpose_down(down)
     L = moe.Layer(d=d, f=f, E=E, S=0, k=k, renormalize=True, router_w=R, up_q=up_q, up_sz=up_sz,
-                  gate_t=gate, down=down, thresholds=thr, up_dense=up_dense)
+                  gate_t=gate, down=down, thresholds=thr, up_dense=up_dense, down_dense=down_dense)
+    L_rowmajor = moe.Layer(d=d, f=f, E=E, S=0, k=k, renormalize=True, router_w=R, up_q=up_q,
+                           up_sz=up_sz, gate_t=gate, down=down, thresholds=thr, up_dense=up_dense)
     x = torch.from_numpy(synth.tokens_f32(cfg, T, d, c["x_scale"])).to(bf).to(dev)
     y = torch.empty((T, d), dtype=torch.float32, device=dev)
     ws = moe.new_workspace(L.workspace_bytes(T), dev)
     cnt = torch.empty(E, dtype=torch.int32, device=dev)
     out = {}
-    for name, path in (("dense_mfma", moe.PATH_DENSE), ("sparse", moe.PATH_SPARSE)):
+    legs = (("dense_mfma", moe.PATH_DENSE, L),
+            ("dense_mfma_rowmajor_down", moe.PATH_DENSE, L_rowmajor),
+            ("sparse", moe.PATH_SPARSE, L))
+    if dense_only:
+        legs, reps = legs[:1], 3
+    for name, path, LL in legs:
         for _ in range(3):
-            moe.layer_forward(L, x, path=path, y=y, ws=ws, trace={"expert_count": cnt})
+            moe.layer_forward(LL, x, path=path, y=y, ws=ws, trace={"expert_count": cnt})
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            moe.layer_forward(L, x, path=path, y=y, ws=ws)
+            moe.layer_forward(LL, x, path=path, y=y, ws=ws)
         e1.record()
         e1.synchronize()
         sec = e0.elapsed_time(e1) / 1e3 / reps
@@ -177,6 +187,9 @@ def batched_measure(reps=10, T=256):
         wbytes = used * 3 * d * f * 2                         # bf16 weights of the experts used
         out[name] = {"ms_per_layer": sec * 1e3, "tokens_per_s": T / sec,
                      "tflops": flops / sec / 1e12}
+        if name == "dense_mfma_rowmajor_down":
+            out[name]["what"] = ("the older bf16 kernels (64/128-token passes, W^down read "
+                                 "row-major), for comparison")
         if path == moe.PATH_DENSE:
             out[name]["mfma_util"] = flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
             out[name]["weight_gbs"] = wbytes / sec / 1e9
@@ -185,7 +198,8 @@ def batched_measure(reps=10, T=256):
             out[name]["mfma_attainable"] = min(1.0, flops / wbytes * HBM_PEAK_GBS / 1e3
                                                / MFMA_BF16_PEAK_TFLOPS)
     out["workload"] = (f"Mixtral-8x22B-shaped layer, 8 experts d={d} f={f} bf16, top-2, "
-                       f"{T} tokens; dense = threshold off on bf16 MFMA, sparse = 70% thresholds")
+                       f"{T} tokens; dense = threshold off on bf16 MFMA (256 x 256 tiles, "
+                       f"W^down transposed once), sparse = 70% thresholds")
     # extra point: the same layer at a micro-batch of 2048 tokens (about 512 per
     # expert, 512 flop per weight byte, above the 312.5 flop/B ridge), where the
     # dense path is a real contraction and MFMA utilisation is the measure
@@ -193,27 +207,31 @@ def batched_measure(reps=10, T=256):
     x2 = torch.from_numpy(synth.tokens_f32(cfg, T2, d, c["x_scale"])).to(bf).to(dev)
     y2 = torch.empty((T2, d), dtype=torch.float32, device=dev)
     ws2 = moe.new_workspace(L.workspace_bytes(T2), dev)
-    for _ in range(2):
-        moe.layer_forward(L, x2, path=moe.PATH_DENSE, y=y2, ws=ws2, trace={"expert_count": cnt})
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        moe.layer_forward(L, x2, path=moe.PATH_DENSE, y=y2, ws=ws2)
-    e1.record()
-    e1.synchronize()
-    sec = e0.elapsed_time(e1) / 1e3 / 5
-    flops = 2.0 * 3 * T2 * k * d * f
-    wbytes = int((cnt.cpu().numpy() > 0).sum()) * 3 * d * f * 2
-    out["dense_mfma_T2048"] = {
-        "workload": f"same layer, micro-batch {T2} tokens, dense bf16 MFMA path",
-        "ms_per_layer": sec * 1e3, "tokens_per_s": T2 / sec, "tflops": flops / sec / 1e12,
-        "mfma_util": flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "flop_per_weight_byte": flops / wbytes,
-        "mfma_attainable": min(1.0, flops / wbytes * HBM_PEAK_GBS / 1e3 / MFMA_BF16_PEAK_TFLOPS)}
+    legs2 = (("dense_mfma_T2048", L), ("dense_mfma_rowmajor_down_T2048", L_rowmajor))
+    for key, LL in (legs2[:1] if dense_only else legs2):
+        for _ in range(2):
+            moe.layer_forward(LL, x2, path=moe.PATH_DENSE, y=y2, ws=ws2, trace={"expert_count": cnt})
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n2 = 3 if dense_only else 5
+        for _ in range(n2):
+            moe.layer_forward(LL, x2, path=moe.PATH_DENSE, y=y2, ws=ws2)
+        e1.record()
+        e1.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / n2
+        flops = 2.0 * 3 * T2 * k * d * f
+        wbytes = int((cnt.cpu().numpy() > 0).sum()) * 3 * d * f * 2
+        out[key] = {
+            "workload": f"same layer, micro-batch {T2} tokens, dense bf16 MFMA path"
+                        + ("" if LL is L else " (older kernels, for comparison)"),
+            "ms_per_layer": sec * 1e3, "tokens_per_s": T2 / sec, "tflops": flops / sec / 1e12,
+            "mfma_util": flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "flop_per_weight_byte": flops / wbytes,
+            "mfma_attainable": min(1.0, flops / wbytes * HBM_PEAK_GBS / 1e3 / MFMA_BF16_PEAK_TFLOPS)}
     del x2, y2, ws2
-    del L, gate, down, up_q, up_sz, up_dense
+    del L, L_rowmajor, gate, down, down_dense, up_q, up_sz, up_dense
     torch.cuda.empty_cache()
     return out
 
@@ -446,8 +464,22 @@ def eamc_measure():
     return res
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(sparsity, budget_s):
-    """The fp64 oracle, as it stands, on instance 0 and the same tokens."""
+    """The fp64 oracle, as it stands, on instance 0 and the same tokens: once on
+    one host thread, then on N threads that each run independent single-token
+    calls (the oracle's C code runs outside the GIL), N = the cores this
+    process may use (at most 16).  Each leg runs for about budget_s / 2."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import synth
     cfg = synth.CFG_MIXTRAL
@@ -461,16 +493,30 @@ def cpu_baseline(sparsity, budget_s):
     del W
     thr = oracle.calibrate_threshold(np.abs(vcal), sparsity)
     toks = synth.to_f16_bits(synth.tokens_f32(cfg, NTOK, D, xs))
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.expert_forward(toks[n % NTOK:n % NTOK + 1], "f16", q, sz, gb, db, "f16", thr)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= NTOK:
-            break
-    return dict(value=n / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{n} single-token calls of the fp64 oracle on expert instance 0 "
-                       f"(d={D}, f={F}, {int(sparsity * 100)}% threshold), {el:.1f} s, one thread")
+
+    def worker(first, leg_s):
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < leg_s:
+            t = (first + n) % NTOK
+            oracle.expert_forward(toks[t:t + 1], "f16", q, sz, gb, db, "f16", thr)
+            n += 1
+        return n, time.perf_counter() - t0
+
+    n1, el1 = worker(0, budget_s / 2)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(lambda i: worker(i, budget_s / 2), range(threads)))
+    eln = time.perf_counter() - t0
+    nn = sum(r[0] for r in res)
+    model = cpu_model()
+    return dict(value=nn / eln, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{nn} single-token calls of the fp64 oracle on expert instance 0 "
+                       f"(d={D}, f={F}, {int(sparsity * 100)}% threshold) on {threads} threads "
+                       f"in {eln:.1f} s, {model}",
+                cpu_model=model,
+                single_thread={"value": n1 / el1, "unit": "tokens/s", "cores": 1,
+                               "sample": f"{n1} calls on one thread in {el1:.1f} s"})
 
 
 def main():
@@ -478,12 +524,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--instances", type=int, default=32)
     ap.add_argument("--sparsity", type=float, default=0.9)
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--dist-replays", type=int, default=15,
+                    help="further timed replays of the K-step graph for the median and p10/p90")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--batched-only", action="store_true",
                     help="only the batched-layer measurement (for profiling)")
+    ap.add_argument("--dense-only", action="store_true",
+                    help="only the dense MFMA path of the batched layer, at 256 and 2048 tokens, "
+                         "three calls each (for profiling)")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the layer workloads (32-layer stack, fine-grained layer)")
     ap.add_argument("--no-batched", action="store_true",
@@ -501,8 +552,8 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
-    if args.batched_only:
-        print(json.dumps({"batched": batched_measure()}), flush=True)
+    if args.batched_only or args.dense_only:
+        print(json.dumps({"batched": batched_measure(dense_only=args.dense_only)}), flush=True)
         return
     if args.variants_only:
         print(json.dumps({"expert_up_bits": bits_measure(), "eamc_match": eamc_measure()}),
@@ -561,6 +612,18 @@ def main():
     ms = e0.elapsed_time(e1)
     sec = ms / 1e3
     K = args.steps
+    # the spread: the same K-step graph replayed again, each replay timed
+    per_step = []
+    with torch.cuda.stream(stream):
+        for _ in range(args.dist_replays):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            graph.replay()
+            a1.record(stream)
+            a1.synchronize()
+            per_step.append(a0.elapsed_time(a1) / K)
+    per_step = np.array(per_step)
     avg_launch_s = sec / K
     achieved = bytes_timed / K / avg_launch_s / 1e9
     out = {
@@ -582,6 +645,13 @@ def main():
             "d": D, "f": F, "tokens_per_step": 1, "sparsity_target": args.sparsity,
             "sparsity_realised": float(1 - nnz.mean() / F), "instances": R,
             "bytes_per_step_mean": bytes_timed / K,
+        },
+        "dist": {
+            "replays": int(len(per_step)),
+            "ms_per_step_median": float(np.median(per_step)) if len(per_step) else None,
+            "ms_per_step_p10": float(np.percentile(per_step, 10)) if len(per_step) else None,
+            "ms_per_step_p90": float(np.percentile(per_step, 90)) if len(per_step) else None,
+            "what": "each further replay of the same K-step graph timed on its own",
         },
         "roofline": {
             "bound": "hbm",

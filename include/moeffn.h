@@ -125,8 +125,13 @@ typedef struct {
     const void *gate_t;         /* [E+S][f][d]                              */
     const void *down;           /* [E+S][f][d]                              */
     const float *thresholds;    /* [E+S] fp32, device                       */
-    const uint16_t *up_dense;   /* [E+S][f][d] bf16 up weights for MOE_PATH_DENSE
-                                   (moe_materialize_up_bf16), else NULL     */
+    const uint16_t *up_dense;   /* [E+S][f][d] up weights in wdt for MOE_PATH_DENSE
+                                   (moe_materialize_up), else NULL          */
+    const void *down_dense;     /* [E+S][d][f] W^down transposed, in wdt, for the
+                                   dense path (moe_transpose_down), or NULL.
+                                   With it the dense path runs the 256 x 256-tile
+                                   MFMA GEMM in bf16 or fp16; without it, bf16
+                                   layers only, the older kernels.          */
 } moe_layer;
 
 /* Optional device outputs of moe_layer_forward (any field may be NULL). */
@@ -326,11 +331,28 @@ moe_status moe_pack_up_bits(const void *w_up_t, moe_dtype dt, int d, int f, int 
                             uint8_t *up_q, uint16_t *up_sz, void *stream);
 
 /*
- * Dense-path up weights: out[j][k] = bf16_rne(s * (q - z)) evaluated exactly,
- * from the INT2 format (one-off preparation for MOE_PATH_DENSE).
+ * Dense-path up weights: out[j][k] = rne(s * (q - z)) evaluated exactly, from
+ * the INT2 format, rounded to dt (MOE_BF16 or MOE_F16): one-off preparation of
+ * moe_layer.up_dense for MOE_PATH_DENSE.  up_q [f][d/4], up_sz [f][d/64][2],
+ * out [f][d].  d % 64 == 0.
  */
+moe_status moe_materialize_up(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
+                              moe_dtype dt, uint16_t *out, void *stream);
+
+/* moe_materialize_up with dt = MOE_BF16. */
 moe_status moe_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
                                    uint16_t *out, void *stream);
+
+/*
+ * Dense-path down weights (one-off preparation of moe_layer.down_dense): for
+ * each of n experts, out [d][f] = the transpose of down [f][d] (16-bit
+ * elements, bf16 or fp16 alike), so that the dense down product reads both of
+ * its operands along the contracted dimension f.  The sparse path keeps
+ * reading `down` row by row (FloE review, "高效稀疏 GEMV 内核": W^down stored
+ * transposed so that an active channel's weights are contiguous); the dense
+ * path contracts over all channels at once and wants the other order.
+ */
+moe_status moe_transpose_down(const void *down, int n, int d, int f, void *out, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_string(moe_status s);

@@ -342,6 +342,16 @@ void oracle_materialize_up_bf16(const uint8_t *up_q, const uint16_t *up_sz, int 
             out[(size_t)j * d + k] = oracle_double_to_bf16_rne(up_weight(up_q, up_sz, d, j, k));
 }
 
+/* The same for fp16 layers (reading R9 in the layer's own 16-bit type):
+ * fp16_rne of the exact dequantised value, out[j][k] as fp16 bits. */
+void oracle_materialize_up_f16(const uint8_t *up_q, const uint16_t *up_sz, int d, int f,
+                               uint16_t *out)
+{
+    for (int j = 0; j < f; ++j)
+        for (int k = 0; k < d; ++k)
+            out[(size_t)j * d + k] = oracle_double_to_half_rne(up_weight(up_q, up_sz, d, j, k));
+}
+
 /* ------------------------------------------------------ C1: one expert */
 
 static double silu(double g) { return g / (1.0 + exp(-g)); }
@@ -510,8 +520,9 @@ void oracle_route_topk(const void *x, int xdt, int T, int d, const void *router_
  * masks_in [T][k+S][f] (optional): fed masks, slot s < k for the routed
  *   choice s of token t, slot k+i for shared expert i.
  * dense != 0 selects the dense grouped-GEMM path (reading R9): every channel
- *   active and the up weights taken as bf16_rne(dequant(INT2)); gate/down are
- *   read in wdt as for the sparse path.
+ *   active and the up weights taken as rne(dequant(INT2)) in the layer's 16-bit
+ *   type (bf16 for bf16 layers, fp16 for fp16 layers); gate/down are read in
+ *   wdt as for the sparse path.
  * Outputs: y [T][d]; optionally topk_idx/topk_w [T][k], masks_out [T][k+S][f].
  */
 void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
@@ -575,10 +586,11 @@ void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
                 oracle_expert_forward(xt, xdt, 1, d, f, uq, us, gt, dn, wdt, thr[e], &sc, mi,
                                       NULL, mo, ytok, 0);
             } else {
-                /* dense SwiGLU on bf16_rne(dequant(up)), all channels active */
+                /* dense SwiGLU on rne(dequant(up)) in wdt, all channels active */
                 if (!ubf) ubf = (uint16_t *)malloc(sizeof(uint16_t) * wstride);
                 if (ubf_expert != e) {
-                    oracle_materialize_up_bf16(uq, us, d, f, ubf);
+                    if (wdt == ODT_F16) oracle_materialize_up_f16(uq, us, d, f, ubf);
+                    else oracle_materialize_up_bf16(uq, us, d, f, ubf);
                     ubf_expert = e;
                 }
                 double *xr = (double *)malloc(sizeof(double) * (size_t)d);
@@ -587,7 +599,8 @@ void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
                 for (int j = 0; j < f; ++j) {
                     double v = 0.0, g = 0.0;
                     for (int q = 0; q < d; ++q) {
-                        v += xr[q] * oracle_bf16_to_double(ubf[(size_t)j * d + q]);
+                        v += xr[q] * (wdt == ODT_F16 ? oracle_half_to_double(ubf[(size_t)j * d + q])
+                                                     : oracle_bf16_to_double(ubf[(size_t)j * d + q]));
                         g += xr[q] * load_typed(gt, wdt, (size_t)j * d + q);
                     }
                     double h = silu(g) * v;

@@ -282,9 +282,12 @@ class DeviceLayer:
                            gate_t=gate, down=down, thresholds=torch.from_numpy(thr).to(DEV),
                            router_bias=None if bias is None else torch.from_numpy(bias).to(DEV))
         if dense:
-            self.L.up_dense = torch.empty((n, f, d), dtype=torch.bfloat16, device=DEV)
+            # dense path: up weights in the layer's type and W^down transposed
+            # (the 256 x 256-tile MFMA kernels)
+            self.L.up_dense = torch.empty((n, f, d), dtype=TORCH_DT[wdt], device=DEV)
             for e in range(n):
-                moe.materialize_up_bf16(up_q[e], up_sz[e], d, out=self.L.up_dense[e])
+                moe.materialize_up(up_q[e], up_sz[e], d, TORCH_DT[wdt], out=self.L.up_dense[e])
+            self.L.down_dense = moe.transpose_down(down)
         torch.cuda.synchronize()
 
     def host_weights(self, experts):

@@ -138,7 +138,7 @@ def test_route_rejects(kw, code):
 def _layer_desc(**kw):
     base = dict(d=4096, f=14336, n_routed=8, n_shared=0, top_k=2, renormalize=1, wdt=0,
                 router_w=FAKE, rdt=0, router_bias=None, up_q=FAKE, up_sz=FAKE, gate_t=FAKE,
-                down=FAKE, thresholds=FAKE, up_dense=None)
+                down=FAKE, thresholds=FAKE, up_dense=None, down_dense=None)
     base.update(kw)
     return moe.LayerDesc(*[base[n] for n, _ in moe.LayerDesc._fields_])
 
@@ -171,6 +171,23 @@ def test_layer_rejects_desc(dkw, code):
 def test_layer_dense_shape_limits():
     d = _layer_desc(wdt=1, up_dense=FAKE, f=14336 + 64)   # f % 256 != 0 for the dense path
     assert _layer(desc=d, xdt=1, path=1) == -2
+    # fp16 layers need the transposed down weights for the dense path
+    assert _layer(desc=_layer_desc(wdt=0, up_dense=FAKE), path=1) == -2
+    # the 256 x 256-tile kernels: d % 256 and f % 128
+    d = _layer_desc(wdt=0, d=128, f=128, up_dense=FAKE, down_dense=FAKE)
+    assert _layer(desc=d, path=1) == -2
+    d = _layer_desc(wdt=0, up_dense=FAKE, down_dense=FAKE + 2)
+    assert _layer(desc=d, path=1) == -3
+
+
+def test_prep_entry_points_reject():
+    L = _lib_or_skip()
+    assert L.moe_materialize_up(FAKE, FAKE, 4096, 8, 2, FAKE, None) == -2   # fp32 out
+    assert L.moe_materialize_up(None, FAKE, 4096, 8, 0, FAKE, None) == -1
+    assert L.moe_materialize_up(FAKE, FAKE, 100, 8, 0, FAKE, None) == -1
+    assert L.moe_transpose_down(None, 1, 4096, 8, FAKE, None) == -1
+    assert L.moe_transpose_down(FAKE, 0, 4096, 8, FAKE, None) == -1
+    assert L.moe_transpose_down(FAKE, 1, 4096, 8, FAKE + 1, None) == -3
 
 
 @pytest.mark.parametrize("field,val,path,code", [

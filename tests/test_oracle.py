@@ -468,6 +468,45 @@ def test_layer_dense_path_is_bf16_swiglu():
     np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-14)
 
 
+def test_layer_dense_path_fp16_rounds_up_weights_to_fp16():
+    """fp16 layers: the dense path's up weights are the dequantised INT2 weights
+    rounded once to fp16 (numpy's float64 -> float16 conversion is round to
+    nearest even), and the layer is the textbook SwiGLU on them.  The weights
+    here are not exact in either 16-bit type, and rounding them to bf16
+    instead would miss the tolerance."""
+    d, f, E, k, T = 128, 64, 3, 2, 4
+    uq, us, g, dn = [], [], [], []
+    for e in range(E):
+        w = synth.normal_f32(90 + e, (f, d), 0.02)
+        q, sz = oracle.pack_up_int2(w)
+        uq.append(q); us.append(sz)
+        g.append(synth.to_f16_bits(synth.normal_f32(93 + e, (f, d), 0.02)))
+        dn.append(synth.to_f16_bits(synth.normal_f32(96 + e, (f, d), 0.02)))
+    uq, us, g, dn = map(np.stack, (uq, us, g, dn))
+    x = synth.to_f16_bits(synth.normal_f32(99, (T, d), 1 / 16))
+    R = synth.to_f16_bits(synth.normal_f32(100, (E, d), 0.02))
+    y, idx, w, m = oracle.layer_forward(x, "f16", R, "f16", None, E, k, 0, True, uq, us, g, dn,
+                                        "f16", np.float32([np.inf] * E), dense=True)
+    assert np.all(m == 1)
+    X = _bits_to_f64(x, "f16")
+
+    def swiglu(t, e, up):
+        hg = X[t] @ _bits_to_f64(g[e], "f16").T
+        hu = X[t] @ up.T
+        return (hg * expit(hg) * hu) @ _bits_to_f64(dn[e], "f16")
+
+    ref = np.zeros((T, d))
+    ref_bf = np.zeros((T, d))
+    for t in range(T):
+        for s in range(k):
+            e = idx[t, s]
+            wq = oracle.dequant_up(uq[e], us[e], d)                     # exact, float64
+            ref[t] += w[t, s] * swiglu(t, e, wq.astype(np.float16).astype(np.float64))
+            ref_bf[t] += w[t, s] * swiglu(t, e, _bits_to_f64(synth.to_bf16_bits(wq), "bf16"))
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-14)
+    assert np.abs(ref_bf - ref).max() > 1e-6 * np.abs(ref).max()
+
+
 def test_layer_fed_topk_and_masks():
     d, f, E, k, S, T = 64, 64, 5, 2, 1, 4
     uq, us, g, dn = _tiny_layer(90, d, f, E, S)

@@ -92,7 +92,13 @@ def device_layer(experts, thr, R_bits, rdt, E, S, k, renorm=True, bias=None, den
                   up_q=up_q, up_sz=up_sz, gate_t=gate, down=down,
                   thresholds=torch.from_numpy(thr).to(DEV),
                   router_bias=None if bias is None else torch.from_numpy(bias).to(DEV))
-    if dense:
+    if dense == "gemm":
+        # the 256 x 256-tile kernels: up weights in the layer's type, W^down transposed
+        L.up_dense = torch.empty((E + S, f, d), dtype=gate.dtype, device=DEV)
+        for e in range(E + S):
+            moe.materialize_up(up_q[e], up_sz[e], d, gate.dtype, out=L.up_dense[e])
+        L.down_dense = moe.transpose_down(down)
+    elif dense:
         L.up_dense = torch.empty((E + S, f, d), dtype=torch.bfloat16, device=DEV)
         for e in range(E + S):
             moe.materialize_up_bf16(up_q[e], up_sz[e], d, out=L.up_dense[e])
@@ -160,6 +166,52 @@ def test_small_layer_dense(T, E, S, k, d, f):
         tokens = np.concatenate([tokens, [150, 200, 250, 280]])
     oracle_layer_check(experts, thr, R_bits, "bf16", None, E, S, k, x_bits, y, tr, tokens, True,
                        f"dense layer T={T} E={E}+{S} k={k} d={d} f={f}")
+
+
+@pytest.mark.parametrize("T,E,S,k,d,f,wdt", [
+    (150, 4, 0, 2, 512, 512, "bf16"),    # ~75 tokens per expert: one chunk, 3 of 8 row subtiles
+    (300, 4, 1, 2, 512, 512, "f16"),     # ~150 per routed expert; the shared one in 2 chunks
+    (700, 3, 1, 3, 256, 384, "bf16"),    # 700 per expert: 3 chunks each, every row subtile
+    (9, 6, 1, 2, 1024, 256, "f16"),      # a few tokens per expert
+    (64, 8, 0, 2, 2048, 1024, "bf16"),   # split of f in the down product
+])
+def test_small_layer_dense_gemm(T, E, S, k, d, f, wdt):
+    """The 256 x 256-tile MFMA GEMM (bf16 and fp16 layers) against the
+    oracle's dense path: ragged chunks, several chunks per expert, shared
+    experts, and a split of f in the down product."""
+    experts, thr = build_host_layer(67, E, S, d, f, wdt, 0.7, 1 / 16, layer=d)
+    R_bits = synth.to_bits(synth.router_f32(67, d, E, d), wdt)
+    x_bits = synth.to_bits(synth.tokens_f32(68, T, d, 1 / 16, layer=d), wdt)
+    L = device_layer(experts, thr, R_bits, wdt, E, S, k, dense="gemm")
+    y, tr = run_layer(L, to_dev_bits(x_bits, wdt), moe.PATH_DENSE)
+    tokens = np.arange(T) if T <= 16 else np.unique(np.array([0, 1, 63, 64, 255, 256, T // 2, T - 1]) % T)
+    oracle_layer_check(experts, thr, R_bits, wdt, None, E, S, k, x_bits, y, tr, tokens, True,
+                       f"dense GEMM layer {wdt} T={T} E={E}+{S} k={k} d={d} f={f}")
+    assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("n,f,d", [(1, 64, 128), (3, 200, 96), (2, 1408, 2048)])
+def test_transpose_down_bit_exact(n, f, d):
+    a = torch.from_numpy(synth.normal_f32(69, (n, f, d), 0.02)).half().to(DEV)
+    t = moe.transpose_down(a)
+    torch.cuda.synchronize()
+    assert torch.equal(t.cpu(), a.cpu().transpose(1, 2).contiguous())
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_materialize_up_matches_oracle(dt):
+    d, f = 2048, 48
+    w = synth.normal_f32(4243, (f, d), 0.02)
+    q_ref, sz_ref = oracle.pack_up_int2(w)
+    out = moe.materialize_up(torch.from_numpy(q_ref).to(DEV),
+                             torch.from_numpy(sz_ref.view(np.int16)).to(DEV), d, dt)
+    torch.cuda.synchronize()
+    exact = oracle.dequant_up(q_ref, sz_ref, d)
+    if dt == torch.float16:
+        ref = exact.astype(np.float16).view(np.uint16)
+    else:
+        ref = oracle.materialize_up_bf16(q_ref, sz_ref, d)
+    assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), ref)
 
 
 @pytest.mark.parametrize("T,E,S,k,d,f,expect", [
