@@ -210,7 +210,7 @@ void *scratch_for_current_device()
 
 // Split of f in the dense down product: enough workgroups (d / 256 column
 // tiles per chunk of tokens) for about two per compute unit, at most 4 (the
-// partial-row region holds 4 slices per row).
+// partial-row region holds 4 slices per row), each slice a multiple of 64.
 int gemm_ksplit(int T, int k, int E, int S, int d, int f)
 {
     const long long tk = (long long)T * k;
@@ -218,7 +218,7 @@ int gemm_ksplit(int T, int k, int E, int S, int d, int f)
     const long long expect = (long long)S * ((T + kGemmChunk - 1) / kGemmChunk) +
                              (tk + kGemmChunk - 1) / kGemmChunk + act / 2;
     int ks = 1;
-    while (ks < kDenseKSplit && expect * (d / 256) * ks < 512 && f % (32 * ks * 2) == 0) ks *= 2;
+    while (ks < kDenseKSplit && expect * (d / 256) * ks < 512 && f % (64 * ks * 2) == 0) ks *= 2;
     return ks;
 }
 

@@ -16,10 +16,11 @@
 //            [d][f], prepared once by moe_transpose_down); epilogue: scaled
 //            by the router weight into partial rows [pair][ksplit][d], summed
 //            by the reduce kernel.
-// A workgroup of 4 waves computes a 256 x 256 tile; wave (wm, wn) owns rows
-// 128 wm .. and 128 columns, as 4 x 4 accumulators of
+// A workgroup of 8 waves (two per SIMD) computes a 256 x 256 tile; wave
+// (wm, wn) owns rows 128 wm .. and 64 columns, as 4 x 2 accumulators of
 // v_mfma_f32_32x32x16_{bf16,f16} (16 fp32 each), so each k step reads 4 A and
-// 4 B fragments from LDS for 16 MFMAs.  Operands move global -> LDS by DMA
+// 2 B fragments from LDS for 8 MFMAs, and one wave's MFMAs run while the
+// other wave of its SIMD waits at a barrier or for LDS.  Operands move global -> LDS by DMA
 // (global_load_lds_dwordx4), in stages of 32 k values (64-byte rows) with
 // four stages and three blocks in flight; the 16-byte chunks of a row are
 // XOR-swizzled so that fragment reads hit distinct banks.  Token rows come in
@@ -40,15 +41,17 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGThreads = 256;                  // 4 waves
+constexpr int kWaves = 8;                       // 2 per SIMD: one's MFMAs cover the other's waits
+constexpr int kGThreads = 64 * kWaves;
+constexpr int kWNB = 16 / kWaves;               // B subtiles (32 columns) per wave
 constexpr int kMT = 256;                        // tile rows (tokens)
 constexpr int kNT = 256;                        // tile columns (B rows)
-constexpr int kKB = 32;                         // k values per stage
-constexpr int kStages = 4;
-constexpr int kStageBytes = (kMT + kNT) * kKB * 2;             // 32 KB
+constexpr int kKB = 64;                         // k values per stage: 128-byte rows, whole lines
+constexpr int kSteps = kKB / 16;                // MFMA k steps per block
+constexpr int kStages = 2;
+constexpr int kStageBytes = (kMT + kNT) * kKB * 2;             // 64 KB
 constexpr int kGLds = kStages * kStageBytes;                    // 128 KB
-constexpr int kCopies = kStageBytes / 16 / kGThreads;           // 8 per thread per stage
-constexpr int kAhead = kStages - 1;
+constexpr int kMaxCopies = kStageBytes / 1024 / kWaves;   // copy instructions per wave
 
 template <bool BF16>
 __device__ __forceinline__ floatx16 mma(const uint4 &a, const uint4 &b, const floatx16 &c)
@@ -61,13 +64,12 @@ __device__ __forceinline__ floatx16 mma(const uint4 &a, const uint4 &b, const fl
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Byte offset of (row, logical 16-byte chunk c) inside a stage: rows of 64
-// bytes, the four chunks XOR-swizzled by bits 1-2 of the row, so the eight
-// (or sixteen) rows a fragment read serves per LDS cycle fall in distinct banks.
-__device__ __forceinline__ int lpos(int row, int c)
-{
-    return row * 64 + 16 * (c ^ (((row >> 1) ^ (row >> 2)) & 3));
-}
+// Byte offset of (row, logical 16-byte chunk c) inside a stage: rows of 128
+// bytes, the eight chunks XOR-swizzled by bits 0-2 of the row and bit 3, so the
+// 8 (or 16) rows that a fragment read serves per LDS cycle fall in distinct
+// banks (for 128- and 256-byte bank rows alike).
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int lpos(int row, int c) { return row * 128 + 16 * (c ^ swz(row)); }
 
 struct Chunk {
     int e, ntok, pos0, hrow0;
@@ -115,40 +117,57 @@ __device__ __forceinline__ uint16_t to16(float v)
     else return float_to_half_bits(v);
 }
 
-// The k loop of one wave over its NSUB row subtiles (those holding tokens):
-// wait for block kb, publish it, refill the stage that block kb - 1 used, and
-// issue the block's MFMAs from LDS fragments.
+// The k loop of one wave over its NSUB row subtiles (those holding tokens).
+// Two stages: block kb + 1 is copied into the stage that block kb - 1 used
+// while block kb is multiplied, and a barrier at the end of each block
+// publishes the next one.  Inside a block the fragments of k step s + 1 are
+// read from LDS while the MFMAs of step s run (sched_barrier keeps the
+// compiler from sinking the reads back next to their MFMAs); the other wave
+// of each SIMD covers the rest of the waiting.
 template <bool BF16, int NSUB, class ISSUE>
-__device__ __forceinline__ void kloop(floatx16 (&acc)[4][4], const unsigned char *smem, int nkb,
-                                      int arow0, const int (&brow)[4], int li, int hk,
+__device__ __forceinline__ void kloop(floatx16 (&acc)[4][kWNB], const unsigned char *smem, int nkb,
+                                      int arow0, const int (&brow)[kWNB], int li, int hk,
                                       ISSUE &issue)
 {
-    for (int kb = 0; kb < nkb; ++kb) {
-        // this thread's copies of block kb are done once at most the blocks
-        // after it remain in flight
-        const int after = min(kAhead - 1, nkb - 1 - kb);
-        if (after >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kCopies) : "memory");
-        else if (after == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        // the stage written next held block kb - 1, which every wave has finished
-        if (kb + kAhead < nkb) issue(kb + kAhead);
+    constexpr int NA = NSUB > 0 ? NSUB : 1;
+    uint4 a0[NA], b0[kWNB], a1[NA], b1[kWNB];
+    auto load = [&](const unsigned char *st, int step, uint4 (&af)[NA], uint4 (&bf)[kWNB]) {
         if constexpr (NSUB > 0) {
-            const unsigned char *st = smem + (size_t)(kb % kStages) * kStageBytes;
+            const int c = 2 * step + hk;
 #pragma unroll
-            for (int s = 0; s < kKB / 16; ++s) {
-                const int c = 2 * s + hk;
-                uint4 bf[4], af[NSUB];
+            for (int j = 0; j < kWNB; ++j) bf[j] = *(const uint4 *)(st + lpos(brow[j] + li, c));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bf[j] = *(const uint4 *)(st + lpos(brow[j] + li, c));
-#pragma unroll
-                for (int i = 0; i < NSUB; ++i) af[i] = *(const uint4 *)(st + lpos(arow0 + 32 * i + li, c));
-#pragma unroll
-                for (int i = 0; i < NSUB; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = mma<BF16>(af[i], bf[j], acc[i][j]);
-            }
+            for (int i = 0; i < NSUB; ++i) af[i] = *(const uint4 *)(st + lpos(arow0 + 32 * i + li, c));
         }
+    };
+    auto mmas = [&](const uint4 (&af)[NA], const uint4 (&bf)[kWNB]) {
+        if constexpr (NSUB > 0) {
+#pragma unroll
+            for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+                for (int j = 0; j < kWNB; ++j) acc[i][j] = mma<BF16>(af[i], bf[j], acc[i][j]);
+        }
+    };
+    // block 0 was issued by the caller
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        if (kb + 1 < nkb) issue(kb + 1);            // the stage block kb - 1 used
+        const unsigned char *st = smem + (size_t)(kb & 1) * kStageBytes;
+        load(st, 0, a0, b0);
+#pragma unroll
+        for (int s2 = 0; s2 < kSteps; s2 += 2) {
+            load(st, s2 + 1, a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            mmas(a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s2 + 2 < kSteps) load(st, s2 + 2, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mmas(a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
+        __syncthreads();
     }
 }
 
@@ -158,36 +177,65 @@ __global__ void __launch_bounds__(kGThreads)
 gemm_kernel(GemmArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int nchunk_grid = a.grid_chunks;
-    const int ci = blockIdx.x % nchunk_grid;
-    const int rest = blockIdx.x / nchunk_grid;
+    // ---- which tile: XCD-aware.  Workgroups are dealt to the 8 XCDs in turn
+    // (block b to XCD b % 8, as its (b / 8)-th).  Each XCD takes a contiguous
+    // run of the tile order, whose consecutive tiles share a pair of token
+    // chunks (usually one expert's) and step through neighbouring weight
+    // tiles, so the workgroups resident on an XCD at one time read the same
+    // token rows and each weight tile about once through that XCD's L2.
+    // Tile order: chunk pair, then split-K slice, then column tile, then the
+    // chunk within the pair.
     const int ntiles = MODE == 0 ? a.f / 128 : a.d / kNT;
-    const int nt = rest % ntiles;
-    const int ks = rest / ntiles;                   // split-K slice (down)
+    const int nsc = (a.T + kMT - 1) / kMT;
+    const int vchunks = a.S * nsc + *a.n_chunks;    // chunks that hold tokens
+    const int per_pair = 2 * ntiles * a.ksplit;
+    const int vtiles = (vchunks + 1) / 2 * per_pair;
+    const int q8 = (vtiles + 7) / 8;
+    const int slot = blockIdx.x / 8;
+    if (slot >= q8) return;
+    const int t = (blockIdx.x % 8) * q8 + slot;
+    if (t >= vtiles) return;
+    const int pair = t / per_pair;
+    const int r0 = t - pair * per_pair;
+    const int ci = 2 * pair + (r0 & 1);
+    const int nt = (r0 >> 1) % ntiles;
+    const int ks = (r0 >> 1) / ntiles;              // split-K slice (down)
+    if (ci >= vchunks) return;
     const Chunk ch = chunk_info(a, ci);
     if (!ch.valid) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 1, wn = wave >> 1;        // row half, column group
     const int d = a.d, f = a.f;
     const int K = MODE == 0 ? d : f;
     const int kspan = K / a.ksplit;
     const int k_beg = ks * kspan;
     const int nkb = kspan / kKB;
 
-    // ---- copy sources: copy q of this thread fills stage bytes
-    // (wave kCopies + q) KB + 16 lane, i.e. row (wave kCopies + q) 16 + lane / 4,
-    // physical chunk lane % 4 (logical chunk pc ^ swizzle) ------------------
-    const uint16_t *src[kCopies];
+    // ---- copy sources.  A block is copied by 8-row instructions (1 KB of
+    // the stage each): ceil(tokens / 8) for the token rows, 32 for the 256 B
+    // rows; instruction q goes to wave q % kWaves, so this wave issues ncopy of
+    // them per block.  Lane l of an instruction covers row base + l / 8,
+    // physical chunk l % 8 (logical chunk pc ^ swizzle).  Token rows past the
+    // chunk are not copied: their (stale) LDS rows only feed MFMA rows that the
+    // epilogue discards.
+    const int na = (min(ch.ntok, kMT) + 7) / 8;
+    const int ninst = na + kNT / 8;
+    const int ncopy = (ninst - wave + kWaves - 1) / kWaves;
+    const uint16_t *src[kMaxCopies];
+    int dst[kMaxCopies];
 #pragma unroll
-    for (int q = 0; q < kCopies; ++q) {
-        const int row = (wave * kCopies + q) * 16 + (lane >> 2);
-        const int pc = lane & 3;
-        const int c = pc ^ (((row >> 1) ^ (row >> 2)) & 3);
+    for (int q = 0; q < kMaxCopies; ++q) {
+        const int inst = min(wave + kWaves * q, ninst - 1);
+        const int base = inst < na ? 8 * inst : kMT + 8 * (inst - na);
+        const int row = base + (lane >> 3);
+        dst[q] = base * 128;
+        const int pc = lane & 7;
+        const int c = pc ^ swz(row);
         const uint16_t *rp;
         if (row < kMT) {
-            const int m = min(row, ch.ntok - 1);        // rows past the chunk: a valid row
+            const int m = min(row, ch.ntok - 1);
             if (MODE == 0) rp = a.x + (size_t)token_at(a, ch, m) * d;
             else rp = a.h16 + (size_t)(ch.hrow0 + m) * f;
         } else {
@@ -202,17 +250,17 @@ gemm_kernel(GemmArgs a)
         src[q] = rp + k_beg + 8 * c;
     }
     auto issue = [&](int kb) {
-        unsigned char *base = smem + (size_t)(kb % kStages) * kStageBytes;
+        unsigned char *base = smem + (size_t)(kb & 1) * kStageBytes;
 #pragma unroll
-        for (int q = 0; q < kCopies; ++q)
-            copy16_to_lds(src[q] + (size_t)kb * kKB, base + (size_t)(wave * kCopies + q) * 1024);
+        for (int q = 0; q < kMaxCopies; ++q)
+            if (q < ncopy) copy16_to_lds(src[q] + (size_t)kb * kKB, base + dst[q]);
     };
 
-    floatx16 acc[4][4];
+    floatx16 acc[4][kWNB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kWNB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -220,17 +268,18 @@ gemm_kernel(GemmArgs a)
     const int vrows = __builtin_amdgcn_readfirstlane(ch.ntok - 128 * wm);
     const int nsub = vrows <= 0 ? 0 : min(4, (vrows + 31) / 32);
     // LDS rows of this wave's B subtiles
-    int brow[4];
+    // gate/up: the wave's gate columns first, then the same channels' up
+    // columns (kWNB / 2 subtiles each); down: kWNB consecutive subtiles
+    constexpr int HB = kWNB / 2;
+    int brow[kWNB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (MODE == 0) brow[j] = kMT + (j < 2 ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2));
-        else brow[j] = kMT + 128 * wn + 32 * j;
+    for (int j = 0; j < kWNB; ++j) {
+        if (MODE == 0) brow[j] = kMT + (j < HB ? 32 * HB * wn + 32 * j : 128 + 32 * HB * wn + 32 * (j - HB));
+        else brow[j] = kMT + 32 * kWNB * wn + 32 * j;
     }
     const int li = lane & 31, hk = lane >> 5;
 
-#pragma unroll
-    for (int p = 0; p < kAhead; ++p)
-        if (p < nkb) issue(p);
+    issue(0);
     switch (nsub) {
     case 4: kloop<BF16, 4>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
     case 3: kloop<BF16, 3>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
@@ -248,14 +297,14 @@ gemm_kernel(GemmArgs a)
         for (int i = 0; i < 4; ++i) {
             if (i >= nsub) continue;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = nt * 128 + 64 * wn + 32 * j + li;
+            for (int j = 0; j < HB; ++j) {
+                const int col = nt * 128 + 32 * HB * wn + 32 * j + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int m = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
                     if (m < ch.ntok)
                         a.h16[(size_t)(ch.hrow0 + m) * f + col] =
-                            to16<BF16>(silu(acc[i][j][r]) * acc[i][j + 2][r]);
+                            to16<BF16>(silu(acc[i][j][r]) * acc[i][j + HB][r]);
                 }
             }
         }
@@ -290,10 +339,10 @@ gemm_kernel(GemmArgs a)
                 const int m = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (m >= ch.ntok) continue;
                 float *dst = a.part + ((size_t)row_s[m] * a.ksplit + ks) * d + (size_t)nt * kNT +
-                             128 * wn + li;
+                             32 * kWNB * wn + li;
                 const float sc = sc_s[m];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dst[32 * j] = sc * acc[i][j][r];
+                for (int j = 0; j < kWNB; ++j) dst[32 * j] = sc * acc[i][j][r];
             }
         }
     }
@@ -339,8 +388,11 @@ hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s)
     e = hipFuncSetAttribute(dn, hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
     if (e != hipSuccess) return e;
     GemmArgs g = a;
-    const dim3 grid_gu((unsigned)a.grid_chunks * (unsigned)(a.f / 128));
-    const dim3 grid_dn((unsigned)a.grid_chunks * (unsigned)(a.d / kNT) * (unsigned)a.ksplit);
+    // tiles are mapped in the kernel (XCD-aware, from the valid chunk count):
+    // the grid covers the bound in pairs of chunks, 8 per XCD turn, plus 8
+    const unsigned pairs = (unsigned)(a.grid_chunks + 1) / 2;
+    const dim3 grid_gu((pairs * 2u * (unsigned)(a.f / 128) + 7u) / 8u * 8u + 8u);
+    const dim3 grid_dn((pairs * 2u * (unsigned)(a.d / kNT) * (unsigned)a.ksplit + 7u) / 8u * 8u + 8u);
     GemmArgs gu_args = g;
     gu_args.ksplit = 1;
     if (a.bf16) hipLaunchKernelGGL((gemm_kernel<true, 0>), grid_gu, dim3(kGThreads), kGLds, s, gu_args);
