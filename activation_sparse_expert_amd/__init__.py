@@ -26,7 +26,8 @@ EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_materialize_up_bf16", "moe_status_string", "moe_calibrate_threshold",
             "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits",
             "moe_build_sources_sha256", "moe_expert_forward_sparse_noalloc",
-            "moe_noalloc_scratch_bytes", "moe_materialize_up", "moe_transpose_down"]
+            "moe_noalloc_scratch_bytes", "moe_materialize_up", "moe_transpose_down",
+            "moe_auto_dense_min"]
 
 
 class MoeError(RuntimeError):
@@ -46,13 +47,13 @@ class LayerDesc(C.Structure):
                 ("router_w", C.c_void_p), ("rdt", C.c_int), ("router_bias", C.c_void_p),
                 ("up_q", C.c_void_p), ("up_sz", C.c_void_p), ("gate_t", C.c_void_p),
                 ("down", C.c_void_p), ("thresholds", C.c_void_p), ("up_dense", C.c_void_p),
-                ("down_dense", C.c_void_p)]
+                ("down_dense", C.c_void_p), ("density", C.c_float)]
 
 
 class LayerTrace(C.Structure):
     _fields_ = [("topk_idx", C.c_void_p), ("topk_w", C.c_void_p), ("logits", C.c_void_p),
                 ("expert_count", C.c_void_p), ("masks", C.c_void_p), ("eam_row", C.c_void_p),
-                ("mask_bits", C.c_void_p), ("nnz", C.c_void_p)]
+                ("mask_bits", C.c_void_p), ("nnz", C.c_void_p), ("expert_dense", C.c_void_p)]
 
 
 _lib = None
@@ -95,6 +96,8 @@ def lib():
         L.moe_materialize_up.argtypes = [P, P, I, I, I, P, P]
         L.moe_transpose_down.restype = I
         L.moe_transpose_down.argtypes = [P, I, I, I, P, P]
+        L.moe_auto_dense_min.restype = I
+        L.moe_auto_dense_min.argtypes = [C.POINTER(LayerDesc), I]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [I]
         L.moe_calibrate_threshold.restype = I
@@ -277,16 +280,23 @@ class Layer:
     router_bias: Optional["torch.Tensor"] = None
     up_dense: Optional["torch.Tensor"] = None   # [E+S][f][d] in the weight type
     down_dense: Optional["torch.Tensor"] = None  # [E+S][d][f] W^down transposed
+    density: float = 0.0                         # expected active fraction (MOE_PATH_AUTO)
 
     def desc(self) -> LayerDesc:
         return LayerDesc(self.d, self.f, self.E, self.S, self.k, int(bool(self.renormalize)),
                          _dt(self.gate_t), _ptr(self.router_w), _dt(self.router_w),
                          _ptr(self.router_bias), _ptr(self.up_q), _ptr(self.up_sz),
                          _ptr(self.gate_t), _ptr(self.down), _ptr(self.thresholds),
-                         _ptr(self.up_dense), _ptr(self.down_dense))
+                         _ptr(self.up_dense), _ptr(self.down_dense), float(self.density))
 
     def workspace_bytes(self, T: int) -> int:
         return workspace_size(OP_LAYER, T, self.d, self.f, self.E, self.k, self.S)
+
+    def auto_dense_min(self, T: int) -> int:
+        """Token count from which MOE_PATH_AUTO sends an expert to the dense
+        path at T tokens (0: the call stays sparse)."""
+        desc = self.desc()
+        return int(lib().moe_auto_dense_min(C.byref(desc), T))
 
 
 def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype=None,
@@ -294,7 +304,8 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
     """Route and combine one layer on x [T][d]; returns y [T][d].
 
     ``trace`` may map any of topk_idx, topk_w, logits, expert_count, masks,
-    mask_bits, nnz to preallocated device tensors that receive those exports,
+    mask_bits, nnz, expert_dense to preallocated device tensors that receive
+    those exports,
     and eam_row to an int32 [E] device tensor that the call's per-expert counts
     are added into."""
     import torch
@@ -308,7 +319,8 @@ def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype
         tr = LayerTrace(_ptr(trace.get("topk_idx")), _ptr(trace.get("topk_w")),
                         _ptr(trace.get("logits")), _ptr(trace.get("expert_count")),
                         _ptr(trace.get("masks")), _ptr(trace.get("eam_row")),
-                        _ptr(trace.get("mask_bits")), _ptr(trace.get("nnz")))
+                        _ptr(trace.get("mask_bits")), _ptr(trace.get("nnz")),
+                        _ptr(trace.get("expert_dense")))
     desc = layer.desc()
     st = lib().moe_layer_forward(C.byref(desc), _ptr(x), _dt(x), T, _ptr(y), _dt(y), path,
                                  C.byref(tr) if tr is not None else None, _ptr(ws), ws.numel(),

@@ -137,6 +137,8 @@ struct LayerWs {
     float *lg;              // [T][E] router logits (wide-router split)
     int32_t *chunk_rec;     // [T*k][4] single-token chunk records
     uint8_t *masks;         // [T][k+S][f] byte masks staged for the bitmask / nnz exports
+    int32_t *chunk_tab2, *n_chunks2;    // dense chunks
+    uint8_t *expert_dense;  // [E] path of each routed expert
 };
 
 size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, void *base)
@@ -145,7 +147,7 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     const TilePlan tp = layer_plan(T, d, f, E, k, S).tp;
     const size_t part_tiles = (size_t)(tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit);
     size_t o = 0;
-    size_t off[15];
+    size_t off[18];
     off[0] = o; o += up(4);
     off[1] = o; o += up((size_t)T * k * 4);
     off[2] = o; o += up((size_t)T * k * 4);
@@ -161,6 +163,9 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
     off[12] = o; o += up((size_t)T * E * 4);
     off[13] = o; o += up((size_t)T * k * 16);
     off[14] = o; o += up((size_t)rows * f);
+    off[15] = o; o += up((size_t)T * k * 4);           // dense chunks (at most one per pair)
+    off[16] = o; o += up(4);
+    off[17] = o; o += up((size_t)E);
     if (out) {
         char *p = (char *)base;
         out->topk_idx = (int32_t *)(p + off[1]);
@@ -177,6 +182,9 @@ size_t layer_ws_bytes(int T, int d, int f, int E, int k, int S, LayerWs *out, vo
         out->lg = (float *)(p + off[12]);
         out->chunk_rec = (int32_t *)(p + off[13]);
         out->masks = (uint8_t *)(p + off[14]);
+        out->chunk_tab2 = (int32_t *)(p + off[15]);
+        out->n_chunks2 = (int32_t *)(p + off[16]);
+        out->expert_dense = (uint8_t *)(p + off[17]);
     }
     return o;
 }
@@ -220,6 +228,21 @@ int gemm_ksplit(int T, int k, int E, int S, int d, int f)
     int ks = 1;
     while (ks < kDenseKSplit && expect * (d / 256) * ks < 512 && f % (64 * ks * 2) == 0) ks *= 2;
     return ks;
+}
+
+// MOE_PATH_AUTO's per-expert rule (classic roofline on bytes moved, MoE-
+// Lightning review, "层次化屋顶模型"): an expert with n tokens costs the sparse
+// path ceil(n / tb) chunks, each reading the INT2 codes and scales (5/16 d f
+// bytes) and the gate and down rows of the union of tb tokens' masks
+// (4 u d f bytes, u = 1 - (1 - density)^tb); the dense path reads the 16-bit
+// gate, up and down weights once (6 d f bytes).  The result is the smallest n
+// with ceil(n / tb) (5/16 + 4 u) > 6.
+int dense_min_tokens(int tb, float density)
+{
+    const double rho = density > 0.f && density <= 1.f ? (double)density : 0.5;
+    const double u = 1.0 - std::pow(1.0 - rho, (double)tb);
+    const double per_chunk = 0.3125 + 4.0 * u;
+    return tb * (int)std::floor(6.0 / per_chunk) + 1;
 }
 
 hipError_t launch_sparse(const SparseArgs &a, bool bf16, int tb, hipStream_t s)
@@ -348,6 +371,16 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
     if (!ws || ws_bytes == 0) return MOE_ERR_INVALID_ARG;
     if (!aligned(ws, 4) || ws_bytes % 4 != 0) return MOE_ERR_ALIGNMENT;
     return hip_status(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+int moe_auto_dense_min(const moe_layer *L, int T)
+{
+    if (!L || T < 1 || L->n_routed < 1 || L->top_k < 1 || L->top_k > L->n_routed) return 0;
+    const bool gemm_ok = L->up_dense && L->down_dense && L->d % 256 == 0 && L->f % 128 == 0;
+    if (!gemm_ok) return 0;
+    const SparsePlan sp = layer_plan(T, L->d, L->f, L->n_routed, L->top_k, L->n_shared);
+    const int n = dense_min_tokens(sp.tb, L->density);
+    return n > T ? 0 : n;
 }
 
 moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void *router_w,
@@ -515,11 +548,21 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     const bool want_masks = trace && (trace->masks || trace->mask_bits || trace->nnz);
     const bool gemm_ok = L->up_dense && L->down_dense && d % 256 == 0 && f % 128 == 0;
     const bool old_ok = L->wdt == MOE_BF16 && L->up_dense && f % 256 == 0 && d % 128 == 0;
+    const SparsePlan sp = layer_plan(T, d, f, E, k, S);
+    const bool dense_aligned = L->up_dense && aligned(L->up_dense, 16) &&
+                               (!L->down_dense || aligned(L->down_dense, 16));
+    int nstar = 0;                  // per expert: experts with >= nstar tokens take the dense path
     if (path == MOE_PATH_AUTO) {
-        const bool dense_ok = (gemm_ok || old_ok) && aligned(L->up_dense, 16) &&
-                              (!L->down_dense || aligned(L->down_dense, 16)) && !want_masks;
-        path = dense_ok && (long long)T * k >= 8ll * E ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+        if (gemm_ok && dense_aligned && !want_masks) {
+            nstar = dense_min_tokens(sp.tb, L->density);
+            if (nstar > T) nstar = 0;               // no expert can reach it
+            path = nstar > 0 ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+        } else {
+            path = old_ok && dense_aligned && !want_masks && (long long)T * k >= 8ll * E
+                       ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+        }
     }
+    const bool mixed = nstar > 1;   // (nstar == 1: every expert with tokens is dense)
     if (path == MOE_PATH_DENSE) {
         if (!gemm_ok && !old_ok) return MOE_ERR_UNSUPPORTED;
         if (!aligned(L->up_dense, 16) || (L->down_dense && !aligned(L->down_dense, 16)))
@@ -549,14 +592,19 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.offset = w.offset; r.pairs = w.pairs;
     r.active = w.active; r.n_active = w.n_active;
     r.lg_buf = route_split(d, E, L->rdt) ? w.lg : nullptr;
-    const SparsePlan sp = layer_plan(T, d, f, E, k, S);
     const bool use_gemm = path == MOE_PATH_DENSE && gemm_ok;
-    if (path == MOE_PATH_SPARSE) {
+    if (path == MOE_PATH_SPARSE || mixed) {
         r.chunk = sp.tb; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;
-        if (sp.tb == 1) r.chunk_rec = w.chunk_rec;
-    } else if (use_gemm) {
-        r.chunk = kGemmChunk; r.chunk_tab = w.chunk_tab; r.n_chunks = w.n_chunks;
+        if (sp.tb == 1 && !mixed) r.chunk_rec = w.chunk_rec;
     }
+    if (path == MOE_PATH_DENSE) {
+        // experts with at least dense_min pairs are listed in 256-token chunks
+        r.dense_min = mixed ? nstar : 1;
+        r.dense_chunk = kGemmChunk; r.chunk_tab2 = w.chunk_tab2; r.n_chunks2 = w.n_chunks2;
+    }
+    r.expert_dense = (trace && trace->expert_dense) ? trace->expert_dense
+                   : (mixed ? w.expert_dense : nullptr);
+    const bool shared_dense = path == MOE_PATH_DENSE && (!mixed || T >= nstar);
     hipError_t he = launch_route(r, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
 
@@ -565,21 +613,52 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     red.d = d; red.T = T; red.layer = 1; red.rows_per_tok = k + S; red.k = k; red.S = S;
     red.part = w.part;
     red.y = y; red.ydt = (int)ydt; red.accumulate = 0;
+    const int ksplit = use_gemm ? gemm_ksplit(T, k, E, S, d, f) : 0;
+    const TilePlan tp = sp.tp;
+    const int stride = mixed ? (tp.tiles > ksplit ? tp.tiles : ksplit) : 0;
+    if (mixed) {
+        // the sparse experts: the sparse kernel over the sparse chunk table
+        // (and the shared experts unless they are dense)
+        SparseArgs a{};
+        a.d = d; a.f = f;
+        a.slots = sp.slots;
+        a.cpw = tp.cpw;
+        a.tiles = tp.tiles;
+        a.up_q = L->up_q; a.up_sz = L->up_sz;
+        a.gate = (const uint16_t *)L->gate_t; a.down = (const uint16_t *)L->down;
+        a.q_stride = qs; a.sz_stride = szs; a.w_stride = wst;
+        a.thr_dev = L->thresholds; a.thr = 0.f;
+        a.x = (const uint16_t *)x; a.T = T;
+        a.layer = 1; a.E = E; a.k = k; a.S = shared_dense ? 0 : S;
+        a.chunk_tab = w.chunk_tab; a.n_chunks = w.n_chunks;
+        a.offset = w.offset; a.pairs = w.pairs;
+        a.topk_w = r.topk_w;
+        a.part = w.part; a.part_stride = stride;
+        he = launch_sparse(a, L->wdt == MOE_BF16, sp.tb, s);
+        if (he != hipSuccess) return MOE_ERR_HIP;
+    }
     if (use_gemm) {
+        const int Sg = shared_dense ? S : 0;
         GemmArgs g{};
-        g.d = d; g.f = f; g.E = E; g.k = k; g.S = S; g.T = T;
+        g.d = d; g.f = f; g.E = E; g.k = k; g.S = Sg; g.T = T;
         g.bf16 = L->wdt == MOE_BF16 ? 1 : 0;
         g.x = (const uint16_t *)x;
         g.gate = (const uint16_t *)L->gate_t; g.up = L->up_dense;
         g.down_t = (const uint16_t *)L->down_dense;
-        g.h16 = (uint16_t *)w.h; g.part = w.part;
-        g.chunk_tab = w.chunk_tab; g.n_chunks = w.n_chunks; g.offset = w.offset; g.pairs = w.pairs;
+        g.h16 = (uint16_t *)w.h; g.part = w.part; g.part_stride = stride;
+        g.chunk_tab = w.chunk_tab2; g.n_chunks = w.n_chunks2; g.offset = w.offset; g.pairs = w.pairs;
         g.topk_w = r.topk_w;
-        g.grid_chunks = gemm_grid_chunks(T, k, E, S);
-        g.ksplit = gemm_ksplit(T, k, E, S, d, f);
+        g.grid_chunks = gemm_grid_chunks(T, k, E, Sg);
+        g.ksplit = ksplit;
         he = launch_gemm_layer(g, s);
         if (he != hipSuccess) return MOE_ERR_HIP;
-        red.tiles = g.ksplit;
+        if (mixed) {
+            red.tiles = tp.tiles; red.stride = stride;
+            red.mix = 1; red.tiles_dense = ksplit; red.shared_dense = shared_dense ? 1 : 0;
+            red.topk_idx = r.topk_idx; red.expert_dense = r.expert_dense;
+        } else {
+            red.tiles = ksplit;
+        }
         return hip_status(launch_reduce(red, s));
     }
     if (path == MOE_PATH_DENSE) {
@@ -596,7 +675,6 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         return hip_status(launch_reduce(red, s));
     }
 
-    const TilePlan tp = sp.tp;
     SparseArgs a{};
     a.d = d; a.f = f;
     a.slots = sp.slots;

@@ -338,7 +338,8 @@ gemm_kernel(GemmArgs a)
             for (int r = 0; r < 16; ++r) {
                 const int m = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (m >= ch.ntok) continue;
-                float *dst = a.part + ((size_t)row_s[m] * a.ksplit + ks) * d + (size_t)nt * kNT +
+                const int pstride = a.part_stride > 0 ? a.part_stride : a.ksplit;
+                float *dst = a.part + ((size_t)row_s[m] * pstride + ks) * d + (size_t)nt * kNT +
                              32 * kWNB * wn + li;
                 const float sc = sc_s[m];
 #pragma unroll

@@ -805,7 +805,8 @@ expert_kernel(SparseArgs a)
     for (int tb = 0; tb < TB; ++tb) {
         if (tb >= nt) continue;
         const float sc = L.tok_sc[tb];
-        float *dst = a.part + ((size_t)L.tok_row[tb] * a.tiles + tile) * d;
+        const int pstride = a.part_stride > 0 ? a.part_stride : a.tiles;
+        float *dst = a.part + ((size_t)L.tok_row[tb] * pstride + tile) * d;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + THREADS * i;

@@ -33,7 +33,8 @@ struct SparseArgs {
     const int32_t *pairs;               // [T*k]
     const float *topk_w;                // [T*k]
     // outputs
-    float *part;                        // partial rows [rows][tiles][d] (workspace)
+    float *part;                        // partial rows [rows][part_stride][d] (workspace)
+    int part_stride;                    // partial slots per row (0: tiles)
     uint8_t *mask_out;                  // single: [T][f]; layer: [T][k+S][f]
     float *v_out;                       // single only: [T][f]
 };
@@ -47,14 +48,21 @@ hipError_t launch_sparse_expert_bf16(const SparseArgs &a, int tb, hipStream_t s)
 constexpr int kMaxExpertsPerToken = 1024;   // k + S of a layer (routed + shared rows per token)
 
 struct ReduceArgs {
-    const float *part;                  // [rows][tiles][d]
+    const float *part;                  // [rows][stride][d]; a row's first slots hold its partials
     int tiles, d, T;
+    int stride;                         // partial slots per row (0: tiles)
     int layer;                          // 0: row of token t is t; 1: routed + shared rows
     int rows_per_tok;                   // 1 or k + S
     int k, S;
     void *y;
     int ydt;
     int accumulate;
+    // path chosen per expert (mix != 0, layer): a routed row holds tiles_dense
+    // partials when its expert took the dense path (expert_dense[topk_idx]),
+    // else tiles; the shared rows hold tiles_dense when shared_dense
+    int mix, tiles_dense, shared_dense;
+    const int32_t *topk_idx;
+    const uint8_t *expert_dense;
 };
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s);
 
@@ -76,6 +84,11 @@ struct RouteArgs {
     float *lg_buf;                      // [T][E] workspace for the wide-router split (route_split)
     int32_t *chunk_rec;                 // nullable, with chunk == 1: [T*k][4] per-chunk records
     int32_t *eam_row;                   // nullable: [E] per-expert counts are added into it
+    // path chosen per expert (dense_min > 0): experts with at least dense_min
+    // pairs go to the dense kernels, listed in chunks of dense_chunk
+    int dense_min, dense_chunk;
+    int32_t *chunk_tab2, *n_chunks2;    // dense chunks
+    uint8_t *expert_dense;              // nullable: [E] 1 where the expert took the dense path
 };
 // Routers with more than 8 experts whose rows are large per token (E d
 // element bytes above 32 KB) compute their logits in a separate kernel spread
@@ -111,7 +124,8 @@ struct GemmArgs {
     const uint16_t *gate, *up;          // [E+S][f][d]
     const uint16_t *down_t;             // [E+S][d][f]
     uint16_t *h16;                      // [T (k + S)][f] workspace, 16-bit
-    float *part;                        // [T (k + S)][ksplit][d] partial rows
+    float *part;                        // [T (k + S)][part_stride][d] partial rows
+    int part_stride;                    // partial slots per row (0: ksplit)
     const int32_t *chunk_tab, *n_chunks, *offset, *pairs;
     const float *topk_w;
     int ksplit;                         // split of f in the down product

@@ -26,6 +26,44 @@ __device__ __forceinline__ int part_row(const ReduceArgs &a, int t, int ri)
     return a.T * a.k + (ri - a.k) * a.T + t;
 }
 
+// Partials held by row ri of token t (at least one).
+__device__ __forceinline__ int part_tiles(const ReduceArgs &a, int t, int ri)
+{
+    if (!a.mix) return a.tiles;
+    if (ri < a.k) return a.expert_dense[a.topk_idx[(size_t)t * a.k + ri]] ? a.tiles_dense : a.tiles;
+    return a.shared_dense ? a.tiles_dense : a.tiles;
+}
+
+// Row table of token t in LDS: partial row, and the first contribution of
+// each row (prefix over the rows' partial counts); returns the total.
+__device__ int stage_rows(const ReduceArgs &a, int t, int *rows_s, int *pre_s)
+{
+    const int R = a.rows_per_tok;
+    for (int ri = threadIdx.x; ri < R; ri += blockDim.x) {
+        rows_s[ri] = part_row(a, t, ri);
+        pre_s[ri + 1] = part_tiles(a, t, ri);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {                       // k + S <= 1024 rows: a short serial prefix
+        pre_s[0] = 0;
+        for (int ri = 0; ri < R; ++ri) pre_s[ri + 1] += pre_s[ri];
+    }
+    __syncthreads();
+    return pre_s[R];
+}
+
+// Row holding contribution c (largest ri with pre_s[ri] <= c).
+__device__ __forceinline__ int row_of(const int *pre_s, int R, int c)
+{
+    int lo = 0, hi = R - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre_s[mid] <= c) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 // One workgroup per (token, 32 columns): d/32 * T workgroups, so the partial
 // rows are read by many compute units at once, in whole 128-byte lines.
 // Contribution c = ri * tiles + tile (row ri of the token, tile `tile`); group g
@@ -38,31 +76,30 @@ reduce_kernel(ReduceArgs a)
 {
     __shared__ float4 sm[kRedThreads / 64][kSeg];
     __shared__ int rows_s[LAYER ? kMaxRowsPerTok : 1];
+    __shared__ int pre_s[LAYER ? kMaxRowsPerTok + 1 : 1];
     const int cblocks = a.d / kCols;
     const int t = blockIdx.x / cblocks;
     const int cb = blockIdx.x - t * cblocks;
-    if constexpr (LAYER) {
-        for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRedThreads) rows_s[ri] = part_row(a, t, ri);
-        __syncthreads();
-    }
+    const int stride = a.stride > 0 ? a.stride : a.tiles;
     const int cq = threadIdx.x % kSeg, tg = threadIdx.x / kSeg;
     const int col = cb * kCols + cq * 4;
-    const int n = a.rows_per_tok * a.tiles;
-    // (row, tile) of this thread's next contribution, advanced by kGroups at a time
-    int ri = tg / a.tiles, tile = tg - ri * a.tiles;
-    const int dri = kGroups / a.tiles, dtile = kGroups - dri * a.tiles;
+    int n;
+    if constexpr (LAYER) n = stage_rows(a, t, rows_s, pre_s);
+    else n = a.tiles;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = tg; c0 < n; c0 += kGroups * kBatch) {
         float4 v[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-            const bool ok = c0 + b * kGroups < n;
-            const int r = ok ? ri : 0, tl = ok ? tile : 0;
-            const int row = LAYER ? rows_s[r] : t;
-            v[b] = load_nt16f(a.part + ((size_t)row * a.tiles + tl) * a.d + col);
-            ri += dri;
-            tile += dtile;
-            if (tile >= a.tiles) { tile -= a.tiles; ++ri; }
+            const int c = c0 + b * kGroups;
+            const bool ok = c < n;
+            int row = t, tl = ok ? c : 0;
+            if constexpr (LAYER) {
+                const int r = ok ? row_of(pre_s, a.rows_per_tok, c) : 0;
+                row = rows_s[r];
+                tl = ok ? c - pre_s[r] : 0;
+            }
+            v[b] = load_nt16f(a.part + ((size_t)row * stride + tl) * a.d + col);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -109,13 +146,13 @@ __global__ void __launch_bounds__(kRowThreads)
 reduce_rows_kernel(ReduceArgs a)
 {
     __shared__ int rows_s[kMaxRowsPerTok];
+    __shared__ int pre_s[kMaxRowsPerTok + 1];
     const int cblocks = (a.d + kRowCols - 1) / kRowCols;
     const int t = blockIdx.x / cblocks;
     const int col = (blockIdx.x - t * cblocks) * kRowCols + threadIdx.x * 4;
-    for (int ri = threadIdx.x; ri < a.rows_per_tok; ri += kRowThreads) rows_s[ri] = part_row(a, t, ri);
-    __syncthreads();
+    const int stride = a.stride > 0 ? a.stride : a.tiles;
+    const int n = stage_rows(a, t, rows_s, pre_s);
     if (col >= a.d) return;
-    const int n = a.rows_per_tok * a.tiles;
     int ri = 0, tile = 0;                       // (row, tile) of contribution c0 + b
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c0 = 0; c0 < n; c0 += kRowBatch) {
@@ -124,8 +161,11 @@ reduce_rows_kernel(ReduceArgs a)
         for (int b = 0; b < kRowBatch; ++b) {
             const bool ok = c0 + b < n;
             const int r = ok ? ri : 0, tl = ok ? tile : 0;
-            v[b] = load_nt16f(a.part + ((size_t)rows_s[r] * a.tiles + tl) * a.d + col);
-            if (++tile == a.tiles) { tile = 0; ++ri; }
+            v[b] = load_nt16f(a.part + ((size_t)rows_s[r] * stride + tl) * a.d + col);
+            if (ok && ++tile == pre_s[ri + 1] - pre_s[ri]) {   // every row holds >= 1
+                tile = 0;
+                ++ri;
+            }
         }
 #pragma unroll
         for (int b = 0; b < kRowBatch; ++b) {
@@ -146,7 +186,8 @@ reduce_rows_kernel(ReduceArgs a)
 hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
     if (a.d % kCols != 0 || a.rows_per_tok > kMaxRowsPerTok) return hipErrorInvalidValue;
-    if (a.rows_per_tok * a.tiles <= kRowMax) {
+    const int most = a.mix && a.tiles_dense > a.tiles ? a.tiles_dense : a.tiles;
+    if (a.rows_per_tok * most <= kRowMax) {
         const int cblocks = (a.d + kRowCols - 1) / kRowCols;
         hipLaunchKernelGGL(reduce_rows_kernel, dim3(a.T * cblocks), dim3(kRowThreads), 0, s, a);
     } else {

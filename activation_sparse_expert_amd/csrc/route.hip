@@ -222,11 +222,59 @@ route_logits_kernel(RouteArgs a)
     if (lane == 0) a.lg_buf[(size_t)t * a.E + e] = v;
 }
 
+// Exclusive scan over the experts of two packed 64-bit values per thread
+// (experts 2 tid and 2 tid + 1): returns the exclusive prefixes and the total.
+__device__ void expert_exscan(unsigned long long v0, unsigned long long v1,
+                              unsigned long long &ex0, unsigned long long &ex1,
+                              unsigned long long &total)
+{
+    __shared__ unsigned long long wsum[kRouteWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned long long incl = v0 + v1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    unsigned long long base = 0ull;
+    total = 0ull;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) {
+        if (w < wave) base += wsum[w];
+        total += wsum[w];
+    }
+    ex0 = base + incl - v0 - v1;
+    ex1 = ex0 + v0;
+    __syncthreads();                                 // wsum is reused by the next scan
+}
+
+// Chunk ci of a table whose experts start at chunks cst[0..E] belongs to the
+// last expert whose first chunk is <= ci (experts without chunks share the
+// next one's start): entry = expert << 16 | first grouped position.
+__device__ void write_chunks(const int *cst, const int *run, int E, int csize, int32_t *tab)
+{
+    const int nc = cst[E];
+    for (int ci = threadIdx.x; ci < nc; ci += kRouteThreads) {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cst[mid] <= ci) lo = mid;
+            else hi = mid - 1;
+        }
+        tab[ci] = (lo << 16) | (run[lo] + (ci - cst[lo]) * csize);
+    }
+}
+
 // Counting sort of the T*k pairs by expert, stable in pair order.  Reads the
 // top-k indices through coherent loads (they were written by this or an
 // earlier kernel).  With a.chunk > 0 it also lists every expert's pairs in
 // chunks of a.chunk consecutive grouped positions (the last one shorter),
-// experts in ascending order: entry = expert << 16 | first position.
+// experts in ascending order: entry = expert << 16 | first position.  With
+// a.dense_min > 0 (a layer call that chooses the path per expert) experts with
+// at least dense_min pairs are listed instead in chunks of a.dense_chunk in a
+// second table (chunk_tab2 / n_chunks2) and flagged in expert_dense.
 __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, int my_e, float my_w)
 {
     // reg: every pair is p = tid and this thread's pair chose expert my_e with
@@ -238,6 +286,7 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
     int *run = cnt + E;                              // [E] running placement base
     int *ce = run + E;                               // [kRouteThreads] experts of a batch of pairs
     int *cst = ce + kRouteThreads;                   // [E+1] first chunk of each expert
+    int *cst2 = cst + E + 1;                         // [E+1] first dense chunk of each expert
     const int P = a.T * a.k;
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
@@ -247,34 +296,37 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
     // one exclusive scan over the experts gives, packed in 64 bits, the pair
     // offset (bits 0-23), the first chunk (24-47) and the position in the
     // active list (48-63) of every expert; no field can overflow (at most
-    // 65536 pairs, chunks or experts)
+    // 65536 pairs, chunks or experts).  A second scan gives the first dense
+    // chunk when the path is chosen per expert.
     {
-        __shared__ unsigned long long wsum[kRouteWaves];
-        const int lane = tid & 63, wave = tid >> 6;
+        auto is_dense = [&](int e) { return a.dense_min > 0 && cnt[e] >= a.dense_min; };
         auto pack = [&](int e) -> unsigned long long {
             if (e >= E) return 0ull;
             const unsigned long long c = (unsigned)cnt[e];
-            const unsigned long long nch = a.chunk > 0 ? (c + a.chunk - 1) / a.chunk : 0ull;
+            const unsigned long long nch =
+                a.chunk > 0 && !is_dense(e) ? (c + a.chunk - 1) / a.chunk : 0ull;
             return c | (nch << 24) | ((unsigned long long)(c > 0) << 48);
         };
         const int e0 = 2 * tid;                      // this thread's experts: e0, e0 + 1 (E <= 1024)
-        const unsigned long long v0 = pack(e0), v1 = pack(e0 + 1);
-        unsigned long long incl = v0 + v1;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const unsigned long long o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        __syncthreads();
-        unsigned long long base = 0ull, total = 0ull;
-#pragma unroll
-        for (int w = 0; w < kRouteWaves; ++w) {
-            if (w < wave) base += wsum[w];
-            total += wsum[w];
-        }
-        const unsigned long long ex0 = base + incl - v0 - v1, ex1 = ex0 + v0;
+        unsigned long long ex0, ex1, total;
+        expert_exscan(pack(e0), pack(e0 + 1), ex0, ex1, total);
         const unsigned long long ex[2] = {ex0, ex1};
+        if (a.dense_min > 0) {
+            auto dpack = [&](int e) -> unsigned long long {
+                return e < E && is_dense(e) ? (unsigned long long)((cnt[e] + a.dense_chunk - 1) /
+                                                                   a.dense_chunk) : 0ull;
+            };
+            unsigned long long d0, d1, dtot;
+            expert_exscan(dpack(e0), dpack(e0 + 1), d0, d1, dtot);
+            if (e0 < E) cst2[e0] = (int)d0;
+            if (e0 + 1 < E) cst2[e0 + 1] = (int)d1;
+            if (tid == 0) {
+                cst2[E] = (int)dtot;
+                *a.n_chunks2 = (int)dtot;
+            }
+        }
+        if (a.expert_dense)
+            for (int e = tid; e < E; e += kRouteThreads) a.expert_dense[e] = is_dense(e) ? 1 : 0;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int e = e0 + i;
@@ -296,20 +348,8 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
         }
     }
     __syncthreads();
-    if (a.chunk > 0) {
-        // chunk ci belongs to the last expert whose first chunk is <= ci
-        // (experts without pairs own no chunk and share the next one's start)
-        const int nc = cst[E];
-        for (int ci = tid; ci < nc; ci += kRouteThreads) {
-            int lo = 0, hi = E - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (cst[mid] <= ci) lo = mid;
-                else hi = mid - 1;
-            }
-            a.chunk_tab[ci] = (lo << 16) | (run[lo] + (ci - cst[lo]) * a.chunk);
-        }
-    }
+    if (a.chunk > 0) write_chunks(cst, run, E, a.chunk, a.chunk_tab);
+    if (a.dense_min > 0) write_chunks(cst2, run, E, a.dense_chunk, a.chunk_tab2);
     __syncthreads();
     // stable placement, one chunk of pairs at a time
     for (int b = 0; b < P; b += kRouteThreads) {
@@ -469,7 +509,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 8 + 32;
-    const size_t lds_group = (size_t)a.E * 12 + kRouteThreads * 4 + 32;
+    const size_t lds_group = (size_t)a.E * 16 + kRouteThreads * 4 + 48;
     if (lds_group > lds) lds = lds_group;
     // 16-byte units per lane of one router row (64 lanes): CB (<= 8) of them per
     // expert and round, GE = 16 / CB experts per wave at a time

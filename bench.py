@@ -165,9 +165,11 @@ def batched_measure(reps=10, T=256, dense_only=False):
     ws = moe.new_workspace(L.workspace_bytes(T), dev)
     cnt = torch.empty(E, dtype=torch.int32, device=dev)
     out = {}
+    L.density = 1.0 - c["sparsity"]          # union-density input of MOE_PATH_AUTO's rule
     legs = (("dense_mfma", moe.PATH_DENSE, L),
             ("dense_mfma_rowmajor_down", moe.PATH_DENSE, L_rowmajor),
-            ("sparse", moe.PATH_SPARSE, L))
+            ("sparse", moe.PATH_SPARSE, L),
+            ("auto", moe.PATH_AUTO, L))
     if dense_only:
         legs, reps = legs[:1], 3
     for name, path, LL in legs:
@@ -190,6 +192,12 @@ def batched_measure(reps=10, T=256, dense_only=False):
         if name == "dense_mfma_rowmajor_down":
             out[name]["what"] = ("the older bf16 kernels (64/128-token passes, W^down read "
                                  "row-major), for comparison")
+        if name == "auto":
+            flags = torch.zeros(E, dtype=torch.uint8, device=dev)
+            moe.layer_forward(LL, x, path=path, y=y, ws=ws, trace={"expert_dense": flags})
+            out[name]["what"] = (f"per expert: dense MFMA at >= {LL.auto_dense_min(T)} tokens, "
+                                 f"density {LL.density:.2f}")
+            out[name]["dense_experts"] = int(flags.sum().item())
         if path == moe.PATH_DENSE:
             out[name]["mfma_util"] = flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
             out[name]["weight_gbs"] = wbytes / sec / 1e9
@@ -268,10 +276,11 @@ def device_layer(cfg, layer, E, S, k, d, f, wdt, xscale, sparsity, bias=None, ro
                      router_bias=None if bias is None else torch.from_numpy(bias).to(dev))
 
 
-def layer_bytes(L, masks, idx):
+def layer_bytes(L, masks, idx, dense=None):
     """Algorithmic bytes of one layer call: router rows, and for every expert
     touched its INT2 codes, scales and the gate and down rows of the union of
-    its tokens' masks; x in and y out."""
+    its tokens' masks; x in and y out.  dense [E+S] (0/1): those experts read
+    their three 16-bit weight matrices whole instead."""
     T = masks.shape[0]
     d, f, E, k = L.d, L.f, L.E, L.k
     b = E * d * 2 + T * d * 2 + T * d * 4
@@ -280,6 +289,10 @@ def layer_bytes(L, masks, idx):
             sel = np.argwhere(idx == e)
             if len(sel) == 0:
                 continue
+        if dense is not None and dense[e]:
+            b += 3 * d * f * 2
+            continue
+        if e < E:
             union = np.zeros(f, dtype=bool)
             for t, s_ in sel:
                 union |= masks[t, s_].astype(bool)
@@ -315,36 +328,53 @@ def time_graph(fn, reps, inner):
     return e0.elapsed_time(e1) / 1e3 / (reps * inner)
 
 
-def layer_workload(layers, xs_by_layer, label):
+def layer_workload(layers, xs_by_layer, label, path=None):
     """Decode step through `layers` (one moe_layer_forward each, captured in a
-    graph): tokens/s and algorithmic GB/s."""
+    graph): tokens/s and algorithmic GB/s.  path: MOE_PATH_SPARSE (default) or
+    MOE_PATH_AUTO, whose per-expert choice is read back and priced (dense
+    experts at their three 16-bit matrices)."""
     import torch
     import activation_sparse_expert_amd as moe
     dev = torch.device("cuda:0")
+    path = moe.PATH_SPARSE if path is None else path
     T = xs_by_layer[0].shape[0]
     ys = [torch.empty((T, L.d), dtype=torch.float32, device=dev) for L in layers]
     wss = [moe.new_workspace(L.workspace_bytes(T), dev) for L in layers]
     total_b = 0
+    n_dense = 0
     for L, x, y, ws in zip(layers, xs_by_layer, ys, wss):
         tr = dict(topk_idx=torch.empty((T, L.k), dtype=torch.int32, device=dev),
                   masks=torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=dev))
         moe.layer_forward(L, x, y=y, ws=ws, trace=tr)
+        dense = None
+        if path == moe.PATH_AUTO:
+            flags = torch.zeros(L.E, dtype=torch.uint8, device=dev)
+            moe.layer_forward(L, x, path=path, y=y, ws=ws, trace=dict(expert_dense=flags))
+            nstar = L.auto_dense_min(T)
+            dense = np.concatenate([flags.cpu().numpy(),
+                                    np.full(L.S, 1 if 0 < nstar <= T else 0, np.uint8)])
+            n_dense += int(dense.sum())
         torch.cuda.synchronize()
-        total_b += layer_bytes(L, tr["masks"].cpu().numpy(), tr["topk_idx"].cpu().numpy())
+        total_b += layer_bytes(L, tr["masks"].cpu().numpy(), tr["topk_idx"].cpu().numpy(), dense)
 
     def step():
         for L, x, y, ws in zip(layers, xs_by_layer, ys, wss):
-            moe.layer_forward(L, x, y=y, ws=ws)
+            moe.layer_forward(L, x, path=path, y=y, ws=ws)
     sec = time_graph(step, reps=5, inner=4)
-    return {"workload": label, "tokens": T, "ms_per_step": sec * 1e3, "tokens_per_s": T / sec,
-            "bytes_per_step": total_b, "achieved_gbs": total_b / sec / 1e9,
-            "hbm_frac": total_b / sec / 1e9 / HBM_PEAK_GBS}
+    out = {"workload": label, "tokens": T, "ms_per_step": sec * 1e3, "tokens_per_s": T / sec,
+           "bytes_per_step": total_b, "achieved_gbs": total_b / sec / 1e9,
+           "hbm_frac": total_b / sec / 1e9 / HBM_PEAK_GBS}
+    if path == moe.PATH_AUTO:
+        out["dense_experts"] = n_dense
+    return out
 
 
-def layers_measure():
+def layers_measure(fine_only=False):
     """The 32-layer Mixtral stack (T = 1, 16) and the fine-grained 64+2 layer
-    (T = 1, 64), each as tokens/s of a decode step, router included."""
+    (T = 1, 64), each as tokens/s of a decode step, router included; the fine
+    layer again with dense copies under MOE_PATH_AUTO (T = 64, 256)."""
     import torch
+    import activation_sparse_expert_amd as moe
     import synth
     dev = torch.device("cuda:0")
     out = {}
@@ -357,8 +387,28 @@ def layers_measure():
         out[f"fine_T{T}"] = layer_workload(
             [fine], [x], f"DeepSeek-V2-Lite-shaped layer, 64 routed (top-6) + 2 shared experts, "
                          f"d=2048 f=1408, Zipf router bias, 70% sparsity, {T} tokens")
+    # the same layer with dense fp16 copies (up materialised, W^down transposed)
+    # under MOE_PATH_AUTO: experts with at least n* tokens take the MFMA path
+    n = c["E"] + c["S"]
+    fine.up_dense = torch.empty((n, c["f"], c["d"]), dtype=torch.float16, device=dev)
+    for e in range(n):
+        moe.materialize_up(fine.up_q[e], fine.up_sz[e], c["d"], torch.float16, out=fine.up_dense[e])
+    fine.down_dense = moe.transpose_down(fine.down)
+    fine.density = 1.0 - c["sparsity"]
+    for T in (64, 256):
+        x = torch.from_numpy(synth.tokens_f32(synth.CFG_FINE, T, c["d"], c["x_scale"])).half().to(dev)
+        r = layer_workload(
+            [fine], [x], f"the same layer with dense fp16 copies, MOE_PATH_AUTO (per expert: "
+                         f"dense MFMA at >= {fine.auto_dense_min(T)} tokens), {T} tokens",
+            path=moe.PATH_AUTO)
+        out[f"fine_T{T}_auto"] = r
+        if T == 256:
+            out["fine_T256"] = layer_workload(
+                [fine], [x], f"the same layer, sparse path for every expert, {T} tokens")
     del fine
     torch.cuda.empty_cache()
+    if fine_only:
+        return out
     c = synth.CONFIGS[synth.CFG_STACK]
     log("drawing the 32-layer stack (64.9 GB)")
     stack = [device_layer(synth.CFG_STACK, l, c["E"], 0, c["k"], c["d"], c["f"], c["wdt"], c["x_scale"],
@@ -539,6 +589,8 @@ def main():
                     help="skip the layer workloads (32-layer stack, fine-grained layer)")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched-layer (dense MFMA vs sparse) measurement")
+    ap.add_argument("--fine-only", action="store_true",
+                    help="only the fine-grained layer workloads (sparse and MOE_PATH_AUTO)")
     ap.add_argument("--variants-only", action="store_true",
                     help="only the 8/4/1-bit expert and EAMC measurements (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -554,6 +606,9 @@ def main():
         return
     if args.batched_only or args.dense_only:
         print(json.dumps({"batched": batched_measure(dense_only=args.dense_only)}), flush=True)
+        return
+    if args.fine_only:
+        print(json.dumps({"more": layers_measure(fine_only=True)}), flush=True)
         return
     if args.variants_only:
         print(json.dumps({"expert_up_bits": bits_measure(), "eamc_match": eamc_measure()}),

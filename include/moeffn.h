@@ -132,6 +132,11 @@ typedef struct {
                                    With it the dense path runs the 256 x 256-tile
                                    MFMA GEMM in bf16 or fp16; without it, bf16
                                    layers only, the older kernels.          */
+    float density;              /* expected fraction of the f channels active per
+                                   token under the thresholds (e.g. measured
+                                   from nnz exports, or 1 - the calibrated
+                                   sparsity); <= 0: 0.5.  Read by MOE_PATH_AUTO
+                                   only.                                     */
 } moe_layer;
 
 /* Optional device outputs of moe_layer_forward (any field may be NULL). */
@@ -153,6 +158,9 @@ typedef struct {
                                    path only)                                */
     int32_t *nnz;               /* [T][k+S] active channels per mask (sparse
                                    path only)                                */
+    uint8_t *expert_dense;      /* [E]: 1 where the routed expert took the dense
+                                   path in this call, else 0 (the shared
+                                   experts' path: moe_auto_dense_min)        */
 } moe_layer_trace;
 
 /*
@@ -248,16 +256,23 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
 /*
  * One MoE layer: route (as moe_route_topk) and combine
  *   y_t = sum_s w_{t,s} a_{e(t,s)}(x_t) + sum_i a_{E+i}(x_t)
- * where a_e is Algorithm 1 (MOE_PATH_SPARSE) or the dense SwiGLU with the bf16
- * up weights in L->up_dense (MOE_PATH_DENSE, which needs wdt == MOE_BF16).
- * MOE_PATH_AUTO picks per call, on the host, from the batch size (MoE-Lightning
- * review, "层次化屋顶模型": the expert FFN's operational intensity grows with the
- * tokens per expert): the dense path when it is available (bf16 weights,
- * up_dense set, its shape limits met, no mask export requested) and the routed
- * tokens average at least 8 per expert (T k >= 8 E), else the sparse path.  At
- * that size a sparse chunk of 4 tokens reads the union of 4 masks' rows (about
- * 76% of the rows at 70% sparsity) again for every chunk, more than one pass
- * over the dense weights.
+ * where a_e is Algorithm 1 (MOE_PATH_SPARSE) or the dense SwiGLU with the up
+ * weights in L->up_dense (MOE_PATH_DENSE: bf16 or fp16 with L->down_dense; bf16
+ * only without it).
+ * MOE_PATH_AUTO chooses per expert (MoE-Lightning review, "层次化屋顶模型", the
+ * classic roofline: the expert FFN's operational intensity grows with its
+ * tokens).  An expert with n tokens read by the sparse path costs
+ * ceil(n / TB) chunks of TB tokens (TB = 1, 2 or 4, as the sparse kernel
+ * chunks this call), each reading the INT2 up codes and scales (5/16 d f
+ * bytes) and the gate and down rows of the union of its tokens' masks, about
+ * 4 u d f bytes with u = 1 - (1 - L->density)^TB; the dense path reads the
+ * 16-bit gate, up and down weights once, 6 d f bytes.  With L->up_dense and
+ * L->down_dense set, the experts (routed and shared) whose token count n
+ * reaches the smallest n with ceil(n / TB) (5/16 + 4 u) > 6 take the dense
+ * path and the others the sparse path, in one call (the routed experts decide
+ * on the device from the call's counts: no host synchronisation).  Without
+ * down_dense (bf16 layers), the whole call takes the dense path when
+ * T k >= 8 E.  A call that exports masks takes the sparse path throughout.
  *   x [T][d] in xdt (== L->wdt), y [T][d] in ydt (overwritten).
  * trace (host struct, NULL allowed) receives the optional exports.
  */
@@ -265,6 +280,15 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
                              void *y, moe_dtype ydt, moe_path path,
                              const moe_layer_trace *trace,
                              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The per-expert rule of MOE_PATH_AUTO for a call of T tokens on this layer:
+ * the token count from which an expert takes the dense path (the shared
+ * experts take it when T reaches it), or 0 when the call takes the sparse
+ * path throughout (no dense weights, or no expert can reach the count).  Host
+ * arithmetic only; the same value the layer call uses.
+ */
+int moe_auto_dense_min(const moe_layer *L, int T);
 
 /*
  * Threshold calibration (FloE review, "高效稀疏 GEMV 内核": t_ij sets the

@@ -63,7 +63,7 @@ def lib():
                                             P, P, P, I]
         L.oracle_route_topk.argtypes = [P, I, I, I, P, I, P, I, I, I, P, P, P, P, P, P]
         L.oracle_layer_forward.argtypes = [P, I, I, I, I, P, I, P, I, I, I, I, P, P, P, P, I,
-                                           P, I, P, P, P, P, P, P]
+                                           P, I, P, P, P, P, P, P, P]
         L.oracle_ream_add.argtypes = [P, I, I, P]
         L.oracle_pack_up_bits.argtypes = [P, I, I, I, P, P]
         L.oracle_dequant_up_bits.argtypes = [P, P, I, I, I, P]
@@ -214,11 +214,12 @@ def route_topk(x_bits, xdt, router_bits, rdt, E, k, renormalize=True, bias=None)
 
 def layer_forward(x_bits, xdt, router_bits, rdt, bias, E, k, S, renormalize,
                   up_q, up_sz, gate_bits, down_bits, wdt, thr, dense=False,
-                  topk_in=None, masks_in=None):
+                  topk_in=None, masks_in=None, dense_experts=None):
     """One MoE layer, E routed (top-k) + S shared experts at a fixed stride.
     up_q [E+S][f][d/4], up_sz [E+S][f][d/64][2], gate/down [E+S][f][d],
-    thr [E+S].  Returns (y [T][d] f64, topk_idx [T][k], topk_w [T][k],
-    masks [T][k+S][f] u8)."""
+    thr [E+S].  dense: every expert on the dense path; dense_experts [E+S]
+    (0/1): that path for the flagged experts only.  Returns (y [T][d] f64,
+    topk_idx [T][k], topk_w [T][k], masks [T][k+S][f] u8)."""
     xa = _c(x_bits, np.float32 if xdt == "f32" else np.uint16)
     T, d = xa.shape
     up_q = _c(up_q, np.uint8)
@@ -233,13 +234,15 @@ def layer_forward(x_bits, xdt, router_bits, rdt, bias, E, k, S, renormalize,
     assert up_q.shape == (E + S, f, d // 4) and g.shape == (E + S, f, d)
     ti = None if topk_in is None else _c(topk_in, np.int32)
     mi = None if masks_in is None else _c(masks_in, np.uint8)
+    de = None if dense_experts is None else _c(dense_experts, np.uint8)
+    assert de is None or de.shape == (E + S,)
     y = np.empty((T, d), dtype=np.float64)
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
     m = np.empty((T, k + S, f), dtype=np.uint8)
     lib().oracle_layer_forward(_p(xa), DT[xdt], T, d, f, _p(ra), DT[rdt], _p(b), E, k, S,
                                int(bool(renormalize)), _p(up_q), _p(up_sz), _p(g), _p(dn),
-                               DT[wdt], _p(th), int(bool(dense)), _p(ti), _p(mi), _p(y),
+                               DT[wdt], _p(th), int(bool(dense)), _p(de), _p(ti), _p(mi), _p(y),
                                _p(idx), _p(w), _p(m))
     return y, idx, w, m
 

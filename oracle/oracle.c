@@ -523,6 +523,10 @@ void oracle_route_topk(const void *x, int xdt, int T, int d, const void *router_
  *   active and the up weights taken as rne(dequant(INT2)) in the layer's 16-bit
  *   type (bf16 for bf16 layers, fp16 for fp16 layers); gate/down are read in
  *   wdt as for the sparse path.
+ * dense_experts [E+S] (optional): the dense path for the experts flagged 1 and
+ *   Algorithm 1 for the others, within one layer (a per-expert choice of path,
+ *   MoE-Lightning review, "层次化屋顶模型"; both compute the same expert, the
+ *   dense one with every channel active).
  * Outputs: y [T][d]; optionally topk_idx/topk_w [T][k], masks_out [T][k+S][f].
  */
 void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
@@ -530,7 +534,7 @@ void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
                           int E, int k, int S, int renormalize,
                           const uint8_t *up_q, const uint16_t *up_sz,
                           const void *gate_t, const void *down, int wdt,
-                          const float *thr, int dense,
+                          const float *thr, int dense, const uint8_t *dense_experts,
                           const int32_t *topk_in, const uint8_t *masks_in,
                           double *y, int32_t *topk_idx_out, double *topk_w_out,
                           uint8_t *masks_out)
@@ -582,7 +586,7 @@ void oracle_layer_forward(const void *x, int xdt, int T, int d, int f,
             const uint8_t *uq = up_q + (size_t)e * qstride;
             const uint16_t *us = up_sz + (size_t)e * szstride;
             const void *xt = (const char *)x + (size_t)t * d * (xdt == ODT_F32 ? 4 : 2);
-            if (!dense) {
+            if (!(dense || (dense_experts && dense_experts[e]))) {
                 oracle_expert_forward(xt, xdt, 1, d, f, uq, us, gt, dn, wdt, thr[e], &sc, mi,
                                       NULL, mo, ytok, 0);
             } else {

@@ -138,7 +138,7 @@ def test_route_rejects(kw, code):
 def _layer_desc(**kw):
     base = dict(d=4096, f=14336, n_routed=8, n_shared=0, top_k=2, renormalize=1, wdt=0,
                 router_w=FAKE, rdt=0, router_bias=None, up_q=FAKE, up_sz=FAKE, gate_t=FAKE,
-                down=FAKE, thresholds=FAKE, up_dense=None, down_dense=None)
+                down=FAKE, thresholds=FAKE, up_dense=None, down_dense=None, density=0.0)
     base.update(kw)
     return moe.LayerDesc(*[base[n] for n, _ in moe.LayerDesc._fields_])
 
@@ -178,6 +178,22 @@ def test_layer_dense_shape_limits():
     assert _layer(desc=d, path=1) == -2
     d = _layer_desc(wdt=0, up_dense=FAKE, down_dense=FAKE + 2)
     assert _layer(desc=d, path=1) == -3
+
+
+@pytest.mark.parametrize("density,T,k,E,expect", [
+    # tb = 4 chunks (d = 4096): one chunk reads 5/16 + 4 (1 - (1 - rho)^4) d f bytes
+    (0.3, 256, 2, 8, 5),       # 3.35 per chunk: a second chunk costs more than 6 -> 5 tokens
+    (0.1, 256, 2, 8, 13),      # 1.69 per chunk: 3 chunks still cost less -> 13 tokens
+    (0.2, 256, 2, 8, 9),       # 2.67 per chunk -> 9
+    (0.0, 256, 2, 8, 5),       # unset: 0.5 -> 3.06 per chunk -> 5
+    (0.1, 8, 2, 8, 0),         # tb = 2 at 2 tokens per expert: 11 tokens, more than the call has
+])
+def test_auto_dense_min(density, T, k, E, expect):
+    L = _lib_or_skip()
+    dsc = _layer_desc(n_routed=E, top_k=k, up_dense=FAKE, down_dense=FAKE, density=density)
+    assert L.moe_auto_dense_min(C.byref(dsc), T) == expect
+    # no dense weights: never
+    assert L.moe_auto_dense_min(C.byref(_layer_desc(density=density)), T) == 0
 
 
 def test_prep_entry_points_reject():

@@ -802,3 +802,42 @@ def test_stack_hidden_stream_keeps_cosine_above_095():
             cos = (a * b).sum(-1) / (np.linalg.norm(a, axis=-1) * np.linalg.norm(b, axis=-1))
             assert cos.shape == (c["L"] - 1, T)
             assert cos.min() >= 0.95, cos.min()
+
+
+def test_layer_per_expert_dense_flags_pick_each_experts_path():
+    """dense_experts: the flagged experts take the dense path (every channel,
+    up weights rounded to the layer type) and the others Algorithm 1; the
+    layer is the weighted sum of those per-expert results, each computed
+    alone."""
+    d, f, E, k, S, T = 128, 64, 4, 2, 1, 5
+    uq, us, g, dn = _tiny_layer(93, d, f, E, S)
+    x, R = _router_case(94, T, d, E)
+    thr = np.float32([0.01] * (E + S))
+    flags = np.array([1, 0, 1, 0, 1], dtype=np.uint8)
+    y, idx, w, m = oracle.layer_forward(x, "f16", R, "f16", None, E, k, S, True, uq, us, g, dn,
+                                        "f16", thr, dense_experts=flags)
+    y_dense, _, _, _ = oracle.layer_forward(x, "f16", R, "f16", None, E, k, S, True, uq, us, g,
+                                            dn, "f16", thr, dense=True)
+    y_sparse, _, _, _ = oracle.layer_forward(x, "f16", R, "f16", None, E, k, S, True, uq, us, g,
+                                             dn, "f16", thr)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for s_ in range(k + S):
+            e = idx[t, s_] if s_ < k else E + s_ - k
+            sc = w[t, s_] if s_ < k else 1.0
+            one_hot = np.zeros(E + S, np.uint8)
+            one_hot[e] = 1
+            # the expert alone through a layer call with only it flagged or not
+            if flags[e]:
+                assert np.all(m[t, s_] == 1)
+                up16 = oracle.dequant_up(uq[e], us[e], d).astype(np.float16).astype(np.float64)
+                X = _bits_to_f64(x[t:t + 1], "f16")
+                hg = X @ _bits_to_f64(g[e], "f16").T
+                hu = X @ up16.T
+                ref[t] += sc * ((hg * expit(hg) * hu) @ _bits_to_f64(dn[e], "f16"))[0]
+            else:
+                _, _, ye = oracle.expert_forward(x[t:t + 1], "f16", uq[e], us[e], g[e], dn[e],
+                                                 "f16", thr[e])
+                ref[t] += sc * ye[0]
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-14)
+    assert not np.allclose(y, y_dense) and not np.allclose(y, y_sparse)

@@ -236,6 +236,54 @@ def test_layer_auto_path(T, E, S, k, d, f, expect):
     assert not np.array_equal(y_auto, y_other)
 
 
+@pytest.mark.parametrize("wdt", ["f16", "bf16"])
+def test_layer_auto_per_expert_mixed(wdt):
+    """MOE_PATH_AUTO with dense weights chooses the path per expert in one call:
+    under a Zipf-skewed router the hot experts (at least moe_auto_dense_min
+    tokens) and the shared expert take the dense MFMA path, the others the
+    sparse kernel.  The exported per-expert flags follow that rule from the
+    call's counts, and y matches the oracle run with the same per-expert
+    paths (the sparse experts fed the masks of a sparse-path call of the same
+    tokens, which the chunking makes identical)."""
+    T, E, S, k, d, f = 64, 16, 1, 4, 512, 256
+    experts, thr = build_host_layer(70, E, S, d, f, wdt, 0.7, 1.0, layer=d)
+    R_bits = synth.to_bits(synth.router_f32(70, d, E, d), wdt)
+    bias = synth.zipf_bias(71, d, E, 1.1)
+    x_bits = synth.to_bits(synth.tokens_f32(72, T, d, 1.0, layer=d), wdt)
+    L = device_layer(experts, thr, R_bits, wdt, E, S, k, bias=bias, dense="gemm")
+    L.density = 0.3
+    nstar = L.auto_dense_min(T)
+    assert 1 < nstar <= T, nstar
+    x = to_dev_bits(x_bits, wdt)
+    flags = torch.zeros(E, dtype=torch.uint8, device=DEV)
+    idx_d = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    cnt_d = torch.empty(E, dtype=torch.int32, device=DEV)
+    w_d = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    y = moe.layer_forward(L, x, path=moe.PATH_AUTO,
+                          trace=dict(expert_dense=flags, topk_idx=idx_d, expert_count=cnt_d,
+                                     topk_w=w_d))
+    torch.cuda.synchronize()
+    cnt = cnt_d.cpu().numpy()
+    fl = flags.cpu().numpy()
+    assert np.array_equal(fl, (cnt >= nstar).astype(np.uint8)), (cnt, fl, nstar)
+    assert fl.any() and not fl[cnt > 0].all(), f"not a mixed call: counts {cnt.tolist()} n*={nstar}"
+    # the sparse experts' masks, from a sparse-path call of the same tokens
+    ys, tr = run_layer(L, x, moe.PATH_SPARSE)
+    assert np.array_equal(tr["topk_idx"], idx_d.cpu().numpy())
+    dense_experts = np.concatenate([fl, np.ones(S, np.uint8) * (T >= nstar)]).astype(np.uint8)
+    uq = np.stack([h.up_q for h in experts])
+    us = np.stack([h.up_sz for h in experts])
+    g = np.stack([h.gate for h in experts])
+    dn = np.stack([h.down for h in experts])
+    tokens = np.array([0, 1, 17, 40, 63])
+    y_ref, _, w_ref, _ = oracle.layer_forward(
+        x_bits[tokens], wdt, R_bits, wdt, bias, E, k, S, True, uq, us, g, dn, wdt, thr,
+        topk_in=tr["topk_idx"][tokens], masks_in=tr["masks"][tokens], dense_experts=dense_experts)
+    err = check_y(y.cpu().numpy()[tokens], y_ref, 2e-3, f"AUTO per-expert layer {wdt}")
+    say(f"AUTO per-expert {wdt}: n*={nstar}, dense experts {np.flatnonzero(fl).tolist()} "
+        f"(counts {cnt.tolist()}), shared dense {bool(T >= nstar)}, max relL2 {err:.2e}")
+
+
 def test_layer_hot_expert_many_chunks():
     """A router bias sends nearly every token to expert 3, which then holds
     about T/tb chunks of the sparse grid with a ragged last one, while the
