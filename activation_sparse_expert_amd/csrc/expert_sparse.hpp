@@ -13,10 +13,11 @@
 //      sum x q = 4 (S' - X_g).  The group's share of v is s (sum x q - z X_g),
 //      X_g being the group sum of x.  SEG lanes share one channel; the
 //      per-channel sums of up to 8 passes are reduced together by a transposed
-//      butterfly (each step halves the values a lane carries).  A single-token
-//      tile issues its code loads a few passes ahead of the decode (buffer
-//      loads over the tile; passes past its end read zeros), so the VALU work
-//      overlaps the stream instead of following it.
+//      butterfly (each step halves the values a lane carries).  Code loads
+//      run a few passes ahead of the decode (buffer loads over the tile;
+//      passes past its end read zeros), so the VALU work overlaps the stream
+//      instead of following it; with several tokens the code registers form
+//      a ring that keeps the lookahead across blocks.
 //   B  mask = |v| > t (fp32), union over the chunk's tokens, compacted into an
 //      ascending list of active channels with a wave ballot.
 //   C  for each active channel j: every thread reads its 16-byte chunk(s) of
@@ -39,6 +40,7 @@ namespace sparse {
 constexpr int kXPad = 72;               // halves per 64-element group slot in LDS (16 B pad)
 constexpr int kPB = 8;                  // channel passes loaded and reduced together
 constexpr int kAhead = 3;               // single-token tiles: passes of codes in flight
+constexpr int kAheadMulti = 6;          // multi-token tiles: passes in flight (rolling)
 
 template <int N>
 struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
@@ -279,11 +281,15 @@ __device__ __forceinline__ uint4 row_load(const uint16_t *p)
     else return *(const uint4 *)p;
 }
 
-// passes of channels per phase-A block (host and device)
+// passes of channels per phase-A block (host and device).  A single-token
+// block holds kPB / NG passes.  A multi-token block holds the same number of
+// passes as a ring of code registers: the loads run kAheadMulti passes
+// ahead across block boundaries, so each lane keeps that many 16-byte units
+// in flight however many tokens the chunk holds.
 template <int TB, class GEO>
 __host__ __device__ constexpr int pass_block()
 {
-    constexpr int pb = (kPB / (TB * GEO::NG)) < 1 ? 1 : (kPB / (TB * GEO::NG));
+    constexpr int pb = (kPB / GEO::NG) < 1 ? 1 : (kPB / GEO::NG);
     return pb < GEO::SEG ? pb : GEO::SEG;
 }
 
@@ -384,50 +390,38 @@ expert_kernel(SparseArgs a)
     const int passes = (nrows + ROWS_PASS - 1) / ROWS_PASS;
     const int CPR = d / 8;                          // 16-byte chunks per d-row
 
-    // phase-A code units of one block of PR passes: loads only, no use.  With
-    // several tokens per chunk a tile has many blocks, and the next block's
-    // units are loaded (into cqn) while the current one is multiplied.
-    uint4 cq[PR][NG], cqn[PR][NG];
-    uint32_t csz[PR][NG], cszn[PR][NG];
-    uint32_t okm = 0, okmn = 0;
-#define LOAD_BLOCK(P0, CQ, CSZ, OKM)                                                        \
-    {                                                                                       \
-        OKM = 0;                                                                            \
-        _Pragma("unroll") for (int p = 0; p < PR; ++p) {                                    \
-            _Pragma("unroll") for (int gi = 0; gi < NG; ++gi) {                             \
-                const int r = ((P0) + p) * ROWS_PASS + wave * RPW + rs;                     \
-                const int g = go + SEG * gi;                                                \
-                const bool ok = r < nrows && g < G;                                         \
-                const int rr = ok ? r : 0, gg = ok ? g : 0;                                 \
-                CQ[p][gi] = load_nt16(upq + (size_t)rr * (d / 4) + (size_t)gg * 16);        \
-                CSZ[p][gi] = load_nt4(upsz + ((size_t)rr * G + gg) * 2);                    \
-                OKM |= (ok ? 1u : 0u) << (p * NG + gi);                                     \
-            }                                                                               \
-        }                                                                                   \
-    }
-    auto load_block = [&](int p0) { LOAD_BLOCK(p0, cq, csz, okm) };
-    // Single-token tiles: the passes of a block are issued kAhead at a time
-    // (buffer loads over the tile; passes past the tile read zeros), so that
-    // the decode of early passes overlaps the rest of the stream.
-    constexpr bool LAZY = TB == 1;
-    constexpr int AH = kAhead < PR ? kAhead : PR;
+    // phase-A code units of one block of PR passes (slot p holds pass p0 + p)
+    uint4 cq[PR][NG];
+    uint32_t csz[PR][NG];
+    // The loads run AH passes ahead of the decode, as raw buffer loads over
+    // the tile (passes past its end read zeros without a memory access), so no
+    // branch separates them and the compiler's wait counts stay exact.  Single
+    // token: the passes of a block are issued AH at a time from its start.
+    // Several tokens (RING): the pass AH ahead goes into the slot freed by the
+    // pass just decoded, across block boundaries, so the stream never drains.
+    constexpr bool RING = TB > 1;
+    constexpr int AH = RING ? (kAheadMulti < PR ? kAheadMulti : PR - 1)
+                            : (kAhead < PR ? kAhead : PR);
+    static_assert(AH >= 1 || PR == 1, "lookahead");
+    constexpr int PRED = (TB >= 4 && PR >= 2) ? PR / 2 : PR;
     const __amdgpu_buffer_rsrc_t rq = tile_rsrc(upq, (uint32_t)nrows * (d / 4));
     const __amdgpu_buffer_rsrc_t rz = tile_rsrc(upsz, (uint32_t)nrows * G * 4);
     const int r_lane = wave * RPW + rs;             // channel of this lane in pass 0
     const uint32_t q_lane = (uint32_t)(r_lane * (d / 4) + go * 16);
     const uint32_t z_lane = (uint32_t)((r_lane * G + go) * 4);
-#define LOAD_PASS(P0, p)                                                                    \
+#define LOAD_SLOT(PP, SLOT)                                                                 \
     {                                                                                       \
-        const int pp = (P0) + (p);                                                          \
+        const int pp = (PP);                                                                \
         const bool rok = r_lane + pp * ROWS_PASS < nrows;                                   \
         _Pragma("unroll") for (int gi = 0; gi < NG; ++gi) {                                 \
             const bool ok = rok && go + SEG * gi < G;                                       \
             const uint32_t oq = q_lane + (uint32_t)(pp * ROWS_PASS * (d / 4) + gi * SEG * 16); \
             const uint32_t oz = z_lane + (uint32_t)((pp * ROWS_PASS * G + gi * SEG) * 4);   \
-            cq[p][gi] = bload_nt16(rq, ok ? oq : kOob);                                     \
-            csz[p][gi] = bload_nt4(rz, ok ? oz : kOob);                                     \
+            cq[SLOT][gi] = bload_nt16(rq, ok ? oq : kOob);                                  \
+            csz[SLOT][gi] = bload_nt4(rz, ok ? oz : kOob);                                  \
         }                                                                                   \
     }
+#define LOAD_PASS(P0, p) LOAD_SLOT((P0) + (p), p)
 
     // 16-byte x chunks each thread stages per token chunk
     constexpr int XL = (TB * 8 * SEG * NG + THREADS - 1) / THREADS;
@@ -490,15 +484,11 @@ expert_kernel(SparseArgs a)
         }
     }
     // up codes do not depend on x: in flight while x is staged (x first)
-    if constexpr (LAZY) {
-        __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int p = 0; p < AH; ++p) {
-            LOAD_PASS(0, p)
-            __builtin_amdgcn_sched_barrier(0);      // keep the passes in order
-        }
-    } else {
-        load_block(0);
+    for (int p = 0; p < AH; ++p) {
+        LOAD_PASS(0, p)
+        __builtin_amdgcn_sched_barrier(0);          // keep the passes in order
     }
 #pragma unroll
     for (int u = 0; u < XL; ++u) {
@@ -558,88 +548,84 @@ expert_kernel(SparseArgs a)
     }
     // ONE: the tile is a single block of passes (straight-line code)
     for (int p0 = 0; p0 < (ONE ? 1 : passes); p0 += PR) {
-        if constexpr (TB > 1) {
-            if (p0 + PR < passes) LOAD_BLOCK(p0 + PR, cqn, cszn, okmn)
-        } else if constexpr (!ONE) {
+        if constexpr (!RING && !ONE) {
             if (p0 > 0) {
 #pragma unroll
                 for (int p = 0; p < AH; ++p) LOAD_PASS(p0, p)
             }
         }
-        // units outside the tile (ok bit clear) get s = 0 when used: the select
-        // is kept away from the loads so that they all issue back to back
-        float part[TB][PR];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int p = 0; p < PR; ++p) part[tb][p] = 0.f;
+        // The passes' per-lane sums are reduced over the segment's lanes in
+        // groups of PRED passes (half a block with four tokens, to bound
+        // registers), right after the group's last pass.
+        float part[TB][PRED];
 #pragma unroll
         for (int p = 0; p < PR; ++p) {
-            if constexpr (LAZY) {
+            const int pg = p % PRED;
+            if (pg == 0) {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int q = 0; q < PRED; ++q) part[tb][q] = 0.f;
+            }
+            if constexpr (RING) {
+                // slot (p + AH) % PR was decoded at pass p + AH - PR of this block
+                if (!ONE || p + AH < PR) LOAD_SLOT(p0 + p + AH, (p + AH) % PR)
+            } else {
                 if (p + AH < PR) LOAD_PASS(p0, p + AH)
-                __builtin_amdgcn_sched_barrier(0);
             }
-            if (p0 + p >= passes) continue;         // uniform: padding passes of the block
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                // fp16: subnormal-pair decode (group_xq_f16); bf16: (1 + q/4) pairs
-                uint32_t pw[BF16 ? 32 : 1];
-                if constexpr (BF16) decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
-                // units outside the tile: s = 0 (zeros from the buffer loads, or
-                // the ok bit of the block loads)
-                const bool ok = LAZY || ((okm >> (p * NG + gi)) & 1u);
-                const float s = ok ? half_bits_to_float(csz[p][gi] & 0xFFFFu) : 0.f;
-                const float z = half_bits_to_float(csz[p][gi] >> 16);
-                const int g = min(go + SEG * gi, G - 1);
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    uint32_t xl_[XREG ? 1 : 32];
-                    if constexpr (!XREG) {
-                        const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const uint4 xx = xv[q];
-                            xl_[4 * q + 0] = xx.x;
-                            xl_[4 * q + 1] = xx.y;
-                            xl_[4 * q + 2] = xx.z;
-                            xl_[4 * q + 3] = xx.w;
-                        }
-                    }
-                    const uint32_t(&xp)[32] = pick_x<XREG>(xr_a[XREG ? tb * NG + gi : 0], xl_);
-                    if constexpr (BF16) {
-                        const float sp = group_dot<BF16>(pw, xp);
-                        part[tb][p] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
-                    } else {
-                        part[tb][p] += s * (group_xq_f16(cq[p][gi], xp) - z * xg_a[tb][gi]);
-                    }
-                }
-            }
-        }
-        // reduce the PR passes of each token over the segment's lanes
-        constexpr int LOGPR = Log2<PR>::v;
-        const int psel = go >> (LOGSEG - LOGPR);              // pass this lane ends up with
-        const bool writer = (go & ((SEG / PR) - 1)) == 0;
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const float v = transposed_reduce<PR, SEG>(part[tb], lane);
-            const int r = (p0 + psel) * ROWS_PASS + wave * RPW + rs;
-            if (writer && r < nrows && tb < nt && p0 + psel < passes) {
-                L.vs[tb * cpw + r] = v;
-                L.mk[tb * cpw + r] = fabsf(v) > thr ? 1 : 0;
-            }
-        }
-        if constexpr (TB > 1) {
-#pragma unroll
-            for (int p = 0; p < PR; ++p)
+            __builtin_amdgcn_sched_barrier(0);
+            if (p0 + p < passes) {                  // uniform: padding passes of the block
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                    cq[p][gi] = cqn[p][gi];
-                    csz[p][gi] = cszn[p][gi];
+                    // fp16: subnormal-pair decode (group_xq_f16); bf16: (1 + q/4) pairs
+                    uint32_t pw[BF16 ? 32 : 1];
+                    if constexpr (BF16) decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
+                    // units outside the tile read zeros from the buffer loads: s = 0
+                    const float s = half_bits_to_float(csz[p][gi] & 0xFFFFu);
+                    const float z = half_bits_to_float(csz[p][gi] >> 16);
+                    const int g = min(go + SEG * gi, G - 1);
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        uint32_t xl_[XREG ? 1 : 32];
+                        if constexpr (!XREG) {
+                            const uint4 *xv = (const uint4 *)(L.xs + ((size_t)tb * G + g) * kXPad);
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) {
+                                const uint4 xx = xv[q];
+                                xl_[4 * q + 0] = xx.x;
+                                xl_[4 * q + 1] = xx.y;
+                                xl_[4 * q + 2] = xx.z;
+                                xl_[4 * q + 3] = xx.w;
+                            }
+                        }
+                        const uint32_t(&xp)[32] = pick_x<XREG>(xr_a[XREG ? tb * NG + gi : 0], xl_);
+                        if constexpr (BF16) {
+                            const float sp = group_dot<BF16>(pw, xp);
+                            part[tb][pg] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
+                        } else {
+                            part[tb][pg] += s * (group_xq_f16(cq[p][gi], xp) - z * xg_a[tb][gi]);
+                        }
+                    }
                 }
-            okm = okmn;
+            }
+            const int base = p0 + p - pg;           // first pass of this group
+            if (pg == PRED - 1 && base < passes) {
+                constexpr int LOGPRED = Log2<PRED>::v;
+                const int psel = go >> (LOGSEG - LOGPRED);    // pass this lane ends up with
+                const bool writer = (go & ((SEG / PRED) - 1)) == 0;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const float v = transposed_reduce<PRED, SEG>(part[tb], lane);
+                    const int r = (base + psel) * ROWS_PASS + wave * RPW + rs;
+                    if (writer && r < nrows && tb < nt && base + psel < passes) {
+                        L.vs[tb * cpw + r] = v;
+                        L.mk[tb * cpw + r] = fabsf(v) > thr ? 1 : 0;
+                    }
+                }
+            }
         }
     }
-#undef LOAD_BLOCK
+#undef LOAD_SLOT
 #undef LOAD_PASS
     __syncthreads();
 
@@ -831,8 +817,9 @@ hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
     constexpr int rows_pass = GEO::W * (64 / GEO::SEG);
     const bool one = (a.cpw + rows_pass - 1) / rows_pass <= pass_block<TB, GEO>();
     auto kern = expert_kernel<BF16, TB, GEO, false>;
-    // (the widest geometry keeps the loop form: its straight-line version spills)
-    if constexpr (GEO::NG < 4) {
+    // (the widest geometry, and several tokens with two groups per lane, keep
+    // the loop form: their straight-line versions spill)
+    if constexpr (GEO::NG < 4 && (TB == 1 || GEO::NG == 1)) {
         if (one) kern = expert_kernel<BF16, TB, GEO, true>;
     }
     if constexpr (TB == 1 && GEO::NG == 1 && 2 * pass_block<TB, GEO>() <= GEO::SEG) {

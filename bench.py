@@ -369,7 +369,7 @@ def layer_workload(layers, xs_by_layer, label, path=None):
     return out
 
 
-def layers_measure(fine_only=False):
+def layers_measure(fine_only=False, stack_only=False):
     """The 32-layer Mixtral stack (T = 1, 16) and the fine-grained 64+2 layer
     (T = 1, 64), each as tokens/s of a decode step, router included; the fine
     layer again with dense copies under MOE_PATH_AUTO (T = 64, 256)."""
@@ -378,6 +378,8 @@ def layers_measure(fine_only=False):
     import synth
     dev = torch.device("cuda:0")
     out = {}
+    if stack_only:
+        return stack_measure(out)
     c = synth.CONFIGS[synth.CFG_FINE]
     bias = synth.zipf_bias(synth.CFG_FINE, 0, c["E"], c["zipf_s"])
     fine = device_layer(synth.CFG_FINE, 0, c["E"], c["S"], c["k"], c["d"], c["f"], c["wdt"],
@@ -409,6 +411,14 @@ def layers_measure(fine_only=False):
     torch.cuda.empty_cache()
     if fine_only:
         return out
+    return stack_measure(out)
+
+
+def stack_measure(out):
+    """The 32-layer Mixtral stack, T = 1 and 16, into `out`."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
     c = synth.CONFIGS[synth.CFG_STACK]
     log("drawing the 32-layer stack (64.9 GB)")
     stack = [device_layer(synth.CFG_STACK, l, c["E"], 0, c["k"], c["d"], c["f"], c["wdt"], c["x_scale"],
@@ -591,6 +601,8 @@ def main():
                     help="skip the batched-layer (dense MFMA vs sparse) measurement")
     ap.add_argument("--fine-only", action="store_true",
                     help="only the fine-grained layer workloads (sparse and MOE_PATH_AUTO)")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="only the 32-layer stack workloads (T = 1, 16)")
     ap.add_argument("--variants-only", action="store_true",
                     help="only the 8/4/1-bit expert and EAMC measurements (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -609,6 +621,9 @@ def main():
         return
     if args.fine_only:
         print(json.dumps({"more": layers_measure(fine_only=True)}), flush=True)
+        return
+    if args.stack_only:
+        print(json.dumps({"more": layers_measure(stack_only=True)}), flush=True)
         return
     if args.variants_only:
         print(json.dumps({"expert_up_bits": bits_measure(), "eamc_match": eamc_measure()}),
