@@ -12,7 +12,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoeffn.so")
+# MOEFFN_LIB names another build of the same sources (the sanitizer build)
+LIB_PATH = os.environ.get("MOEFFN_LIB") or os.path.join(HERE, "libmoeffn.so")
 
 MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
 PATH_SPARSE, PATH_DENSE, PATH_AUTO = 0, 1, 2

@@ -41,9 +41,18 @@ def sources_sha256() -> str:
     return h.hexdigest()
 
 
-def _compile(src: str, sha: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, f'-DMOE_SOURCES_SHA256="{sha}"', "-x", "hip", "-c",
+# Host-only AddressSanitizer + UndefinedBehaviorSanitizer: each -fsanitize
+# applies to the host compilation only (the kernels are built as usual).
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+BUILD_SAN = os.path.join(HERE, "_build_san")
+OUT_SAN = os.path.join(BUILD_SAN, "libmoeffn_san.so")
+
+
+def _compile(src: str, sha: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, f'-DMOE_SOURCES_SHA256="{sha}"', "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -65,6 +74,26 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print("built", OUT)
     return OUT
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The same library with the host code (argument checks, workspace
+    layout, launch set-up) built under ASan + UBSan, for the CPU tests; it is
+    loaded through MOEFFN_LIB with the sanitizer runtime preloaded."""
+    os.makedirs(BUILD_SAN, exist_ok=True)
+    sha = sources_sha256()
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, sha, BUILD_SAN, SAN_HOST), SOURCES))
+    tmp = OUT_SAN + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-shared-libsan", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT_SAN)
+    if verbose:
+        print("built", OUT_SAN)
+    return OUT_SAN
 
 
 if __name__ == "__main__":

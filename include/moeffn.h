@@ -71,7 +71,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums are int-sized in C and C++ alike.  C++ callers (and the library
+ * itself) see them with a fixed int underlying type, so that any int a caller
+ * passes is a valid value of the type and is rejected by the argument checks
+ * rather than being undefined. */
+#ifdef __cplusplus
+#define MOE_ENUM enum : int
+#else
+#define MOE_ENUM enum
+#endif
+
+typedef MOE_ENUM {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, k outside [1, E], ... */
     MOE_ERR_UNSUPPORTED = -2,   /* shape or dtype combination not implemented    */
@@ -80,15 +90,15 @@ typedef enum {
     MOE_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed    */
 } moe_status;
 
-typedef enum { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
+typedef MOE_ENUM { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
 
-typedef enum {
+typedef MOE_ENUM {
     MOE_PATH_SPARSE = 0,        /* Algorithm 1: INT2 up, threshold mask, row gathers */
     MOE_PATH_DENSE = 1,         /* bf16 MFMA grouped GEMM, threshold off            */
     MOE_PATH_AUTO = 2           /* dense when it moves fewer bytes, else sparse     */
 } moe_path;
 
-typedef enum {
+typedef MOE_ENUM {
     MOE_OP_EXPERT = 0,          /* moe_expert_forward_sparse */
     MOE_OP_ROUTE = 1,           /* moe_route_topk           */
     MOE_OP_LAYER = 2,           /* moe_layer_forward        */

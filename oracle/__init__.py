@@ -37,15 +37,30 @@ def build() -> None:
                            "-shared", "-o", LIB, SRC, "-lm"])
 
 
+def build_sanitized(out: str) -> str:
+    """The oracle under ASan + UBSan (clang, so that one sanitizer runtime
+    serves it and the library's sanitizer build in the same process); loaded
+    through ORACLE_LIB."""
+    clang = os.environ.get("ORACLE_SAN_CC", "/opt/rocm/llvm/bin/clang")
+    subprocess.check_call([clang, "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           "-fno-omit-frame-pointer", "-shared-libsan", "-shared", "-o", out, SRC,
+                           "-lm"])
+    return out
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build()
-        L = C.CDLL(LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = LIB
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+        L = C.CDLL(path)
         P = C.c_void_p
         I = C.c_int
         L.oracle_half_to_double.restype = C.c_double
