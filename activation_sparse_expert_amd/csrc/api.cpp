@@ -605,7 +605,23 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     r.expert_dense = (trace && trace->expert_dense) ? trace->expert_dense
                    : (mixed ? w.expert_dense : nullptr);
     const bool shared_dense = path == MOE_PATH_DENSE && (!mixed || T >= nstar);
-    hipError_t he = launch_route(r, s);
+    // A single token on the sparse path is routed inside the expert kernel:
+    // each routed workgroup ranks the logits itself (formed there for routers
+    // up to kInlineRouterBytes, else by the logits kernel first), so neither
+    // the ranking nor the grouping kernel runs.
+    const bool inline_route = path == MOE_PATH_SPARSE && !mixed && T == 1 && sp.tb == 1;
+    const size_t router_bytes = (size_t)E * d * (L->rdt == MOE_F32 ? 4 : 2);
+    const bool inline_logits_kernel =
+        inline_route && (route_split(d, E, L->rdt) || router_bytes > kInlineRouterBytes);
+    hipError_t he = hipSuccess;
+    if (inline_route) {
+        if (inline_logits_kernel) {
+            r.lg_buf = w.lg;
+            he = launch_route_logits(r, s);
+        }
+    } else {
+        he = launch_route(r, s);
+    }
     if (he != hipSuccess) return MOE_ERR_HIP;
 
     const size_t qs = (size_t)f * (d / 4), szs = (size_t)f * (d / 64) * 2, wst = (size_t)f * d;
@@ -689,6 +705,18 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     a.layer = 1; a.E = E; a.k = k; a.S = S;
     a.chunk_tab = w.chunk_tab; a.n_chunks = w.n_chunks;
     a.chunk_rec = sp.tb == 1 ? w.chunk_rec : nullptr;
+    if (inline_route) {
+        a.route = 1;
+        a.chunk_rec = nullptr;
+        a.route_lg = inline_logits_kernel ? w.lg : nullptr;
+        a.route_w = L->router_w; a.rdt = (int)L->rdt; a.route_bias = L->router_bias;
+        a.renorm = L->renormalize ? 1 : 0;
+        if (trace) {
+            a.ex_topk_idx = trace->topk_idx; a.ex_topk_w = trace->topk_w;
+            a.ex_logits = trace->logits; a.ex_count = trace->expert_count;
+            a.ex_eam_row = trace->eam_row;
+        }
+    }
     a.offset = w.offset; a.pairs = w.pairs;
     a.topk_w = r.topk_w;
     a.part = w.part;

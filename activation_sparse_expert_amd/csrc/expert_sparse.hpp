@@ -33,6 +33,7 @@
 #pragma once
 #include "device.hpp"
 #include "internal.hpp"
+#include "route_common.hpp"
 
 namespace moeffn {
 namespace sparse {
@@ -206,11 +207,17 @@ struct Lds {
     int32_t *tok_row;   // [TB] partial row
     float *tok_sc;      // [TB] scale
     int32_t *misc;      // [0] n_act
+    float *rlg;         // [E rounded up to 4] logits (inline routing)
+    int32_t *rsel;      // [k] the token's choices (inline routing)
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-__host__ __device__ inline size_t lds_layout(int d, int cpw, int tb, int waves, int rb, size_t *off)
+// LDS bytes of the inline routing: E logits (padded to 4) and k choices
+__host__ __device__ inline size_t route_lds(int E, int k) { return (size_t)(((E + 3) & ~3) + k) * 4; }
+
+__host__ __device__ inline size_t lds_layout(int d, int cpw, int tb, int waves, int rb, size_t *off,
+                                             size_t route_bytes = 0)
 {
     const int G = d / 64;
     size_t o = 0;
@@ -225,6 +232,7 @@ __host__ __device__ inline size_t lds_layout(int d, int cpw, int tb, int waves, 
     off[8] = o; o = align16(o + (size_t)tb * 4);
     off[9] = o; o = align16(o + (size_t)tb * 4);
     off[10] = o; o = align16(o + 16);
+    off[11] = o; o = align16(o + route_bytes);
     return o;
 }
 
@@ -293,10 +301,55 @@ __host__ __device__ constexpr int pass_block()
     return pb < GEO::SEG ? pb : GEO::SEG;
 }
 
+// Inline routing of a single token (layer calls at T = 1): the logits come
+// from the logits kernel or are formed here, one wave per expert; then the
+// shared ranking and gate weights, exactly as the routing kernel forms them.
+// Returns this slot's expert and weight; the writer workgroup also writes the
+// trace exports (choices, weights, logits, per-expert counts, EAM row).
+template <bool BF16, int THREADS>
+__device__ __forceinline__ void route_token(const SparseArgs &a, const Lds &L, int slot, bool writer,
+                                            int tid, int lane, int wave, int &e, float &w)
+{
+    constexpr int W = THREADS / 64;
+    const int E = a.E, k = a.k, E4 = (E + 3) & ~3;
+    float *lg = L.rlg;
+    int32_t *sel = L.rsel;
+    if (a.route_lg) {
+        for (int i = tid; i < E; i += THREADS) lg[i] = a.route_lg[i];
+    } else {
+        for (int i = wave; i < E; i += W) {
+            const float v = rc::wave_logit_rows<BF16 ? 1 : 0>(a.x, a.route_w, a.rdt, a.d,
+                                                              a.route_bias, i, lane);
+            if (lane == 0) lg[i] = v;
+        }
+    }
+    for (int i = E + tid; i < E4; i += THREADS) lg[i] = -INFINITY;
+    __syncthreads();
+    rc::rank_topk(lg, E, k, sel, tid, THREADS);
+    __syncthreads();
+    const float m = lg[sel[0]];
+    const float den = rc::gate_den(lg, sel, E, k, a.renorm, m, lane);
+    e = sel[slot];
+    w = __expf(lg[e] - m) / den;
+    if (writer) {
+        for (int s = tid; s < k; s += THREADS) {
+            if (a.ex_topk_idx) a.ex_topk_idx[s] = sel[s];
+            if (a.ex_topk_w) a.ex_topk_w[s] = __expf(lg[sel[s]] - m) / den;
+        }
+        for (int i = tid; i < E; i += THREADS) {
+            if (a.ex_logits) a.ex_logits[i] = lg[i];
+            int c = 0;
+            for (int s = 0; s < k; ++s) c |= (int)(sel[s] == i);
+            if (a.ex_count) a.ex_count[i] = c;
+            if (a.ex_eam_row && c) a.ex_eam_row[i] += 1;
+        }
+    }
+}
+
 // ONE: the tile is a single block of passes (straight-line code).  PBX: the
 // block is PBX times the usual pass block (2 for single-token tiles of 9-16
 // passes, so that they too run straight-line with a continuous lookahead).
-template <bool BF16, int TB, class GEO, bool ONE, int PBX = 1>
+template <bool BF16, int TB, class GEO, bool ONE, int PBX = 1, bool ROUTE = false>
 __global__ void __launch_bounds__(GEO::THREADS)
 expert_kernel(SparseArgs a)
 {
@@ -319,8 +372,8 @@ expert_kernel(SparseArgs a)
     const int d = a.d, f = a.f, G = d / 64;
     const int cpw = a.cpw;
 
-    size_t off[11];
-    lds_layout(d, cpw, TB, W, RB, off);
+    size_t off[12];
+    lds_layout(d, cpw, TB, W, RB, off, ROUTE ? route_lds(a.E, a.k) : 0);
     Lds L;
     L.xs = (uint16_t *)(smem + off[0]);
     L.xg = (float *)(smem + off[1]);
@@ -333,6 +386,8 @@ expert_kernel(SparseArgs a)
     L.tok_row = (int32_t *)(smem + off[8]);
     L.tok_sc = (float *)(smem + off[9]);
     L.misc = (int32_t *)(smem + off[10]);
+    L.rlg = (float *)(smem + off[11]);
+    L.rsel = (int32_t *)(L.rlg + ((a.E + 3) & ~3));
 
     // ---- which expert and which tokens ------------------------------------
     // The grid is (token chunk) x (tile).  Single expert: chunk c holds tokens
@@ -357,7 +412,12 @@ expert_kernel(SparseArgs a)
             shared_slot = true;
         } else {
             const int ci = chunk - a.S * nsc;
-            if (TB == 1 && a.chunk_rec) {
+            if constexpr (ROUTE) {
+                // one token, slot ci: rank its logits here
+                route_token<BF16, THREADS>(a, L, ci, ci == 0 && tile == 0, tid, lane, wave, e, rec_w);
+                rec_p = ci;                         // pair ci of token 0
+                nt = 1;
+            } else if (TB == 1 && a.chunk_rec) {
                 // one pair per chunk: the grid holds exactly T k routed chunks
                 const int4 rec = *(const int4 *)(a.chunk_rec + 4 * (size_t)ci);
                 e = rec.x;
@@ -809,33 +869,51 @@ expert_kernel(SparseArgs a)
     }
 }
 
-template <bool BF16, int TB, class GEO>
-hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
+// The kernel instance for this call: straight-line (ONE, PBX) or loop form;
+// ROUTE: single-token layer calls that route inside the kernel (a separate
+// instance, so that the other calls' code is unchanged by it).
+template <bool BF16, int TB, class GEO, bool ROUTE>
+const void *pick_kernel(const SparseArgs &a)
 {
-    size_t off[11];
-    const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off);
     constexpr int rows_pass = GEO::W * (64 / GEO::SEG);
-    const bool one = (a.cpw + rows_pass - 1) / rows_pass <= pass_block<TB, GEO>();
-    auto kern = expert_kernel<BF16, TB, GEO, false>;
+    const int passes = (a.cpw + rows_pass - 1) / rows_pass;
+    const bool one = passes <= pass_block<TB, GEO>();
     // (the widest geometry, and several tokens with two groups per lane, keep
     // the loop form: their straight-line versions spill)
     if constexpr (GEO::NG < 4 && (TB == 1 || GEO::NG == 1)) {
-        if (one) kern = expert_kernel<BF16, TB, GEO, true>;
+        if (one) return (const void *)expert_kernel<BF16, TB, GEO, true, 1, ROUTE>;
     }
     if constexpr (TB == 1 && GEO::NG == 1 && 2 * pass_block<TB, GEO>() <= GEO::SEG) {
-        const int passes = (a.cpw + rows_pass - 1) / rows_pass;
-        if (!one && passes <= 2 * pass_block<TB, GEO>()) kern = expert_kernel<BF16, TB, GEO, true, 2>;
+        if (!one && passes <= 2 * pass_block<TB, GEO>())
+            return (const void *)expert_kernel<BF16, TB, GEO, true, 2, ROUTE>;
+    }
+    return (const void *)expert_kernel<BF16, TB, GEO, false, 1, ROUTE>;
+}
+
+template <bool BF16, int TB, class GEO>
+hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
+{
+    size_t off[12];
+    const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off,
+                                  a.route ? route_lds(a.E, a.k) : 0);
+    const void *kern;
+    if constexpr (TB == 1) {
+        kern = a.route ? pick_kernel<BF16, TB, GEO, true>(a) : pick_kernel<BF16, TB, GEO, false>(a);
+    } else {
+        if (a.route) return hipErrorInvalidValue;       // inline routing is for one token
+        kern = pick_kernel<BF16, TB, GEO, false>(a);
     }
     SparseArgs args = a;
     args.dec_mask = decode_const<BF16>().mask;
     args.dec_one = decode_const<BF16>().one;
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.slots * a.tiles), dim3(GEO::THREADS), lds, s, args);
-    return hipGetLastError();
+    void *kargs[] = {(void *)&args};
+    hipError_t e = hipLaunchKernel(kern, dim3(a.slots * a.tiles), dim3(GEO::THREADS), kargs, lds, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e;
 }
 
 template <bool BF16, class GEO>

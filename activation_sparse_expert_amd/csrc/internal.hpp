@@ -32,6 +32,22 @@ struct SparseArgs {
     const int32_t *offset;              // [E+1]
     const int32_t *pairs;               // [T*k]
     const float *topk_w;                // [T*k]
+    // single-token layer calls with route != 0: each routed workgroup ranks
+    // the token's logits itself (no grouping step).  route_lg: the E logits,
+    // bias included, from the logits kernel; nullptr: the workgroup forms
+    // them from route_w [E][d] (type rdt) and route_bias.
+    int route;
+    const float *route_lg;
+    const void *route_w;
+    int rdt;
+    const float *route_bias;
+    int renorm;
+    // trace exports of such calls, written by the workgroup of slot 0, tile 0
+    int32_t *ex_topk_idx;               // [k]
+    float *ex_topk_w;                   // [k]
+    float *ex_logits;                   // [E]
+    int32_t *ex_count;                  // [E]
+    int32_t *ex_eam_row;                // [E], incremented
     // outputs
     float *part;                        // partial rows [rows][part_stride][d] (workspace)
     int part_stride;                    // partial slots per row (0: tiles)
@@ -95,6 +111,11 @@ struct RouteArgs {
 // over many workgroups.
 bool route_split(int d, int E, int rdt);
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+// the logits alone (a.lg_buf [T][E], bias included), for inline routing
+hipError_t launch_route_logits(const RouteArgs &a, hipStream_t s);
+// single-token layer calls route inside the expert kernel; routers up to this
+// size are read there by every routed workgroup, larger ones by the logits kernel
+constexpr size_t kInlineRouterBytes = 64u << 10;
 
 struct DenseArgs {
     int d, f, E, k, S, T;

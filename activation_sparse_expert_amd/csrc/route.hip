@@ -16,6 +16,7 @@
 // host synchronisation, atomics across workgroups or fences are involved.
 #include "device.hpp"
 #include "internal.hpp"
+#include "route_common.hpp"
 
 namespace moeffn {
 
@@ -24,12 +25,7 @@ namespace {
 constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-// 16-bit float bits to float (bf16 or fp16), chosen at compile time
-template <bool BF>
-__device__ __forceinline__ float f16bits(uint32_t b)
-{
-    return BF ? bf16_bits_to_float((uint16_t)b) : half_bits_to_float((uint16_t)b);
-}
+using rc::f16bits;
 
 // x of one token into LDS as fp32, 8 elements per 16-byte unit (32 for fp32
 // input), four loads in flight per thread; one copy per input type, so that no
@@ -147,58 +143,17 @@ __device__ __forceinline__ void logits(const RouteArgs &a, const float *xs, cons
     }
 }
 
-// 8 elements of a 16-bit (XT/WT 0 fp16, 1 bf16) or fp32 (2) array at element
-// offset 8 g, as floats (one or two 16-byte loads)
-template <int T_>
-__device__ __forceinline__ void load8(const void *base, size_t g, float (&v)[8])
-{
-    if constexpr (T_ == 2) {
-        const float4 a = *((const float4 *)base + 2 * g), b = *((const float4 *)base + 2 * g + 1);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        const uint4 u = *((const uint4 *)base + g);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = f16bits<T_ == 1>(w[i] & 0xFFFFu);
-            v[2 * i + 1] = f16bits<T_ == 1>(w[i] >> 16);
-        }
-    }
-}
-
 // Wide routers: logits only, one wave per (token, expert), eight experts per
 // workgroup, so the router rows of a token are read by many compute units at
-// once.  Lane l takes the 8-element groups l, l + 64, ... of the row and of x
-// (4 of each in flight), in ascending order, and the lanes' sums are
-// added by a fixed butterfly: every expert's logit is formed the same way, so
-// identical router rows tie exactly.  route_kernel then ranks them.
+// once (the shared fixed-order wave dot, so identical router rows tie
+// exactly).  route_kernel then ranks them.
 template <int XT, int WT>
 __device__ __forceinline__ float wave_logit(const RouteArgs &a, int t, int e, int lane)
 {
     constexpr int xsz = XT == 2 ? 4 : 2, wsz = WT == 2 ? 4 : 2;
     const unsigned char *xr = (const unsigned char *)a.x + (size_t)t * a.d * xsz;
     const unsigned char *wr = (const unsigned char *)a.rw + (size_t)e * a.d * wsz;
-    const int ng = a.d / 8;
-    constexpr int CB = 4;                               // groups per lane per round
-    float acc = 0.f;
-    for (int g0 = 0; g0 < ng; g0 += 64 * CB) {
-        float xv[CB][8], wv[CB][8];
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int g = min(g0 + lane + 64 * i, ng - 1);
-            load8<XT>(xr, g, xv[i]);
-            load8<WT>(wr, g, wv[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            float q = acc;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) q += xv[i][j] * wv[i][j];
-            if (g0 + lane + 64 * i < ng) acc = q;
-        }
-    }
-    return seg_sum<64>(acc) + (a.bias ? a.bias[e] : 0.f);
+    return rc::wave_row_dot<XT, WT>(xr, wr, a.d, lane) + (a.bias ? a.bias[e] : 0.f);
 }
 
 template <int XT>
@@ -424,34 +379,13 @@ route_kernel(RouteArgs a)
         const int E4 = (E + 3) & ~3;
         for (int e = E + tid; e < E4; e += kRouteThreads) lg[e] = -INFINITY;
         __syncthreads();
-        for (int e = tid; e < E; e += kRouteThreads) {
-            const float le = lg[e] != lg[e] ? -INFINITY : lg[e];
-            int r = 0;
-#pragma unroll 4
-            for (int e2 = 0; e2 < E4; e2 += 4) {
-                const float4 l4 = *(const float4 *)&lg[e2];
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float l2 = lv[j] != lv[j] ? -INFINITY : lv[j];
-                    // branch-free: ahead if larger, or equal with a lower index
-                    r += (int)(l2 > le) | ((int)(l2 == le) & (int)(e2 + j < e));
-                }
-            }
-            if (r < k) sel[r] = e;
-        }
+        rc::rank_topk(lg, E, k, sel, tid, kRouteThreads);
         __syncthreads();
     }
     if (wave == 0) {
-        const float m_sel = lg[sel[0]];
         // weights
-        float m = m_sel, den = 0.f;
-        if (a.renorm) {
-            for (int s = lane; s < k; s += 64) den += __expf(lg[sel[s]] - m);
-        } else {
-            for (int e = lane; e < E; e += 64) den += __expf(lg[e] - m);
-        }
-        den = seg_sum<64>(den);
+        const float m = lg[sel[0]];
+        const float den = rc::gate_den(lg, sel, E, k, a.renorm, m, lane);
         for (int s = lane; s < k; s += 64) {
             const int e = sel[s];
             const float w = __expf(lg[e] - m) / den;
@@ -497,15 +431,21 @@ const void *logits_kernel_for(int rdt)
 }
 }  // namespace
 
+hipError_t launch_route_logits(const RouteArgs &a, hipStream_t s)
+{
+    const void *lk = a.xdt == 2 ? logits_kernel_for<2>(a.rdt)
+                   : a.xdt == 1 ? logits_kernel_for<1>(a.rdt) : logits_kernel_for<0>(a.rdt);
+    const int nblk = (a.E + kRouteWaves - 1) / kRouteWaves;
+    void *largs[] = {(void *)&a};
+    hipError_t e = hipLaunchKernel(lk, dim3((unsigned)a.T * nblk), dim3(kRouteThreads), largs, 0, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e;
+}
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t s)
 {
     if (a.lg_buf) {
-        const void *lk = a.xdt == 2 ? logits_kernel_for<2>(a.rdt)
-                       : a.xdt == 1 ? logits_kernel_for<1>(a.rdt) : logits_kernel_for<0>(a.rdt);
-        const int nblk = (a.E + kRouteWaves - 1) / kRouteWaves;
-        void *largs[] = {(void *)&a};
-        hipError_t e = hipLaunchKernel(lk, dim3((unsigned)a.T * nblk), dim3(kRouteThreads), largs, 0, s);
-        if (e == hipSuccess) e = hipGetLastError();
+        const hipError_t e = launch_route_logits(a, s);
         if (e != hipSuccess) return e;
     }
     size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 8 + 32;
