@@ -13,7 +13,7 @@ BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "expert_sparse_f16.hip", "expert_sparse_bf16.hip", "reduce.hip", "route.hip",
            "pack.hip", "dense_mfma.hip", "dense_gemm.hip", "calibrate.hip",
-           "eamc.hip", "expert_bits.hip"]
+           "eamc.hip", "expert_sparse_bits.hip"]
 
 HEADER = os.path.join(os.path.dirname(HERE), "include", "moeffn.h")
 

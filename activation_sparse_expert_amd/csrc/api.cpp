@@ -109,16 +109,6 @@ SparsePlan layer_plan(int T, int d, int f, int E, int k, int S)
     return SparsePlan{tb, (int)bound, plan_tiles(f, (int)expect, (long long)T * (k + S), d)};
 }
 
-// Byte masks staged for the bitmask / nnz exports when the caller asks for
-// those but not for the byte masks themselves: T f bytes after the rest.
-size_t bits_ws_core(int T, int d, int f)
-{
-    const size_t tiles = (size_t)(f + kBitsTile - 1) / kBitsTile;
-    return up((size_t)T * f * 4) + up((size_t)T * tiles * d * 4);
-}
-
-size_t bits_ws_bytes(int T, int d, int f) { return bits_ws_core(T, d, f) + up((size_t)T * f); }
-
 size_t expert_ws_core(int T, int d, int f)
 {
     const TilePlan tp = expert_plan(T, d, f).tp;
@@ -319,11 +309,8 @@ size_t moe_workspace_size(moe_op op, int T, int d, int f, int E, int k, int S)
         return layer_ws_bytes(T, d, f, E, k, S, nullptr, nullptr);
     case MOE_OP_CALIBRATE:
         return up(calibrate_ws_bytes());
-    case MOE_OP_EXPERT_BITS: {
-        if (f < 1) return 0;
-        const size_t a = expert_ws_bytes(T, d, f), b = bits_ws_bytes(T, d, f);
-        return a > b ? a : b;
-    }
+    case MOE_OP_EXPERT_BITS:
+        return f < 1 ? 0 : expert_ws_bytes(T, d, f);
     case MOE_OP_EAMC:
         return d > kEamcMaxLen ? 0 : up((size_t)T * 8);   // T stored EAMs of d entries
     }
@@ -407,16 +394,20 @@ moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void
     return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
-moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe_dtype wdt,
-                                     const void *x, moe_dtype xdt, int T,
-                                     const float *token_scale, int accumulate, void *y,
-                                     moe_dtype ydt, uint64_t *mask_bits, int32_t *nnz_out,
-                                     uint8_t *mask_out, float *v_out, void *ws,
-                                     size_t ws_bytes, void *stream)
+namespace {
+// One expert over T tokens with the up codes at `bits` (2: the INT2 format,
+// 8 / 4 / 1: plain packing, d = 512 ... 4096): the fused kernel, the reduce,
+// and the bitmask / nnz exports when asked for.
+moe_status expert_forward(const moe_expert_view *e, int bits, int d, int f, moe_dtype wdt,
+                          const void *x, moe_dtype xdt, int T, const float *token_scale,
+                          int accumulate, void *y, moe_dtype ydt, uint64_t *mask_bits,
+                          int32_t *nnz_out, uint8_t *mask_out, float *v_out, void *ws,
+                          size_t ws_bytes, void *stream)
 {
     if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
     moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
     if (st != MOE_OK) return st;
+    if (bits != 2 && d != 512 && d != 1024 && d != 2048 && d != 4096) return MOE_ERR_UNSUPPORTED;
     st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
     if (st != MOE_OK) return st;
     if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||
@@ -445,7 +436,8 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     a.layer = 0;
     a.part = (float *)ws;
     a.mask_out = mask_out; a.v_out = v_out;
-    hipError_t he = launch_sparse(a, wdt == MOE_BF16, sp.tb, s);
+    hipError_t he = bits == 2 ? launch_sparse(a, wdt == MOE_BF16, sp.tb, s)
+                              : launch_sparse_expert_bits(a, bits, wdt == MOE_BF16, sp.tb, s);
     if (he != hipSuccess) return MOE_ERR_HIP;
     ReduceArgs r{};
     r.part = a.part; r.tiles = tp.tiles; r.d = d; r.T = T;
@@ -454,6 +446,18 @@ moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe
     he = launch_reduce(r, s);
     if (he == hipSuccess && want_bits) he = launch_mask_bits(mask_out, T, f, mask_bits, nnz_out, s);
     return hip_status(he);
+}
+}  // namespace
+
+moe_status moe_expert_forward_sparse(const moe_expert_view *e, int d, int f, moe_dtype wdt,
+                                     const void *x, moe_dtype xdt, int T,
+                                     const float *token_scale, int accumulate, void *y,
+                                     moe_dtype ydt, uint64_t *mask_bits, int32_t *nnz_out,
+                                     uint8_t *mask_out, float *v_out, void *ws,
+                                     size_t ws_bytes, void *stream)
+{
+    return expert_forward(e, 2, d, f, wdt, x, xdt, T, token_scale, accumulate, y, ydt, mask_bits,
+                          nnz_out, mask_out, v_out, ws, ws_bytes, stream);
 }
 
 size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
@@ -482,46 +486,9 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
                                           uint8_t *mask_out, float *v_out,
                                           void *ws, size_t ws_bytes, void *stream)
 {
-    if (bits == 2)
-        return moe_expert_forward_sparse(e, d, f, wdt, x, xdt, T, token_scale, accumulate, y, ydt,
-                                         mask_bits, nnz_out, mask_out, v_out, ws, ws_bytes, stream);
-    if (bits != 1 && bits != 4 && bits != 8) return MOE_ERR_INVALID_ARG;
-    if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
-    moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
-    if (st != MOE_OK) return st;
-    if ((d != 512 && d != 1024 && d != 2048 && d != 4096) || T > kBitsMaxT ||
-        bits_lds_up(T, d) > kBitsMaxLds)
-        return MOE_ERR_UNSUPPORTED;
-    st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
-    if (st != MOE_OK) return st;
-    if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||
-        (token_scale && !aligned(token_scale, 4)) || (v_out && !aligned(v_out, 4)) ||
-        (mask_bits && !aligned(mask_bits, 8)) || (nnz_out && !aligned(nnz_out, 4)))
-        return MOE_ERR_ALIGNMENT;
-    if (!ws || ws_bytes < bits_ws_bytes(T, d, f)) return MOE_ERR_WORKSPACE;
-    if (!aligned(ws, 16)) return MOE_ERR_ALIGNMENT;
-    hipStream_t s = (hipStream_t)stream;
-    const bool want_bits = mask_bits || nnz_out;
-    if (want_bits && !mask_out) mask_out = (uint8_t *)ws + bits_ws_core(T, d, f);
-    BitsArgs a{};
-    a.up_q = e->up_q; a.up_sz = e->up_sz;
-    a.gate = (const uint16_t *)e->gate_t; a.down = (const uint16_t *)e->down;
-    a.bits = bits; a.d = d; a.f = f; a.T = T; a.bf16 = wdt == MOE_BF16 ? 1 : 0;
-    a.thr = e->threshold;
-    a.x = (const uint16_t *)x; a.token_scale = token_scale;
-    a.v = v_out ? v_out : (float *)ws;
-    a.mask_out = mask_out;
-    a.part = (float *)((char *)ws + up((size_t)T * f * 4));
-    a.tiles = (f + kBitsTile - 1) / kBitsTile;
-    hipError_t he = launch_expert_bits(a, s);
-    if (he != hipSuccess) return MOE_ERR_HIP;
-    ReduceArgs r{};
-    r.part = a.part; r.tiles = a.tiles; r.d = d; r.T = T;
-    r.layer = 0; r.rows_per_tok = 1; r.k = 1; r.S = 0;
-    r.y = y; r.ydt = (int)ydt; r.accumulate = accumulate ? 1 : 0;
-    he = launch_reduce(r, s);
-    if (he == hipSuccess && want_bits) he = launch_mask_bits(mask_out, T, f, mask_bits, nnz_out, s);
-    return hip_status(he);
+    if (bits != 1 && bits != 2 && bits != 4 && bits != 8) return MOE_ERR_INVALID_ARG;
+    return expert_forward(e, bits, d, f, wdt, x, xdt, T, token_scale, accumulate, y, ydt,
+                          mask_bits, nnz_out, mask_out, v_out, ws, ws_bytes, stream);
 }
 
 moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, int T, void *y,

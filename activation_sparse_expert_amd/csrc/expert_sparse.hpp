@@ -278,6 +278,133 @@ __device__ __forceinline__ uint32_t bload_nt4(__amdgpu_buffer_rsrc_t r, uint32_t
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2 /* nt */);
 }
 
+// ---- other up-code widths (FloE review, "敏感度分析": INT8, INT4, INT1) ----
+// The codes are packed plainly: input k of a channel at bits [k b, k b + b) of
+// its row, with the same group-64 scale and zero point as the INT2 format.  A
+// lane still takes one 64-input group (2 b code words).  In a code word the
+// two 16-bit halves hold inputs at the same bit position, so a mask and a
+// shift that put those two codes at the top of an fp16 mantissa give an
+// fp16 subnormal pair q 2^(top - 24) (bf16: a normal pair 1 + q 2^-n),
+// which one packed dot product multiplies with the matching pair of x.  The
+// lane's x pairs are permuted once to that order (perm_pairs).
+template <int BITS>
+struct CodeUnit {
+    uint32_t w[2 * BITS];
+};
+template <>
+struct CodeUnit<2> {
+    uint4 v;
+};
+
+template <int BITS>
+__device__ __forceinline__ CodeUnit<BITS> bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    CodeUnit<BITS> c;
+    if constexpr (BITS == 2) {
+        c.v = bload_nt16(r, off);
+    } else if constexpr (BITS == 1) {
+        typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+        const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 2 /* nt */);
+        c.w[0] = v.x;
+        c.w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < BITS / 2; ++i) {
+            // an offset past the tile stays past it: every part reads zeros
+            const uint4 u = bload_nt16(r, off >= kOob ? kOob : off + 16u * i);
+            c.w[4 * i] = u.x;
+            c.w[4 * i + 1] = u.y;
+            c.w[4 * i + 2] = u.z;
+            c.w[4 * i + 3] = u.w;
+        }
+    }
+    return c;
+}
+
+// x pairs in the order the BITS-wide code words pair their inputs, from the
+// natural pairs n[j] = (x[2j], x[2j+1]) of one 64-input group.  Word i of the
+// codes covers inputs 32 i / b ...; its pair m holds inputs (i0 + m, i0 + m +
+// 16 / b) (lo, hi half).  v_perm_b32 takes 16-bit halves of two natural pairs.
+template <int BITS>
+__device__ __forceinline__ void perm_pairs(uint32_t (&xp)[32])
+{
+    if constexpr (BITS != 2) {
+        uint32_t n[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) n[j] = xp[j];
+        constexpr int IW = 32 / BITS;               // inputs per code word
+        constexpr int H = IW / 2;                   // inputs per half word (pairs per word)
+#pragma unroll
+        for (int i = 0; i < 2 * BITS; ++i)
+#pragma unroll
+            for (int m = 0; m < H; ++m) {
+                const int lo = i * IW + m, hi = lo + H;          // inputs of pair (i, m)
+                // both have the parity of m: the low half of their natural pair if even
+                const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+                xp[i * H + m] = __builtin_amdgcn_perm(n[hi >> 1], n[lo >> 1], sel);
+            }
+    }
+}
+
+// sum_k x_k q_k over one group for BITS in {8, 4, 1}, fp16 activations: each
+// pair of codes moved to mantissa bits [10 - b', 10) (b' = min(b, 8)) as a
+// subnormal pair, four accumulators, one exact power of two at the end.
+template <int BITS>
+__device__ __forceinline__ float group_xq_bits_f16(const CodeUnit<BITS> &c, const uint32_t (&xp)[32])
+{
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    constexpr int H = 16 / BITS;                    // pairs per code word
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; ++i) {
+        const uint32_t w = c.w[i];
+#pragma unroll
+        for (int m = 0; m < H; ++m) {
+            constexpr int top = 10;                 // codes end at mantissa bit 9
+            const int sh = top - BITS * (m + 1);    // shift that moves pair m there
+            const uint32_t mask = ((1u << BITS) - 1u) << (top - BITS);
+            const uint32_t t = sh >= 0 ? (w << sh) : (w >> (-sh));
+            const uint32_t pw = t & (mask | (mask << 16));
+            acc[(i * H + m) & 3] = dot2<false>(pw, xp[i * H + m], acc[(i * H + m) & 3]);
+        }
+    }
+    // a code q sits at q 2^(top - b - 24) = q 2^-(14 + b)
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * (float)(1u << (14 + BITS));
+}
+
+// bf16 activations: pair words (1 + q 2^-n) from one v_and_or per pair, the
+// code placed at mantissa bits [7 - b', 7); sum x q = 2^n (S' - X_g).  Eight
+// bits are taken as two nibbles, 16 (S'_lo - X_g) + 256 (S'_hi - X_g).
+template <int BITS>
+__device__ __forceinline__ float group_xq_bits_bf16(const CodeUnit<BITS> &c, const uint32_t (&xp)[32],
+                                                    float xg, uint32_t one)
+{
+    constexpr int NB = BITS == 8 ? 4 : BITS;        // bits per decoded field
+    constexpr int NF = BITS == 8 ? 2 : 1;           // fields per code
+    constexpr int H = 16 / BITS;
+    constexpr uint32_t fmask = ((1u << NB) - 1u) << (7 - NB);
+    float acc[NF][2];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f][0] = acc[f][1] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; ++i) {
+        const uint32_t w = c.w[i];
+#pragma unroll
+        for (int m = 0; m < H; ++m)
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const int sh = 7 - (BITS * m + NB * f + NB);  // field's top bit to mantissa bit 6
+                const uint32_t t = sh >= 0 ? (w << sh) : (w >> (-sh));
+                const uint32_t pw = and_or(t, fmask | (fmask << 16), one);
+                acc[f][m & 1] = dot2<true>(pw, xp[i * H + m], acc[f][m & 1]);
+            }
+    }
+    // field f (value v) reads 1 + v 2^-NB and weighs 2^(NB f) in the code
+    float r = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) r += ((acc[f][0] + acc[f][1]) - xg) * (float)(1u << (NB * (f + 1)));
+    return r;
+}
+
 // Gate/down row chunk of phase C.  A single-token chunk reads each active row
 // once, so the rows are streamed (nontemporal); chunks of several tokens keep
 // ordinary loads, because other chunks of the same expert read the same rows
@@ -294,10 +421,15 @@ __device__ __forceinline__ uint4 row_load(const uint16_t *p)
 // passes as a ring of code registers: the loads run kAheadMulti passes
 // ahead across block boundaries, so each lane keeps that many 16-byte units
 // in flight however many tokens the chunk holds.
-template <int TB, class GEO>
+// Other code widths hold 2 BITS code words per group: a block holds at most
+// 32 code words per lane and kPB passes (2 passes at 8 bits, 4 at 4 bits).
+template <int TB, class GEO, int BITS = 2>
 __host__ __device__ constexpr int pass_block()
 {
-    constexpr int pb = (kPB / GEO::NG) < 1 ? 1 : (kPB / GEO::NG);
+    constexpr int per = 2 * BITS * GEO::NG;                 // code words per pass and lane
+    constexpr int pw = (32 / per) < 1 ? 1 : (32 / per);
+    constexpr int pb = BITS == 2 ? ((kPB / GEO::NG) < 1 ? 1 : (kPB / GEO::NG))
+                                 : (pw < kPB ? pw : kPB);
     return pb < GEO::SEG ? pb : GEO::SEG;
 }
 
@@ -349,7 +481,7 @@ __device__ __forceinline__ void route_token(const SparseArgs &a, const Lds &L, i
 // ONE: the tile is a single block of passes (straight-line code).  PBX: the
 // block is PBX times the usual pass block (2 for single-token tiles of 9-16
 // passes, so that they too run straight-line with a continuous lookahead).
-template <bool BF16, int TB, class GEO, bool ONE, int PBX = 1, bool ROUTE = false>
+template <bool BF16, int TB, class GEO, bool ONE, int PBX = 1, bool ROUTE = false, int BITS = 2>
 __global__ void __launch_bounds__(GEO::THREADS)
 expert_kernel(SparseArgs a)
 {
@@ -361,9 +493,11 @@ expert_kernel(SparseArgs a)
     constexpr int LOGSEG = Log2<SEG>::v;
     // channel passes loaded and reduced together (<= SEG; fewer when a lane
     // carries several tokens or groups, to bound registers)
-    constexpr int PR = pass_block<TB, GEO>() * PBX;
+    constexpr int PR = pass_block<TB, GEO, BITS>() * PBX;
     static_assert(PR <= GEO::SEG, "passes of a block exceed the segment");
     constexpr bool XREG = (TB * NG) <= 4;            // x pairs of the lane's groups kept in registers
+    static_assert(BITS == 2 || XREG, "other code widths keep x in registers");
+    constexpr int QB = 8 * BITS;                     // code bytes per 64-input group
 
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -440,7 +574,8 @@ expert_kernel(SparseArgs a)
     const int nrows = min(cpw, f - j0);
     if (nrows <= 0) return;
 
-    const uint8_t *upq = a.up_q + (size_t)e * a.q_stride + (size_t)j0 * (d / 4);
+    const int rowb = d * BITS / 8;                   // code bytes per channel
+    const uint8_t *upq = a.up_q + (size_t)e * a.q_stride + (size_t)j0 * rowb;
     const uint16_t *upsz = a.up_sz + (size_t)e * a.sz_stride + (size_t)j0 * G * 2;
     const uint16_t *gate = a.gate + (size_t)e * a.w_stride + (size_t)j0 * d;
     const uint16_t *down = a.down + (size_t)e * a.w_stride + (size_t)j0 * d;
@@ -451,7 +586,7 @@ expert_kernel(SparseArgs a)
     const int CPR = d / 8;                          // 16-byte chunks per d-row
 
     // phase-A code units of one block of PR passes (slot p holds pass p0 + p)
-    uint4 cq[PR][NG];
+    CodeUnit<BITS> cq[PR][NG];
     uint32_t csz[PR][NG];
     // The loads run AH passes ahead of the decode, as raw buffer loads over
     // the tile (passes past its end read zeros without a memory access), so no
@@ -459,15 +594,15 @@ expert_kernel(SparseArgs a)
     // token: the passes of a block are issued AH at a time from its start.
     // Several tokens (RING): the pass AH ahead goes into the slot freed by the
     // pass just decoded, across block boundaries, so the stream never drains.
-    constexpr bool RING = TB > 1;
+    constexpr bool RING = TB > 1 || BITS != 2;
     constexpr int AH = RING ? (kAheadMulti < PR ? kAheadMulti : PR - 1)
                             : (kAhead < PR ? kAhead : PR);
     static_assert(AH >= 1 || PR == 1, "lookahead");
     constexpr int PRED = (TB >= 4 && PR >= 2) ? PR / 2 : PR;
-    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(upq, (uint32_t)nrows * (d / 4));
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(upq, (uint32_t)nrows * rowb);
     const __amdgpu_buffer_rsrc_t rz = tile_rsrc(upsz, (uint32_t)nrows * G * 4);
     const int r_lane = wave * RPW + rs;             // channel of this lane in pass 0
-    const uint32_t q_lane = (uint32_t)(r_lane * (d / 4) + go * 16);
+    const uint32_t q_lane = (uint32_t)(r_lane * rowb + go * QB);
     const uint32_t z_lane = (uint32_t)((r_lane * G + go) * 4);
 #define LOAD_SLOT(PP, SLOT)                                                                 \
     {                                                                                       \
@@ -475,9 +610,9 @@ expert_kernel(SparseArgs a)
         const bool rok = r_lane + pp * ROWS_PASS < nrows;                                   \
         _Pragma("unroll") for (int gi = 0; gi < NG; ++gi) {                                 \
             const bool ok = rok && go + SEG * gi < G;                                       \
-            const uint32_t oq = q_lane + (uint32_t)(pp * ROWS_PASS * (d / 4) + gi * SEG * 16); \
+            const uint32_t oq = q_lane + (uint32_t)(pp * ROWS_PASS * rowb + gi * SEG * QB);  \
             const uint32_t oz = z_lane + (uint32_t)((pp * ROWS_PASS * G + gi * SEG) * 4);   \
-            cq[SLOT][gi] = bload_nt16(rq, ok ? oq : kOob);                                  \
+            cq[SLOT][gi] = bload_codes<BITS>(rq, ok ? oq : kOob);                           \
             csz[SLOT][gi] = bload_nt4(rz, ok ? oz : kOob);                                  \
         }                                                                                   \
     }
@@ -601,6 +736,7 @@ expert_kernel(SparseArgs a)
                     s3 = dot2<BF16>(xr_a[tb * NG + gi][m + 3], a.dec_one, s3);
                 }
                 xg_a[tb][gi] = (s0 + s1) + (s2 + s3);
+                perm_pairs<BITS>(xr_a[tb * NG + gi]);   // the code words' pair order
             } else {
                 xg_a[tb][gi] = L.xg[tb * G + g];
             }
@@ -638,8 +774,8 @@ expert_kernel(SparseArgs a)
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     // fp16: subnormal-pair decode (group_xq_f16); bf16: (1 + q/4) pairs
-                    uint32_t pw[BF16 ? 32 : 1];
-                    if constexpr (BF16) decode_unit<BF16>(cq[p][gi], pw, a.dec_mask, a.dec_one);
+                    uint32_t pw[BF16 && BITS == 2 ? 32 : 1];
+                    if constexpr (BF16 && BITS == 2) decode_unit<BF16>(cq[p][gi].v, pw, a.dec_mask, a.dec_one);
                     // units outside the tile read zeros from the buffer loads: s = 0
                     const float s = half_bits_to_float(csz[p][gi] & 0xFFFFu);
                     const float z = half_bits_to_float(csz[p][gi] >> 16);
@@ -659,11 +795,18 @@ expert_kernel(SparseArgs a)
                             }
                         }
                         const uint32_t(&xp)[32] = pick_x<XREG>(xr_a[XREG ? tb * NG + gi : 0], xl_);
-                        if constexpr (BF16) {
+                        if constexpr (BITS != 2) {
+                            float xq;
+                            if constexpr (BF16)
+                                xq = group_xq_bits_bf16<BITS>(cq[p][gi], xp, xg_a[tb][gi], a.dec_one);
+                            else
+                                xq = group_xq_bits_f16<BITS>(cq[p][gi], xp);
+                            part[tb][pg] += s * (xq - z * xg_a[tb][gi]);
+                        } else if constexpr (BF16) {
                             const float sp = group_dot<BF16>(pw, xp);
                             part[tb][pg] += s * (4.0f * sp - (4.0f + z) * xg_a[tb][gi]);
                         } else {
-                            part[tb][pg] += s * (group_xq_f16(cq[p][gi], xp) - z * xg_a[tb][gi]);
+                            part[tb][pg] += s * (group_xq_f16(cq[p][gi].v, xp) - z * xg_a[tb][gi]);
                         }
                     }
                 }
@@ -872,36 +1015,38 @@ expert_kernel(SparseArgs a)
 // The kernel instance for this call: straight-line (ONE, PBX) or loop form;
 // ROUTE: single-token layer calls that route inside the kernel (a separate
 // instance, so that the other calls' code is unchanged by it).
-template <bool BF16, int TB, class GEO, bool ROUTE>
+template <bool BF16, int TB, class GEO, bool ROUTE, int BITS>
 const void *pick_kernel(const SparseArgs &a)
 {
     constexpr int rows_pass = GEO::W * (64 / GEO::SEG);
+    constexpr int pb = pass_block<TB, GEO, BITS>();
     const int passes = (a.cpw + rows_pass - 1) / rows_pass;
-    const bool one = passes <= pass_block<TB, GEO>();
+    const bool one = passes <= pb;
     // (the widest geometry, and several tokens with two groups per lane, keep
     // the loop form: their straight-line versions spill)
     if constexpr (GEO::NG < 4 && (TB == 1 || GEO::NG == 1)) {
-        if (one) return (const void *)expert_kernel<BF16, TB, GEO, true, 1, ROUTE>;
+        if (one) return (const void *)expert_kernel<BF16, TB, GEO, true, 1, ROUTE, BITS>;
     }
-    if constexpr (TB == 1 && GEO::NG == 1 && 2 * pass_block<TB, GEO>() <= GEO::SEG) {
-        if (!one && passes <= 2 * pass_block<TB, GEO>())
-            return (const void *)expert_kernel<BF16, TB, GEO, true, 2, ROUTE>;
+    if constexpr (BITS == 2 && TB == 1 && GEO::NG == 1 && 2 * pb <= GEO::SEG) {
+        if (!one && passes <= 2 * pb)
+            return (const void *)expert_kernel<BF16, TB, GEO, true, 2, ROUTE, BITS>;
     }
-    return (const void *)expert_kernel<BF16, TB, GEO, false, 1, ROUTE>;
+    return (const void *)expert_kernel<BF16, TB, GEO, false, 1, ROUTE, BITS>;
 }
 
-template <bool BF16, int TB, class GEO>
+template <bool BF16, int TB, class GEO, int BITS>
 hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
 {
     size_t off[12];
     const size_t lds = lds_layout(a.d, a.cpw, TB, GEO::W, rows_per_batch<TB, GEO::NCH>(), off,
                                   a.route ? route_lds(a.E, a.k) : 0);
     const void *kern;
-    if constexpr (TB == 1) {
-        kern = a.route ? pick_kernel<BF16, TB, GEO, true>(a) : pick_kernel<BF16, TB, GEO, false>(a);
+    if constexpr (TB == 1 && BITS == 2) {
+        kern = a.route ? pick_kernel<BF16, TB, GEO, true, BITS>(a)
+                       : pick_kernel<BF16, TB, GEO, false, BITS>(a);
     } else {
-        if (a.route) return hipErrorInvalidValue;       // inline routing is for one token
-        kern = pick_kernel<BF16, TB, GEO, false>(a);
+        if (a.route) return hipErrorInvalidValue;       // inline routing: one token, INT2
+        kern = pick_kernel<BF16, TB, GEO, false, BITS>(a);
     }
     SparseArgs args = a;
     args.dec_mask = decode_const<BF16>().mask;
@@ -916,39 +1061,49 @@ hipError_t launch_tb(const SparseArgs &a, hipStream_t s)
     return e;
 }
 
-template <bool BF16, class GEO>
+template <bool BF16, class GEO, int BITS>
 hipError_t launch_geo(const SparseArgs &a, int tb, hipStream_t s)
 {
     switch (tb) {
-    case 1: return launch_tb<BF16, 1, GEO>(a, s);
+    case 1: return launch_tb<BF16, 1, GEO, BITS>(a, s);
     case 2:
-        if constexpr (GEO::NG <= 2) return launch_tb<BF16, 2, GEO>(a, s);
+        if constexpr (GEO::NG <= 2) return launch_tb<BF16, 2, GEO, BITS>(a, s);
         break;
     case 4:
-        if constexpr (GEO::NG == 1) return launch_tb<BF16, 4, GEO>(a, s);
+        if constexpr (GEO::NG == 1) return launch_tb<BF16, 4, GEO, BITS>(a, s);
         break;
     default: break;
     }
     return hipErrorInvalidValue;
 }
 
-// Geometry by hidden size: see Geo.
-template <bool BF16>
+// Geometry by hidden size: see Geo.  Other code widths: d = 512 ... 4096.
+template <bool BF16, int BITS = 2>
 hipError_t launch_dtype(const SparseArgs &a, int tb, hipStream_t s)
 {
-    switch (a.d) {
-    case 64: return launch_geo<BF16, Geo<1, 1, 1, 64>>(a, tb, s);
-    case 128: return launch_geo<BF16, Geo<2, 1, 1, 64>>(a, tb, s);
-    case 256: return launch_geo<BF16, Geo<4, 1, 1, 64>>(a, tb, s);
-    case 512: return launch_geo<BF16, Geo<8, 1, 1, 64>>(a, tb, s);
-    case 1024: return launch_geo<BF16, Geo<16, 1, 1, 128>>(a, tb, s);
-    case 2048: return launch_geo<BF16, Geo<32, 1, 1, 256>>(a, tb, s);
-    case 4096: return launch_geo<BF16, Geo<64, 1, 1, 512>>(a, tb, s);
-    default: break;
+    if constexpr (BITS != 2) {
+        switch (a.d) {
+        case 512: return launch_geo<BF16, Geo<8, 1, 1, 64>, BITS>(a, tb, s);
+        case 1024: return launch_geo<BF16, Geo<16, 1, 1, 128>, BITS>(a, tb, s);
+        case 2048: return launch_geo<BF16, Geo<32, 1, 1, 256>, BITS>(a, tb, s);
+        case 4096: return launch_geo<BF16, Geo<64, 1, 1, 512>, BITS>(a, tb, s);
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (a.d) {
+        case 64: return launch_geo<BF16, Geo<1, 1, 1, 64>, 2>(a, tb, s);
+        case 128: return launch_geo<BF16, Geo<2, 1, 1, 64>, 2>(a, tb, s);
+        case 256: return launch_geo<BF16, Geo<4, 1, 1, 64>, 2>(a, tb, s);
+        case 512: return launch_geo<BF16, Geo<8, 1, 1, 64>, 2>(a, tb, s);
+        case 1024: return launch_geo<BF16, Geo<16, 1, 1, 128>, 2>(a, tb, s);
+        case 2048: return launch_geo<BF16, Geo<32, 1, 1, 256>, 2>(a, tb, s);
+        case 4096: return launch_geo<BF16, Geo<64, 1, 1, 512>, 2>(a, tb, s);
+        default: break;
+        }
+        if (a.d > 4096 && a.d <= 8192) return launch_geo<BF16, Geo<64, 2, 2, 512>, 2>(a, tb, s);
+        if (a.d > 8192 && a.d <= 16384) return launch_geo<BF16, Geo<64, 4, 4, 512>, 2>(a, tb, s);
+        return hipErrorInvalidValue;
     }
-    if (a.d > 4096 && a.d <= 8192) return launch_geo<BF16, Geo<64, 2, 2, 512>>(a, tb, s);
-    if (a.d > 8192 && a.d <= 16384) return launch_geo<BF16, Geo<64, 4, 4, 512>>(a, tb, s);
-    return hipErrorInvalidValue;
 }
 
 }  // namespace sparse

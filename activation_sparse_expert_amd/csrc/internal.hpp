@@ -59,6 +59,8 @@ struct SparseArgs {
 // Launch the fused Algorithm-1 kernel; tb = tokens per chunk (1, 2, 4).
 hipError_t launch_sparse_expert_f16(const SparseArgs &a, int tb, hipStream_t s);
 hipError_t launch_sparse_expert_bf16(const SparseArgs &a, int tb, hipStream_t s);
+// the same kernel with the up codes at bits = 8, 4 or 1 (plain packing, d = 512 ... 4096)
+hipError_t launch_sparse_expert_bits(const SparseArgs &a, int bits, bool bf16, int tb, hipStream_t s);
 
 // Second kernel: output rows from the partial rows.
 constexpr int kMaxExpertsPerToken = 1024;   // k + S of a layer (routed + shared rows per token)
@@ -165,27 +167,7 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_mask_bits(const uint8_t *m, int rows, int f, uint64_t *bits, int32_t *nnz,
                             hipStream_t s);
 
-// Threshold calibration: out = linear-interpolation quantile of |v| between
-// order statistics r_lo and r_hi with weight gamma (computed on the host).
-// The sparse expert with 8-, 4- or 1-bit up codes (plain packing, same scales).
-constexpr int kBitsTile = 64;                   // channels per gather workgroup
-constexpr size_t kBitsMaxLds = 144u << 10;      // x staging of the up kernel
-constexpr int kBitsMaxT = 8;                    // tokens per call
-struct BitsArgs {
-    const uint8_t *up_q;                // [f][d*bits/8]
-    const uint16_t *up_sz;              // [f][d/64][2]
-    const uint16_t *gate, *down;        // [f][d]
-    int bits, d, f, T, bf16;
-    float thr;
-    const uint16_t *x;                  // [T][d]
-    const float *token_scale;           // nullable
-    float *v;                           // [T][f] written by the up kernel
-    uint8_t *mask_out;                  // nullable
-    float *part;                        // [T][tiles][d]
-    int tiles;                          // ceil(f / kBitsTile)
-};
-size_t bits_lds_up(int T, int d);
-hipError_t launch_expert_bits(const BitsArgs &a, hipStream_t s);
+// Up codes at 8, 4 or 1 bits (plain packing) and the group-64 scales.
 hipError_t launch_pack_bits(const void *w, int dt, int d, int f, int bits, uint8_t *q,
                             uint16_t *sz, hipStream_t s);
 
@@ -193,6 +175,8 @@ hipError_t launch_pack_bits(const void *w, int dt, int d, int f, int bits, uint8
 hipError_t launch_eamc_match(const int32_t *eamc, int n, int len, const int32_t *query,
                              int32_t *idx_out, double *dist, hipStream_t s);
 
+// Threshold calibration: out = linear-interpolation quantile of |v| between
+// order statistics r_lo and r_hi with weight gamma (computed on the host).
 size_t calibrate_ws_bytes();
 hipError_t launch_calibrate(const float *v, long long n, long long r_lo, long long r_hi,
                             double gamma, float *out, void *ws, hipStream_t s);

@@ -435,7 +435,7 @@ def stack_measure(out):
 
 
 def bits_measure(sparsity=0.9):
-    """One Mixtral-8x7B-shaped expert with the up codes at 8, 4 and 1 bits,
+    """One Mixtral-8x7B-shaped expert with the up codes at 8, 4, 2 and 1 bits,
     one token per call, 90% sparsity: time per call and algorithmic bytes
     (codes d f bits/8, scales f d/16, gate + down rows of the active channels,
     x) per call."""
@@ -449,7 +449,7 @@ def bits_measure(sparsity=0.9):
     u = synth.device_normal(synth.seed_of(2, 0, 0, synth.T_UP), (f, d), 0.02, dev)
     xs = synth.device_normal(synth.seed_of(2, 0, 0, synth.T_X), (64, d), 1 / 64, dev, torch.float16)
     res = {}
-    for bits in (8, 4, 1):
+    for bits in (8, 4, 2, 1):
         up_q, up_sz = moe.pack_up_bits(u, bits)
         ex = moe.Expert(up_q, up_sz, g, dn, 0.0)
         v = torch.empty((64, f), dtype=torch.float32, device=dev)
@@ -497,8 +497,9 @@ def bits_measure(sparsity=0.9):
                              "batch4_tokens_per_s": 4 / sec4,
                              "batch4_union_channels": uni}
         del up_q, up_sz, ex
-    res["workload"] = ("one Mixtral-8x7B-shaped expert (d=4096, f=14336), up codes at 8/4/1 bits, "
-                       "90% sparsity, batch 1")
+    res["workload"] = ("one Mixtral-8x7B-shaped expert (d=4096, f=14336), up codes at 8/4/2/1 bits "
+                       "(2 bits: the INT2 format, for comparison on the same schedule), "
+                       "90% sparsity, batch 1 and 4")
     return res
 
 

@@ -251,9 +251,11 @@ size_t moe_noalloc_scratch_bytes(void);
  * (least significant bits first), up_sz [f][d/64][2] as for INT2 with
  * 2^bits - 1 levels (moe_pack_up_bits).  Other arguments, outputs and the
  * mask rule as moe_expert_forward_sparse; the output is bit-reproducible.
- * Limits for 8, 4, 1 bits: d in {512, 1024, 2048, 4096}, T <= 8 with
- * T*d*4.25 bytes <= 144 KiB (else MOE_ERR_UNSUPPORTED).
- * Workspace: moe_workspace_size(MOE_OP_EXPERT_BITS, T, d, f) bytes.
+ * The same fused kernel runs every width (only the decode of the codes
+ * differs).  Limits for 8, 4, 1 bits: d in {512, 1024, 2048, 4096} (else
+ * MOE_ERR_UNSUPPORTED); T as for INT2.
+ * Workspace: moe_workspace_size(MOE_OP_EXPERT_BITS, T, d, f) bytes (the INT2
+ * call's workspace at the same sizes).
  */
 moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, int d, int f,
                                           moe_dtype wdt, const void *x, moe_dtype xdt, int T,
