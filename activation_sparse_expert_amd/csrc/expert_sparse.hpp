@@ -352,6 +352,28 @@ __device__ __forceinline__ void perm_pairs(uint32_t (&xp)[32])
 template <int BITS>
 __device__ __forceinline__ float group_xq_bits_f16(const CodeUnit<BITS> &c, const uint32_t (&xp)[32])
 {
+    if constexpr (BITS == 1) {
+        // one bit per code: bit m of each half is the subnormal 2^(m - 24) as
+        // it stands (m <= 9); bits 10..15 are shifted down by 6, to positions
+        // 4..9.  One accumulator per position, exact powers of two at the end.
+        float acc[10];
+#pragma unroll
+        for (int p = 0; p < 10; ++p) acc[p] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t w = c.w[i], ws = w >> 6;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int p = m < 10 ? m : m - 6;
+                const uint32_t pw = (m < 10 ? w : ws) & (0x00010001u << p);
+                acc[p] = dot2<false>(pw, xp[i * 16 + m], acc[p]);
+            }
+        }
+        float r = 0.f;
+#pragma unroll
+        for (int p = 0; p < 10; ++p) r += acc[p] * (float)(1u << (24 - p));
+        return r;
+    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     constexpr int H = 16 / BITS;                    // pairs per code word
 #pragma unroll
