@@ -597,7 +597,20 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     red.part = w.part;
     red.y = y; red.ydt = (int)ydt; red.accumulate = 0;
     const int ksplit = use_gemm ? gemm_ksplit(T, k, E, S, d, f) : 0;
-    const TilePlan tp = sp.tp;
+    TilePlan tp = sp.tp;
+    if (mixed) {
+        // The sparse kernel sees only experts below n* tokens (at most
+        // ceil((n* - 1) / tb) chunks each) and the shared experts unless they
+        // are dense: tiles sized for those fill the chip; the partial rows
+        // stay within the workspace's max(tiles, kDenseKSplit) slots per row.
+        const long long tk = (long long)T * k;
+        const long long act = E < tk ? E : tk;
+        const long long per = (nstar - 1 + sp.tb - 1) / sp.tb;
+        const long long expect = act * per + (shared_dense ? 0 : (long long)S * ((T + sp.tb - 1) / sp.tb));
+        const TilePlan tm = plan_tiles(f, (int)(expect > 0 ? expect : 1), (long long)T * (k + S), d);
+        const int cap = tp.tiles > kDenseKSplit ? tp.tiles : kDenseKSplit;
+        if (tm.tiles > tp.tiles && tm.tiles <= cap) tp = tm;
+    }
     const int stride = mixed ? (tp.tiles > ksplit ? tp.tiles : ksplit) : 0;
     if (mixed) {
         // the sparse experts: the sparse kernel over the sparse chunk table

@@ -53,7 +53,7 @@ D, F = 4096, 14336
 NTOK = 16
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_expert_sparse_mixtral_b1_s90.md")
 KERNEL_SOURCES = ["expert_sparse.hpp", "expert_sparse_f16.hip", "reduce.hip", "internal.hpp",
-                  "device.hpp", "api.cpp"]
+                  "device.hpp", "route_common.hpp", "api.cpp"]
 
 
 def log(*a):
@@ -81,6 +81,7 @@ def build_instances(R, sparsity, dev):
         torch.cuda.synchronize()
         ex.threshold = float(np.float32(np.quantile(np.abs(v.cpu().numpy()).ravel(), sparsity)))
         experts.append(ex)
+        log(f"instance {i + 1}/{R} ready")
     return experts
 
 
@@ -596,6 +597,9 @@ def main():
     ap.add_argument("--dense-only", action="store_true",
                     help="only the dense MFMA path of the batched layer, at 256 and 2048 tokens, "
                          "three calls each (for profiling)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline expert call (no batch-4, layer, batched or CPU legs; "
+                         "for counter passes)")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the layer workloads (32-layer stack, fine-grained layer)")
     ap.add_argument("--no-batched", action="store_true",
@@ -653,12 +657,14 @@ def main():
         for t in range(NTOK):
             moe.expert_forward_sparse(experts[r], xs[t], y=y, ws=ws, mask_out=m)
             nnz[r, t] = float(m.sum().item())
+        log(f"masks of instance {r + 1}/{R} counted")
     fixed = D * F // 4 + F * (D // 64) * 4 + D * 2 + D * 4     # INT2 up + scales + x + y
     per_call = fixed + 2 * nnz * D * 2                            # + gate and down rows
     sched = [(i % R, (i // R) % NTOK) for i in range(args.steps)]
     bytes_timed = float(sum(per_call[r, t] for r, t in sched))
 
     stream = torch.cuda.Stream()
+    log(f"timing {args.steps} steps")
     # warmup (eager), then capture the K steps in one graph
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -733,6 +739,9 @@ def main():
             "traffic": counted_traffic(),
         },
     }
+    if args.headline_only:
+        print(json.dumps(out), flush=True)
+        return
     # the same expert call at batch 4 (Mixtral shape, 90% sparsity)
     x4 = [x_all[i:i + 4] for i in range(0, NTOK, 4)]
     y4 = torch.empty((4, D), dtype=torch.float32, device=dev)
@@ -744,6 +753,7 @@ def main():
             moe.expert_forward_sparse(experts[r], x4[t], y=y4, ws=ws4, mask_out=m4)
             u = int(m4.any(dim=0).sum().item())
             b4 += D * F // 4 + F * (D // 64) * 4 + 4 * D * (2 + 4) + 2 * u * D * 2
+        log(f"batch-4 masks of instance {r + 1}/{R} counted")
     b4 /= R * len(x4)
     calls = [(experts[i % R], x4[(i // R) % len(x4)]) for i in range(R * len(x4))]
     ci = [0]
