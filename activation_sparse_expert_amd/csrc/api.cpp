@@ -209,12 +209,20 @@ void *scratch_for_current_device()
 // Split of f in the dense down product: enough workgroups (d / 256 column
 // tiles per chunk of tokens) for about two per compute unit, at most 4 (the
 // partial-row region holds 4 slices per row), each slice a multiple of 64.
-int gemm_ksplit(int T, int k, int E, int S, int d, int f)
+// Token rows per dense chunk and tile: 64 when the routed experts average at
+// most 32 tokens (two workgroups per compute unit; the weight stream bounds
+// these), else 256.  Near 64 tokens on average many experts would spill into
+// a second, nearly empty 64-row chunk that streams the weights again.
+int gemm_tile_rows(int T, int k, int E)
+{
+    return (long long)T * k <= (long long)(kGemmChunkSmall / 2) * E ? kGemmChunkSmall : kGemmChunk;
+}
+
+int gemm_ksplit(int T, int k, int E, int S, int d, int f, int mt)
 {
     const long long tk = (long long)T * k;
     const long long act = E < tk ? E : tk;
-    const long long expect = (long long)S * ((T + kGemmChunk - 1) / kGemmChunk) +
-                             (tk + kGemmChunk - 1) / kGemmChunk + act / 2;
+    const long long expect = (long long)S * ((T + mt - 1) / mt) + (tk + mt - 1) / mt + act / 2;
     int ks = 1;
     while (ks < kDenseKSplit && expect * (d / 256) * ks < 512 && f % (64 * ks * 2) == 0) ks *= 2;
     return ks;
@@ -567,7 +575,7 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     if (path == MOE_PATH_DENSE) {
         // experts with at least dense_min pairs are listed in 256-token chunks
         r.dense_min = mixed ? nstar : 1;
-        r.dense_chunk = kGemmChunk; r.chunk_tab2 = w.chunk_tab2; r.n_chunks2 = w.n_chunks2;
+        r.dense_chunk = gemm_tile_rows(T, k, E); r.chunk_tab2 = w.chunk_tab2; r.n_chunks2 = w.n_chunks2;
     }
     r.expert_dense = (trace && trace->expert_dense) ? trace->expert_dense
                    : (mixed ? w.expert_dense : nullptr);
@@ -596,7 +604,8 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     red.d = d; red.T = T; red.layer = 1; red.rows_per_tok = k + S; red.k = k; red.S = S;
     red.part = w.part;
     red.y = y; red.ydt = (int)ydt; red.accumulate = 0;
-    const int ksplit = use_gemm ? gemm_ksplit(T, k, E, S, d, f) : 0;
+    const int mt = gemm_tile_rows(T, k, E);
+    const int ksplit = use_gemm ? gemm_ksplit(T, k, E, S, d, f, mt) : 0;
     TilePlan tp = sp.tp;
     if (mixed) {
         // The sparse kernel sees only experts below n* tokens (at most
@@ -644,7 +653,8 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         g.h16 = (uint16_t *)w.h; g.part = w.part; g.part_stride = stride;
         g.chunk_tab = w.chunk_tab2; g.n_chunks = w.n_chunks2; g.offset = w.offset; g.pairs = w.pairs;
         g.topk_w = r.topk_w;
-        g.grid_chunks = gemm_grid_chunks(T, k, E, Sg);
+        g.grid_chunks = gemm_grid_chunks(T, k, E, Sg, mt);
+        g.mt = mt;
         g.ksplit = ksplit;
         he = launch_gemm_layer(g, s);
         if (he != hipSuccess) return MOE_ERR_HIP;

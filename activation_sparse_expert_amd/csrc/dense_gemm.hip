@@ -21,15 +21,14 @@
 // v_mfma_f32_32x32x16_{bf16,f16} (16 fp32 each), so each k step reads 4 A and
 // 2 B fragments from LDS for 8 MFMAs, and one wave's MFMAs run while the
 // other wave of its SIMD waits at a barrier or for LDS.  Operands move global -> LDS by DMA
-// (global_load_lds_dwordx4), in stages of 32 k values (64-byte rows) with
-// four stages and three blocks in flight; the 16-byte chunks of a row are
-// XOR-swizzled so that fragment reads hit distinct banks.  Token rows come in
-// chunks of at most 256 of one expert from the grouping kernel's chunk table;
-// the grid takes the chunk index fastest, so the chunks that share a weight
-// tile run side by side and the tile streams from HBM about once.  Row
-// subtiles past a chunk's tokens are skipped (their MFMAs are not issued);
-// their rows are still copied (clamped to a valid token) to keep every wave's
-// copy count fixed.
+// (global_load_lds_dwordx4), in blocks of 64 k values (128-byte rows) through
+// two stages, one block copied while the other is multiplied; the 16-byte
+// chunks of a row are XOR-swizzled so that fragment reads hit distinct banks.
+// Token rows come in chunks of at most 256 (or 64, see GT) of one expert from
+// the grouping kernel's chunk table.  Tiles are dealt to the XCDs so that the
+// workgroups resident on one XCD share token chunks and neighbouring weight
+// tiles (see the kernel).  Rows past a chunk's tokens are neither copied nor
+// multiplied (their row subtiles issue no MFMAs).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -44,14 +43,21 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kWaves = 8;                       // 2 per SIMD: one's MFMAs cover the other's waits
 constexpr int kGThreads = 64 * kWaves;
 constexpr int kWNB = 16 / kWaves;               // B subtiles (32 columns) per wave
-constexpr int kMT = 256;                        // tile rows (tokens)
 constexpr int kNT = 256;                        // tile columns (B rows)
 constexpr int kKB = 64;                         // k values per stage: 128-byte rows, whole lines
 constexpr int kSteps = kKB / 16;                // MFMA k steps per block
 constexpr int kStages = 2;
-constexpr int kStageBytes = (kMT + kNT) * kKB * 2;             // 64 KB
-constexpr int kGLds = kStages * kStageBytes;                    // 128 KB
-constexpr int kMaxCopies = kStageBytes / 1024 / kWaves;   // copy instructions per wave
+// Tile rows (tokens): MT = 256, or MT = 64 for experts with few tokens each,
+// whose 40 KB stages let two workgroups share a compute unit (twice the
+// weight bytes in flight per CU for the weight-bound case).
+template <int MT>
+struct GT {
+    static constexpr int kStageBytes = (MT + kNT) * kKB * 2;            // 64 KB / 40 KB
+    static constexpr int kLds = kStages * kStageBytes;                  // 128 KB / 80 KB
+    static constexpr int kMaxCopies = kStageBytes / 1024 / kWaves;      // copy instructions per wave
+    static constexpr int kRH = MT / 2;                                  // rows per wave row-half
+    static constexpr int kSub = kRH / 32;                               // row subtiles per wave
+};
 
 template <bool BF16>
 __device__ __forceinline__ floatx16 mma(const uint4 &a, const uint4 &b, const floatx16 &c)
@@ -78,15 +84,16 @@ struct Chunk {
 
 // Chunk ci of the grid: the S shared experts' chunks of ceil(T / 256) tokens
 // first, then the routed chunks listed by the grouping kernel.
+template <int MT>
 __device__ __forceinline__ Chunk chunk_info(const GemmArgs &a, int ci)
 {
     Chunk c{};
-    const int nsc = (a.T + kMT - 1) / kMT;
+    const int nsc = (a.T + MT - 1) / MT;
     if (ci < a.S * nsc) {
         const int sh = ci / nsc;
-        const int m0 = (ci - sh * nsc) * kMT;
+        const int m0 = (ci - sh * nsc) * MT;
         c.e = a.E + sh;
-        c.ntok = min(kMT, a.T - m0);
+        c.ntok = min(MT, a.T - m0);
         c.pos0 = m0;
         c.hrow0 = a.T * a.k + sh * a.T + m0;
         c.shared = true;
@@ -99,7 +106,7 @@ __device__ __forceinline__ Chunk chunk_info(const GemmArgs &a, int ci)
     const int ent = a.chunk_tab[r];
     c.e = ent >> 16;
     c.pos0 = ent & 0xFFFF;
-    c.ntok = min(kMT, a.offset[c.e + 1] - c.pos0);
+    c.ntok = min(MT, a.offset[c.e + 1] - c.pos0);
     c.hrow0 = c.pos0;
     c.shared = false;
     return c;
@@ -124,8 +131,8 @@ __device__ __forceinline__ uint16_t to16(float v)
 // read from LDS while the MFMAs of step s run (sched_barrier keeps the
 // compiler from sinking the reads back next to their MFMAs); the other wave
 // of each SIMD covers the rest of the waiting.
-template <bool BF16, int NSUB, class ISSUE>
-__device__ __forceinline__ void kloop(floatx16 (&acc)[4][kWNB], const unsigned char *smem, int nkb,
+template <bool BF16, int MT, int NSUB, class ISSUE>
+__device__ __forceinline__ void kloop(floatx16 (&acc)[GT<MT>::kSub][kWNB], const unsigned char *smem, int nkb,
                                       int arow0, const int (&brow)[kWNB], int li, int hk,
                                       ISSUE &issue)
 {
@@ -153,7 +160,7 @@ __device__ __forceinline__ void kloop(floatx16 (&acc)[4][kWNB], const unsigned c
     __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
         if (kb + 1 < nkb) issue(kb + 1);            // the stage block kb - 1 used
-        const unsigned char *st = smem + (size_t)(kb & 1) * kStageBytes;
+        const unsigned char *st = smem + (size_t)(kb & 1) * GT<MT>::kStageBytes;
         load(st, 0, a0, b0);
 #pragma unroll
         for (int s2 = 0; s2 < kSteps; s2 += 2) {
@@ -171,11 +178,13 @@ __device__ __forceinline__ void kloop(floatx16 (&acc)[4][kWNB], const unsigned c
     }
 }
 
-// MODE 0: gate/up, MODE 1: down.
-template <bool BF16, int MODE>
-__global__ void __launch_bounds__(kGThreads)
+// MODE 0: gate/up, MODE 1: down.  MT: tile rows (256, or 64 with two
+// workgroups per compute unit).
+template <bool BF16, int MODE, int MT>
+__global__ void __launch_bounds__(kGThreads, MT == 64 ? 2 : 1)
 gemm_kernel(GemmArgs a)
 {
+    using G = GT<MT>;
     extern __shared__ __align__(16) unsigned char smem[];
     // ---- which tile: XCD-aware.  Workgroups are dealt to the 8 XCDs in turn
     // (block b to XCD b % 8, as its (b / 8)-th).  Each XCD takes a contiguous
@@ -186,7 +195,7 @@ gemm_kernel(GemmArgs a)
     // Tile order: chunk pair, then split-K slice, then column tile, then the
     // chunk within the pair.
     const int ntiles = MODE == 0 ? a.f / 128 : a.d / kNT;
-    const int nsc = (a.T + kMT - 1) / kMT;
+    const int nsc = (a.T + MT - 1) / MT;
     const int vchunks = a.S * nsc + *a.n_chunks;    // chunks that hold tokens
     const int per_pair = 2 * ntiles * a.ksplit;
     const int vtiles = (vchunks + 1) / 2 * per_pair;
@@ -201,7 +210,7 @@ gemm_kernel(GemmArgs a)
     const int nt = (r0 >> 1) % ntiles;
     const int ks = (r0 >> 1) / ntiles;              // split-K slice (down)
     if (ci >= vchunks) return;
-    const Chunk ch = chunk_info(a, ci);
+    const Chunk ch = chunk_info<MT>(a, ci);
     if (!ch.valid) return;
 
     const int tid = threadIdx.x;
@@ -220,26 +229,26 @@ gemm_kernel(GemmArgs a)
     // physical chunk l % 8 (logical chunk pc ^ swizzle).  Token rows past the
     // chunk are not copied: their (stale) LDS rows only feed MFMA rows that the
     // epilogue discards.
-    const int na = (min(ch.ntok, kMT) + 7) / 8;
+    const int na = (min(ch.ntok, MT) + 7) / 8;
     const int ninst = na + kNT / 8;
     const int ncopy = (ninst - wave + kWaves - 1) / kWaves;
-    const uint16_t *src[kMaxCopies];
-    int dst[kMaxCopies];
+    const uint16_t *src[G::kMaxCopies];
+    int dst[G::kMaxCopies];
 #pragma unroll
-    for (int q = 0; q < kMaxCopies; ++q) {
+    for (int q = 0; q < G::kMaxCopies; ++q) {
         const int inst = min(wave + kWaves * q, ninst - 1);
-        const int base = inst < na ? 8 * inst : kMT + 8 * (inst - na);
+        const int base = inst < na ? 8 * inst : MT + 8 * (inst - na);
         const int row = base + (lane >> 3);
         dst[q] = base * 128;
         const int pc = lane & 7;
         const int c = pc ^ swz(row);
         const uint16_t *rp;
-        if (row < kMT) {
+        if (row < MT) {
             const int m = min(row, ch.ntok - 1);
             if (MODE == 0) rp = a.x + (size_t)token_at(a, ch, m) * d;
             else rp = a.h16 + (size_t)(ch.hrow0 + m) * f;
         } else {
-            const int br = row - kMT;
+            const int br = row - MT;
             if (MODE == 0) {
                 const size_t ch0 = (size_t)ch.e * f + (size_t)nt * 128;
                 rp = br < 128 ? a.gate + (ch0 + br) * d : a.up + (ch0 + br - 128) * d;
@@ -250,23 +259,23 @@ gemm_kernel(GemmArgs a)
         src[q] = rp + k_beg + 8 * c;
     }
     auto issue = [&](int kb) {
-        unsigned char *base = smem + (size_t)(kb & 1) * kStageBytes;
+        unsigned char *base = smem + (size_t)(kb & 1) * G::kStageBytes;
 #pragma unroll
-        for (int q = 0; q < kMaxCopies; ++q)
+        for (int q = 0; q < G::kMaxCopies; ++q)
             if (q < ncopy) copy16_to_lds(src[q] + (size_t)kb * kKB, base + dst[q]);
     };
 
-    floatx16 acc[4][kWNB];
+    floatx16 acc[G::kSub][kWNB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G::kSub; ++i)
 #pragma unroll
         for (int j = 0; j < kWNB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // row subtiles of this wave that hold tokens (wave-uniform)
-    const int vrows = __builtin_amdgcn_readfirstlane(ch.ntok - 128 * wm);
-    const int nsub = vrows <= 0 ? 0 : min(4, (vrows + 31) / 32);
+    const int vrows = __builtin_amdgcn_readfirstlane(ch.ntok - G::kRH * wm);
+    const int nsub = vrows <= 0 ? 0 : min(G::kSub, (vrows + 31) / 32);
     // LDS rows of this wave's B subtiles
     // gate/up: the wave's gate columns first, then the same channels' up
     // columns (kWNB / 2 subtiles each); down: kWNB consecutive subtiles
@@ -274,18 +283,23 @@ gemm_kernel(GemmArgs a)
     int brow[kWNB];
 #pragma unroll
     for (int j = 0; j < kWNB; ++j) {
-        if (MODE == 0) brow[j] = kMT + (j < HB ? 32 * HB * wn + 32 * j : 128 + 32 * HB * wn + 32 * (j - HB));
-        else brow[j] = kMT + 32 * kWNB * wn + 32 * j;
+        if (MODE == 0) brow[j] = MT + (j < HB ? 32 * HB * wn + 32 * j : 128 + 32 * HB * wn + 32 * (j - HB));
+        else brow[j] = MT + 32 * kWNB * wn + 32 * j;
     }
     const int li = lane & 31, hk = lane >> 5;
 
     issue(0);
-    switch (nsub) {
-    case 4: kloop<BF16, 4>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
-    case 3: kloop<BF16, 3>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
-    case 2: kloop<BF16, 2>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
-    case 1: kloop<BF16, 1>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
-    default: kloop<BF16, 0>(acc, smem, nkb, 128 * wm, brow, li, hk, issue); break;
+    if constexpr (G::kSub == 4) {
+        switch (nsub) {
+        case 4: kloop<BF16, MT, 4>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
+        case 3: kloop<BF16, MT, 3>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
+        case 2: kloop<BF16, MT, 2>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
+        case 1: kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
+        default: kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
+        }
+    } else {
+        if (nsub == 1) kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue);
+        else kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue);
     }
 
     // ---- epilogue --------------------------------------------------------
@@ -294,14 +308,14 @@ gemm_kernel(GemmArgs a)
     if (MODE == 0) {
         if (nsub == 0) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < G::kSub; ++i) {
             if (i >= nsub) continue;
 #pragma unroll
             for (int j = 0; j < HB; ++j) {
                 const int col = nt * 128 + 32 * HB * wn + 32 * j + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
+                    const int m = G::kRH * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
                     if (m < ch.ntok)
                         a.h16[(size_t)(ch.hrow0 + m) * f + col] =
                             to16<BF16>(silu(acc[i][j][r]) * acc[i][j + HB][r]);
@@ -312,8 +326,8 @@ gemm_kernel(GemmArgs a)
         // partial row and router weight of each token row of the chunk
         __syncthreads();                            // the stages are done with
         int *row_s = (int *)smem;
-        float *sc_s = (float *)(smem + kMT * 4);
-        for (int m = tid; m < kMT; m += kGThreads) {
+        float *sc_s = (float *)(smem + MT * 4);
+        for (int m = tid; m < MT; m += kGThreads) {
             int row = 0;
             float sc = 0.f;
             if (m < ch.ntok) {
@@ -332,11 +346,11 @@ gemm_kernel(GemmArgs a)
         __syncthreads();
         if (nsub == 0) return;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < G::kSub; ++i) {
             if (i >= nsub) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
+                const int m = G::kRH * wm + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
                 if (m >= ch.ntok) continue;
                 const int pstride = a.part_stride > 0 ? a.part_stride : a.ksplit;
                 float *dst = a.part + ((size_t)row_s[m] * pstride + ks) * d + (size_t)nt * kNT +
@@ -370,39 +384,46 @@ transpose16_kernel(const uint16_t *in, int rows, int cols, uint16_t *out)
 
 }  // namespace
 
-int gemm_grid_chunks(int T, int k, int E, int S)
+int gemm_grid_chunks(int T, int k, int E, int S, int mt)
 {
     const long long tk = (long long)T * k;
     const long long act = E < tk ? E : tk;
-    return (int)(S * ((T + kMT - 1) / kMT) + (tk + act * (kMT - 1)) / kMT);
+    return (int)(S * ((T + mt - 1) / mt) + (tk + act * (mt - 1)) / mt);
 }
 
-hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s)
+namespace {
+template <bool BF16, int MT>
+hipError_t launch_gemm_mt(const GemmArgs &a, hipStream_t s)
 {
-    if (a.d % kNT != 0 || a.f % 128 != 0 || a.d % kKB != 0 ||
-        a.f % (kKB * a.ksplit) != 0 || a.ksplit < 1)
-        return hipErrorInvalidValue;
-    const void *gu = a.bf16 ? (const void *)gemm_kernel<true, 0> : (const void *)gemm_kernel<false, 0>;
-    const void *dn = a.bf16 ? (const void *)gemm_kernel<true, 1> : (const void *)gemm_kernel<false, 1>;
-    hipError_t e = hipFuncSetAttribute(gu, hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+    using G = GT<MT>;
+    const void *gu = (const void *)gemm_kernel<BF16, 0, MT>;
+    const void *dn = (const void *)gemm_kernel<BF16, 1, MT>;
+    hipError_t e = hipFuncSetAttribute(gu, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(dn, hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+    e = hipFuncSetAttribute(dn, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
     if (e != hipSuccess) return e;
-    GemmArgs g = a;
     // tiles are mapped in the kernel (XCD-aware, from the valid chunk count):
     // the grid covers the bound in pairs of chunks, 8 per XCD turn, plus 8
     const unsigned pairs = (unsigned)(a.grid_chunks + 1) / 2;
     const dim3 grid_gu((pairs * 2u * (unsigned)(a.f / 128) + 7u) / 8u * 8u + 8u);
     const dim3 grid_dn((pairs * 2u * (unsigned)(a.d / kNT) * (unsigned)a.ksplit + 7u) / 8u * 8u + 8u);
-    GemmArgs gu_args = g;
+    GemmArgs gu_args = a;
     gu_args.ksplit = 1;
-    if (a.bf16) hipLaunchKernelGGL((gemm_kernel<true, 0>), grid_gu, dim3(kGThreads), kGLds, s, gu_args);
-    else hipLaunchKernelGGL((gemm_kernel<false, 0>), grid_gu, dim3(kGThreads), kGLds, s, gu_args);
+    hipLaunchKernelGGL((gemm_kernel<BF16, 0, MT>), grid_gu, dim3(kGThreads), G::kLds, s, gu_args);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.bf16) hipLaunchKernelGGL((gemm_kernel<true, 1>), grid_dn, dim3(kGThreads), kGLds, s, g);
-    else hipLaunchKernelGGL((gemm_kernel<false, 1>), grid_dn, dim3(kGThreads), kGLds, s, g);
+    hipLaunchKernelGGL((gemm_kernel<BF16, 1, MT>), grid_dn, dim3(kGThreads), G::kLds, s, a);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s)
+{
+    if (a.d % kNT != 0 || a.f % 128 != 0 || a.d % kKB != 0 ||
+        a.f % (kKB * a.ksplit) != 0 || a.ksplit < 1 || (a.mt != 64 && a.mt != 256))
+        return hipErrorInvalidValue;
+    if (a.mt == 64) return a.bf16 ? launch_gemm_mt<true, 64>(a, s) : launch_gemm_mt<false, 64>(a, s);
+    return a.bf16 ? launch_gemm_mt<true, 256>(a, s) : launch_gemm_mt<false, 256>(a, s);
 }
 
 hipError_t launch_transpose16(const uint16_t *in, int mats, int rows, int cols, uint16_t *out,

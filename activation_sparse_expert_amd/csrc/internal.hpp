@@ -153,9 +153,11 @@ struct GemmArgs {
     const float *topk_w;
     int ksplit;                         // split of f in the down product
     int grid_chunks;                    // chunk slots in the grid (an upper bound)
+    int mt;                             // token rows per chunk and tile: 256 or 64
 };
 constexpr int kGemmChunk = 256;         // token rows per chunk
-int gemm_grid_chunks(int T, int k, int E, int S);
+constexpr int kGemmChunkSmall = 64;     // ... when the experts average at most 32 tokens
+int gemm_grid_chunks(int T, int k, int E, int S, int mt);
 hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s);
 // out [mats][cols][rows] = in [mats][rows][cols], 16-bit elements
 hipError_t launch_transpose16(const uint16_t *in, int mats, int rows, int cols, uint16_t *out,

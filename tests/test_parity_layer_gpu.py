@@ -174,11 +174,14 @@ def test_small_layer_dense(T, E, S, k, d, f):
     (700, 3, 1, 3, 256, 384, "bf16"),    # 700 per expert: 3 chunks each, every row subtile
     (9, 6, 1, 2, 1024, 256, "f16"),      # a few tokens per expert
     (64, 8, 0, 2, 2048, 1024, "bf16"),   # split of f in the down product
+    (120, 8, 1, 2, 512, 256, "f16"),     # 64-row tiles (30 tokens per expert on average):
+                                         # the shared expert's 120 tokens in two chunks
 ])
 def test_small_layer_dense_gemm(T, E, S, k, d, f, wdt):
-    """The 256 x 256-tile MFMA GEMM (bf16 and fp16 layers) against the
-    oracle's dense path: ragged chunks, several chunks per expert, shared
-    experts, and a split of f in the down product."""
+    """The MFMA GEMM (bf16 and fp16 layers; 256-row tiles, or 64-row tiles
+    when the experts average at most 64 tokens) against the oracle's dense
+    path: ragged chunks, several chunks per expert, shared experts, and a
+    split of f in the down product."""
     experts, thr = build_host_layer(67, E, S, d, f, wdt, 0.7, 1 / 16, layer=d)
     R_bits = synth.to_bits(synth.router_f32(67, d, E, d), wdt)
     x_bits = synth.to_bits(synth.tokens_f32(68, T, d, 1 / 16, layer=d), wdt)
@@ -236,16 +239,17 @@ def test_layer_auto_path(T, E, S, k, d, f, expect):
     assert not np.array_equal(y_auto, y_other)
 
 
-@pytest.mark.parametrize("wdt", ["f16", "bf16"])
-def test_layer_auto_per_expert_mixed(wdt):
+@pytest.mark.parametrize("wdt,T,k", [("f16", 64, 4), ("bf16", 64, 4), ("f16", 160, 2)])
+def test_layer_auto_per_expert_mixed(wdt, T, k):
     """MOE_PATH_AUTO with dense weights chooses the path per expert in one call:
     under a Zipf-skewed router the hot experts (at least moe_auto_dense_min
     tokens) and the shared expert take the dense MFMA path, the others the
     sparse kernel.  The exported per-expert flags follow that rule from the
     call's counts, and y matches the oracle run with the same per-expert
     paths (the sparse experts fed the masks of a sparse-path call of the same
-    tokens, which the chunking makes identical)."""
-    T, E, S, k, d, f = 64, 16, 1, 4, 512, 256
+    tokens, which the chunking makes identical).  At 160 tokens the hot
+    experts hold more than one 64-row dense chunk."""
+    E, S, d, f = 16, 1, 512, 256
     experts, thr = build_host_layer(70, E, S, d, f, wdt, 0.7, 1.0, layer=d)
     R_bits = synth.to_bits(synth.router_f32(70, d, E, d), wdt)
     bias = synth.zipf_bias(71, d, E, 1.1)
@@ -267,6 +271,8 @@ def test_layer_auto_per_expert_mixed(wdt):
     fl = flags.cpu().numpy()
     assert np.array_equal(fl, (cnt >= nstar).astype(np.uint8)), (cnt, fl, nstar)
     assert fl.any() and not fl[cnt > 0].all(), f"not a mixed call: counts {cnt.tolist()} n*={nstar}"
+    if T > 64:
+        assert cnt.max() > 64, "no expert spans several 64-row dense chunks"
     # the sparse experts' masks, from a sparse-path call of the same tokens
     ys, tr = run_layer(L, x, moe.PATH_SPARSE)
     assert np.array_equal(tr["topk_idx"], idx_d.cpu().numpy())
@@ -275,7 +281,7 @@ def test_layer_auto_per_expert_mixed(wdt):
     us = np.stack([h.up_sz for h in experts])
     g = np.stack([h.gate for h in experts])
     dn = np.stack([h.down for h in experts])
-    tokens = np.array([0, 1, 17, 40, 63])
+    tokens = np.unique(np.array([0, 1, 17, 40, 63, T - 1, T // 2]) % T)
     y_ref, _, w_ref, _ = oracle.layer_forward(
         x_bits[tokens], wdt, R_bits, wdt, bias, E, k, S, True, uq, us, g, dn, wdt, thr,
         topk_in=tr["topk_idx"][tokens], masks_in=tr["masks"][tokens], dense_experts=dense_experts)
