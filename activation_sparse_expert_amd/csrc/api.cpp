@@ -209,13 +209,18 @@ void *scratch_for_current_device()
 // Split of f in the dense down product: enough workgroups (d / 256 column
 // tiles per chunk of tokens) for about two per compute unit, at most 4 (the
 // partial-row region holds 4 slices per row), each slice a multiple of 64.
-// Token rows per dense chunk and tile: 64 when the routed experts average at
-// most 32 tokens (two workgroups per compute unit; the weight stream bounds
-// these), else 256.  Near 64 tokens on average many experts would spill into
-// a second, nearly empty 64-row chunk that streams the weights again.
+// Token rows per dense chunk and tile, from the routed experts' average
+// token count: up to 32, 64 rows (two workgroups per compute unit); up to 96,
+// 128 rows (three stages, two blocks in flight); else 256.  The weight stream
+// and its latency bound the smaller cases.  Near 64 tokens on average many
+// experts would spill into a second, nearly empty 64-row chunk that streams
+// the weights again, hence the margins.
 int gemm_tile_rows(int T, int k, int E)
 {
-    return (long long)T * k <= (long long)(kGemmChunkSmall / 2) * E ? kGemmChunkSmall : kGemmChunk;
+    const long long tk = (long long)T * k;
+    if (tk <= 32ll * E) return 64;
+    if (tk <= 96ll * E) return 128;
+    return kGemmChunk;
 }
 
 int gemm_ksplit(int T, int k, int E, int S, int d, int f, int mt)

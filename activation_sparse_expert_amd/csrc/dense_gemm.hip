@@ -46,18 +46,35 @@ constexpr int kWNB = 16 / kWaves;               // B subtiles (32 columns) per w
 constexpr int kNT = 256;                        // tile columns (B rows)
 constexpr int kKB = 64;                         // k values per stage: 128-byte rows, whole lines
 constexpr int kSteps = kKB / 16;                // MFMA k steps per block
-constexpr int kStages = 2;
-// Tile rows (tokens): MT = 256, or MT = 64 for experts with few tokens each,
-// whose 40 KB stages let two workgroups share a compute unit (twice the
-// weight bytes in flight per CU for the weight-bound case).
+// Tile rows (tokens): MT = 256; MT = 128 with three stages (two blocks in
+// flight: experts averaging up to 96 tokens, where the weight stream and its
+// latency bound the kernel); MT = 64 for experts with few tokens each, whose
+// 40 KB stages let two workgroups share a compute unit.
 template <int MT>
 struct GT {
-    static constexpr int kStageBytes = (MT + kNT) * kKB * 2;            // 64 KB / 40 KB
-    static constexpr int kLds = kStages * kStageBytes;                  // 128 KB / 80 KB
+    static constexpr int kStages = MT == 128 ? 3 : 2;
+    static constexpr int kStageBytes = (MT + kNT) * kKB * 2;            // 64 / 48 / 40 KB
+    static constexpr int kLds = kStages * kStageBytes;                  // 128 / 144 / 80 KB
     static constexpr int kMaxCopies = kStageBytes / 1024 / kWaves;      // copy instructions per wave
     static constexpr int kRH = MT / 2;                                  // rows per wave row-half
     static constexpr int kSub = kRH / 32;                               // row subtiles per wave
 };
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0..7 (the copies this wave may
+// leave in flight; the immediate must be a constant)
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    }
+}
 
 template <bool BF16>
 __device__ __forceinline__ floatx16 mma(const uint4 &a, const uint4 &b, const floatx16 &c)
@@ -125,17 +142,19 @@ __device__ __forceinline__ uint16_t to16(float v)
 }
 
 // The k loop of one wave over its NSUB row subtiles (those holding tokens).
-// Two stages: block kb + 1 is copied into the stage that block kb - 1 used
-// while block kb is multiplied, and a barrier at the end of each block
-// publishes the next one.  Inside a block the fragments of k step s + 1 are
+// S stages: block kb + S - 1 is copied into the stage that block kb - 1 used
+// while block kb is multiplied; at the end of each block the wave waits for
+// its copies of block kb + 1 (leaving the later blocks' ncopy copies each in
+// flight) and a barrier publishes it.  Inside a block the fragments of k step s + 1 are
 // read from LDS while the MFMAs of step s run (sched_barrier keeps the
 // compiler from sinking the reads back next to their MFMAs); the other wave
 // of each SIMD covers the rest of the waiting.
 template <bool BF16, int MT, int NSUB, class ISSUE>
 __device__ __forceinline__ void kloop(floatx16 (&acc)[GT<MT>::kSub][kWNB], const unsigned char *smem, int nkb,
                                       int arow0, const int (&brow)[kWNB], int li, int hk,
-                                      ISSUE &issue)
+                                      ISSUE &issue, int ncopy)
 {
+    constexpr int S = GT<MT>::kStages;
     constexpr int NA = NSUB > 0 ? NSUB : 1;
     uint4 a0[NA], b0[kWNB], a1[NA], b1[kWNB];
     auto load = [&](const unsigned char *st, int step, uint4 (&af)[NA], uint4 (&bf)[kWNB]) {
@@ -155,12 +174,16 @@ __device__ __forceinline__ void kloop(floatx16 (&acc)[GT<MT>::kSub][kWNB], const
                 for (int j = 0; j < kWNB; ++j) acc[i][j] = mma<BF16>(af[i], bf[j], acc[i][j]);
         }
     };
-    // block 0 was issued by the caller
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // blocks 0 .. S - 2 are issued here; block 0 must land first
+#pragma unroll
+    for (int b = 0; b < S - 1; ++b)
+        if (b < nkb) issue(b);
+    if constexpr (S == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else wait_vm((nkb > S - 2 ? S - 2 : nkb - 1) * ncopy);
     __syncthreads();
     for (int kb = 0; kb < nkb; ++kb) {
-        if (kb + 1 < nkb) issue(kb + 1);            // the stage block kb - 1 used
-        const unsigned char *st = smem + (size_t)(kb & 1) * GT<MT>::kStageBytes;
+        if (kb + S - 1 < nkb) issue(kb + S - 1);    // the stage block kb - 1 used
+        const unsigned char *st = smem + (size_t)(kb % S) * GT<MT>::kStageBytes;
         load(st, 0, a0, b0);
 #pragma unroll
         for (int s2 = 0; s2 < kSteps; s2 += 2) {
@@ -173,13 +196,19 @@ __device__ __forceinline__ void kloop(floatx16 (&acc)[GT<MT>::kSub][kWNB], const
             mmas(a1, b1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
+        if constexpr (S == 2) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb + 1 has landed
+        } else {
+            // blocks issued after kb + 1 may stay in flight
+            const int later = (nkb - 1 < kb + S - 1 ? nkb - 1 : kb + S - 1) - (kb + 1);
+            wait_vm((later > 0 ? later : 0) * ncopy);
+        }
         __syncthreads();
     }
 }
 
-// MODE 0: gate/up, MODE 1: down.  MT: tile rows (256, or 64 with two
-// workgroups per compute unit).
+// MODE 0: gate/up, MODE 1: down.  MT: tile rows (256; 128 with three
+// stages; 64 with two workgroups per compute unit).
 template <bool BF16, int MODE, int MT>
 __global__ void __launch_bounds__(kGThreads, MT == 64 ? 2 : 1)
 gemm_kernel(GemmArgs a)
@@ -259,7 +288,7 @@ gemm_kernel(GemmArgs a)
         src[q] = rp + k_beg + 8 * c;
     }
     auto issue = [&](int kb) {
-        unsigned char *base = smem + (size_t)(kb & 1) * G::kStageBytes;
+        unsigned char *base = smem + (size_t)(kb % G::kStages) * G::kStageBytes;
 #pragma unroll
         for (int q = 0; q < G::kMaxCopies; ++q)
             if (q < ncopy) copy16_to_lds(src[q] + (size_t)kb * kKB, base + dst[q]);
@@ -288,18 +317,21 @@ gemm_kernel(GemmArgs a)
     }
     const int li = lane & 31, hk = lane >> 5;
 
-    issue(0);
     if constexpr (G::kSub == 4) {
         switch (nsub) {
-        case 4: kloop<BF16, MT, 4>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
-        case 3: kloop<BF16, MT, 3>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
-        case 2: kloop<BF16, MT, 2>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
-        case 1: kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
-        default: kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue); break;
+        case 4: kloop<BF16, MT, 4>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy); break;
+        case 3: kloop<BF16, MT, 3>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy); break;
+        case 2: kloop<BF16, MT, 2>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy); break;
+        case 1: kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy); break;
+        default: kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy); break;
         }
+    } else if constexpr (G::kSub == 2) {
+        if (nsub == 2) kloop<BF16, MT, 2>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy);
+        else if (nsub == 1) kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy);
+        else kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy);
     } else {
-        if (nsub == 1) kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue);
-        else kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue);
+        if (nsub == 1) kloop<BF16, MT, 1>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy);
+        else kloop<BF16, MT, 0>(acc, smem, nkb, G::kRH * wm, brow, li, hk, issue, ncopy);
     }
 
     // ---- epilogue --------------------------------------------------------
@@ -420,9 +452,10 @@ hipError_t launch_gemm_mt(const GemmArgs &a, hipStream_t s)
 hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s)
 {
     if (a.d % kNT != 0 || a.f % 128 != 0 || a.d % kKB != 0 ||
-        a.f % (kKB * a.ksplit) != 0 || a.ksplit < 1 || (a.mt != 64 && a.mt != 256))
+        a.f % (kKB * a.ksplit) != 0 || a.ksplit < 1 || (a.mt != 64 && a.mt != 128 && a.mt != 256))
         return hipErrorInvalidValue;
     if (a.mt == 64) return a.bf16 ? launch_gemm_mt<true, 64>(a, s) : launch_gemm_mt<false, 64>(a, s);
+    if (a.mt == 128) return a.bf16 ? launch_gemm_mt<true, 128>(a, s) : launch_gemm_mt<false, 128>(a, s);
     return a.bf16 ? launch_gemm_mt<true, 256>(a, s) : launch_gemm_mt<false, 256>(a, s);
 }
 

@@ -155,8 +155,7 @@ struct GemmArgs {
     int grid_chunks;                    // chunk slots in the grid (an upper bound)
     int mt;                             // token rows per chunk and tile: 256 or 64
 };
-constexpr int kGemmChunk = 256;         // token rows per chunk
-constexpr int kGemmChunkSmall = 64;     // ... when the experts average at most 32 tokens
+constexpr int kGemmChunk = 256;         // token rows per chunk (64 or 128 for experts with fewer tokens)
 int gemm_grid_chunks(int T, int k, int E, int S, int mt);
 hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s);
 // out [mats][cols][rows] = in [mats][rows][cols], 16-bit elements

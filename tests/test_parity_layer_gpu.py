@@ -176,6 +176,8 @@ def test_small_layer_dense(T, E, S, k, d, f):
     (64, 8, 0, 2, 2048, 1024, "bf16"),   # split of f in the down product
     (120, 8, 1, 2, 512, 256, "f16"),     # 64-row tiles (30 tokens per expert on average):
                                          # the shared expert's 120 tokens in two chunks
+    (300, 8, 1, 2, 1024, 512, "bf16"),   # 128-row tiles, three stages (75 per expert on
+                                         # average); the shared expert in three chunks
 ])
 def test_small_layer_dense_gemm(T, E, S, k, d, f, wdt):
     """The MFMA GEMM (bf16 and fp16 layers; 256-row tiles, or 64-row tiles
