@@ -58,14 +58,52 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Strides 32 and 16 exchange whole halves (rows) of the wave: gfx950's
+// v_permlane32_swap / v_permlane16_swap move lane l's `hi` to its partner
+// and bring the partner's `lo` back, so one swap and one add replace two
+// selects and a cross-lane LDS permute.  Lanes with bit S clear get
+// lo(own) + lo(partner), the others hi(partner) + hi(own): the same sums as
+// the permute form (addition commutes exactly).
+template <int S>
+__device__ __forceinline__ float swap_add(float lo, float hi)
+{
+    static_assert(S == 32 || S == 16, "row swaps");
+    const uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+    if constexpr (S == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
+// The value of lane l ^ S for S < 16: a DPP quad permute for 1 and 2, an
+// LDS swizzle in xor mode (no address register) for 4 and 8.
+template <int S>
+__device__ __forceinline__ float xor_lane(float x)
+{
+    const int xi = __float_as_int(x);
+    if constexpr (S == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false));
+    else if constexpr (S == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false));
+    else return __int_as_float(__builtin_amdgcn_ds_swizzle(xi, (S << 10) | 0x1F));
+}
+
+// v + the value of lane l ^ S (every lane gets the pair's sum)
+template <int S>
+__device__ __forceinline__ float bfly_add(float v)
+{
+    if constexpr (S >= 16) return swap_add<S>(v, v);
+    else return v + xor_lane<S>(v);
+}
+
 // Sum over aligned groups of SEG lanes (SEG a power of two <= 64); every lane
 // of the group receives the total.  Fixed butterfly order: bit-reproducible.
-template <int SEG>
+template <int SEG, int S = SEG / 2>
 __device__ __forceinline__ float seg_sum(float v)
 {
-#pragma unroll
-    for (int off = SEG / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    if constexpr (S == 0) return v;
+    else return seg_sum<SEG, S / 2>(bfly_add<S>(v));
 }
 
 __device__ __forceinline__ float silu(float g)

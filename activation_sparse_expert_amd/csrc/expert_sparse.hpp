@@ -171,6 +171,15 @@ __device__ __forceinline__ float treduce_step(float (&v)[P], int lane)
 {
     if constexpr (S == 0) {
         return v[0];
+    } else if constexpr (S >= 16) {
+        if constexpr (N > 1) {
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) v[i] = swap_add<S>(v[i], v[i + N / 2]);
+            return treduce_step<P, S / 2, N / 2>(v, lane);
+        } else {
+            v[0] = swap_add<S>(v[0], v[0]);
+            return treduce_step<P, S / 2, 1>(v, lane);
+        }
     } else {
         const bool hi = (lane & S) != 0;
         if constexpr (N > 1) {
@@ -178,11 +187,11 @@ __device__ __forceinline__ float treduce_step(float (&v)[P], int lane)
             for (int i = 0; i < N / 2; ++i) {
                 const float send = hi ? v[i] : v[i + N / 2];
                 const float keep = hi ? v[i + N / 2] : v[i];
-                v[i] = keep + __shfl_xor(send, S, 64);
+                v[i] = keep + xor_lane<S>(send);
             }
             return treduce_step<P, S / 2, N / 2>(v, lane);
         } else {
-            v[0] += __shfl_xor(v[0], S, 64);
+            v[0] += xor_lane<S>(v[0]);
             return treduce_step<P, S / 2, 1>(v, lane);
         }
     }

@@ -110,13 +110,11 @@ reduce_kernel(ReduceArgs a)
     }
     // groups of one wave by butterfly (lanes with the same column slot), then
     // the waves in order through LDS: a fixed order
-#pragma unroll
-    for (int off = kSeg; off < 64; off <<= 1) {
-        s.x += __shfl_xor(s.x, off, 64);
-        s.y += __shfl_xor(s.y, off, 64);
-        s.z += __shfl_xor(s.z, off, 64);
-        s.w += __shfl_xor(s.w, off, 64);
-    }
+    static_assert(kSeg == 8, "butterfly strides 8, 16, 32");
+    s.x = bfly_add<32>(bfly_add<16>(bfly_add<8>(s.x)));
+    s.y = bfly_add<32>(bfly_add<16>(bfly_add<8>(s.y)));
+    s.z = bfly_add<32>(bfly_add<16>(bfly_add<8>(s.z)));
+    s.w = bfly_add<32>(bfly_add<16>(bfly_add<8>(s.w)));
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) < kSeg) sm[wave][cq] = s;
     __syncthreads();
