@@ -439,12 +439,14 @@ __device__ __forceinline__ float group_xq_bits_bf16(const CodeUnit<BITS> &c, con
 // Gate/down row chunk of phase C.  A single-token chunk reads each active row
 // once, so the rows are streamed (nontemporal); chunks of several tokens keep
 // ordinary loads, because other chunks of the same expert read the same rows
-// and find them in cache.
-template <int TB>
-__device__ __forceinline__ uint4 row_load(const uint16_t *p)
+// and find them in cache (and load from a buffer over the tile's rows, where
+// an offset of kOob reads zeros without a memory access).
+__device__ __forceinline__ uint4 row_load_nt(const uint16_t *p) { return load_nt16(p); }
+__device__ __forceinline__ uint4 row_bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    if constexpr (TB == 1) return load_nt16(p);
-    else return *(const uint4 *)p;
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // passes of channels per phase-A block (host and device).  A single-token
@@ -935,18 +937,35 @@ expert_kernel(SparseArgs a)
             }
             return h;
         };
-        // loads of the batch of rows starting at list entry B0 (none past the list)
+        // loads of the batch of rows starting at list entry B0.  One token:
+        // none past the list (a uniform branch per row; its single batch in
+        // flight is waited for whole).  Several tokens: issued on every path,
+        // an entry past the list reading zeros with no memory access, so the
+        // count of loads in flight is the same on every path and the wait
+        // before a batch's use leaves the next batch's loads in flight.
+        const __amdgpu_buffer_rsrc_t rg = tile_rsrc(gate, (uint32_t)nrows * (uint32_t)d * 2u);
+        const __amdgpu_buffer_rsrc_t rdn = tile_rsrc(down, (uint32_t)nrows * (uint32_t)d * 2u);
+        uint32_t coff[NCH];                         // this thread's 16-byte piece of a row
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) coff[i] = (uint32_t)min(tid + THREADS * i, CPR - 1);
 #define C_LOAD(B0, GW, DW, ROWS)                                                               \
     _Pragma("unroll") for (int q = 0; q < RB; ++q) {                                           \
         const int ent = min((B0) + q, n_act - 1);                                              \
         ROWS[q] = (int)L.list[ent];                                                            \
+        const bool okq = (B0) + q < n_act;          /* uniform */                              \
         _Pragma("unroll") for (int i = 0; i < NCH; ++i) {                                      \
-            GW[q][i] = make_uint4(0, 0, 0, 0);                                                 \
-            DW[q][i] = make_uint4(0, 0, 0, 0);                                                 \
-            if ((B0) + q < n_act) {                 /* uniform: no loads past the list */      \
-                const int c = min(tid + THREADS * i, CPR - 1);                                 \
-                GW[q][i] = row_load<TB>(gate + (size_t)ROWS[q] * d + (size_t)c * 8);           \
-                DW[q][i] = row_load<TB>(down + (size_t)ROWS[q] * d + (size_t)c * 8);           \
+            if constexpr (TB == 1) {                                                           \
+                GW[q][i] = make_uint4(0, 0, 0, 0);                                             \
+                DW[q][i] = make_uint4(0, 0, 0, 0);                                             \
+                if (okq) {                                                                     \
+                    GW[q][i] = row_load_nt(gate + (size_t)ROWS[q] * d + (size_t)coff[i] * 8);  \
+                    DW[q][i] = row_load_nt(down + (size_t)ROWS[q] * d + (size_t)coff[i] * 8);  \
+                }                                                                              \
+            } else {                                                                           \
+                const uint32_t off =                                                           \
+                    okq ? ((uint32_t)ROWS[q] * (uint32_t)d + coff[i] * 8u) * 2u : kOob;        \
+                GW[q][i] = row_bload(rg, off);                                                 \
+                DW[q][i] = row_bload(rdn, off);                                                \
             }                                                                                  \
         }                                                                                      \
     }
@@ -1003,12 +1022,13 @@ expert_kernel(SparseArgs a)
             // is multiplied (sets a and b alternate)
             uint4 gb[RB][NCH], db[RB][NCH];
             int rowsb[RB];
+            // (a batch past the list issues loads that touch no memory)
             C_LOAD(0, gw, dw, rows)
             for (int b0 = 0; b0 < n_act; b0 += 2 * RB) {
-                if (b0 + RB < n_act) C_LOAD(b0 + RB, gb, db, rowsb)
+                C_LOAD(b0 + RB, gb, db, rowsb)
                 C_COMPUTE(b0, gw, dw, rows)
                 if (b0 + RB >= n_act) break;
-                if (b0 + 2 * RB < n_act) C_LOAD(b0 + 2 * RB, gw, dw, rows)
+                C_LOAD(b0 + 2 * RB, gw, dw, rows)
                 C_COMPUTE(b0 + RB, gb, db, rowsb)
             }
         } else {
