@@ -263,10 +263,12 @@ gemm_kernel(GemmArgs a)
     const int ncopy = (ninst - wave + kWaves - 1) / kWaves;
     const uint16_t *src[G::kMaxCopies];
     int dst[G::kMaxCopies];
+    bool isw[G::kMaxCopies];                    // instruction copies weight rows (wave-uniform)
 #pragma unroll
     for (int q = 0; q < G::kMaxCopies; ++q) {
         const int inst = min(wave + kWaves * q, ninst - 1);
         const int base = inst < na ? 8 * inst : MT + 8 * (inst - na);
+        isw[q] = inst >= na;
         const int row = base + (lane >> 3);
         dst[q] = base * 128;
         const int pc = lane & 7;
@@ -291,7 +293,12 @@ gemm_kernel(GemmArgs a)
         unsigned char *base = smem + (size_t)(kb % G::kStages) * G::kStageBytes;
 #pragma unroll
         for (int q = 0; q < G::kMaxCopies; ++q)
-            if (q < ncopy) copy16_to_lds(src[q] + (size_t)kb * kKB, base + dst[q]);
+            if (q < ncopy) {
+                // weight rows are streamed (nontemporal); token rows are
+                // re-read by the other column tiles and stay cached
+                if (isw[q]) copy16_to_lds<true>(src[q] + (size_t)kb * kKB, base + dst[q]);
+                else copy16_to_lds(src[q] + (size_t)kb * kKB, base + dst[q]);
+            }
     };
 
     floatx16 acc[G::kSub][kWNB];

@@ -157,17 +157,25 @@ __device__ __forceinline__ float4 load_nt16f(const float *p)
 // wait-count pass does not treat the copy as a possible alias of every later
 // LDS access (it would drain vmcnt before each): the issuing wave waits for its
 // copies itself (vmcnt) before a barrier that publishes them.  m0 is saved and
-// restored.
+// restored.  NT: the nontemporal (streaming) cache policy, for data read once.
+template <bool NT = false>
 __device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_base)
 {
     typedef __attribute__((address_space(3))) void lvoid;
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lvoid *)lds_base);
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(src), "s"(m)
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(src), "s"(m)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(src), "s"(m)
+                     : "memory");
 }
 
 // Store one fp32 result into an output of type dt (0 f16, 1 bf16, 2 f32),
