@@ -31,6 +31,12 @@ both kernels, each scaled by what the same counter reads for an elementwise
 kernel of known size, ``--copy-probe``); it is read from the committed
 counter summary and reported only while the kernel sources it was taken on
 are unchanged (their SHA-256 is recorded there), else null.
+
+``cpu_baseline`` is the fp64 oracle on the host cores (one thread, then N
+threads of independent calls) on the headline workload; ``cpu_baseline.more``
+times it the same way on the fine-grained layer and on one layer of the
+32-layer stack (host copies of the device-built layers; the decode step of
+the stack is extrapolated from that layer), and on the small d=256 expert.
 """
 from __future__ import annotations
 
@@ -370,7 +376,81 @@ def layer_workload(layers, xs_by_layer, label, path=None):
     return out
 
 
-def layers_measure(fine_only=False, stack_only=False):
+# oracle timings of the layer workloads, filled by layers_measure(cpu=True)
+ORACLE_LAYERS = {}
+
+
+def oracle_layer_rate(L, x_bits, budget_s, label, per_step_layers=1):
+    """The fp64 oracle's layer_forward, as it stands, on a host copy of the
+    device layer L (same weights, codes, thresholds and router): single-token
+    calls over the tokens x_bits (uint16 [n][d]) on one host thread, then on N
+    threads with independent calls (the oracle's C code runs outside the GIL),
+    each leg about budget_s / 2 and at least one call per thread.  A decode
+    step of per_step_layers such layers is extrapolated from the per-layer
+    time (labelled as such)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    h = lambda t: t.detach().cpu().numpy()
+    wdt = "bf16" if L.gate_t.dtype == __import__("torch").bfloat16 else "f16"
+    up_q, up_sz = h(L.up_q), h(L.up_sz).view(np.uint16)
+    g, dn = h(L.gate_t).view(np.uint16), h(L.down).view(np.uint16)
+    rw = h(L.router_w).view(np.uint16)
+    bias = None if L.router_bias is None else h(L.router_bias).astype(np.float32)
+    thr = h(L.thresholds).astype(np.float32)
+
+    def worker(first, leg_s):
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < leg_s:
+            t = (first + n) % len(x_bits)
+            oracle.layer_forward(x_bits[t:t + 1], wdt, rw, wdt, bias, L.E, L.k, L.S, L.renormalize,
+                                 up_q, up_sz, g, dn, wdt, thr)
+            n += 1
+        return n, time.perf_counter() - t0
+
+    n1, el1 = worker(0, budget_s / 2)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(lambda i: worker(i, budget_s / 2), range(threads)))
+    eln = time.perf_counter() - t0
+    nn = sum(r[0] for r in res)
+    r = {"workload": label, "unit": "tokens/s", "kind": "oracle",
+         "value": nn / eln / per_step_layers, "cores": threads,
+         "single_thread": n1 / el1 / per_step_layers,
+         "sample": f"{n1} single-token layer calls on one thread in {el1:.1f} s, {nn} on "
+                   f"{threads} threads in {eln:.1f} s"}
+    if per_step_layers > 1:
+        r["extrapolated"] = (f"one of the {per_step_layers} layers timed; tokens/s of a decode "
+                             f"step = layer calls/s / {per_step_layers}")
+    return r
+
+
+def oracle_tiny_rate(budget_s):
+    """The oracle's expert_forward on the small d=256, f=704 expert (host-drawn,
+    50% threshold from its 64 calibration vectors), single tokens, one thread."""
+    import oracle
+    import synth
+    cfg = synth.CFG_TINY
+    c = synth.CONFIGS[cfg]
+    d, f = c["d"], c["f"]
+    g, u, dn = synth.expert_weights_f32(cfg, 0, 0, d, f)
+    q, sz = oracle.pack_up_int2(u)
+    W = oracle.dequant_up(q, sz, d)
+    xc = synth.to_f16_bits(synth.calibration_f32(cfg, d, c["x_scale"], 0, 0))
+    thr = oracle.calibrate_threshold(np.abs(xc.view(np.float16).astype(np.float64) @ W.T), 0.5)
+    toks = synth.to_f16_bits(synth.tokens_f32(cfg, NTOK, d, c["x_scale"]))
+    gb, db = synth.to_f16_bits(g), synth.to_f16_bits(dn)
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.expert_forward(toks[n % NTOK:n % NTOK + 1], "f16", q, sz, gb, db, "f16", thr)
+        n += 1
+    el = time.perf_counter() - t0
+    return {"workload": f"one expert d={d} f={f}, 50% threshold, batch 1", "unit": "tokens/s",
+            "kind": "oracle", "value": n / el, "cores": 1,
+            "sample": f"{n} single-token calls on one thread in {el:.1f} s"}
+
+
+def layers_measure(fine_only=False, stack_only=False, cpu=False):
     """The 32-layer Mixtral stack (T = 1, 16) and the fine-grained 64+2 layer
     (T = 1, 64), each as tokens/s of a decode step, router included; the fine
     layer again with dense copies under MOE_PATH_AUTO (T = 64, 256)."""
@@ -380,7 +460,7 @@ def layers_measure(fine_only=False, stack_only=False):
     dev = torch.device("cuda:0")
     out = {}
     if stack_only:
-        return stack_measure(out)
+        return stack_measure(out, cpu)
     c = synth.CONFIGS[synth.CFG_FINE]
     bias = synth.zipf_bias(synth.CFG_FINE, 0, c["E"], c["zipf_s"])
     fine = device_layer(synth.CFG_FINE, 0, c["E"], c["S"], c["k"], c["d"], c["f"], c["wdt"],
@@ -390,6 +470,12 @@ def layers_measure(fine_only=False, stack_only=False):
         out[f"fine_T{T}"] = layer_workload(
             [fine], [x], f"DeepSeek-V2-Lite-shaped layer, 64 routed (top-6) + 2 shared experts, "
                          f"d=2048 f=1408, Zipf router bias, 70% sparsity, {T} tokens")
+    if cpu:
+        log("timing the oracle on the fine-grained layer")
+        xb = synth.to_f16_bits(synth.tokens_f32(synth.CFG_FINE, NTOK, c["d"], c["x_scale"]))
+        ORACLE_LAYERS["fine_T1"] = oracle_layer_rate(
+            fine, xb, 6.0, "the fine-grained layer (64 routed top-6 + 2 shared, d=2048 f=1408, "
+                           "70% sparsity), 1 token per call, router included")
     # the same layer with dense fp16 copies (up materialised, W^down transposed)
     # under MOE_PATH_AUTO: experts with at least n* tokens take the MFMA path
     n = c["E"] + c["S"]
@@ -412,10 +498,10 @@ def layers_measure(fine_only=False, stack_only=False):
     torch.cuda.empty_cache()
     if fine_only:
         return out
-    return stack_measure(out)
+    return stack_measure(out, cpu)
 
 
-def stack_measure(out):
+def stack_measure(out, cpu=False):
     """The 32-layer Mixtral stack, T = 1 and 16, into `out`."""
     import torch
     import synth
@@ -430,6 +516,13 @@ def stack_measure(out):
         out[f"stack_T{T}"] = layer_workload(
             stack, xl, f"32 Mixtral-8x7B-shaped layers x 8 experts (d=4096 f=14336), top-2, "
                        f"80% sparsity, {T} tokens per decode step through all layers")
+    if cpu:
+        log("timing the oracle on layer 0 of the stack")
+        xs0 = synth.hidden_stream_f32(synth.CFG_STACK, 1, NTOK, c["d"], c["x_scale"])[0]
+        ORACLE_LAYERS["stack_T1"] = oracle_layer_rate(
+            stack[0], synth.to_f16_bits(xs0), 8.0,
+            "decode step through the 32-layer Mixtral-shaped stack (8 experts per layer, top-2, "
+            "80% sparsity), 1 token", per_step_layers=c["L"])
     del stack
     torch.cuda.empty_cache()
     return out
@@ -771,7 +864,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_layers:
         log("measuring the layer workloads")
-        out["more"].update(layers_measure())
+        out["more"].update(layers_measure(cpu=not args.no_cpu))
         log("measuring the 8/4/1-bit up variants")
         out["more"]["expert_up_bits"] = bits_measure()
         log("measuring the EAMC match")
@@ -782,6 +875,9 @@ def main():
     if not args.no_cpu:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(args.sparsity, args.cpu_budget)
+        more = dict(ORACLE_LAYERS)
+        more["tiny_T1"] = oracle_tiny_rate(2.0)
+        out["cpu_baseline"]["more"] = more
     print(json.dumps(out), flush=True)
 
 
