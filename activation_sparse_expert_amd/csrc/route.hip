@@ -239,14 +239,27 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
     const int E = a.E;
     int *cnt = (int *)smem;                          // [E] counts
     int *run = cnt + E;                              // [E] running placement base
-    int *ce = run + E;                               // [kRouteThreads] experts of a batch of pairs
-    int *cst = ce + kRouteThreads;                   // [E+1] first chunk of each expert
+    int *cst = run + E;                              // [E+1] first chunk of each expert
     int *cst2 = cst + E + 1;                         // [E+1] first dense chunk of each expert
+    // [E][kRouteWaves] lanes of each wave whose pair of the batch chose expert e
+    unsigned long long *msk = (unsigned long long *)(cnt + ((4 * E + 2 + 1) & ~1));
     const int P = a.T * a.k;
+    // the experts of this thread's first kHeld pairs (p = tid + kRouteThreads i)
+    // are loaded once, all in flight together, and kept for the placement
+    constexpr int kHeld = 8;
+    int held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+        const int p = tid + kRouteThreads * i;
+        held[i] = p >= P ? -1 : reg ? (i == 0 ? my_e : -1) : load_coherent_i32(a.topk_idx + p);
+    }
     for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += kRouteThreads)
-        atomicAdd(&cnt[reg ? my_e : load_coherent_i32(a.topk_idx + p)], 1);
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i)
+        if (held[i] >= 0) atomicAdd(&cnt[held[i]], 1);
+    for (int p = tid + kRouteThreads * kHeld; p < P; p += kRouteThreads)
+        atomicAdd(&cnt[load_coherent_i32(a.topk_idx + p)], 1);
     __syncthreads();
     // one exclusive scan over the experts gives, packed in 64 bits, the pair
     // offset (bits 0-23), the first chunk (24-47) and the position in the
@@ -306,15 +319,29 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
     if (a.chunk > 0) write_chunks(cst, run, E, a.chunk, a.chunk_tab);
     if (a.dense_min > 0) write_chunks(cst2, run, E, a.dense_chunk, a.chunk_tab2);
     __syncthreads();
-    // stable placement, one chunk of pairs at a time
-    for (int b = 0; b < P; b += kRouteThreads) {
+    // stable placement, one chunk of pairs at a time: a pair's rank among the
+    // chunk's earlier pairs of its expert is the count of set bits below it in
+    // that expert's lane masks (its own wave's, then the earlier waves')
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int b = 0, bi = 0; b < P; b += kRouteThreads, ++bi) {
         const int p = b + tid;
-        const int e = p < P ? (reg ? my_e : load_coherent_i32(a.topk_idx + p)) : -1;
-        ce[tid] = e;
+        int e = -1;                                  // expert of pair p (held, else loaded)
+        if (p < P) {
+            if (bi < kHeld) {
+                e = held[0];
+#pragma unroll
+                for (int j = 1; j < kHeld; ++j) e = bi == j ? held[j] : e;
+            } else {
+                e = load_coherent_i32(a.topk_idx + p);
+            }
+        }
+        for (int i = tid; i < E * kRouteWaves; i += kRouteThreads) msk[i] = 0ull;
+        __syncthreads();
+        if (e >= 0) atomicOr(&msk[e * kRouteWaves + wave], 1ull << lane);
         __syncthreads();
         if (e >= 0) {
-            int rank = 0;
-            for (int q = 0; q < tid; ++q) rank += (ce[q] == e);
+            int rank = __popcll(msk[e * kRouteWaves + wave] & ((1ull << lane) - 1ull));
+            for (int w = 0; w < wave; ++w) rank += __popcll(msk[e * kRouteWaves + w]);
             const int pos = run[e] + rank;
             a.pairs[pos] = p;
             if (a.chunk_rec) {
@@ -325,7 +352,12 @@ __device__ void group_pairs(const RouteArgs &a, unsigned char *smem, bool reg, i
             }
         }
         __syncthreads();
-        if (e >= 0) atomicAdd(&run[e], 1);          // the batch's pairs of e follow these
+        for (int ee = tid; ee < E; ee += kRouteThreads) {   // the batch's pairs of ee follow these
+            int c = 0;
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) c += __popcll(msk[ee * kRouteWaves + w]);
+            run[ee] += c;
+        }
         __syncthreads();
     }
 }
@@ -449,7 +481,9 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     size_t lds = (size_t)a.d * 4 + (size_t)a.E * 8 + (size_t)a.k * 8 + 32;
-    const size_t lds_group = (size_t)a.E * 16 + kRouteThreads * 4 + 48;
+    // counts, bases and chunk starts (4 E + 2 ints), then the lane masks
+    // ([E][8] u64)
+    const size_t lds_group = (size_t)a.E * 16 + 16 + (size_t)a.E * kRouteWaves * 8 + 64;
     if (lds_group > lds) lds = lds_group;
     // 16-byte units per lane of one router row (64 lanes): CB (<= 8) of them per
     // expert and round, GE = 16 / CB experts per wave at a time
@@ -468,6 +502,11 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s)
     hipError_t e = hipLaunchKernel(kern, dim3(a.T), dim3(kRouteThreads), args, lds, s);
     if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess || !a.count || a.T == 1) return e;
+    if (lds_group > 64 * 1024) {
+        e = hipFuncSetAttribute((const void *)group_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds_group);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kRouteThreads), lds_group, s, a);
     return hipGetLastError();
 }
