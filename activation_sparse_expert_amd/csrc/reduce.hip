@@ -137,7 +137,9 @@ reduce_kernel(ReduceArgs a)
 // adds that token's contributions in order, all of them in flight at once.
 constexpr int kRowThreads = 256;
 constexpr int kRowCols = 4 * kRowThreads;   // columns per workgroup
-constexpr int kRowMax = 64;                 // contributions handled this way
+constexpr int kRowMax = 64;                 // contributions handled this way ...
+constexpr int kRowFew = 16;                 // ... always up to this many, else only
+constexpr int kRowMinBlocks = 256;          // when the grid still has this many workgroups
 constexpr int kRowBatch = 16;
 
 __global__ void __launch_bounds__(kRowThreads)
@@ -185,8 +187,13 @@ hipError_t launch_reduce(const ReduceArgs &a, hipStream_t s)
 {
     if (a.d % kCols != 0 || a.rows_per_tok > kMaxRowsPerTok) return hipErrorInvalidValue;
     const int most = a.mix && a.tiles_dense > a.tiles ? a.tiles_dense : a.tiles;
-    if (a.rows_per_tok * most <= kRowMax) {
-        const int cblocks = (a.d + kRowCols - 1) / kRowCols;
+    // few contributions: a thread per 4 columns adds them all; more of them
+    // over few tokens (a grid of T * d / 1024 workgroups would leave most of
+    // the chip idle while each thread loads them in sequence): the 32-column
+    // kernel, whose thread groups hold a token's contributions in flight at once
+    const int cblocks = (a.d + kRowCols - 1) / kRowCols;
+    const int contrib = a.rows_per_tok * most;
+    if (contrib <= kRowMax && (contrib <= kRowFew || (long long)a.T * cblocks >= kRowMinBlocks)) {
         hipLaunchKernelGGL(reduce_rows_kernel, dim3(a.T * cblocks), dim3(kRowThreads), 0, s, a);
     } else {
         if (a.layer)
