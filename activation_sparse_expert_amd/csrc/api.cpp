@@ -27,10 +27,11 @@ bool valid_out(moe_dtype t) { return t == MOE_F16 || t == MOE_BF16 || t == MOE_F
 
 // Hidden sizes the kernels are built for: powers of two up to 2048, or
 // multiples of 512 from 4096 to 16384.
+// Hidden sizes of the INT2 sparse path: whole groups of 64 inputs, up to the
+// widest kernel geometry (256 groups).
 bool supported_d(int d)
 {
-    if (d == 64 || d == 128 || d == 256 || d == 512 || d == 1024 || d == 2048) return true;
-    return d >= 4096 && d <= 16384 && d % 512 == 0;
+    return d >= 64 && d <= 16384 && d % 64 == 0;
 }
 
 int pow2ceil(int v)

@@ -246,7 +246,8 @@ __host__ __device__ inline size_t lds_layout(int d, int cpw, int tb, int waves, 
 }
 
 // Compile-time geometry for a hidden size class.
-//   SEG     lanes sharing one channel in phase A (= d/64 when d <= 4096)
+//   SEG     lanes sharing one channel in phase A (the power of two >= d/64
+//           when d <= 4096; lanes past d/64 groups read zeros)
 //   NG      64-input groups per lane in phase A
 //   NCH     16-byte column chunks per thread in phase C
 //   THREADS workgroup size
@@ -1141,18 +1142,19 @@ hipError_t launch_dtype(const SparseArgs &a, int tb, hipStream_t s)
         default: return hipErrorInvalidValue;
         }
     } else {
-        switch (a.d) {
-        case 64: return launch_geo<BF16, Geo<1, 1, 1, 64>, 2>(a, tb, s);
-        case 128: return launch_geo<BF16, Geo<2, 1, 1, 64>, 2>(a, tb, s);
-        case 256: return launch_geo<BF16, Geo<4, 1, 1, 64>, 2>(a, tb, s);
-        case 512: return launch_geo<BF16, Geo<8, 1, 1, 64>, 2>(a, tb, s);
-        case 1024: return launch_geo<BF16, Geo<16, 1, 1, 128>, 2>(a, tb, s);
-        case 2048: return launch_geo<BF16, Geo<32, 1, 1, 256>, 2>(a, tb, s);
-        case 4096: return launch_geo<BF16, Geo<64, 1, 1, 512>, 2>(a, tb, s);
-        default: break;
-        }
-        if (a.d > 4096 && a.d <= 8192) return launch_geo<BF16, Geo<64, 2, 2, 512>, 2>(a, tb, s);
-        if (a.d > 8192 && a.d <= 16384) return launch_geo<BF16, Geo<64, 4, 4, 512>, 2>(a, tb, s);
+        // the smallest geometry whose SEG x NG groups and THREADS x NCH 16-byte
+        // chunks cover d (d % 64 == 0); lanes past the G = d / 64 groups read
+        // zeros, threads past the d / 8 chunks of a row hold none
+        if (a.d < 64 || a.d % 64 != 0) return hipErrorInvalidValue;
+        if (a.d <= 64) return launch_geo<BF16, Geo<1, 1, 1, 64>, 2>(a, tb, s);
+        if (a.d <= 128) return launch_geo<BF16, Geo<2, 1, 1, 64>, 2>(a, tb, s);
+        if (a.d <= 256) return launch_geo<BF16, Geo<4, 1, 1, 64>, 2>(a, tb, s);
+        if (a.d <= 512) return launch_geo<BF16, Geo<8, 1, 1, 64>, 2>(a, tb, s);
+        if (a.d <= 1024) return launch_geo<BF16, Geo<16, 1, 1, 128>, 2>(a, tb, s);
+        if (a.d <= 2048) return launch_geo<BF16, Geo<32, 1, 1, 256>, 2>(a, tb, s);
+        if (a.d <= 4096) return launch_geo<BF16, Geo<64, 1, 1, 512>, 2>(a, tb, s);
+        if (a.d <= 8192) return launch_geo<BF16, Geo<64, 2, 2, 512>, 2>(a, tb, s);
+        if (a.d <= 16384) return launch_geo<BF16, Geo<64, 4, 4, 512>, 2>(a, tb, s);
         return hipErrorInvalidValue;
     }
 }

@@ -36,7 +36,7 @@
  * a fixed per-expert stride in each of these four arrays.
  *
  * Constraints checked on the host before anything is enqueued:
- *   d a power of two from 64 to 2048, or a multiple of 512 from 4096 to 16384;
+ *   d a multiple of 64 from 64 to 16384;
  *   f % 64 == 0;  T >= 1;
  *   activations and gate/down weights have the same 16-bit type (fp16 or bf16);
  *   16-byte aligned up_q/gate_t/down/x and 4-byte aligned up_sz.

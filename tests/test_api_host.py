@@ -85,8 +85,9 @@ def _expert(view=None, d=4096, f=14336, wdt=0, x=FAKE, xdt=0, T=1, y=FAKE, ydt=2
     (dict(y=None), -1),
     (dict(T=0), -1),
     (dict(f=100), -1),                  # f % 64 != 0
-    (dict(d=4160), -2),                 # d unsupported
-    (dict(d=1536), -2),
+    (dict(d=4128), -2),                 # d unsupported: not whole groups of 64
+    (dict(d=16448), -2),                # wider than the widest geometry
+    (dict(d=1000), -2),
     (dict(wdt=2), -2),                  # weights must be 16-bit
     (dict(xdt=1), -2),                  # x type differs from weight type
     (dict(ydt=7), -2),

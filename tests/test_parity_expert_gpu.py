@@ -175,6 +175,10 @@ def test_mixtral_expert_infinite_threshold(mixtral):
     (2048, 1408, 9, "f16"), (6144, 256, 3, "bf16"), (4096, 320, 17, "f16"), (8192, 128, 2, "bf16"),
     # the widest geometry (4 groups of 64 inputs per lane): d in (8192, 16384]
     (12288, 128, 1, "f16"), (16384, 64, 2, "bf16"), (9216, 192, 3, "f16"),
+    # hidden sizes between the geometries' widths: lanes past d/64 groups and
+    # threads past d/8 row chunks idle (a multiple of 64 throughout)
+    (320, 128, 1, "bf16"), (768, 256, 3, "f16"), (1536, 192, 1, "f16"), (2560, 64, 4, "bf16"),
+    (3584, 128, 2, "f16"), (3584, 64, 1, "bf16"), (4160, 64, 1, "f16"), (14336, 64, 1, "bf16"),
 ])
 def test_expert_shapes(d, f, T, wdt):
     hx = HostExpert(90, d, T, d, f, wdt=wdt)

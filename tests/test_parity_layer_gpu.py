@@ -132,7 +132,8 @@ def oracle_layer_check(experts, thr, R_bits, rdt, bias, E, S, k, x_bits, y, tr, 
 
 
 @pytest.mark.parametrize("T,E,S,k,d,f", [(5, 6, 2, 2, 512, 256), (1, 8, 0, 2, 1024, 512),
-                                         (12, 4, 1, 4, 2048, 320)])
+                                         (12, 4, 1, 4, 2048, 320), (1, 6, 1, 2, 1536, 192),
+                                         (7, 4, 0, 2, 3584, 128)])
 def test_small_layer_sparse(T, E, S, k, d, f):
     experts, thr = build_host_layer(60, E, S, d, f, "f16", 0.7, 1.0, layer=d)
     R_bits = synth.to_f16_bits(synth.router_f32(60, d, E, d))
