@@ -421,7 +421,7 @@ moe_status expert_forward(const moe_expert_view *e, int bits, int d, int f, moe_
     if (!e || !x || !y) return MOE_ERR_INVALID_ARG;
     moe_status st = check_expert_shape(d, f, wdt, xdt, T, ydt);
     if (st != MOE_OK) return st;
-    if (bits != 2 && d != 512 && d != 1024 && d != 2048 && d != 4096) return MOE_ERR_UNSUPPORTED;
+    if (bits != 2 && (d < 512 || d > 4096 || d % 64 != 0)) return MOE_ERR_UNSUPPORTED;
     st = check_weight_ptrs(e->up_q, e->up_sz, e->gate_t, e->down);
     if (st != MOE_OK) return st;
     if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) ||

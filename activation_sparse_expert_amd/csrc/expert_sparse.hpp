@@ -1130,22 +1130,21 @@ hipError_t launch_geo(const SparseArgs &a, int tb, hipStream_t s)
 }
 
 // Geometry by hidden size: see Geo.  Other code widths: d = 512 ... 4096.
+// The smallest geometry whose SEG x NG groups and THREADS x NCH 16-byte
+// chunks cover d (d % 64 == 0); lanes past the G = d / 64 groups read zeros,
+// threads past the d / 8 chunks of a row hold none.
 template <bool BF16, int BITS = 2>
 hipError_t launch_dtype(const SparseArgs &a, int tb, hipStream_t s)
 {
+    if (a.d < 64 || a.d % 64 != 0) return hipErrorInvalidValue;
     if constexpr (BITS != 2) {
-        switch (a.d) {
-        case 512: return launch_geo<BF16, Geo<8, 1, 1, 64>, BITS>(a, tb, s);
-        case 1024: return launch_geo<BF16, Geo<16, 1, 1, 128>, BITS>(a, tb, s);
-        case 2048: return launch_geo<BF16, Geo<32, 1, 1, 256>, BITS>(a, tb, s);
-        case 4096: return launch_geo<BF16, Geo<64, 1, 1, 512>, BITS>(a, tb, s);
-        default: return hipErrorInvalidValue;
-        }
+        if (a.d < 512) return hipErrorInvalidValue;
+        if (a.d <= 512) return launch_geo<BF16, Geo<8, 1, 1, 64>, BITS>(a, tb, s);
+        if (a.d <= 1024) return launch_geo<BF16, Geo<16, 1, 1, 128>, BITS>(a, tb, s);
+        if (a.d <= 2048) return launch_geo<BF16, Geo<32, 1, 1, 256>, BITS>(a, tb, s);
+        if (a.d <= 4096) return launch_geo<BF16, Geo<64, 1, 1, 512>, BITS>(a, tb, s);
+        return hipErrorInvalidValue;
     } else {
-        // the smallest geometry whose SEG x NG groups and THREADS x NCH 16-byte
-        // chunks cover d (d % 64 == 0); lanes past the G = d / 64 groups read
-        // zeros, threads past the d / 8 chunks of a row hold none
-        if (a.d < 64 || a.d % 64 != 0) return hipErrorInvalidValue;
         if (a.d <= 64) return launch_geo<BF16, Geo<1, 1, 1, 64>, 2>(a, tb, s);
         if (a.d <= 128) return launch_geo<BF16, Geo<2, 1, 1, 64>, 2>(a, tb, s);
         if (a.d <= 256) return launch_geo<BF16, Geo<4, 1, 1, 64>, 2>(a, tb, s);

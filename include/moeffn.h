@@ -252,8 +252,8 @@ size_t moe_noalloc_scratch_bytes(void);
  * 2^bits - 1 levels (moe_pack_up_bits).  Other arguments, outputs and the
  * mask rule as moe_expert_forward_sparse; the output is bit-reproducible.
  * The same fused kernel runs every width (only the decode of the codes
- * differs).  Limits for 8, 4, 1 bits: d in {512, 1024, 2048, 4096} (else
- * MOE_ERR_UNSUPPORTED); T as for INT2.
+ * differs).  Limits for 8, 4, 1 bits: d a multiple of 64 from 512 to 4096
+ * (else MOE_ERR_UNSUPPORTED); T as for INT2.
  * Workspace: moe_workspace_size(MOE_OP_EXPERT_BITS, T, d, f) bytes (the INT2
  * call's workspace at the same sizes).
  */

@@ -274,7 +274,8 @@ def test_eamc_match_rejects(kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(bits=3), -1), (dict(bits=0), -1), (dict(d=6144), -2), (dict(d=8192), -2),
+    (dict(bits=3), -1), (dict(bits=0), -1), (dict(d=6144), -2), (dict(d=8192), -2), (dict(d=1000), -2),
+    (dict(d=448), -2),
     (dict(T=70000), -1), (dict(T=0), -1), (dict(d=256), -2), (dict(f=100), -1), (dict(x=None), -1),
     (dict(x=FAKE + 8), -3), (dict(ws=None), -4), (dict(ws_bytes=1024), -4), (dict(wdt=2), -2),
 ])

@@ -93,7 +93,9 @@ def test_pack_bits_matches_oracle_bit_exact(bits, d, f, wdt):
 @pytest.mark.parametrize("bits", [8, 4, 1])
 @pytest.mark.parametrize("d,f,T,wdt,sp", [(512, 320, 1, "f16", 0.9), (1024, 192, 3, "bf16", 0.7),
                                           (2048, 448, 8, "f16", 0.8), (4096, 256, 2, "bf16", 0.5),
-                                          (1024, 576, 13, "f16", 0.7), (2048, 128, 1, "bf16", 0.0)])
+                                          (1024, 576, 13, "f16", 0.7), (2048, 128, 1, "bf16", 0.0),
+                                          # between the geometries' widths
+                                          (768, 128, 2, "f16", 0.7), (3584, 128, 1, "bf16", 0.9)])
 def test_expert_bits_small(bits, d, f, T, wdt, sp):
     h = host_expert(30 + bits, d, f, bits, wdt)
     x_bits = synth.to_bits(synth.normal_f32(synth.seed_of(31, 0, bits, 4), (T, d), 1 / 16), wdt)
