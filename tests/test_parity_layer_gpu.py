@@ -32,6 +32,12 @@ def _gpu():
     (33, 512, 16, 4, False, "f32", False, 1.0),
     (5, 256, 7, 7, True, "f16", False, 1.0),
     (300, 1024, 128, 8, True, "f16", True, 1.0),
+    # grouping: more than 8 x 512 pairs (later chunks reload their experts);
+    # 1024 experts (the lane masks take the workgroup past 64 KB of LDS), also
+    # for a single token, grouped by its own workgroup
+    (700, 256, 128, 8, True, "f16", True, 1.0),
+    (20, 64, 1024, 4, True, "f16", False, 1.0),
+    (1, 64, 1024, 8, True, "bf16", False, 1.0),
 ])
 def test_router(T, d, E, k, renorm, xdt, zipf, xscale):
     xf = synth.tokens_f32(50, T, d, xscale, layer=E)
