@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOEFFN_LIB") or os.path.join(HERE, "libmoeffn.so")
 
 MOE_F16, MOE_BF16, MOE_F32 = 0, 1, 2
-PATH_SPARSE, PATH_DENSE, PATH_AUTO = 0, 1, 2
+PATH_SPARSE, PATH_DENSE, PATH_AUTO, PATH_MIXED = 0, 1, 2, 3
 OP_EXPERT, OP_ROUTE, OP_LAYER, OP_CALIBRATE, OP_EAMC, OP_EXPERT_BITS = 0, 1, 2, 3, 4, 5
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
@@ -28,7 +28,7 @@ EXPORTED = ["moe_route_topk", "moe_expert_forward_sparse", "moe_layer_forward",
             "moe_eamc_match", "moe_expert_forward_sparse_bits", "moe_pack_up_bits",
             "moe_build_sources_sha256", "moe_expert_forward_sparse_noalloc",
             "moe_noalloc_scratch_bytes", "moe_materialize_up", "moe_transpose_down",
-            "moe_auto_dense_min"]
+            "moe_auto_dense_min", "moe_mixed_dense_min"]
 
 
 class MoeError(RuntimeError):
@@ -99,6 +99,8 @@ def lib():
         L.moe_transpose_down.argtypes = [P, I, I, I, P, P]
         L.moe_auto_dense_min.restype = I
         L.moe_auto_dense_min.argtypes = [C.POINTER(LayerDesc), I]
+        L.moe_mixed_dense_min.restype = I
+        L.moe_mixed_dense_min.argtypes = [C.POINTER(LayerDesc), I]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [I]
         L.moe_calibrate_threshold.restype = I
@@ -281,7 +283,7 @@ class Layer:
     router_bias: Optional["torch.Tensor"] = None
     up_dense: Optional["torch.Tensor"] = None   # [E+S][f][d] in the weight type
     down_dense: Optional["torch.Tensor"] = None  # [E+S][d][f] W^down transposed
-    density: float = 0.0                         # expected active fraction (MOE_PATH_AUTO)
+    density: float = 0.0                         # expected active fraction (AUTO, MIXED)
 
     def desc(self) -> LayerDesc:
         return LayerDesc(self.d, self.f, self.E, self.S, self.k, int(bool(self.renormalize)),
@@ -294,10 +296,16 @@ class Layer:
         return workspace_size(OP_LAYER, T, self.d, self.f, self.E, self.k, self.S)
 
     def auto_dense_min(self, T: int) -> int:
-        """Token count from which MOE_PATH_AUTO sends an expert to the dense
-        path at T tokens (0: the call stays sparse)."""
+        """MOE_PATH_AUTO's choice at T tokens: 1 when the call takes the dense
+        path (every expert with tokens), 0 when it stays sparse."""
         desc = self.desc()
         return int(lib().moe_auto_dense_min(C.byref(desc), T))
+
+    def mixed_dense_min(self, T: int) -> int:
+        """Token count from which MOE_PATH_MIXED sends an expert to the dense
+        path at T tokens (0: the call stays sparse)."""
+        desc = self.desc()
+        return int(lib().moe_mixed_dense_min(C.byref(desc), T))
 
 
 def layer_forward(layer: Layer, x, *, path: int = PATH_SPARSE, y=None, out_dtype=None,

@@ -25,8 +25,6 @@ bool is16(moe_dtype t) { return t == MOE_F16 || t == MOE_BF16; }
 
 bool valid_out(moe_dtype t) { return t == MOE_F16 || t == MOE_BF16 || t == MOE_F32; }
 
-// Hidden sizes the kernels are built for: powers of two up to 2048, or
-// multiples of 512 from 4096 to 16384.
 // Hidden sizes of the INT2 sparse path: whole groups of 64 inputs, up to the
 // widest kernel geometry (256 groups).
 bool supported_d(int d)
@@ -234,19 +232,86 @@ int gemm_ksplit(int T, int k, int E, int S, int d, int f, int mt)
     return ks;
 }
 
-// MOE_PATH_AUTO's per-expert rule (classic roofline on bytes moved, MoE-
-// Lightning review, "层次化屋顶模型"): an expert with n tokens costs the sparse
-// path ceil(n / tb) chunks, each reading the INT2 codes and scales (5/16 d f
-// bytes) and the gate and down rows of the union of tb tokens' masks
-// (4 u d f bytes, u = 1 - (1 - density)^tb); the dense path reads the 16-bit
-// gate, up and down weights once (6 d f bytes).  The result is the smallest n
-// with ceil(n / tb) (5/16 + 4 u) > 6.
+// Cost model of MOE_PATH_AUTO and MOE_PATH_MIXED (MoE-Lightning review,
+// "层次化屋顶模型": time = bytes moved / attainable bandwidth, the expert FFN's
+// operational intensity growing with its tokens).  Bytes in units of d f:
+// the sparse path reads, per chunk of m <= tb tokens of one expert, the INT2
+// codes and scales (5/16) and the gate and down rows of the union of the m
+// masks (4 u, u = 1 - (1 - density)^m); the dense path reads the three 16-bit
+// matrices once (6).  The dense GEMM streams its weights at about twice the
+// rate at which the multi-token sparse kernel streams codes and rows (4-6
+// against 2-3 TB/s on MI355X), so dense wins when its bytes are under twice
+// the sparse bytes.
+constexpr double kDenseBytes = 6.0;
+constexpr double kDenseOverSparseRate = 2.0;
+
+struct PathCost {
+    int tb;                 // 1, 2 or 4
+    double ch[5];           // a chunk of m tokens
+    PathCost(int tb_, float density) : tb(tb_)
+    {
+        const double rho = density > 0.f && density <= 1.f ? (double)density : 0.5;
+        ch[0] = 0.0;
+        for (int m = 1; m <= 4; ++m) ch[m] = 0.3125 + 4.0 * (1.0 - std::pow(1.0 - rho, (double)m));
+    }
+    // one expert with n tokens on the sparse path
+    double sparse(long long n) const { return (double)(n / tb) * ch[tb] + ch[n % tb]; }
+    bool dense_wins(double dense_bytes, double sparse_bytes) const
+    {
+        return dense_bytes < kDenseOverSparseRate * sparse_bytes;
+    }
+};
+
+// MOE_PATH_MIXED, per expert: the smallest token count n whose sparse chunks
+// take longer than reading the dense weights once.
 int dense_min_tokens(int tb, float density)
 {
-    const double rho = density > 0.f && density <= 1.f ? (double)density : 0.5;
-    const double u = 1.0 - std::pow(1.0 - rho, (double)tb);
-    const double per_chunk = 0.3125 + 4.0 * u;
-    return tb * (int)std::floor(6.0 / per_chunk) + 1;
+    const PathCost c(tb, density);
+    int n = 1;
+    while (!c.dense_wins(kDenseBytes, c.sparse(n))) ++n;    // sparse(n) grows by >= 5/16 per chunk
+    return n;
+}
+
+// E[g(n)] for n ~ Binomial(T, p), 0 < p < 1: outward from the mode, where the
+// probability is at least about 1 / (2.5 sqrt(T p (1 - p)) + 1), until the
+// terms are negligible.
+template <class G>
+double binomial_mean(int T, double p, G g)
+{
+    const int n0 = (int)std::floor((T + 1) * p) > T ? T : (int)std::floor((T + 1) * p);
+    const double r = p / (1.0 - p);
+    const double p0 = std::exp(std::lgamma(T + 1.0) - std::lgamma(n0 + 1.0) - std::lgamma(T - n0 + 1.0) +
+                               n0 * std::log(p) + (T - n0) * std::log1p(-p));
+    double s = p0 * g(n0), q = p0;
+    for (int n = n0; n < T && q > 1e-18; ++n) {
+        q *= (double)(T - n) / (n + 1) * r;
+        s += q * g(n + 1);
+    }
+    q = p0;
+    for (int n = n0; n > 0 && q > 1e-18; --n) {
+        q *= (double)n / (T - n + 1) / r;
+        s += q * g(n - 1);
+    }
+    return s;
+}
+
+// MOE_PATH_AUTO, per call: the expected bytes of the whole call on each path,
+// with every routed expert receiving each token with probability k / E
+// (uniform routing; the call's counts are known only on the device) and the
+// shared experts all T tokens.
+bool auto_takes_dense(int T, int E, int k, int S, int tb, float density)
+{
+    const PathCost c(tb, density);
+    double sparse = S * c.sparse(T), dense = S * kDenseBytes;
+    if (k >= E) {
+        sparse += E * c.sparse(T);
+        dense += E * kDenseBytes;
+    } else {
+        const double p = (double)k / E;
+        sparse += E * binomial_mean(T, p, [&](int n) { return c.sparse(n); });
+        dense += E * kDenseBytes * -std::expm1(T * std::log1p(-p));     // P(n > 0)
+    }
+    return c.dense_wins(dense, sparse);
 }
 
 hipError_t launch_sparse(const SparseArgs &a, bool bf16, int tb, hipStream_t s)
@@ -285,6 +350,43 @@ moe_status check_weight_ptrs(const uint8_t *q, const uint16_t *sz, const void *g
     if (!aligned(q, 16) || !aligned(g, 16) || !aligned(dn, 16) || !aligned(sz, 4))
         return MOE_ERR_ALIGNMENT;
     return MOE_OK;
+}
+
+// The dense kernels a layer can run: the 256 x 256-tile GEMM (bf16 or fp16,
+// needs the transposed down weights) or the older bf16 kernels (row-major down).
+bool layer_gemm_ok(const moe_layer *L)
+{
+    return L->up_dense && L->down_dense && L->d % 256 == 0 && L->f % 128 == 0;
+}
+bool layer_old_ok(const moe_layer *L)
+{
+    return L->wdt == MOE_BF16 && L->up_dense && L->f % 256 == 0 && L->d % 128 == 0;
+}
+bool layer_args_ok(const moe_layer *L, int T)
+{
+    return L && T >= 1 && L->n_routed >= 1 && L->top_k >= 1 && L->top_k <= L->n_routed &&
+           L->n_shared >= 0 && L->d > 0 && L->f > 0;
+}
+
+// MOE_PATH_AUTO for T tokens: the GEMM layers by the expected-time rule, the
+// older bf16 kernels from T k >= 8 E (they serve whole calls only)
+bool auto_dense(const moe_layer *L, int T)
+{
+    if (layer_gemm_ok(L)) {
+        const SparsePlan sp = layer_plan(T, L->d, L->f, L->n_routed, L->top_k, L->n_shared);
+        return auto_takes_dense(T, L->n_routed, L->top_k, L->n_shared, sp.tb, L->density);
+    }
+    return layer_old_ok(L) && (long long)T * L->top_k >= 8ll * L->n_routed;
+}
+
+// MOE_PATH_MIXED for T tokens: the per-expert token threshold, or 0 when no
+// expert can reach it (or the layer has no GEMM weights)
+int mixed_dense_min(const moe_layer *L, int T)
+{
+    if (!layer_gemm_ok(L)) return 0;
+    const SparsePlan sp = layer_plan(T, L->d, L->f, L->n_routed, L->top_k, L->n_shared);
+    const int n = dense_min_tokens(sp.tb, L->density);
+    return n > T ? 0 : n;
 }
 
 }  // namespace
@@ -376,12 +478,14 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
 
 int moe_auto_dense_min(const moe_layer *L, int T)
 {
-    if (!L || T < 1 || L->n_routed < 1 || L->top_k < 1 || L->top_k > L->n_routed) return 0;
-    const bool gemm_ok = L->up_dense && L->down_dense && L->d % 256 == 0 && L->f % 128 == 0;
-    if (!gemm_ok) return 0;
-    const SparsePlan sp = layer_plan(T, L->d, L->f, L->n_routed, L->top_k, L->n_shared);
-    const int n = dense_min_tokens(sp.tb, L->density);
-    return n > T ? 0 : n;
+    if (!layer_args_ok(L, T)) return 0;
+    return auto_dense(L, T) ? 1 : 0;
+}
+
+int moe_mixed_dense_min(const moe_layer *L, int T)
+{
+    if (!layer_args_ok(L, T)) return 0;
+    return mixed_dense_min(L, T);
 }
 
 moe_status moe_route_topk(const void *x, moe_dtype xdt, int T, int d, const void *router_w,
@@ -412,7 +516,7 @@ namespace {
 // One expert over T tokens with the up codes at `bits` (2: the INT2 format,
 // 8 / 4 / 1: plain packing, d = 512 ... 4096): the fused kernel, the reduce,
 // and the bitmask / nnz exports when asked for.
-moe_status expert_forward(const moe_expert_view *e, int bits, int d, int f, moe_dtype wdt,
+static moe_status expert_forward(const moe_expert_view *e, int bits, int d, int f, moe_dtype wdt,
                           const void *x, moe_dtype xdt, int T, const float *token_scale,
                           int accumulate, void *y, moe_dtype ydt, uint64_t *mask_bits,
                           int32_t *nnz_out, uint8_t *mask_out, float *v_out, void *ws,
@@ -522,26 +626,23 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
     if (!L->thresholds) return MOE_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(y, ydt == MOE_F32 ? 4 : 2) || !aligned(L->thresholds, 4))
         return MOE_ERR_ALIGNMENT;
-    if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE && path != MOE_PATH_AUTO)
+    if (path != MOE_PATH_SPARSE && path != MOE_PATH_DENSE && path != MOE_PATH_AUTO &&
+        path != MOE_PATH_MIXED)
         return MOE_ERR_INVALID_ARG;
     // dense kernels: the 256 x 256-tile GEMM (bf16 or fp16; needs the
     // transposed down weights) or the older bf16 kernels (row-major down)
     const bool want_masks = trace && (trace->masks || trace->mask_bits || trace->nnz);
-    const bool gemm_ok = L->up_dense && L->down_dense && d % 256 == 0 && f % 128 == 0;
-    const bool old_ok = L->wdt == MOE_BF16 && L->up_dense && f % 256 == 0 && d % 128 == 0;
+    const bool gemm_ok = layer_gemm_ok(L);
+    const bool old_ok = layer_old_ok(L);
     const SparsePlan sp = layer_plan(T, d, f, E, k, S);
     const bool dense_aligned = L->up_dense && aligned(L->up_dense, 16) &&
                                (!L->down_dense || aligned(L->down_dense, 16));
     int nstar = 0;                  // per expert: experts with >= nstar tokens take the dense path
-    if (path == MOE_PATH_AUTO) {
-        if (gemm_ok && dense_aligned && !want_masks) {
-            nstar = dense_min_tokens(sp.tb, L->density);
-            if (nstar > T) nstar = 0;               // no expert can reach it
-            path = nstar > 0 ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
-        } else {
-            path = old_ok && dense_aligned && !want_masks && (long long)T * k >= 8ll * E
-                       ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
-        }
+    if (path == MOE_PATH_MIXED && gemm_ok && dense_aligned && !want_masks) {
+        nstar = mixed_dense_min(L, T);              // 0: no expert can reach it
+        path = nstar > 0 ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
+    } else if (path == MOE_PATH_AUTO || path == MOE_PATH_MIXED) {
+        path = dense_aligned && !want_masks && auto_dense(L, T) ? MOE_PATH_DENSE : MOE_PATH_SPARSE;
     }
     const bool mixed = nstar > 1;   // (nstar == 1: every expert with tokens is dense)
     if (path == MOE_PATH_DENSE) {
@@ -596,7 +697,9 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         inline_route && (route_split(d, E, L->rdt) || router_bytes > kInlineRouterBytes);
     hipError_t he = hipSuccess;
     if (inline_route) {
-        if (inline_logits_kernel) {
+        // no grouping kernel writes the per-expert path flags: all sparse
+        if (trace && trace->expert_dense) he = launch_fill_u8(trace->expert_dense, (size_t)E, 0, s);
+        if (he == hipSuccess && inline_logits_kernel) {
             r.lg_buf = w.lg;
             he = launch_route_logits(r, s);
         }

@@ -162,6 +162,7 @@ hipError_t launch_gemm_layer(const GemmArgs &a, hipStream_t s);
 hipError_t launch_transpose16(const uint16_t *in, int mats, int rows, int cols, uint16_t *out,
                               hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_fill_u8(uint8_t *p, size_t n, uint8_t v, hipStream_t s);
 // Bitmask and population count of `rows` 0/1 byte masks of f channels (f % 64
 // == 0): bits [rows][f/64] (channel 64 i + l at bit l of word i) and nnz [rows];
 // either may be null.

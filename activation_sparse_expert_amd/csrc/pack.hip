@@ -160,6 +160,14 @@ fill_zero_kernel(uint32_t *p, size_t n)
         p[i] = 0;
 }
 
+__global__ void __launch_bounds__(256)
+fill_u8_kernel(uint8_t *p, size_t n, uint8_t v)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
 }  // namespace
 
 hipError_t launch_pack_int2(const void *w, int dt, int d, int f, uint8_t *q, uint16_t *sz,
@@ -234,6 +242,15 @@ hipError_t launch_mask_bits(const uint8_t *m, int rows, int f, uint64_t *bits, i
 {
     if (rows < 1 || f % 64 != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mask_bits_kernel, dim3(rows), dim3(kPackThreads), 0, s, m, f, bits, nnz);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u8(uint8_t *p, size_t n, uint8_t v, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
 }
 

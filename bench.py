@@ -172,7 +172,7 @@ def batched_measure(reps=10, T=256, dense_only=False):
     ws = moe.new_workspace(L.workspace_bytes(T), dev)
     cnt = torch.empty(E, dtype=torch.int32, device=dev)
     out = {}
-    L.density = 1.0 - c["sparsity"]          # union-density input of MOE_PATH_AUTO's rule
+    L.density = 1.0 - c["sparsity"]          # union-density input of the AUTO / MIXED rules
     legs = (("dense_mfma", moe.PATH_DENSE, L),
             ("dense_mfma_rowmajor_down", moe.PATH_DENSE, L_rowmajor),
             ("sparse", moe.PATH_SPARSE, L),
@@ -202,8 +202,8 @@ def batched_measure(reps=10, T=256, dense_only=False):
         if name == "auto":
             flags = torch.zeros(E, dtype=torch.uint8, device=dev)
             moe.layer_forward(LL, x, path=path, y=y, ws=ws, trace={"expert_dense": flags})
-            out[name]["what"] = (f"per expert: dense MFMA at >= {LL.auto_dense_min(T)} tokens, "
-                                 f"density {LL.density:.2f}")
+            out[name]["what"] = (f"per call: {'dense' if LL.auto_dense_min(T) else 'sparse'} "
+                                 f"(expected bytes of both paths, density {LL.density:.2f})")
             out[name]["dense_experts"] = int(flags.sum().item())
         if path == moe.PATH_DENSE:
             out[name]["mfma_util"] = flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
@@ -337,9 +337,9 @@ def time_graph(fn, reps, inner):
 
 def layer_workload(layers, xs_by_layer, label, path=None):
     """Decode step through `layers` (one moe_layer_forward each, captured in a
-    graph): tokens/s and algorithmic GB/s.  path: MOE_PATH_SPARSE (default) or
-    MOE_PATH_AUTO, whose per-expert choice is read back and priced (dense
-    experts at their three 16-bit matrices)."""
+    graph): tokens/s and algorithmic GB/s.  path: MOE_PATH_SPARSE (default),
+    MOE_PATH_AUTO or MOE_PATH_MIXED, whose per-expert paths are read back and
+    priced (dense experts at their three 16-bit matrices)."""
     import torch
     import activation_sparse_expert_amd as moe
     dev = torch.device("cuda:0")
@@ -354,10 +354,11 @@ def layer_workload(layers, xs_by_layer, label, path=None):
                   masks=torch.empty((T, L.k + L.S, L.f), dtype=torch.uint8, device=dev))
         moe.layer_forward(L, x, y=y, ws=ws, trace=tr)
         dense = None
-        if path == moe.PATH_AUTO:
+        if path in (moe.PATH_AUTO, moe.PATH_MIXED):
             flags = torch.zeros(L.E, dtype=torch.uint8, device=dev)
             moe.layer_forward(L, x, path=path, y=y, ws=ws, trace=dict(expert_dense=flags))
-            nstar = L.auto_dense_min(T)
+            # the shared experts are dense from n* tokens (AUTO: n* = 1 on a dense call)
+            nstar = L.auto_dense_min(T) if path == moe.PATH_AUTO else L.mixed_dense_min(T)
             dense = np.concatenate([flags.cpu().numpy(),
                                     np.full(L.S, 1 if 0 < nstar <= T else 0, np.uint8)])
             n_dense += int(dense.sum())
@@ -371,7 +372,7 @@ def layer_workload(layers, xs_by_layer, label, path=None):
     out = {"workload": label, "tokens": T, "ms_per_step": sec * 1e3, "tokens_per_s": T / sec,
            "bytes_per_step": total_b, "achieved_gbs": total_b / sec / 1e9,
            "hbm_frac": total_b / sec / 1e9 / HBM_PEAK_GBS}
-    if path == moe.PATH_AUTO:
+    if path in (moe.PATH_AUTO, moe.PATH_MIXED):
         out["dense_experts"] = n_dense
     return out
 
@@ -453,7 +454,8 @@ def oracle_tiny_rate(budget_s):
 def layers_measure(fine_only=False, stack_only=False, cpu=False):
     """The 32-layer Mixtral stack (T = 1, 16) and the fine-grained 64+2 layer
     (T = 1, 64), each as tokens/s of a decode step, router included; the fine
-    layer again with dense copies under MOE_PATH_AUTO (T = 64, 256)."""
+    layer again with dense copies under MOE_PATH_AUTO (T = 64, 256) and
+    MOE_PATH_MIXED (T = 64)."""
     import torch
     import activation_sparse_expert_amd as moe
     import synth
@@ -477,7 +479,8 @@ def layers_measure(fine_only=False, stack_only=False, cpu=False):
             fine, xb, 6.0, "the fine-grained layer (64 routed top-6 + 2 shared, d=2048 f=1408, "
                            "70% sparsity), 1 token per call, router included")
     # the same layer with dense fp16 copies (up materialised, W^down transposed)
-    # under MOE_PATH_AUTO: experts with at least n* tokens take the MFMA path
+    # under MOE_PATH_AUTO (one path per call, from the expected bytes of both)
+    # and MOE_PATH_MIXED (per expert: dense from n* tokens)
     n = c["E"] + c["S"]
     fine.up_dense = torch.empty((n, c["f"], c["d"]), dtype=torch.float16, device=dev)
     for e in range(n):
@@ -486,11 +489,16 @@ def layers_measure(fine_only=False, stack_only=False, cpu=False):
     fine.density = 1.0 - c["sparsity"]
     for T in (64, 256):
         x = torch.from_numpy(synth.tokens_f32(synth.CFG_FINE, T, c["d"], c["x_scale"])).half().to(dev)
+        choice = "dense MFMA" if fine.auto_dense_min(T) else "sparse"
         r = layer_workload(
-            [fine], [x], f"the same layer with dense fp16 copies, MOE_PATH_AUTO (per expert: "
-                         f"dense MFMA at >= {fine.auto_dense_min(T)} tokens), {T} tokens",
-            path=moe.PATH_AUTO)
+            [fine], [x], f"the same layer with dense fp16 copies, MOE_PATH_AUTO (per call: "
+                         f"{choice}), {T} tokens", path=moe.PATH_AUTO)
         out[f"fine_T{T}_auto"] = r
+        if T == 64:
+            out["fine_T64_mixed"] = layer_workload(
+                [fine], [x], f"the same layer, MOE_PATH_MIXED (per expert: dense MFMA at >= "
+                             f"{fine.mixed_dense_min(T)} tokens, the others sparse), {T} tokens",
+                path=moe.PATH_MIXED)
         if T == 256:
             out["fine_T256"] = layer_workload(
                 [fine], [x], f"the same layer, sparse path for every expert, {T} tokens")
@@ -698,7 +706,7 @@ def main():
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched-layer (dense MFMA vs sparse) measurement")
     ap.add_argument("--fine-only", action="store_true",
-                    help="only the fine-grained layer workloads (sparse and MOE_PATH_AUTO)")
+                    help="only the fine-grained layer workloads (sparse, AUTO, MIXED)")
     ap.add_argument("--stack-only", action="store_true",
                     help="only the 32-layer stack workloads (T = 1, 16)")
     ap.add_argument("--variants-only", action="store_true",

@@ -94,8 +94,9 @@ typedef MOE_ENUM { MOE_F16 = 0, MOE_BF16 = 1, MOE_F32 = 2 } moe_dtype;
 
 typedef MOE_ENUM {
     MOE_PATH_SPARSE = 0,        /* Algorithm 1: INT2 up, threshold mask, row gathers */
-    MOE_PATH_DENSE = 1,         /* bf16 MFMA grouped GEMM, threshold off            */
-    MOE_PATH_AUTO = 2           /* dense when it moves fewer bytes, else sparse     */
+    MOE_PATH_DENSE = 1,         /* MFMA grouped GEMM (bf16, fp16), threshold off    */
+    MOE_PATH_AUTO = 2,          /* per call: the path with the lower expected time  */
+    MOE_PATH_MIXED = 3          /* per expert: dense from a token count, in one call */
 } moe_path;
 
 typedef MOE_ENUM {
@@ -146,7 +147,7 @@ typedef struct {
                                    token under the thresholds (e.g. measured
                                    from nnz exports, or 1 - the calibrated
                                    sparsity); <= 0: 0.5.  Read by MOE_PATH_AUTO
-                                   only.                                     */
+                                   and MOE_PATH_MIXED only.                  */
 } moe_layer;
 
 /* Optional device outputs of moe_layer_forward (any field may be NULL). */
@@ -170,7 +171,9 @@ typedef struct {
                                    path only)                                */
     uint8_t *expert_dense;      /* [E]: 1 where the routed expert took the dense
                                    path in this call, else 0 (the shared
-                                   experts' path: moe_auto_dense_min)        */
+                                   experts take it when the call is dense, or
+                                   under MOE_PATH_MIXED when T reaches
+                                   moe_mixed_dense_min)                      */
 } moe_layer_trace;
 
 /*
@@ -271,20 +274,29 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
  * where a_e is Algorithm 1 (MOE_PATH_SPARSE) or the dense SwiGLU with the up
  * weights in L->up_dense (MOE_PATH_DENSE: bf16 or fp16 with L->down_dense; bf16
  * only without it).
- * MOE_PATH_AUTO chooses per expert (MoE-Lightning review, "层次化屋顶模型", the
- * classic roofline: the expert FFN's operational intensity grows with its
- * tokens).  An expert with n tokens read by the sparse path costs
- * ceil(n / TB) chunks of TB tokens (TB = 1, 2 or 4, as the sparse kernel
- * chunks this call), each reading the INT2 up codes and scales (5/16 d f
- * bytes) and the gate and down rows of the union of its tokens' masks, about
- * 4 u d f bytes with u = 1 - (1 - L->density)^TB; the dense path reads the
- * 16-bit gate, up and down weights once, 6 d f bytes.  With L->up_dense and
- * L->down_dense set, the experts (routed and shared) whose token count n
- * reaches the smallest n with ceil(n / TB) (5/16 + 4 u) > 6 take the dense
- * path and the others the sparse path, in one call (the routed experts decide
- * on the device from the call's counts: no host synchronisation).  Without
- * down_dense (bf16 layers), the whole call takes the dense path when
- * T k >= 8 E.  A call that exports masks takes the sparse path throughout.
+ * MOE_PATH_AUTO and MOE_PATH_MIXED choose by one cost model (MoE-Lightning
+ * review, "层次化屋顶模型": time = bytes / attainable bandwidth, the expert FFN's
+ * operational intensity growing with its tokens).  In units of d f bytes, an
+ * expert with n tokens read by the sparse path costs its chunks of at most TB
+ * tokens (TB = 1, 2 or 4, as the sparse kernel chunks this call), a chunk of
+ * m tokens reading the INT2 up codes and scales (5/16) and the gate and down
+ * rows of the union of its tokens' masks (4 u, u = 1 - (1 - L->density)^m);
+ * the dense path reads the 16-bit gate, up and down weights once (6).  The
+ * dense GEMM streams its weights at about twice the rate of the multi-token
+ * sparse kernel, so the dense path is taken when its bytes are under twice
+ * the sparse path's.  Both need L->up_dense and L->down_dense (the 256 x
+ * 256-tile GEMM) and a call without mask exports; otherwise they take the
+ * sparse path, except that bf16 layers with up_dense alone take the older
+ * dense kernels for the whole call when T k >= 8 E.
+ *   MOE_PATH_AUTO decides per call, on the host, from the expected bytes of
+ *   each path with every routed expert receiving each token with probability
+ *   k / E (the shared experts all T tokens).  The whole call then takes one
+ *   path: serialising a partly filled sparse kernel and partly filled GEMMs
+ *   is slower than either path alone on the measured layers.
+ *   MOE_PATH_MIXED decides per expert, on the device, from the call's
+ *   counts (no host synchronisation): the experts (routed and shared) whose
+ *   token count reaches moe_mixed_dense_min take the dense path and the
+ *   others the sparse path, in one call.
  *   x [T][d] in xdt (== L->wdt), y [T][d] in ydt (overwritten).
  * trace (host struct, NULL allowed) receives the optional exports.
  */
@@ -294,13 +306,22 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
                              void *ws, size_t ws_bytes, void *stream);
 
 /*
- * The per-expert rule of MOE_PATH_AUTO for a call of T tokens on this layer:
- * the token count from which an expert takes the dense path (the shared
- * experts take it when T reaches it), or 0 when the call takes the sparse
- * path throughout (no dense weights, or no expert can reach the count).  Host
- * arithmetic only; the same value the layer call uses.
+ * MOE_PATH_AUTO's choice for a call of T tokens on this layer (without mask
+ * exports, dense weights 16-byte aligned): 1 when the call takes the dense
+ * path (every expert with tokens), 0 when it takes the sparse path.  Host
+ * arithmetic only; the same value the layer call uses.  0 for invalid
+ * arguments.
  */
 int moe_auto_dense_min(const moe_layer *L, int T);
+
+/*
+ * MOE_PATH_MIXED's per-expert rule for a call of T tokens on this layer: the
+ * token count from which an expert takes the dense path (the shared experts
+ * take it when T reaches it), or 0 when the call takes the sparse path
+ * throughout (no GEMM weights, or no expert can reach the count).  Host
+ * arithmetic only; the same value the layer call uses.
+ */
+int moe_mixed_dense_min(const moe_layer *L, int T);
 
 /*
  * Threshold calibration (FloE review, "高效稀疏 GEMV 内核": t_ij sets the

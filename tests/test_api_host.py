@@ -151,8 +151,9 @@ def _layer(desc=None, x=FAKE, xdt=0, T=4, y=FAKE, ydt=2, path=0, ws=FAKE, ws_byt
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(x=None), -1), (dict(T=0), -1), (dict(path=3), -1), (dict(ws=None), -4),
+    (dict(x=None), -1), (dict(T=0), -1), (dict(path=4), -1), (dict(path=-1), -1), (dict(ws=None), -4),
     (dict(path=2, ws_bytes=4096), -4),      # MOE_PATH_AUTO is a valid path: the workspace check follows
+    (dict(path=3, ws_bytes=4096), -4),      # and MOE_PATH_MIXED
     (dict(ws_bytes=4096), -4), (dict(xdt=1), -2), (dict(path=1), -2),   # dense needs bf16 + up_dense
 ])
 def test_layer_rejects(kw, code):
@@ -182,19 +183,79 @@ def test_layer_dense_shape_limits():
 
 
 @pytest.mark.parametrize("density,T,k,E,expect", [
-    # tb = 4 chunks (d = 4096): one chunk reads 5/16 + 4 (1 - (1 - rho)^4) d f bytes
-    (0.3, 256, 2, 8, 5),       # 3.35 per chunk: a second chunk costs more than 6 -> 5 tokens
-    (0.1, 256, 2, 8, 13),      # 1.69 per chunk: 3 chunks still cost less -> 13 tokens
-    (0.2, 256, 2, 8, 9),       # 2.67 per chunk -> 9
-    (0.0, 256, 2, 8, 5),       # unset: 0.5 -> 3.06 per chunk -> 5
-    (0.1, 8, 2, 8, 0),         # tb = 2 at 2 tokens per expert: 11 tokens, more than the call has
+    # tb = 4 chunks (d = 4096): a chunk of m tokens reads 5/16 + 4 (1 - (1 - rho)^m)
+    # d f bytes; an expert goes dense once its chunks cost more than 6 / 2 = 3
+    (0.3, 256, 2, 8, 4),       # chunks of 1..4 tokens: 1.51, 2.35, 2.94, 3.35 -> 4 tokens
+    (0.1, 256, 2, 8, 7),       # 1.69 for a full chunk, + 1.40 for 3 more tokens -> 7
+    (0.2, 256, 2, 8, 5),       # 2.67 + 1.11 -> 5
+    (0.0, 256, 2, 8, 2),       # unset: 0.5 -> 2.31, 3.31 -> 2
+    (0.1, 8, 2, 8, 6),         # tb = 2 at 2 tokens per expert: 3 x 1.07 + ... -> 6 <= 8
+    (0.1, 4, 2, 8, 0),         # tb = 1: 6 tokens, more than the call has
 ])
-def test_auto_dense_min(density, T, k, E, expect):
+def test_mixed_dense_min(density, T, k, E, expect):
     L = _lib_or_skip()
     dsc = _layer_desc(n_routed=E, top_k=k, up_dense=FAKE, down_dense=FAKE, density=density)
-    assert L.moe_auto_dense_min(C.byref(dsc), T) == expect
+    assert L.moe_mixed_dense_min(C.byref(dsc), T) == expect
     # no dense weights: never
-    assert L.moe_auto_dense_min(C.byref(_layer_desc(density=density)), T) == 0
+    assert L.moe_mixed_dense_min(C.byref(_layer_desc(density=density)), T) == 0
+
+
+# MOE_PATH_AUTO decides per call.  The boundaries below are where a sweep of
+# both pure paths on MI355X found the dense path overtaking the sparse one: the
+# DeepSeek-V2-Lite-shaped layer (64 routed top-6 + 2 shared, d=2048, f=1408,
+# 70% sparsity) was faster sparse at 12 tokens (78 against 93 us) and dense at
+# 16 (98 against 101 us); the Mixtral-8x22B-shaped layer (8 routed top-2,
+# d=6144, f=16384) sparse at 8 tokens (645 against 694 us), dense at 16 (821
+# against 1013 us).
+@pytest.mark.parametrize("shape,sparse_at,dense_at", [
+    (dict(d=2048, f=1408, n_routed=64, n_shared=2, top_k=6, density=0.3), (1, 2, 4, 8, 12),
+     (16, 64, 256, 4096)),
+    (dict(d=6144, f=16384, n_routed=8, n_shared=0, top_k=2, density=0.3, wdt=1), (1, 2, 4, 8),
+     (16, 32, 256)),
+])
+def test_auto_per_call_choice(shape, sparse_at, dense_at):
+    L = _lib_or_skip()
+    dsc = _layer_desc(up_dense=FAKE, down_dense=FAKE, **shape)
+    for T in sparse_at:
+        assert L.moe_auto_dense_min(C.byref(dsc), T) == 0, T
+    for T in dense_at:
+        assert L.moe_auto_dense_min(C.byref(dsc), T) == 1, T
+    # without the transposed down weights the GEMM cannot run: sparse, except
+    # the older bf16 kernels for whole calls from T k >= 8 E
+    nodown = _layer_desc(up_dense=FAKE, **shape)
+    for T in dense_at:
+        old = shape.get("wdt", 0) == 1 and T * shape["top_k"] >= 8 * shape["n_routed"]
+        assert L.moe_auto_dense_min(C.byref(nodown), T) == int(old), T
+    # invalid arguments
+    assert L.moe_auto_dense_min(None, 16) == 0
+    assert L.moe_auto_dense_min(C.byref(dsc), 0) == 0
+    assert L.moe_mixed_dense_min(None, 16) == 0
+
+
+def test_auto_expected_bytes_limits():
+    """AUTO's expected-bytes rule at its limits.  One token: an expert reads
+    (5/16 + 4 rho) d f on the sparse path against 6 d f dense, so it stays
+    sparse while 6 >= 2 (5/16 + 4 rho), i.e. rho <= 0.67, and goes dense at
+    rho = 1 (thresholds that keep every channel).  A router that sends every
+    token to every expert (k = E) is priced without the binomial; a huge call
+    goes dense; and a tiny density keeps even many tokens per expert sparse
+    (a chunk reads little more than the codes)."""
+    L = _lib_or_skip()
+    for rho, want in ((0.01, 0), (0.3, 0), (0.65, 0), (0.7, 1), (1.0, 1)):
+        for E, k, S in ((8, 2, 0), (64, 6, 2), (4, 4, 1)):
+            dsc = _layer_desc(n_routed=E, top_k=k, n_shared=S, up_dense=FAKE, down_dense=FAKE,
+                              density=rho)
+            assert L.moe_auto_dense_min(C.byref(dsc), 1) == want, (rho, E, k, S)
+    dsc = _layer_desc(n_routed=4, top_k=4, n_shared=1, up_dense=FAKE, down_dense=FAKE, density=0.3)
+    assert L.moe_auto_dense_min(C.byref(dsc), 64) == 1
+    dsc = _layer_desc(n_routed=64, top_k=6, up_dense=FAKE, down_dense=FAKE, density=0.3)
+    assert L.moe_auto_dense_min(C.byref(dsc), 10000) == 1
+    # rho = 0.001, tb = 4: a chunk of four tokens reads 0.3285 d f, so about 16
+    # tokens per expert cost about 4 x 0.3285 = 1.3 d f, under half of the
+    # dense 6 d f: the call stays sparse; at 64 per expert (5.3) it goes dense
+    dsc = _layer_desc(n_routed=8, top_k=2, up_dense=FAKE, down_dense=FAKE, density=0.001)
+    assert L.moe_auto_dense_min(C.byref(dsc), 64) == 0
+    assert L.moe_auto_dense_min(C.byref(dsc), 256) == 1
 
 
 def test_prep_entry_points_reject():

@@ -248,10 +248,47 @@ def test_layer_auto_path(T, E, S, k, d, f, expect):
     assert not np.array_equal(y_auto, y_other)
 
 
+@pytest.mark.parametrize("wdt,T,expect", [("f16", 1, "sparse"), ("f16", 4, "sparse"),
+                                           ("f16", 24, "dense"), ("bf16", 4, "sparse"),
+                                           ("bf16", 24, "dense")])
+def test_layer_auto_gemm_per_call(wdt, T, expect):
+    """MOE_PATH_AUTO on a layer with the GEMM weights decides per call from
+    the expected bytes of both paths (16 routed top-2 + 1 shared, d=512,
+    f=256, density 0.3: sparse at 1 and 4 tokens, dense at 24).  Its output
+    is bit-identical to the path it names and differs from the other, and the
+    exported per-expert flags are all-or-none: every expert with tokens on a
+    dense call, none on a sparse one (one token included, which is routed
+    inside the expert kernel without the grouping step)."""
+    E, S, k, d, f = 16, 1, 2, 512, 256
+    experts, thr = build_host_layer(74, E, S, d, f, wdt, 0.7, 1.0, layer=d)
+    R_bits = synth.to_bits(synth.router_f32(74, d, E, d), wdt)
+    x_bits = synth.to_bits(synth.tokens_f32(75, T, d, 1.0, layer=d), wdt)
+    L = device_layer(experts, thr, R_bits, wdt, E, S, k, dense="gemm")
+    L.density = 0.3
+    assert L.auto_dense_min(T) == (1 if expect == "dense" else 0)
+    x = to_dev_bits(x_bits, wdt)
+    flags = torch.full((E,), 7, dtype=torch.uint8, device=DEV)
+    cnt_d = torch.empty(E, dtype=torch.int32, device=DEV)
+    y_auto = moe.layer_forward(L, x, path=moe.PATH_AUTO,
+                               trace=dict(expert_dense=flags, expert_count=cnt_d))
+    torch.cuda.synchronize()
+    y_auto = y_auto.cpu().numpy()
+    named = moe.PATH_DENSE if expect == "dense" else moe.PATH_SPARSE
+    other = moe.PATH_SPARSE if expect == "dense" else moe.PATH_DENSE
+    y_named, _ = run_layer(L, x, named, want_masks=False)
+    y_other, _ = run_layer(L, x, other, want_masks=False)
+    assert np.array_equal(y_auto, y_named), f"AUTO at T={T} is not the {expect} path"
+    assert not np.array_equal(y_auto, y_other)
+    cnt, fl = cnt_d.cpu().numpy(), flags.cpu().numpy()
+    want = (cnt > 0) if expect == "dense" else np.zeros(E, bool)
+    assert np.array_equal(fl, want.astype(np.uint8)), (cnt, fl)
+    say(f"AUTO per call {wdt} T={T}: {expect}, counts {cnt.tolist()}")
+
+
 @pytest.mark.parametrize("wdt,T,k", [("f16", 64, 4), ("bf16", 64, 4), ("f16", 160, 2)])
-def test_layer_auto_per_expert_mixed(wdt, T, k):
-    """MOE_PATH_AUTO with dense weights chooses the path per expert in one call:
-    under a Zipf-skewed router the hot experts (at least moe_auto_dense_min
+def test_layer_mixed_per_expert(wdt, T, k):
+    """MOE_PATH_MIXED with dense weights chooses the path per expert in one call:
+    under a Zipf-skewed router the hot experts (at least moe_mixed_dense_min
     tokens) and the shared expert take the dense MFMA path, the others the
     sparse kernel.  The exported per-expert flags follow that rule from the
     call's counts, and y matches the oracle run with the same per-expert
@@ -265,14 +302,14 @@ def test_layer_auto_per_expert_mixed(wdt, T, k):
     x_bits = synth.to_bits(synth.tokens_f32(72, T, d, 1.0, layer=d), wdt)
     L = device_layer(experts, thr, R_bits, wdt, E, S, k, bias=bias, dense="gemm")
     L.density = 0.3
-    nstar = L.auto_dense_min(T)
+    nstar = L.mixed_dense_min(T)
     assert 1 < nstar <= T, nstar
     x = to_dev_bits(x_bits, wdt)
     flags = torch.zeros(E, dtype=torch.uint8, device=DEV)
     idx_d = torch.empty((T, k), dtype=torch.int32, device=DEV)
     cnt_d = torch.empty(E, dtype=torch.int32, device=DEV)
     w_d = torch.empty((T, k), dtype=torch.float32, device=DEV)
-    y = moe.layer_forward(L, x, path=moe.PATH_AUTO,
+    y = moe.layer_forward(L, x, path=moe.PATH_MIXED,
                           trace=dict(expert_dense=flags, topk_idx=idx_d, expert_count=cnt_d,
                                      topk_w=w_d))
     torch.cuda.synchronize()
@@ -294,8 +331,8 @@ def test_layer_auto_per_expert_mixed(wdt, T, k):
     y_ref, _, w_ref, _ = oracle.layer_forward(
         x_bits[tokens], wdt, R_bits, wdt, bias, E, k, S, True, uq, us, g, dn, wdt, thr,
         topk_in=tr["topk_idx"][tokens], masks_in=tr["masks"][tokens], dense_experts=dense_experts)
-    err = check_y(y.cpu().numpy()[tokens], y_ref, 2e-3, f"AUTO per-expert layer {wdt}")
-    say(f"AUTO per-expert {wdt}: n*={nstar}, dense experts {np.flatnonzero(fl).tolist()} "
+    err = check_y(y.cpu().numpy()[tokens], y_ref, 2e-3, f"MIXED per-expert layer {wdt}")
+    say(f"MIXED per-expert {wdt}: n*={nstar}, dense experts {np.flatnonzero(fl).tolist()} "
         f"(counts {cnt.tolist()}), shared dense {bool(T >= nstar)}, max relL2 {err:.2e}")
 
 
