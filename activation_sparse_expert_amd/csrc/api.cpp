@@ -205,6 +205,49 @@ void *scratch_for_current_device()
     return g_scratch_ptr[dev];
 }
 
+// ---- second stream of mixed layer calls ------------------------------------
+// A call that runs both the sparse kernel and the GEMMs (MOE_PATH_MIXED)
+// launches the GEMMs on a library stream of the caller's device, forked from
+// and joined back into the caller's stream by events.  The two kernel
+// families write disjoint partial rows, so they can share the compute units
+// instead of each running partly filled.  The stream (default priority) and
+// the events are created by the device's first such call; a call under graph
+// capture that finds none runs both in order on the caller's stream.  The
+// fork, the launches on the library stream and the join are made under one
+// lock, so that concurrent calls from several host threads keep their own
+// dependencies.
+struct ForkState {
+    hipStream_t s2 = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_fork_mu;
+ForkState g_fork[kMaxDevices];
+
+// The current device's fork state (g_fork_mu held), or null: creation failed,
+// or it does not exist yet and `s` is capturing.
+ForkState *fork_state(hipStream_t s)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    ForkState &fs = g_fork[dev];
+    if (fs.s2) return &fs;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t s2 = nullptr;
+    hipEvent_t e1 = nullptr, e2 = nullptr;
+    if (hipStreamCreateWithFlags(&s2, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e1, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&e2, hipEventDisableTiming) != hipSuccess) {
+        if (e1) (void)hipEventDestroy(e1);
+        (void)hipStreamDestroy(s2);
+        return nullptr;
+    }
+    fs.s2 = s2;
+    fs.fork = e1;
+    fs.join = e2;
+    return &fs;
+}
+
 // Split of f in the dense down product: enough workgroups (d / 256 column
 // tiles per chunk of tokens) for about two per compute unit, at most 4 (the
 // partial-row region holds 4 slices per row), each slice a multiple of 64.
@@ -730,6 +773,21 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         if (tm.tiles > tp.tiles && tm.tiles <= cap) tp = tm;
     }
     const int stride = mixed ? (tp.tiles > ksplit ? tp.tiles : ksplit) : 0;
+    // mixed: the GEMMs go to the library stream, forked here and joined before the reduce
+    std::unique_lock<std::mutex> fork_lk(g_fork_mu, std::defer_lock);
+    ForkState *fs = nullptr;
+    hipStream_t sg = s;
+    if (mixed && use_gemm) {
+        fork_lk.lock();
+        fs = fork_state(s);
+        if (fs) {
+            if (hipEventRecord(fs->fork, s) != hipSuccess || hipStreamWaitEvent(fs->s2, fs->fork, 0) != hipSuccess)
+                return MOE_ERR_HIP;
+            sg = fs->s2;
+        } else {
+            fork_lk.unlock();
+        }
+    }
     if (mixed) {
         // the sparse experts: the sparse kernel over the sparse chunk table
         // (and the shared experts unless they are dense)
@@ -765,8 +823,13 @@ moe_status moe_layer_forward(const moe_layer *L, const void *x, moe_dtype xdt, i
         g.grid_chunks = gemm_grid_chunks(T, k, E, Sg, mt);
         g.mt = mt;
         g.ksplit = ksplit;
-        he = launch_gemm_layer(g, s);
+        he = launch_gemm_layer(g, sg);
         if (he != hipSuccess) return MOE_ERR_HIP;
+        if (fs) {
+            if (hipEventRecord(fs->join, sg) != hipSuccess || hipStreamWaitEvent(s, fs->join, 0) != hipSuccess)
+                return MOE_ERR_HIP;
+            fork_lk.unlock();
+        }
         if (mixed) {
             red.tiles = tp.tiles; red.stride = stride;
             red.mix = 1; red.tiles_dense = ksplit; red.shared_dense = shared_dense ? 1 : 0;

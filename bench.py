@@ -454,8 +454,8 @@ def oracle_tiny_rate(budget_s):
 def layers_measure(fine_only=False, stack_only=False, cpu=False):
     """The 32-layer Mixtral stack (T = 1, 16) and the fine-grained 64+2 layer
     (T = 1, 64), each as tokens/s of a decode step, router included; the fine
-    layer again with dense copies under MOE_PATH_AUTO (T = 64, 256) and
-    MOE_PATH_MIXED (T = 64)."""
+    layer again with dense copies under MOE_PATH_AUTO and MOE_PATH_MIXED
+    (T = 64, 256)."""
     import torch
     import activation_sparse_expert_amd as moe
     import synth
@@ -494,11 +494,10 @@ def layers_measure(fine_only=False, stack_only=False, cpu=False):
             [fine], [x], f"the same layer with dense fp16 copies, MOE_PATH_AUTO (per call: "
                          f"{choice}), {T} tokens", path=moe.PATH_AUTO)
         out[f"fine_T{T}_auto"] = r
-        if T == 64:
-            out["fine_T64_mixed"] = layer_workload(
-                [fine], [x], f"the same layer, MOE_PATH_MIXED (per expert: dense MFMA at >= "
-                             f"{fine.mixed_dense_min(T)} tokens, the others sparse), {T} tokens",
-                path=moe.PATH_MIXED)
+        out[f"fine_T{T}_mixed"] = layer_workload(
+            [fine], [x], f"the same layer, MOE_PATH_MIXED (per expert: dense MFMA at >= "
+                         f"{fine.mixed_dense_min(T)} tokens, the others sparse, the GEMMs on a "
+                         f"second stream), {T} tokens", path=moe.PATH_MIXED)
         if T == 256:
             out["fine_T256"] = layer_workload(
                 [fine], [x], f"the same layer, sparse path for every expert, {T} tokens")

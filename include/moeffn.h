@@ -296,7 +296,13 @@ moe_status moe_expert_forward_sparse_bits(const moe_expert_view *e, int bits, in
  *   MOE_PATH_MIXED decides per expert, on the device, from the call's
  *   counts (no host synchronisation): the experts (routed and shared) whose
  *   token count reaches moe_mixed_dense_min take the dense path and the
- *   others the sparse path, in one call.
+ *   others the sparse path, in one call.  Its GEMMs run on a library stream
+ *   of the current device, forked from `stream` after the routing and joined
+ *   back before the reduce by events, so that the sparse kernel and the
+ *   GEMMs share the GPU.  That stream (default priority) and its events are
+ *   created by the device's first MIXED call and kept until the process
+ *   ends; a call made under graph capture before then runs both on `stream`
+ *   in order.  The fork and join are serialised across host threads.
  *   x [T][d] in xdt (== L->wdt), y [T][d] in ydt (overwritten).
  * trace (host struct, NULL allowed) receives the optional exports.
  */

@@ -285,6 +285,51 @@ def test_layer_auto_gemm_per_call(wdt, T, expect):
     say(f"AUTO per call {wdt} T={T}: {expect}, counts {cnt.tolist()}")
 
 
+def test_layer_mixed_graph_replay():
+    """MOE_PATH_MIXED runs its GEMMs on a library stream forked from the
+    caller's stream and joined before the reduce.  Captured in a HIP graph
+    (three calls on different tokens sharing one workspace) and replayed three
+    times, with eager calls on the same workspace between the replays, every
+    replay reproduces the eager outputs bit for bit."""
+    E, S, k, d, f, T = 16, 1, 4, 512, 256, 64
+    experts, thr = build_host_layer(70, E, S, d, f, "f16", 0.7, 1.0, layer=d)
+    R_bits = synth.to_bits(synth.router_f32(70, d, E, d), "f16")
+    bias = synth.zipf_bias(71, d, E, 1.1)
+    L = device_layer(experts, thr, R_bits, "f16", E, S, k, bias=bias, dense="gemm")
+    L.density = 0.3
+    assert 1 < L.mixed_dense_min(T) <= T
+    xs = [to_dev_bits(synth.to_bits(synth.tokens_f32(76 + i, T, d, 1.0, layer=d), "f16"), "f16")
+          for i in range(3)]
+    ws = moe.new_workspace(L.workspace_bytes(T))
+    ys = torch.zeros((3, T, d), dtype=torch.float32, device=DEV)
+    flags = torch.zeros((3, E), dtype=torch.uint8, device=DEV)
+    for i in range(3):
+        moe.layer_forward(L, xs[i], path=moe.PATH_MIXED, y=ys[i], ws=ws,
+                          trace=dict(expert_dense=flags[i]))
+    torch.cuda.synchronize()
+    y_eager = ys.cpu().numpy().copy()
+    fl = flags.cpu().numpy()
+    assert fl.any() and not fl.all(), f"not a mixed call: {fl.tolist()}"
+    y_dense, _ = run_layer(L, xs[0], moe.PATH_DENSE, want_masks=False)
+    assert not np.array_equal(y_eager[0], y_dense)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(3):
+            moe.layer_forward(L, xs[i], path=moe.PATH_MIXED, y=ys[i], ws=ws)
+    for rep in range(3):
+        ys.fill_(7.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        stream.synchronize()
+        assert np.array_equal(ys.cpu().numpy(), y_eager), f"replay {rep}"
+        moe.layer_forward(L, xs[2], path=moe.PATH_MIXED, y=ys[0], ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(ys[0].cpu().numpy(), y_eager[2]), f"eager call after replay {rep}"
+    say("MIXED graph replays reproduce the eager outputs bit for bit")
+
+
 @pytest.mark.parametrize("wdt,T,k", [("f16", 64, 4), ("bf16", 64, 4), ("f16", 160, 2)])
 def test_layer_mixed_per_expert(wdt, T, k):
     """MOE_PATH_MIXED with dense weights chooses the path per expert in one call:
