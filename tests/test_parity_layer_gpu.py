@@ -330,6 +330,58 @@ def test_layer_mixed_graph_replay():
     say("MIXED graph replays reproduce the eager outputs bit for bit")
 
 
+def test_layer_mixed_two_host_threads():
+    """Two host threads make MOE_PATH_MIXED calls at the same time, each on
+    its own stream and workspace (the binding's foreign calls release the
+    interpreter lock).  Both share the device's library stream and fork
+    events, which the library serialises; every output equals the one the
+    same call gives alone."""
+    import threading
+    E, S, k, d, f, T = 16, 1, 4, 512, 256, 64
+    experts, thr = build_host_layer(70, E, S, d, f, "f16", 0.7, 1.0, layer=d)
+    R_bits = synth.to_bits(synth.router_f32(70, d, E, d), "f16")
+    bias = synth.zipf_bias(71, d, E, 1.1)
+    L = device_layer(experts, thr, R_bits, "f16", E, S, k, bias=bias, dense="gemm")
+    L.density = 0.3
+    xs = [to_dev_bits(synth.to_bits(synth.tokens_f32(80 + i, T, d, 1.0, layer=d), "f16"), "f16")
+          for i in range(2)]
+    want = []
+    for i in range(2):
+        y = moe.layer_forward(L, xs[i], path=moe.PATH_MIXED)
+        torch.cuda.synchronize()
+        want.append(y.cpu().numpy())
+    assert not np.array_equal(want[0], want[1])
+    n = 20
+    outs = [torch.zeros((n, T, d), dtype=torch.float32, device=DEV) for _ in range(2)]
+    wss = [moe.new_workspace(L.workspace_bytes(T)) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()                    # the buffers are filled before the threads start
+    errors = []
+
+    def worker(i):
+        try:
+            torch.cuda.set_device(0)
+            with torch.cuda.stream(streams[i]):
+                for j in range(n):
+                    moe.layer_forward(L, xs[i], path=moe.PATH_MIXED, y=outs[i][j], ws=wss[i])
+            streams[i].synchronize()
+        except Exception as exc:                 # reported below
+            errors.append(repr(exc))
+
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        got = outs[i].cpu().numpy()
+        for j in range(n):
+            assert np.array_equal(got[j], want[i]), f"thread {i} call {j}"
+    say(f"MIXED from two host threads: {2 * n} calls, all bit-identical to the single calls")
+
+
 @pytest.mark.parametrize("wdt,T,k", [("f16", 64, 4), ("bf16", 64, 4), ("f16", 160, 2)])
 def test_layer_mixed_per_expert(wdt, T, k):
     """MOE_PATH_MIXED with dense weights chooses the path per expert in one call:
