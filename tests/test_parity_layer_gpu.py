@@ -1,5 +1,7 @@
 """GPU parity of routing, grouping and whole MoE layers (sparse and dense paths)
 against the fp64 oracle, through the C ABI."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -380,6 +382,20 @@ def test_layer_mixed_two_host_threads():
         for j in range(n):
             assert np.array_equal(got[j], want[i]), f"thread {i} call {j}"
     say(f"MIXED from two host threads: {2 * n} calls, all bit-identical to the single calls")
+
+
+def test_layer_mixed_first_call_under_capture():
+    """A process whose first MOE_PATH_MIXED call is captured in a graph (the
+    library cannot create its stream then) runs that call in order on the
+    capturing stream; its replays equal the later forked eager calls.  Run in
+    a fresh child process, since this process already holds the stream."""
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    r = subprocess.run([sys.executable, os.path.join(here, "mixed_first_capture.py")],
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    say(r.stdout.strip().splitlines()[-1])
 
 
 @pytest.mark.parametrize("wdt,T,k", [("f16", 64, 4), ("bf16", 64, 4), ("f16", 160, 2)])
