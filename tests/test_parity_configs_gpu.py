@@ -6,7 +6,9 @@ outputs the fp64 oracle computes token by token:
 * a Mixtral-8x22B-shaped layer (8 experts, d=6144, f=16384, top-2, bf16,
   256 tokens) on the dense MFMA path and on the 70%-sparse path;
 * a DeepSeek-V2-Lite-shaped layer (64 routed top-6 + 2 shared experts,
-  d=2048, f=1408, Zipf-skewed router bias, 70% sparsity) at 1 and 64 tokens.
+  d=2048, f=1408, Zipf-skewed router bias, 70% sparsity) at 1 and 64 tokens
+  on the sparse path, and at 64 tokens under MOE_PATH_AUTO (the dense fp16
+  MFMA call) and MOE_PATH_MIXED (per expert, on two streams).
 
 Weights are drawn on the device (torch generator), INT2-packed by the
 library's packer and held bit-exact against the oracle's packer for every
@@ -18,7 +20,8 @@ import torch
 
 import activation_sparse_expert_amd as moe
 import synth
-from gpu_helpers import DeviceLayer, check_layer_tokens, check_route, run_layer, say, to_dev_bits
+from gpu_helpers import (DeviceLayer, check_layer_tokens, check_route, check_y, run_layer, say,
+                         to_dev_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,7 +111,8 @@ def fine():
     say("drawing and packing 64 + 2 experts (d=2048, f=1408) on the device")
     bias = synth.zipf_bias(synth.CFG_FINE, 0, c["E"], c["zipf_s"])
     lay = DeviceLayer(synth.CFG_FINE, 0, c["E"], c["S"], c["k"], c["d"], c["f"], c["wdt"],
-                      c["x_scale"], c["sparsity"], bias=bias)
+                      c["x_scale"], c["sparsity"], bias=bias, dense=True)
+    lay.L.density = 1.0 - c["sparsity"]
     yield lay, c
     lay.free()
 
@@ -124,3 +128,57 @@ def test_fine_layer(fine, T):
     say(f"fine T={T}: experts used {int((hist > 0).sum())}/{c['E']}, max load {hist.max()}")
     tokens = np.arange(T) if T == 1 else np.array([0, 1, 31, 63])
     check_layer_tokens(lay, x_bits, y, tr, tokens, False, f"fine 64+2 T={T}")
+
+
+def test_fine_layer_auto_dense_T64(fine):
+    """The fine layer at 64 tokens under MOE_PATH_AUTO, which takes the dense
+    fp16 MFMA path for the whole call (64-row tiles; the Zipf-hot experts and
+    the shared ones in several chunks), against the oracle's dense path."""
+    lay, c = fine
+    T = 64
+    assert lay.L.auto_dense_min(T) == 1
+    x_bits = synth.to_f16_bits(synth.tokens_f32(synth.CFG_FINE, T, c["d"], c["x_scale"]))
+    y, tr = run_layer(lay.L, to_dev_bits(x_bits, "f16"), moe.PATH_AUTO, want_masks=False)
+    check_route(x_bits, "f16", lay.R_bits, "f16", c["E"], c["k"], True, lay.bias,
+                route_view(tr, c["E"]), "fine router T=64 (AUTO)")
+    check_layer_tokens(lay, x_bits, y, tr, np.array([0, 1, 31, 63]), True,
+                       "fine 64+2 T=64 AUTO (dense fp16 MFMA)")
+
+
+def test_fine_layer_mixed_T64(fine):
+    """The fine layer at 64 tokens under MOE_PATH_MIXED: experts with at
+    least n* tokens (the shared ones included) on the dense MFMA path, the
+    others on the sparse kernel, the two on separate streams.  The per-expert
+    flags follow n* from the call's counts, and y on sampled tokens matches
+    the oracle run with the same per-expert paths (the sparse experts fed the
+    masks of a sparse-path call of the same tokens)."""
+    import oracle
+    lay, c = fine
+    T, E, S, k = 64, c["E"], c["S"], c["k"]
+    nstar = lay.L.mixed_dense_min(T)
+    assert 1 < nstar <= T
+    x_bits = synth.to_f16_bits(synth.tokens_f32(synth.CFG_FINE, T, c["d"], c["x_scale"]))
+    x = to_dev_bits(x_bits, "f16")
+    flags = torch.zeros(E, dtype=torch.uint8, device="cuda")
+    cnt_d = torch.empty(E, dtype=torch.int32, device="cuda")
+    idx_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    y = moe.layer_forward(lay.L, x, path=moe.PATH_MIXED,
+                          trace=dict(expert_dense=flags, expert_count=cnt_d, topk_idx=idx_d))
+    torch.cuda.synchronize()
+    cnt, fl = cnt_d.cpu().numpy(), flags.cpu().numpy()
+    assert np.array_equal(fl, (cnt >= nstar).astype(np.uint8))
+    assert fl.any() and not fl[cnt > 0].all(), "not a mixed call"
+    _, tr = run_layer(lay.L, x, moe.PATH_SPARSE)
+    assert np.array_equal(tr["topk_idx"], idx_d.cpu().numpy())
+    tokens = np.array([0, 1, 31, 63])
+    used = set(range(E, E + S))
+    for t in tokens:
+        used.update(int(e) for e in tr["topk_idx"][t])
+    uq, us, g, dn = lay.host_weights(used)
+    dense_experts = np.concatenate([fl, np.full(S, 1 if T >= nstar else 0, np.uint8)])
+    y_ref, _, _, _ = oracle.layer_forward(
+        x_bits[tokens], "f16", lay.R_bits, "f16", lay.bias, E, k, S, True, uq, us, g, dn, "f16",
+        lay.thr, topk_in=tr["topk_idx"][tokens], masks_in=tr["masks"][tokens],
+        dense_experts=dense_experts)
+    err = check_y(y.cpu().numpy()[tokens], y_ref, 2e-3, "fine 64+2 T=64 MIXED")
+    say(f"fine T=64 MIXED: n*={nstar}, {int(fl.sum())} routed experts dense, max relL2 {err:.2e}")
