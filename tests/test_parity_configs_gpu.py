@@ -4,7 +4,8 @@ outputs the fp64 oracle computes token by token:
 * a 32-layer stack of 8 Mixtral-shaped experts (d=4096, f=14336, top-2,
   80% sparsity), 64.8 GB resident, hidden state carried across layers;
 * a Mixtral-8x22B-shaped layer (8 experts, d=6144, f=16384, top-2, bf16,
-  256 tokens) on the dense MFMA path and on the 70%-sparse path;
+  256 tokens) on the dense MFMA path and on the 70%-sparse path, and at 16
+  tokens under MOE_PATH_MIXED;
 * a DeepSeek-V2-Lite-shaped layer (64 routed top-6 + 2 shared experts,
   d=2048, f=1408, Zipf-skewed router bias, 70% sparsity) at 1 and 64 tokens
   on the sparse path, and at 64 tokens under MOE_PATH_AUTO (the dense fp16
@@ -101,6 +102,45 @@ def test_wide_layer(wide, path):
     check_layer_tokens(lay, x_bits, y, tr, tokens, dense,
                        f"wide d=6144 f=16384 T=256 {'dense MFMA' if dense else '70% sparse'}")
     assert np.isfinite(y).all()
+
+
+def test_wide_layer_mixed_T16(wide):
+    """The wide bf16 layer at 16 tokens under MOE_PATH_MIXED (the sparse
+    kernel and the 256 x 256-tile GEMM on two streams): experts with at least
+    n* tokens on the dense path, the others sparse.  The flags follow n* from
+    the call's counts, and y on sampled tokens matches the oracle run with the
+    same per-expert paths (sparse experts fed a sparse-path call's masks)."""
+    import oracle
+    lay, x_all, c = wide
+    T, E, k = 16, c["E"], c["k"]
+    x_bits = x_all[:T]
+    lay.L.density = 1.0 - c["sparsity"]
+    nstar = lay.L.mixed_dense_min(T)
+    assert 1 < nstar <= T
+    x = to_dev_bits(x_bits, "bf16")
+    flags = torch.zeros(E, dtype=torch.uint8, device="cuda")
+    cnt_d = torch.empty(E, dtype=torch.int32, device="cuda")
+    idx_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    y = moe.layer_forward(lay.L, x, path=moe.PATH_MIXED,
+                          trace=dict(expert_dense=flags, expert_count=cnt_d, topk_idx=idx_d))
+    torch.cuda.synchronize()
+    cnt, fl = cnt_d.cpu().numpy(), flags.cpu().numpy()
+    assert np.array_equal(fl, (cnt >= nstar).astype(np.uint8))
+    assert fl.any() and not fl[cnt > 0].all(), f"not a mixed call: counts {cnt.tolist()}"
+    _, tr = run_layer(lay.L, x, moe.PATH_SPARSE)
+    assert np.array_equal(tr["topk_idx"], idx_d.cpu().numpy())
+    tokens = np.array([0, 7, 15])
+    used = set()
+    for t in tokens:
+        used.update(int(e) for e in tr["topk_idx"][t])
+    uq, us, g, dn = lay.host_weights(used)
+    y_ref, _, _, _ = oracle.layer_forward(
+        x_bits[tokens], "bf16", lay.R_bits, "bf16", None, E, k, 0, True, uq, us, g, dn, "bf16",
+        lay.thr, topk_in=tr["topk_idx"][tokens], masks_in=tr["masks"][tokens],
+        dense_experts=fl)
+    err = check_y(y.cpu().numpy()[tokens], y_ref, 2e-3, "wide d=6144 f=16384 T=16 MIXED")
+    say(f"wide T=16 MIXED: n*={nstar}, dense experts {np.flatnonzero(fl).tolist()} "
+        f"(counts {cnt.tolist()}), max relL2 {err:.2e}")
 
 
 # ------------------------------------------------------------------ fine-grained layer
