@@ -146,9 +146,9 @@ __device__ __forceinline__ uint16_t to16(float v)
 // while block kb is multiplied; at the end of each block the wave waits for
 // its copies of block kb + 1 (leaving the later blocks' ncopy copies each in
 // flight) and a barrier publishes it.  Inside a block the fragments of k step s + 1 are
-// read from LDS while the MFMAs of step s run (sched_barrier keeps the
-// compiler from sinking the reads back next to their MFMAs); the other wave
-// of each SIMD covers the rest of the waiting.
+// read from LDS while the MFMAs of step s run, interleaved with them
+// (sched_barrier keeps the compiler from sinking the reads back next to
+// their MFMAs); the other wave of each SIMD covers the rest of the waiting.
 template <bool BF16, int MT, int NSUB, class ISSUE>
 __device__ __forceinline__ void kloop(floatx16 (&acc)[GT<MT>::kSub][kWNB], const unsigned char *smem, int nkb,
                                       int arow0, const int (&brow)[kWNB], int li, int hk,
@@ -185,15 +185,27 @@ __device__ __forceinline__ void kloop(floatx16 (&acc)[GT<MT>::kSub][kWNB], const
         if (kb + S - 1 < nkb) issue(kb + S - 1);    // the stage block kb - 1 used
         const unsigned char *st = smem + (size_t)(kb % S) * GT<MT>::kStageBytes;
         load(st, 0, a0, b0);
+        // the fragment reads of the next step are interleaved with the MFMAs
+        // of this one, one read after each MFMA (sched_group_barrier: mask 8
+        // MFMA, 0x100 LDS read), so that reads issue while the matrix core is busy
+        constexpr int NM = (NSUB > 0 ? NSUB : 1) * kWNB, ND = (NSUB > 0 ? NSUB : 1) + kWNB;
+        auto interleave = [&]() {
+#pragma unroll
+            for (int i = 0; i < ND; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - ND > 0 ? NM - ND : 0, 0);
+        };
 #pragma unroll
         for (int s2 = 0; s2 < kSteps; s2 += 2) {
             load(st, s2 + 1, a1, b1);
-            __builtin_amdgcn_sched_barrier(0);
             mmas(a0, b0);
+            interleave();
             __builtin_amdgcn_sched_barrier(0);
             if (s2 + 2 < kSteps) load(st, s2 + 2, a0, b0);
-            __builtin_amdgcn_sched_barrier(0);
             mmas(a1, b1);
+            if (s2 + 2 < kSteps) interleave();
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (S == 2) {
